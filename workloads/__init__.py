@@ -1,0 +1,295 @@
+"""Seeded synthetic inputs for batched draft-token verification.
+
+This module only *constructs inputs*: Gaussian and Zipf-biased logits, their
+rounding to bfloat16, draft tokens drawn for the drafting stage, the
+pre-generated uniforms, and random draft trees.  None of the verification
+arithmetic (row normalisers, acceptance test, first-rejection scan, residual
+distribution, inverse CDF) lives here.  The CPU oracle and the GPU library
+consume the arrays produced here unchanged, so both see bit-identical inputs.
+
+Random streams: every purpose (target noise, draft noise, vocabulary
+permutation, draft sampling, uniforms, tree shape, ...) draws from its own
+numpy ``Philox`` generator keyed by ``(seed, purpose)``.  Generation loops over
+sequences in a fixed order, so an input set is a pure function of
+``(shape, seed)``.
+
+Draft tokens are drawn from the draft model's temperature softmax with the
+Gumbel-max construction: ``argmax_v(d_v / T + G_v)`` with ``G_v`` iid standard
+Gumbel is distributed exactly as ``softmax(d / T)``, without computing any
+normaliser.  At ``T == 0`` the draft is its own argmax (greedy drafting).
+
+Logits are returned as ``numpy.float32`` arrays (dtype code ``F32``) or as
+``numpy.uint16`` bfloat16 bit patterns (dtype code ``BF16``).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F32 = 0
+BF16 = 1
+DTYPE_NAMES = {F32: "f32", BF16: "bf16"}
+
+_PURPOSE = {
+    "target": 1,
+    "draft": 2,
+    "perm": 3,
+    "draft_tokens": 4,
+    "uniforms": 5,
+    "tree": 6,
+    "temperature": 7,
+    "sigma": 8,
+    "tree_tokens": 9,
+    "greedy_tokens": 10,
+}
+
+
+def rng_for(seed: int, purpose: str) -> np.random.Generator:
+    """Philox stream for one random purpose of one seed."""
+    return np.random.Generator(np.random.Philox(key=[int(seed), _PURPOSE[purpose]]))
+
+
+# ---------------------------------------------------------------- bfloat16 ---
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    Inputs must be finite.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float32, exactly."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_dtype(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float values to the storage dtype (float32 array or bf16 bits)."""
+    if dtype == BF16:
+        return bf16_bits(x)
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(f"unknown dtype code {dtype}")
+
+
+def values(arr: np.ndarray, dtype: int) -> np.ndarray:
+    """Stored logits -> their exact float32 values."""
+    return bf16_to_f32(arr) if dtype == BF16 else np.asarray(arr, dtype=np.float32)
+
+
+# ------------------------------------------------------------ primitives ---
+
+def zipf_bias(V: int, s: float, seed: int) -> np.ndarray:
+    """Zipf log-frequency bias over a seeded vocabulary permutation.
+
+    Token v gets rank ``perm[v]`` (0 = most frequent) and bias
+    ``-s * ln(1 + rank)``; a Zipf(s) frequency law is ``freq ~ rank**-s``, and the
+    additive normalising constant cancels in any softmax.
+    """
+    perm = rng_for(seed, "perm").permutation(V)
+    return (-s * np.log1p(perm.astype(np.float64))).astype(np.float32)
+
+
+def _other_token(rng: np.random.Generator, avoid: int, V: int) -> int:
+    """Uniform over the V-1 tokens different from ``avoid``."""
+    r = int(rng.integers(0, V - 1))
+    return r if r < avoid else r + 1
+
+
+def gumbel_max_tokens(vals: np.ndarray, temperature: float, rng: np.random.Generator) -> np.ndarray:
+    """Draft tokens for rows ``vals[..., V]`` drawn from softmax(vals / T).
+
+    Gumbel-max: argmax(vals / T + G) with G iid standard Gumbel.  T == 0 gives
+    the (first) argmax, i.e. greedy drafting.
+    """
+    v64 = np.asarray(vals, dtype=np.float64)
+    if temperature > 0:
+        g = rng.gumbel(size=v64.shape)
+        return np.argmax(v64 / float(temperature) + g, axis=-1).astype(np.int32)
+    return np.argmax(v64, axis=-1).astype(np.int32)
+
+
+# ------------------------------------------------------------ chain ---
+
+def chain_inputs(B: int, k: int, V: int, dtype: int, seed: int, *,
+                 target_sigma: float = 2.0, zipf_s: float | None = None,
+                 draft_sigma=0.5, temperature=1.0) -> dict:
+    """Inputs for chain verification.
+
+    target logits  t[b, j, :] = target_sigma * N(0,1) (+ Zipf bias), j = 0..k
+    draft logits   d[b, i, :] = t[b, i, :] + sigma_b * N(0,1),      i = 0..k-1
+    (both rounded to ``dtype``; draft noise is added to the rounded target).
+    ``draft_sigma`` / ``temperature``: a scalar, a (lo, hi) tuple meaning a
+    per-sequence uniform draw, or an explicit length-B sequence.
+    Draft tokens x[b, i] ~ softmax(d[b, i, :] / T_b) (Gumbel-max).
+    uniforms u[b, 0..k] float32 in [0, 1): u[b, i] tests draft i, u[b, k] drives
+    the final (residual or bonus) sample.
+    """
+    temps = _per_seq(temperature, B, seed, "temperature")
+    sigmas = _per_seq(draft_sigma, B, seed, "sigma")
+    bias = zipf_bias(V, zipf_s, seed) if zipf_s else None
+    rt, rd, rx = rng_for(seed, "target"), rng_for(seed, "draft"), rng_for(seed, "draft_tokens")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, k + 1, V), dtype=np_dt)
+    draft = np.empty((B, k, V), dtype=np_dt)
+    tokens = np.empty((B, k), dtype=np.int32)
+    for b in range(B):
+        t = (target_sigma * rt.standard_normal((k + 1, V), dtype=np.float32))
+        if bias is not None:
+            t = t + bias
+        target[b] = to_dtype(t, dtype)
+        tv = values(target[b, :k], dtype)
+        d = tv + np.float32(sigmas[b]) * rd.standard_normal((k, V), dtype=np.float32)
+        draft[b] = to_dtype(d, dtype)
+        tokens[b] = gumbel_max_tokens(values(draft[b], dtype), float(temps[b]), rx)
+    uniforms = rng_for(seed, "uniforms").random((B, k + 1), dtype=np.float32)
+    return dict(kind="chain", B=B, k=k, V=V, dtype=dtype, draft_tokens=tokens,
+                draft_logits=draft, target_logits=target,
+                temperature=temps.astype(np.float32), uniforms=uniforms,
+                draft_sigma=sigmas.astype(np.float32))
+
+
+def _per_seq(spec, B: int, seed: int, purpose: str) -> np.ndarray:
+    if isinstance(spec, tuple):
+        lo, hi = spec
+        return rng_for(seed, purpose).uniform(lo, hi, size=B).astype(np.float32)
+    arr = np.asarray(spec, dtype=np.float32)
+    if arr.ndim == 0:
+        return np.full(B, float(arr), dtype=np.float32)
+    assert arr.shape == (B,)
+    return arr
+
+
+def repeated_trials(target_vals: np.ndarray, draft_vals: np.ndarray, temperature: float,
+                    n: int, seed: int, block: int = 0) -> dict:
+    """``n`` independent trials of one fixed (draft, target) row set.
+
+    ``target_vals`` [k+1, V] and ``draft_vals`` [k, V] are float32 values used as
+    F32 logits; every trial draws its own draft tokens (from softmax(d / T)) and
+    uniforms.  ``block`` selects a sub-stream so that large trial counts can be
+    produced block by block.
+    """
+    k1, V = target_vals.shape
+    k = k1 - 1
+    rx = np.random.Generator(np.random.Philox(key=[int(seed), 1000 + 2 * int(block)]))
+    ru = np.random.Generator(np.random.Philox(key=[int(seed), 1001 + 2 * int(block)]))
+    dv = np.broadcast_to(draft_vals.astype(np.float32), (n, k, V))
+    tokens = gumbel_max_tokens(dv, temperature, rx)
+    return dict(kind="chain", B=n, k=k, V=V, dtype=F32, draft_tokens=tokens,
+                draft_logits=np.ascontiguousarray(dv),
+                target_logits=np.ascontiguousarray(np.broadcast_to(target_vals.astype(np.float32), (n, k1, V))),
+                temperature=np.full(n, temperature, dtype=np.float32),
+                uniforms=ru.random((n, k + 1), dtype=np.float32))
+
+
+# ------------------------------------------------------------ greedy ---
+
+def greedy_inputs(B: int, k: int, V: int, dtype: int, seed: int, *,
+                  target_sigma: float = 2.0, match_p: float = 0.8) -> dict:
+    """Inputs for greedy (temperature 0) chain verification.
+
+    target logits t[b, j, :] = target_sigma * N(0,1), j = 0..k, rounded to dtype.
+    draft token x[b, i] = first argmax of t[b, i, :] with probability match_p,
+    otherwise uniform over the other V-1 tokens.
+    """
+    rt, rx = rng_for(seed, "target"), rng_for(seed, "greedy_tokens")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, k + 1, V), dtype=np_dt)
+    tokens = np.empty((B, k), dtype=np.int32)
+    for b in range(B):
+        target[b] = to_dtype(target_sigma * rt.standard_normal((k + 1, V), dtype=np.float32), dtype)
+        top = np.argmax(values(target[b, :k], dtype), axis=-1)
+        for i in range(k):
+            hit = rx.random() < match_p
+            tokens[b, i] = int(top[i]) if hit else _other_token(rx, int(top[i]), V)
+    return dict(kind="greedy", B=B, k=k, V=V, dtype=dtype, draft_tokens=tokens, target_logits=target)
+
+
+# ------------------------------------------------------------ tree ---
+
+def random_tree(N: int, seed: int, max_branch: int = 4, max_depth: int = 6) -> np.ndarray:
+    """Parent array of a random rooted tree: parent[0] = -1, parent[i] < i.
+
+    Node i attaches to a uniform choice among earlier nodes of depth < max_depth
+    that have fewer than max_branch children.
+    """
+    rng = rng_for(seed, "tree")
+    parent = np.full(N, -1, dtype=np.int32)
+    depth = np.zeros(N, dtype=np.int64)
+    children = np.zeros(N, dtype=np.int64)
+    for i in range(1, N):
+        cand = [j for j in range(i) if depth[j] < max_depth and children[j] < max_branch]
+        if not cand:
+            raise ValueError("tree bounds too tight for N nodes")
+        p = int(cand[int(rng.integers(0, len(cand)))])
+        parent[i] = p
+        depth[i] = depth[p] + 1
+        children[p] += 1
+    return parent
+
+
+def tree_inputs(B: int, N: int, V: int, dtype: int, seed: int, *,
+                target_sigma: float = 2.0, max_branch: int = 4, max_depth: int = 6,
+                match_p: float = 0.6, parent: np.ndarray | None = None) -> dict:
+    """Inputs for greedy static-tree verification.
+
+    One parent array shared by all B sequences; target logits per node
+    t[b, n, :] = target_sigma * N(0,1) rounded to dtype (row n is the target's
+    prediction for the children of node n).  Node 0 is the root (its token is
+    never matched); node i >= 1 carries the first argmax of its parent's row with
+    probability match_p, otherwise a uniform other token.
+    """
+    if parent is None:
+        parent = random_tree(N, seed, max_branch, max_depth)
+    rt, rx = rng_for(seed, "target"), rng_for(seed, "tree_tokens")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, N, V), dtype=np_dt)
+    tokens = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        target[b] = to_dtype(target_sigma * rt.standard_normal((N, V), dtype=np.float32), dtype)
+        top = np.argmax(values(target[b], dtype), axis=-1)
+        tokens[b, 0] = int(rx.integers(0, V))
+        for i in range(1, N):
+            g = int(top[parent[i]])
+            tokens[b, i] = g if rx.random() < match_p else _other_token(rx, g, V)
+    depth = np.zeros(N, dtype=np.int64)
+    for i in range(1, N):
+        depth[i] = depth[parent[i]] + 1
+    return dict(kind="tree", B=B, N=N, V=V, dtype=dtype, node_tokens=tokens,
+                parent=parent.astype(np.int32), max_depth=int(max(max_depth, depth.max())),
+                target_logits=target)
+
+
+# ------------------------------------------------------------ the five workloads ---
+
+CONFIGS = {
+    1: dict(name="tiny chain verify", kind="chain", B=1, k=4, V=1024, dtype=F32,
+            target_sigma=2.0, zipf_s=None, draft_sigma=0.5, temperature=1.0),
+    2: dict(name="Llama-scale chain verify", kind="chain", B=64, k=4, V=128256, dtype=BF16,
+            target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
+    3: dict(name="greedy chain verify", kind="greedy", B=256, k=5, V=128256, dtype=BF16,
+            target_sigma=2.0, match_p=0.8),
+    4: dict(name="DeepSeek-scale chain verify", kind="chain", B=32, k=8, V=129280, dtype=F32,
+            target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=(0.3, 1.3)),
+    5: dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
+            target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6),
+}
+
+
+def make_inputs(config: int, seed: int = 1, **override) -> dict:
+    """Inputs for one of the five named workloads (sizes may be overridden)."""
+    c = dict(CONFIGS[config])
+    c.update(override)
+    kind = c.pop("kind")
+    c.pop("name")
+    if kind == "chain":
+        return chain_inputs(c.pop("B"), c.pop("k"), c.pop("V"), c.pop("dtype"), seed, **c)
+    if kind == "greedy":
+        return greedy_inputs(c.pop("B"), c.pop("k"), c.pop("V"), c.pop("dtype"), seed, **c)
+    if kind == "tree":
+        return tree_inputs(c.pop("B"), c.pop("N"), c.pop("V"), c.pop("dtype"), seed, **c)
+    raise ValueError(kind)
