@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of batched draft-token verification on one MI355X.
+
+One step = one sv_verify_chain call over one batch of the Llama-scale
+workload (B = 64 sequences, k = 4 drafts, V = 128256, bfloat16 logits,
+temperature 0.7): the whole path -- row normalisers of every draft and target
+row, acceptance tests, first-rejection scan, residual or bonus draw.  Inputs
+are resident in HBM before the timed region; several identical copies are
+rotated so that successive steps read HBM rather than the 256 MB Infinity
+Cache.  A spin kernel queued ahead of the timed steps builds a backlog, so the
+steps run back to back on the GPU and host launch overhead stays outside the
+measured time.  Per-kernel durations come from HIP events the library records
+on the launch stream around each kernel.
+
+Prints one JSON line (see the metric, roofline and cpu_baseline fields).
+Other workloads (--config 3 greedy, 5 tree, 4 DeepSeek-scale chain) are for
+exploration; the default line is the Llama-scale chain.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
+METRIC = "verified draft tokens/sec and HBM GB/s (% of peak) at B=64,k=4,V=128256 bf16"
+KERNEL_SOURCES = ["draft_token_verification_chain_amd/csrc/sv_common.hpp",
+                  "draft_token_verification_chain_amd/csrc/sv_kernels.hpp",
+                  "draft_token_verification_chain_amd/csrc/specverify.hip"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def to_device(inp, torch, W):
+    import numpy as np
+
+    def logits(a):
+        if inp["dtype"] == W.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t = dict(target_logits=logits(inp["target_logits"]))
+    if inp["kind"] == "chain":
+        t.update(draft_logits=logits(inp["draft_logits"]),
+                 draft_tokens=torch.from_numpy(inp["draft_tokens"]).cuda(),
+                 temperature=torch.from_numpy(inp["temperature"]).cuda(),
+                 uniforms=torch.from_numpy(inp["uniforms"]).cuda())
+    elif inp["kind"] == "greedy":
+        t.update(draft_tokens=torch.from_numpy(inp["draft_tokens"]).cuda())
+    else:
+        t.update(node_tokens=torch.from_numpy(inp["node_tokens"]).cuda(),
+                 parent=torch.from_numpy(inp["parent"]).cuda())
+    return t
+
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle as it stands, on this host's cores, repeated on the same
+    batch for about `seconds`."""
+    import oracle
+
+    fn = {"chain": oracle.verify_chain, "greedy": oracle.verify_greedy, "tree": oracle.verify_tree}[inp["kind"]]
+    fn(inp)  # warm-up (page faults, thread pool)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn(inp)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return reps, el, oracle.max_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs on a single MI355X and the "
+              "workload is one GPU's batch; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_token_verification_chain_amd as svl
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    svl.load()
+    cfg = W.CONFIGS[args.config]
+    inp = W.make_inputs(args.config, args.seed)
+    kind = inp["kind"]
+    es = 2 if inp["dtype"] == W.BF16 else 4
+    in_bytes = sum(v.nbytes for k, v in inp.items() if isinstance(v, np.ndarray))
+    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / in_bytes))
+    dev = [to_device(inp, torch, W) for _ in range(copies)]
+    B, V = inp["B"], inp["V"]
+
+    if kind == "chain":
+        k = inp["k"]
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"),
+                   accept_prob=torch.empty((B, k), dtype=torch.float32, device="cuda"))
+        ws = torch.empty(svl.chain_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            t = dev[i % copies]
+            svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                             t["uniforms"], workspace=ws, out=out)
+        units = B * k                       # verified draft tokens per step
+        dominant = "chain_rowstats"
+        dominant_bytes = 2 * B * k * V * es  # every draft row and target rows 0..k-1, once
+    elif kind == "greedy":
+        k = inp["k"]
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"))
+        ws = torch.empty(svl.greedy_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            t = dev[i % copies]
+            svl.verify_greedy(t["draft_tokens"], t["target_logits"], workspace=ws, out=out)
+        units = B * k
+        dominant = "argmax_rows"
+        dominant_bytes = B * (k + 1) * V * es
+    else:
+        N = inp["N"]
+        md = inp["max_depth"]
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                   emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
+                   accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
+        ws = torch.empty(svl.tree_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            t = dev[i % copies]
+            svl.verify_tree(t["node_tokens"], t["parent"], md, t["target_logits"], workspace=ws, out=out)
+        units = B * (N - 1)                 # verified draft nodes per step
+        dominant = "argmax_rows"
+        dominant_bytes = B * N * V * es
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # bytes the final draw reads, from this batch's outcome (identical in every copy)
+    final_bytes = 0
+    if kind == "chain":
+        a = out["accepted_len"].cpu().numpy()
+        T = inp["temperature"]
+        k = inp["k"]
+        for b in range(B):
+            if T[b] > 0:
+                final_bytes += (2 if a[b] < k else 1) * V * es
+            elif a[b] == k:
+                final_bytes += V * es
+    step_bytes = dominant_bytes + final_bytes
+
+    # timed region: backlog, then K steps back to back, library events on
+    svl.profile_begin(8 * args.steps)
+    torch.cuda._sleep(int(50e6))  # a spin kernel of ~20 ms keeps the GPU busy while the steps are queued
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    prof = svl.profile_end()
+    ms_per_step = ms_total / args.steps
+    s_per_step = ms_per_step * 1e-3
+
+    kernels = {name: dict(launches=n, avg_us=1e3 * tot / max(n, 1)) for name, (n, tot) in prof.items()}
+    dom_us = kernels[dominant]["avg_us"]
+    achieved = dominant_bytes / (dom_us * 1e-6) / 1e9
+    traffic = load_traffic(dominant, f"config{args.config}")
+
+    result = {
+        "metric": METRIC if args.config == 2 else f"verified draft tokens/sec ({cfg['name']})",
+        "value": units / s_per_step,
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.DTYPE_NAMES[inp["dtype"]],
+        "data": "synthetic (seeded generator, shapes of the named workload)",
+        "config": {"workload": cfg["name"], "B": B, "k": inp.get("k"), "N": inp.get("N"), "V": V,
+                   "logits": W.DTYPE_NAMES[inp["dtype"]], "temperature": cfg.get("temperature"),
+                   "seed": args.seed, "input_copies_rotated": copies, "parallelism": "single GPU"},
+        "hbm_gbs": step_bytes / s_per_step / 1e9,
+        "hbm_frac_of_peak": step_bytes / s_per_step / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "bytes_per_verified_token": step_bytes / units,
+        "emitted_tokens_per_s": (float(out["accepted_len"].sum().item() + B) / s_per_step
+                                 if kind != "tree" else float(out["accepted_len"].sum().item() + B) / s_per_step),
+        "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "bytes_per_launch": dominant_bytes, "avg_launch_us": dom_us},
+    }
+
+    if not args.no_cpu:
+        reps, el, threads = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"] = {"value": units * reps / el, "unit": "verified draft tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"the full {cfg['name']} batch (B={B}) x {reps} repetitions, {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+"""libspecverify: batched verification of speculative-decoding draft tokens on
+AMD Instinct MI355X (gfx950), behind a C ABI (include/specverify.h).
+
+The Python names mirror the C entry points:
+  verify_chain   -> sv_verify_chain   (acceptance test, first rejection, residual / bonus draw)
+  verify_greedy  -> sv_verify_greedy  (temperature-0 argmax matching)
+  verify_tree    -> sv_verify_tree    (EAGLE-style static tree, greedy)
+The shared library is loaded on first use; calls raise if it is missing.
+"""
+
+from ._binding import (  # noqa: F401
+    SV_BF16,
+    SV_F32,
+    SpecVerifyError,
+    chain_workspace_bytes,
+    greedy_workspace_bytes,
+    load,
+    profile_begin,
+    profile_end,
+    status_string,
+    tree_workspace_bytes,
+    verify_chain,
+    verify_greedy,
+    verify_tree,
+    version,
+)

@@ -1,0 +1,334 @@
+// specverify.hip -- host side of libspecverify: the C ABI declared in
+// include/specverify.h (argument validation, workspace layout, dtype and
+// alignment dispatch, launches, optional kernel timing).
+//
+// Scheme: "Accelerating Sonar through speculation" (Perplexity, 2025); the
+// entry points correspond to its sections "Target-Draft" (chain
+// verification with sampling), "Speculative decoding" (greedy matching) and
+// "EAGLE" (tree verification).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "specverify.h"
+#include "sv_kernels.hpp"
+
+namespace {
+
+using sv::Partial;
+using sv::SeqInfo;
+
+// Vectors of 16 bytes per lane per tile.
+constexpr int kU = 8;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(sv_dtype dt) { return dt == SV_BF16 ? 2 : 4; }
+
+bool valid_dtype(sv_dtype dt) { return dt == SV_F32 || dt == SV_BF16; }
+
+// Tiles per row: NV = ceil(V / VE) vectors of 16 bytes, 64 * kU vectors per tile.
+int64_t tiles_per_row(int V, sv_dtype dt) {
+    const int64_t ve = 16 / elem_bytes(dt);
+    const int64_t nv = (V + ve - 1) / ve;
+    return (nv + 64 * kU - 1) / (64 * kU);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Blocks of kBlock threads for `waves` independent wave64 tiles.
+int64_t blocks_for_waves(int64_t waves) { return (waves + sv::kWavesPerBlock - 1) / sv::kWavesPerBlock; }
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// ---------------------------------------------------------------- workspace layouts ---
+
+struct ChainLayout {
+    size_t part, info, seg, tile, total;
+};
+
+ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
+    const int64_t nT = tiles_per_row(V, dt);
+    ChainLayout L{};
+    L.part = 0;
+    L.info = align_up(L.part + sizeof(Partial) * static_cast<size_t>(2) * B * k * nT);
+    L.seg = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
+    L.tile = align_up(L.seg + sizeof(float) * static_cast<size_t>(B) * nT * kU);
+    L.total = align_up(L.tile + sizeof(Partial) * static_cast<size_t>(B) * nT);
+    return L;
+}
+
+// ---------------------------------------------------------------- kernel timing ---
+
+struct ProfSlot {
+    std::string name;
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool used = false;
+};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    std::vector<ProfSlot> slots;
+    size_t next = 0;
+} g_prof;
+
+// Launch `fn` on `stream`, bracketing it with an event pair while profiling.
+template <typename F>
+sv_status timed_launch(const char* name, hipStream_t stream, F&& fn) {
+    ProfSlot* slot = nullptr;
+    if (g_prof.on) {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.next < g_prof.slots.size()) slot = &g_prof.slots[g_prof.next++];
+    }
+    if (slot && hipEventRecord(slot->start, stream) != hipSuccess) return SV_ERR_HIP;
+    fn();
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    if (slot) {
+        if (hipEventRecord(slot->stop, stream) != hipSuccess) return SV_ERR_HIP;
+        slot->name = name;
+        slot->used = true;
+    }
+    return SV_OK;
+}
+
+// ---------------------------------------------------------------- dispatch ---
+
+template <int DT, bool VEC>
+sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draft, const void* target,
+                    const float* temperature, const float* uniforms, int32_t* accepted_len, int32_t* emitted,
+                    float* accept_prob, char* ws, const ChainLayout& L, int nT, hipStream_t stream) {
+    auto* part = reinterpret_cast<Partial*>(ws + L.part);
+    auto* info = reinterpret_cast<SeqInfo*>(ws + L.info);
+    auto* seg = reinterpret_cast<float*>(ws + L.seg);
+    auto* tile = reinterpret_cast<Partial*>(ws + L.tile);
+    sv_status st = SV_OK;
+    if (k > 0) {
+        const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * k * nT);
+        st = timed_launch("chain_rowstats", stream, [&] {
+            sv::chain_rowstats_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(blocks)), dim3(sv::kBlock), 0,
+                                                      stream>>>(target, draft, temperature, B, k, V, nT, part);
+        });
+        if (st != SV_OK) return st;
+    }
+    st = timed_launch("chain_accept", stream, [&] {
+        sv::chain_accept_kernel<DT><<<dim3(B), dim3(sv::kWave), 0, stream>>>(
+            tokens, draft, target, temperature, uniforms, B, k, V, nT, part, info, accepted_len, emitted,
+            accept_prob);
+    });
+    if (st != SV_OK) return st;
+    const int64_t fblocks = blocks_for_waves(static_cast<int64_t>(B) * nT);
+    st = timed_launch("chain_final_part", stream, [&] {
+        sv::chain_final_part_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(fblocks)), dim3(sv::kBlock), 0,
+                                                   stream>>>(draft, target, B, k, V, nT, info, seg, tile);
+    });
+    if (st != SV_OK) return st;
+    return timed_launch("chain_final_pick", stream, [&] {
+        sv::chain_final_pick_kernel<DT, VEC, kU><<<dim3(B), dim3(sv::kWave), 0, stream>>>(
+            draft, target, B, k, V, nT, info, seg, tile, emitted);
+    });
+}
+
+template <int DT, bool VEC>
+sv_status run_argmax_rows(const void* logits, int64_t nrows, int V, int nT, Partial* part, hipStream_t stream) {
+    const int64_t blocks = blocks_for_waves(nrows * nT);
+    return timed_launch("argmax_rows", stream, [&] {
+        sv::argmax_rows_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(blocks)), dim3(sv::kBlock), 0, stream>>>(
+            logits, nrows, V, nT, part);
+    });
+}
+
+sv_status argmax_rows(sv_dtype dt, bool vec, const void* logits, int64_t nrows, int V, int nT, Partial* part,
+                      hipStream_t stream) {
+    if (dt == SV_BF16)
+        return vec ? run_argmax_rows<SV_BF16, true>(logits, nrows, V, nT, part, stream)
+                   : run_argmax_rows<SV_BF16, false>(logits, nrows, V, nT, part, stream);
+    return vec ? run_argmax_rows<SV_F32, true>(logits, nrows, V, nT, part, stream)
+               : run_argmax_rows<SV_F32, false>(logits, nrows, V, nT, part, stream);
+}
+
+// Checks shared by the entry points: a positive vocabulary within limits and a
+// grid that fits the launch limits for `rows` rows.
+sv_status check_rows(int64_t rows, int V, sv_dtype dt) {
+    if (V < 1 || !valid_dtype(dt)) return SV_ERR_INVALID_ARGUMENT;
+    if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+    const int64_t nT = tiles_per_row(V, dt);
+    if (rows > 0 && blocks_for_waves(rows * nT) > kMaxGrid) return SV_ERR_UNSUPPORTED;
+    return SV_OK;
+}
+
+sv_status check_workspace(void* ws, size_t have, size_t need) {
+    if (have < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (need > 0 && (ws == nullptr || !aligned16(ws))) return SV_ERR_INVALID_ARGUMENT;
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_version(void) { return 100; }
+
+const char* sv_status_string(sv_status s) {
+    switch (s) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_INVALID_ARGUMENT: return "SV_ERR_INVALID_ARGUMENT: invalid argument";
+        case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL: workspace smaller than required";
+        case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: size beyond the supported limits";
+        case SV_ERR_HIP: return "SV_ERR_HIP: HIP runtime or launch failure";
+    }
+    return "unknown sv_status";
+}
+
+size_t sv_chain_workspace_bytes(int B, int k, int V, sv_dtype dt) {
+    if (B < 0 || k < 0 || k > SV_MAX_DRAFTS || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
+    return chain_layout(B, k, V, dt).total;
+}
+
+size_t sv_greedy_workspace_bytes(int B, int k, int V, sv_dtype dt) {
+    if (B < 0 || k < 0 || k > SV_MAX_DRAFTS || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
+    return align_up(sizeof(Partial) * static_cast<size_t>(B) * (k + 1) * tiles_per_row(V, dt));
+}
+
+size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt) {
+    if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
+    return align_up(sizeof(Partial) * static_cast<size_t>(B) * N * tiles_per_row(V, dt));
+}
+
+sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* draft_logits,
+                          const void* target_logits, const float* temperature, const float* uniforms,
+                          int32_t* accepted_len, int32_t* emitted, float* accept_prob, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || k < 0) return SV_ERR_INVALID_ARGUMENT;
+    if (k > SV_MAX_DRAFTS) return SV_ERR_UNSUPPORTED;
+    sv_status st = check_rows(static_cast<int64_t>(2) * B * (k + 1), V, dt);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !temperature || !uniforms || !accepted_len || !emitted) return SV_ERR_INVALID_ARGUMENT;
+    if (k > 0 && (!draft_tokens || !draft_logits)) return SV_ERR_INVALID_ARGUMENT;
+    const ChainLayout L = chain_layout(B, k, V, dt);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK) return st;
+    const int nT = static_cast<int>(tiles_per_row(V, dt));
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits) &&
+                     (k == 0 || aligned16(draft_logits));
+    char* ws = static_cast<char*>(workspace);
+    if (dt == SV_BF16)
+        return vec ? run_chain<SV_BF16, true>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
+                                              uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream)
+                   : run_chain<SV_BF16, false>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
+                                               uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream);
+    return vec ? run_chain<SV_F32, true>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
+                                         uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream)
+               : run_chain<SV_F32, false>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
+                                          uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream);
+}
+
+sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* target_logits,
+                           int32_t* accepted_len, int32_t* emitted, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (B < 0 || k < 0) return SV_ERR_INVALID_ARGUMENT;
+    if (k > SV_MAX_DRAFTS) return SV_ERR_UNSUPPORTED;
+    sv_status st = check_rows(static_cast<int64_t>(B) * (k + 1), V, dt);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !accepted_len || !emitted || (k > 0 && !draft_tokens)) return SV_ERR_INVALID_ARGUMENT;
+    if ((st = check_workspace(workspace, workspace_bytes, sv_greedy_workspace_bytes(B, k, V, dt))) != SV_OK)
+        return st;
+    const int nT = static_cast<int>(tiles_per_row(V, dt));
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits);
+    auto* part = static_cast<Partial*>(workspace);
+    if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * (k + 1), V, nT, part, stream)) != SV_OK)
+        return st;
+    return timed_launch("greedy_finalize", stream, [&] {
+        sv::greedy_finalize_kernel<<<dim3(B), dim3(sv::kWave), 0, stream>>>(draft_tokens, k, nT, part,
+                                                                            accepted_len, emitted);
+    });
+}
+
+sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_tokens, const int32_t* parent,
+                         int parent_stride, int max_depth, const void* target_logits, int32_t* accepted_len,
+                         int32_t* emitted, int32_t* accepted_nodes, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (B < 0 || N < 1 || max_depth < 0 || parent_stride < 0 || (parent_stride != 0 && parent_stride < N))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
+    sv_status st = check_rows(static_cast<int64_t>(B) * N, V, dt);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!node_tokens || !parent || !target_logits || !accepted_len || !emitted) return SV_ERR_INVALID_ARGUMENT;
+    if ((st = check_workspace(workspace, workspace_bytes, sv_tree_workspace_bytes(B, N, V, dt))) != SV_OK)
+        return st;
+    const int nT = static_cast<int>(tiles_per_row(V, dt));
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits);
+    auto* part = static_cast<Partial*>(workspace);
+    if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) != SV_OK)
+        return st;
+    const int threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
+    return timed_launch("tree_finalize", stream, [&] {
+        sv::tree_finalize_kernel<<<dim3(B), dim3(threads), 0, stream>>>(
+            node_tokens, parent, parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
+    });
+}
+
+sv_status sv_profile_begin(int max_launches) {
+    if (max_launches < 0) return SV_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (auto& s : g_prof.slots) {
+        if (s.start) (void)hipEventDestroy(s.start);
+        if (s.stop) (void)hipEventDestroy(s.stop);
+    }
+    g_prof.slots.assign(static_cast<size_t>(max_launches), ProfSlot{});
+    for (auto& s : g_prof.slots) {
+        if (hipEventCreate(&s.start) != hipSuccess || hipEventCreate(&s.stop) != hipSuccess) {
+            g_prof.on = false;
+            return SV_ERR_HIP;
+        }
+    }
+    g_prof.next = 0;
+    g_prof.on = true;
+    return SV_OK;
+}
+
+int sv_profile_end(sv_kernel_time* out, int max_out) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = false;
+    std::vector<sv_kernel_time> agg;
+    int rc = 0;
+    for (auto& s : g_prof.slots) {
+        if (!s.used) continue;
+        float ms = 0.f;
+        if (hipEventSynchronize(s.stop) != hipSuccess || hipEventElapsedTime(&ms, s.start, s.stop) != hipSuccess) {
+            rc = -1;
+            continue;
+        }
+        sv_kernel_time* rec = nullptr;
+        for (auto& a : agg)
+            if (s.name == a.name) rec = &a;
+        if (!rec) {
+            agg.push_back(sv_kernel_time{});
+            rec = &agg.back();
+            std::strncpy(rec->name, s.name.c_str(), sizeof(rec->name) - 1);
+        }
+        rec->launches += 1;
+        rec->total_ms += ms;
+    }
+    for (auto& s : g_prof.slots) {
+        if (s.start) (void)hipEventDestroy(s.start);
+        if (s.stop) (void)hipEventDestroy(s.stop);
+    }
+    g_prof.slots.clear();
+    g_prof.next = 0;
+    if (rc < 0) return -1;
+    const int n = static_cast<int>(agg.size()) < max_out ? static_cast<int>(agg.size()) : max_out;
+    if (out)
+        for (int i = 0; i < n; ++i) out[i] = agg[i];
+    return n;
+}
+
+}  // extern "C"

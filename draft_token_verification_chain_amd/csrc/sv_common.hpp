@@ -1,0 +1,213 @@
+// sv_common.hpp -- device helpers shared by the libspecverify kernels (gfx950).
+//
+// Row geometry.  A logits row of V elements is read as NV = ceil(V / VE)
+// "vectors" of VE = 16 / sizeof(element) consecutive elements.  When every row
+// starts on a 16-byte boundary (V * element size a multiple of 16 and a
+// 16-byte aligned base) a vector is one 128-bit load; otherwise it is VE
+// element loads masked against V.  A wave64 owns a *tile* of 64 * U
+// consecutive vectors; lane l of the wave reads vectors tile*64U + i*64 + l
+// for i < U, so each of the U load instructions of a wave touches 64
+// consecutive 16-byte vectors (1 KiB, fully coalesced), and the 64 vectors
+// touched by load i form a *segment* of 64 * VE consecutive tokens.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kNoIndex = 0x7fffffff;
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<SV_F32> {
+    static constexpr int bytes = 4;
+    static constexpr int per_vec = 4;
+    static constexpr uint32_t neg_inf_word = 0xff800000u;  // -inf
+};
+template <>
+struct Elem<SV_BF16> {
+    static constexpr int bytes = 2;
+    static constexpr int per_vec = 8;
+    static constexpr uint32_t neg_inf_word = 0xff80ff80u;  // two bf16 -inf
+};
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- loads ---
+
+// The 16-byte vector vi of a row whose first element is at byte `row`
+// (16-byte aligned).  Vectors past the row end (vi >= nv) read as -inf.
+__device__ __forceinline__ uint4 load_vec_aligned(const char* row, int64_t vi, int64_t nv,
+                                                  uint32_t neg_inf) {
+    if (vi < nv) return *reinterpret_cast<const uint4*>(row + vi * 16);
+    return make_uint4(neg_inf, neg_inf, neg_inf, neg_inf);
+}
+
+// Unpack a 16-byte vector into VE floats.
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4 w, float* out);
+
+template <>
+__device__ __forceinline__ void unpack<SV_F32>(const uint4 w, float* out) {
+    out[0] = __uint_as_float(w.x);
+    out[1] = __uint_as_float(w.y);
+    out[2] = __uint_as_float(w.z);
+    out[3] = __uint_as_float(w.w);
+}
+
+// bfloat16 -> float is exact: the bf16 bits become the upper half of a binary32.
+template <>
+__device__ __forceinline__ void unpack<SV_BF16>(const uint4 w, float* out) {
+    out[0] = __uint_as_float(w.x << 16);
+    out[1] = __uint_as_float(w.x & 0xffff0000u);
+    out[2] = __uint_as_float(w.y << 16);
+    out[3] = __uint_as_float(w.y & 0xffff0000u);
+    out[4] = __uint_as_float(w.z << 16);
+    out[5] = __uint_as_float(w.z & 0xffff0000u);
+    out[6] = __uint_as_float(w.w << 16);
+    out[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+// One element of a row, as float.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx);
+template <>
+__device__ __forceinline__ float load_elem<SV_F32>(const void* base, int64_t idx) {
+    return static_cast<const float*>(base)[idx];
+}
+template <>
+__device__ __forceinline__ float load_elem<SV_BF16>(const void* base, int64_t idx) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+}
+
+// Vector vi of a row (element offset `row_elem` into `base`, V elements) as VE
+// floats, with element loads masked against V: the path for rows that are not
+// 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ void load_vec_masked(const void* base, int64_t row_elem, int64_t vi,
+                                                int V, float* out) {
+    constexpr int VE = Elem<DT>::per_vec;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        const int64_t j = vi * VE + e;
+        out[e] = (j < V) ? load_elem<DT>(base, row_elem + j) : -__builtin_inff();
+    }
+}
+
+// U vectors of lane `lane` of tile `tile`, unpacked into U*VE floats.
+template <int DT, bool VEC, int U>
+__device__ __forceinline__ void load_tile(const void* base, int64_t row_elem, int V, int64_t tile,
+                                          int lane, float* v) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int64_t nv = (V + VE - 1) / VE;
+    const int64_t v0 = tile * (64 * U) + lane;
+    if constexpr (VEC) {
+        const char* row = static_cast<const char*>(base) + row_elem * Elem<DT>::bytes;
+        uint4 raw[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) raw[i] = load_vec_aligned(row, v0 + i * 64, nv, Elem<DT>::neg_inf_word);
+#pragma unroll
+        for (int i = 0; i < U; ++i) unpack<DT>(raw[i], v + i * VE);
+    } else {
+#pragma unroll
+        for (int i = 0; i < U; ++i) load_vec_masked<DT>(base, row_elem, v0 + i * 64, V, v + i * VE);
+    }
+}
+
+// ---------------------------------------------------------------- arithmetic ---
+
+// Pairwise (tree) sum of N register values; N a power of two.
+template <int N>
+__device__ __forceinline__ float pairwise_sum(const float* x) {
+    if constexpr (N == 1) {
+        return x[0];
+    } else {
+        return pairwise_sum<N / 2>(x) + pairwise_sum<N / 2>(x + N / 2);
+    }
+}
+
+// exp2(l * c - r) with c = c_hi + c_lo (a double-float split of log2(e) / T)
+// and an integer-valued reference r: the product l * c_hi is exact inside the
+// fma, so the argument carries about one rounding of its own (small) value.
+__device__ __forceinline__ float scaled_exp2(float l, float c_hi, float c_lo, float r) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(l, c_lo, __builtin_fmaf(l, c_hi, -r)));
+}
+
+// ---------------------------------------------------------------- wave64 reductions ---
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+    return x;
+}
+
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m, kWave));
+    return x;
+}
+
+// (value, index) maximum with ties resolved to the lowest index.
+struct ArgMax {
+    float val;
+    int idx;
+};
+
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+    return (b.val > a.val || (b.val == a.val && b.idx < a.idx)) ? b : a;
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        ArgMax o{__shfl_xor(a.val, m, kWave), __shfl_xor(a.idx, m, kWave)};
+        a = better(a, o);
+    }
+    return a;
+}
+
+// Inclusive prefix sum across the wave (Hillis-Steele, fixed order).
+__device__ __forceinline__ double wave_inclusive_scan(double x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const double y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Index of the lowest lane whose predicate holds, or -1.
+__device__ __forceinline__ int first_lane(bool pred) {
+    const uint64_t m = __ballot(pred);
+    return m ? __builtin_ctzll(m) : -1;
+}
+
+// Per-(row, tile) partial result written by the streaming passes: softmax
+// mode stores (s, r) with s = sum exp2(l c - r) over the tile and r an
+// integer-valued reference; argmax mode stores (max value, lowest index).
+struct Partial {
+    float f;
+    int i;
+};
+
+}  // namespace sv

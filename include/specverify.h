@@ -1,0 +1,198 @@
+/*
+ * specverify.h -- C ABI of libspecverify: batched verification of
+ * speculative-decoding draft tokens against target logits on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The scheme is the one of "Accelerating Sonar through speculation"
+ * (Perplexity; N. Licker, E. McKnight; 2025):
+ *   - section "Speculative decoding": each prefix of the drafted tokens is
+ *     scored and the longest prefix that passes acceptance is kept; n drafts
+ *     yield up to n+1 tokens per step because the target's logits at the
+ *     mismatch, or after the last draft, are sampled as well;
+ *   - section "Target-Draft": acceptance compares the full draft and target
+ *     probability distributions, and the target's extra logits row after the
+ *     accepted drafts is sampled ("bonus" token);
+ *   - section "EAGLE": for a tree of drafts the longest suitable root path is
+ *     kept and one more target token is appended;
+ *   - section "MTP": logits row i predicts token i+1, hence target row j
+ *     scores draft j and row k follows the last draft;
+ *   - sections "Inference with speculative decoding" and "MTP schedule": the
+ *     accepted lengths are what forces a device-to-host synchronisation, and a
+ *     device kernel can place the next tokens without one -- so every result
+ *     here stays in device memory and no call synchronises the host.
+ * The acceptance rule (keep draft x with probability min(1, p(x)/q(x)); at
+ * the first rejection draw from max(0, p - q) renormalised) is the
+ * speculative sampling of Leviathan et al., "Fast Inference from
+ * Transformers via Speculative Decoding", first in the pages' references.
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers (hipMalloc memory, or a torch
+ *     tensor's data_ptr()).  The caller owns every buffer; the library never
+ *     allocates, frees, or copies between host and device.
+ *   - Logit tensors are dense row-major; any alignment works, but rows that
+ *     start on 16-byte boundaries (V * element size a multiple of 16 and a
+ *     16-byte aligned base) take the vectorised path.
+ *   - Calls are asynchronous on `stream` (NULL = the null stream) and never
+ *     synchronise the host.  Outputs are valid once the stream has executed
+ *     the call.
+ *   - Argument errors are found on the host before any launch; the outputs are
+ *     then untouched.  A failed launch returns SV_ERR_HIP.  Faults raised by
+ *     a kernel surface at the caller's next synchronisation, as for any HIP
+ *     call.
+ *   - Not checked (preconditions): logits are finite; temperatures are
+ *     finite and >= 0; uniforms lie in [0, 1); |l_v - max_w l_w| / T < 700
+ *     within a row (no probability underflows to zero in double precision)
+ *     and |l_v| / T < 10^6.  Draft token ids should lie in [0, V); an id
+ *     outside that range is rejected (tau = 0), never used as an index.
+ *   - The workspace must hold at least the number of bytes the matching
+ *     sv_*_workspace_bytes() query returns and be 16-byte aligned.  It needs
+ *     no initialisation.  Two calls in flight at the same time must not share
+ *     one workspace.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARGUMENT = 1,    /* a null pointer, a negative size, an unknown dtype ... */
+    SV_ERR_WORKSPACE_TOO_SMALL = 2, /* workspace_bytes below the matching query */
+    SV_ERR_UNSUPPORTED = 3,         /* a size beyond the documented limits */
+    SV_ERR_HIP = 4                  /* a HIP runtime call or kernel launch failed */
+} sv_status;
+
+typedef enum {
+    SV_F32 = 0,  /* IEEE binary32 logits */
+    SV_BF16 = 1  /* bfloat16 logits (upper half of a binary32) */
+} sv_dtype;
+
+/* Limits: k <= SV_MAX_DRAFTS draft tokens per sequence; N <= SV_MAX_TREE_NODES
+ * tree nodes; V <= SV_MAX_VOCAB. */
+#define SV_MAX_DRAFTS 64
+#define SV_MAX_TREE_NODES 1024
+#define SV_MAX_VOCAB (1 << 30)
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int sv_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *sv_status_string(sv_status s);
+
+/* Workspace bytes for one call of the matching entry point with these sizes;
+ * 0 when the sizes are invalid. */
+size_t sv_chain_workspace_bytes(int B, int k, int V, sv_dtype dt);
+size_t sv_greedy_workspace_bytes(int B, int k, int V, sv_dtype dt);
+size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt);
+
+/*
+ * Chain verification with sampling (sections "Speculative decoding" and
+ * "Target-Draft" of the pages above).
+ *
+ * Sizes: B >= 0 sequences, 0 <= k <= SV_MAX_DRAFTS drafts each, vocabulary
+ * 1 <= V <= SV_MAX_VOCAB.  B == 0 returns SV_OK without launching anything.
+ * k == 0 is plain temperature sampling of target row 0.
+ *
+ *   draft_tokens  int32  [B][k]        drafted token ids (may be NULL if k == 0)
+ *   draft_logits  dt     [B][k][V]     draft row i is the draft distribution that drew
+ *                                      draft i (may be NULL if k == 0)
+ *   target_logits dt     [B][k+1][V]   target row j scores draft j; row k is the bonus row
+ *   temperature   fp32   [B]           T_b >= 0 scales sequence b's draft and target rows;
+ *                                      T_b == 0 makes each row the one-hot distribution at
+ *                                      its first (lowest-index) argmax
+ *   uniforms      fp32   [B][k+1]      u[b][i] (i < k) tests draft i with "u < tau";
+ *                                      u[b][k] drives the final draw
+ *   accepted_len  int32  [B]      out  a_b = number of leading drafts accepted, 0..k
+ *   emitted       int32  [B][k+1] out  drafts 0..a_b-1, then the final token, then -1
+ *   accept_prob   fp32   [B][k]   out  optional (NULL to skip): tau_i = min(1, p_i/q_i)
+ *                                      for every i < k (also past the first rejection)
+ *
+ * With P = softmax(logits / T_b) per row, p_i = P_target,i(x_i), q_i =
+ * P_draft,i(x_i): draft i passes when u[b][i] < tau_i, a_b is the index of the
+ * first failure (k if none).  The final token is drawn by inverse CDF over
+ * ascending token ids with u[b][k]: from max(0, P_target,a - P_draft,a)
+ * renormalised when a_b < k (from P_target,a if that residual is empty), from
+ * P_target,k when a_b == k: y = min{ m : sum_{v<=m} w_v > u * sum_v w_v }.
+ */
+sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
+                          const int32_t *draft_tokens, const void *draft_logits,
+                          const void *target_logits, const float *temperature,
+                          const float *uniforms, int32_t *accepted_len, int32_t *emitted,
+                          float *accept_prob, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * Greedy chain verification (temperature 0; section "Speculative decoding").
+ *
+ *   draft_tokens  int32 [B][k]        (may be NULL if k == 0)
+ *   target_logits dt    [B][k+1][V]
+ *   accepted_len  int32 [B]      out  a_b = first i with x_i != g_i, else k, where g_j is
+ *                                     the lowest-index argmax of target row j
+ *   emitted       int32 [B][k+1] out  x_0..x_{a-1}, g_a, then -1
+ */
+sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt,
+                           const int32_t *draft_tokens, const void *target_logits,
+                           int32_t *accepted_len, int32_t *emitted,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy static-tree verification, EAGLE-style (section "EAGLE").
+ *
+ *   node_tokens   int32 [B][N]   node 0 is the root (the last accepted token; its
+ *                                own token is never matched)
+ *   parent        int32 [N] when parent_stride == 0 (one tree shared by all
+ *                                sequences), else [B][parent_stride], parent_stride >= N;
+ *                                parent[i] in [0, i) for i >= 1, parent[0] ignored
+ *   max_depth     >= 0, at least the depth of every node; width of the outputs is
+ *                 max_depth + 1
+ *   target_logits dt    [B][N][V] row n is the target's prediction after node n
+ *   accepted_len  int32 [B]                out  depth d of the chosen node, or -1 when
+ *                                               the parent array breaks the bounds above or
+ *                                               a node is deeper than max_depth
+ *   emitted       int32 [B][max_depth+1]   out  tokens of the path's nodes below the root,
+ *                                               then the lowest-index argmax of the chosen
+ *                                               node's row, then -1 (all -1 when invalid)
+ *   accepted_nodes int32 [B][max_depth+1]  out  optional (NULL to skip): the path's node
+ *                                               ids below the root, then -1
+ *
+ * Node i >= 1 is accepted when its parent is accepted and its token equals
+ * the lowest-index argmax of its parent's row; the chosen node is the deepest
+ * accepted node, the lowest index among equally deep ones.
+ */
+sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
+                         const int32_t *node_tokens, const int32_t *parent, int parent_stride,
+                         int max_depth, const void *target_logits,
+                         int32_t *accepted_len, int32_t *emitted, int32_t *accepted_nodes,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Kernel timing, for benchmarks.  Between sv_profile_begin() and
+ * sv_profile_end() every entry point records a HIP event pair around each of
+ * its kernel launches (host memory for at most max_launches launches is
+ * reserved by sv_profile_begin; later launches are not timed).
+ * sv_profile_end() waits for the recorded events and fills up to max_out
+ * records, one per kernel name, returning how many it wrote (or -1 on error).
+ * Not thread-safe; calls from several host threads must not overlap with it.
+ */
+typedef struct {
+    char name[48];     /* kernel name */
+    int launches;      /* timed launches */
+    double total_ms;   /* sum of event-measured durations */
+} sv_kernel_time;
+
+sv_status sv_profile_begin(int max_launches);
+int sv_profile_end(sv_kernel_time *out, int max_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,148 @@
+"""The C ABI library on the CPU: it loads, exports every function that
+include/*.h declares, and rejects invalid arguments on the host, before any
+HIP call (so none of these tests needs a GPU or launches a kernel)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+from draft_token_verification_chain_amd import _binding as bnd  # noqa: E402
+
+OK, INVALID, WS_SMALL, UNSUPPORTED, HIPERR = range(5)
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    # These calls pass placeholder pointers that validation must reject; with a
+    # GPU present a validation slip would launch on them, so run only where no
+    # device is visible.
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-validation tests run where no GPU is visible")
+    from draft_token_verification_chain_amd import build as b
+
+    if b.is_stale():
+        b.build(verbose=False)
+    return bnd.load()
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(sv_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for must in ("sv_verify_chain", "sv_verify_greedy", "sv_verify_tree", "sv_chain_workspace_bytes",
+                 "sv_greedy_workspace_bytes", "sv_tree_workspace_bytes", "sv_status_string", "sv_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sv_version() >= 100
+    for s in range(5):
+        assert bnd.status_string(s).startswith("SV_")
+    assert "unknown" in bnd.status_string(99)
+
+
+def test_workspace_queries(lib):
+    a = lib.sv_chain_workspace_bytes(64, 4, 128256, BF16)
+    b = lib.sv_chain_workspace_bytes(64, 4, 128256, F32)
+    assert a > 0 and b >= a and a % 256 == 0
+    assert lib.sv_chain_workspace_bytes(-1, 4, 10, F32) == 0
+    assert lib.sv_chain_workspace_bytes(1, 65, 10, F32) == 0
+    assert lib.sv_chain_workspace_bytes(1, 4, 0, F32) == 0
+    assert lib.sv_chain_workspace_bytes(1, 4, 10, 7) == 0
+    assert lib.sv_greedy_workspace_bytes(256, 5, 128256, BF16) > 0
+    assert lib.sv_tree_workspace_bytes(16, 64, 128256, BF16) > 0
+    assert lib.sv_tree_workspace_bytes(16, 1025, 128256, BF16) == 0
+    # grows with every size
+    assert lib.sv_chain_workspace_bytes(128, 4, 128256, BF16) > a
+    assert lib.sv_chain_workspace_bytes(64, 8, 128256, BF16) > a
+
+
+def _chain(lib, B=2, k=2, V=100, dt=F32, ws_bytes=None, **ptrs):
+    p = dict(tokens=FAKE, draft=FAKE, target=FAKE, temp=FAKE, u=FAKE, acc=FAKE, em=FAKE, ap=None, ws=FAKE)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = max(lib.sv_chain_workspace_bytes(max(B, 0), max(k, 0), max(V, 1), dt if dt in (0, 1) else 0), 1)
+    return lib.sv_verify_chain(B, k, V, dt, p["tokens"], p["draft"], p["target"], p["temp"], p["u"], p["acc"],
+                               p["em"], p["ap"], p["ws"], ws_bytes, None)
+
+
+def test_chain_rejects_bad_arguments_on_the_host(lib):
+    assert _chain(lib, B=-1) == INVALID
+    assert _chain(lib, k=-1) == INVALID
+    assert _chain(lib, V=0) == INVALID
+    assert _chain(lib, dt=5) == INVALID
+    assert _chain(lib, k=65) == UNSUPPORTED
+    assert _chain(lib, V=(1 << 30) + 1) == UNSUPPORTED
+    for key in ("target", "temp", "u", "acc", "em", "tokens", "draft"):
+        assert _chain(lib, **{key: None}) == INVALID, key
+    assert _chain(lib, ws_bytes=16) == WS_SMALL
+    assert _chain(lib, ws=None) == INVALID
+    assert _chain(lib, ws=ctypes.c_void_p(0x1004)) == INVALID  # not 16-byte aligned
+
+
+def test_chain_empty_batch_and_k0_pointer_rules(lib):
+    # B == 0: nothing to do, no pointer is looked at
+    assert _chain(lib, B=0, target=None, temp=None, u=None, acc=None, em=None, ws=None, ws_bytes=0) == OK
+    # k == 0 needs neither draft tokens nor draft logits: validation passes those checks
+    # and stops at the (deliberately) too-small workspace
+    assert _chain(lib, k=0, tokens=None, draft=None, ws_bytes=1) == WS_SMALL
+
+
+def test_greedy_rejects_bad_arguments_on_the_host(lib):
+    def g(B=2, k=3, V=50, dt=BF16, tokens=FAKE, target=FAKE, acc=FAKE, em=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.sv_verify_greedy(B, k, V, dt, tokens, target, acc, em, ws, ws_bytes, None)
+
+    assert g(B=-1) == INVALID
+    assert g(k=-2) == INVALID
+    assert g(V=-3) == INVALID
+    assert g(dt=2) == INVALID
+    assert g(k=100) == UNSUPPORTED
+    assert g(tokens=None) == INVALID
+    assert g(target=None) == INVALID
+    assert g(ws_bytes=8) == WS_SMALL
+    assert g(B=0, tokens=None, target=None, acc=None, em=None, ws=None, ws_bytes=0) == OK
+
+
+def test_tree_rejects_bad_arguments_on_the_host(lib):
+    def t(B=2, N=8, V=50, dt=F32, tok=FAKE, par=FAKE, stride=0, md=3, target=FAKE, acc=FAKE, em=FAKE,
+          nodes=None, ws=FAKE, ws_bytes=1 << 20):
+        return lib.sv_verify_tree(B, N, V, dt, tok, par, stride, md, target, acc, em, nodes, ws, ws_bytes, None)
+
+    assert t(N=0) == INVALID
+    assert t(md=-1) == INVALID
+    assert t(stride=4) == INVALID  # a per-sequence parent stride shorter than N
+    assert t(stride=-1) == INVALID
+    assert t(N=1025) == UNSUPPORTED
+    assert t(par=None) == INVALID
+    assert t(tok=None) == INVALID
+    assert t(ws_bytes=8) == WS_SMALL
+    assert t(B=0, tok=None, par=None, target=None, acc=None, em=None, ws=None, ws_bytes=0) == OK
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(bnd, "_lib", None)
+    monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        bnd.load()

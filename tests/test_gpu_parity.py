@@ -1,0 +1,268 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+accepted_len and emitted must match bit-exactly, except for sequences the
+oracle flags as lying within 1e-5 of an acceptance threshold or CDF boundary
+(those are counted and reported); accept_prob must agree within 1e-5
+absolute.  Greedy and tree results are integer decisions on raw logits and
+must match exactly everywhere.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_common import compare_chain, dev, dev_logits, run_chain, run_greedy, run_tree
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svl():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_token_verification_chain_amd as svl
+
+    svl.load()
+    return svl
+
+
+def _record(kind, label, stats):
+    path = os.environ.get("SV_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(kind=kind, case=label, **stats)) + "\n")
+    print(f"[parity] {kind} {label} {stats}", flush=True)
+
+
+def _check_chain(svl, orc, inp, label):
+    got = run_chain(svl, inp)
+    ref = orc.verify_chain(inp)
+    stats = compare_chain(inp, got, ref, label)
+    _record("chain", label, stats)
+    return got, ref
+
+
+# ------------------------------------------------------------ small shapes ---
+
+SMALL_CHAIN = [
+    # B, k, V, dtype, temperature -- several tiles with ragged tails; odd V takes the element-load path
+    (7, 4, 9000, W.BF16, 0.7),
+    (5, 3, 5000, W.F32, 1.0),
+    (3, 1, 1000, W.BF16, 1.3),
+    (4, 8, 4097, W.BF16, 0.5),
+    (2, 0, 3000, W.F32, 0.9),
+    (6, 5, 128257, W.BF16, 0.8),
+    (3, 2, 7001, W.F32, 0.6),
+    (2, 64, 600, W.BF16, 1.0),
+    (1, 4, 1024, W.F32, 1.0),
+]
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("shape", SMALL_CHAIN, ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_small_chain_parity(svl, orc, shape, seed):
+    B, k, V, dt, T = shape
+    inp = W.chain_inputs(B, k, V, dt, seed, target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=T)
+    _check_chain(svl, orc, inp, f"B{B}k{k}V{V}dt{dt}s{seed}")
+
+
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+def test_mixed_temperatures_including_zero(svl, orc, dt):
+    B, k, V = 12, 4, 6000
+    T = np.array([0.0, 0.7, 0.0, 1.3, 0.3, 0.0, 1.0, 0.0, 0.5, 2.0, 0.0, 0.9], np.float32)
+    inp = W.chain_inputs(B, k, V, dt, 5, target_sigma=2.0, draft_sigma=0.5, temperature=T)
+    # give the greedy rows some accepted drafts
+    top = np.argmax(W.values(inp["target_logits"], dt), axis=-1)
+    for b in np.flatnonzero(T == 0):
+        inp["draft_tokens"][b, :2] = top[b, :2]
+    got, ref = _check_chain(svl, orc, inp, f"mixedT dt{dt}")
+    assert (got["accepted_len"][T == 0] >= 2).all()
+
+
+def test_identical_rows_accept_every_draft(svl, orc):
+    inp = W.chain_inputs(16, 5, 9000, W.BF16, 3, target_sigma=3.0, draft_sigma=0.0, temperature=0.8)
+    inp["uniforms"][:, :5] = np.float32(1.0) - np.float32(2.0 ** -24)
+    got, ref = _check_chain(svl, orc, inp, "identical rows")
+    assert (got["accepted_len"] == 5).all()
+    assert (got["accept_prob"] == 1.0).all()
+
+
+def test_unaligned_logits_take_the_element_path(svl, orc):
+    import torch
+
+    B, k, V = 3, 3, 4096
+    inp = W.chain_inputs(B, k, V, W.BF16, 7, target_sigma=3.0, draft_sigma=1.0, temperature=0.7)
+    ref = orc.verify_chain(inp)
+    # same logits, but stored one element past a 16-byte boundary
+    def shifted(arr):
+        flat = dev_logits(np.concatenate([np.zeros(1, np.uint16), arr.reshape(-1)]), W.BF16)
+        return flat[1:].view(arr.shape)
+
+    d, t = shifted(inp["draft_logits"]), shifted(inp["target_logits"])
+    assert d.data_ptr() % 16 != 0
+    out = svl.verify_chain(dev(inp["draft_tokens"]), d, t, dev(inp["temperature"]), dev(inp["uniforms"]))
+    torch.cuda.synchronize()
+    got = {kk: v.cpu().numpy() for kk, v in out.items()}
+    _record("chain", "unaligned", compare_chain(inp, got, ref, "unaligned"))
+
+
+def test_empty_batch_is_a_no_op(svl):
+    import torch
+
+    e = torch.empty((0, 4, 100), dtype=torch.bfloat16, device="cuda")
+    out = svl.verify_chain(torch.empty((0, 3), dtype=torch.int32, device="cuda"), e[:, :3], e,
+                           torch.empty(0, device="cuda"), torch.empty((0, 4), device="cuda"))
+    torch.cuda.synchronize()
+    assert out["accepted_len"].numel() == 0
+
+
+# ------------------------------------------------------------ full workloads ---
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [1, 2, 4])
+def test_full_chain_configs(svl, orc, config, seed):
+    inp = W.make_inputs(config, seed)
+    _check_chain(svl, orc, inp, f"config{config} seed{seed}")
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+def test_full_greedy_config(svl, orc, seed):
+    inp = W.make_inputs(3, seed)
+    got = run_greedy(svl, inp)
+    ref = orc.verify_greedy(inp)
+    np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+    np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+    _record("greedy", f"config3 seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
+def test_full_tree_config(svl, orc, seed):
+    inp = W.make_inputs(5, seed)
+    got = run_tree(svl, inp)
+    ref = orc.verify_tree(inp)
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    _record("tree", f"config5 seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
+
+
+def test_determinism(svl):
+    inp = W.make_inputs(2, 1)
+    a = run_chain(svl, inp)
+    b = run_chain(svl, inp)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+# ------------------------------------------------------------ greedy / tree edges ---
+
+def _next_above(bits, dtype):
+    """The representable value just above a stored logit (bit patterns)."""
+    if dtype == W.BF16:
+        b = int(bits)
+        return np.uint16(b + 1 if b < 0x8000 else (b - 1 if b != 0x8000 else 0x0001))
+    return np.nextafter(np.float32(bits), np.float32(np.inf))
+
+
+def _plant_tile_ties(t, dtype, rng):
+    """Give every row a new strict maximum stored twice, in two different tiles
+    (tiles hold 64 * 8 vectors of 16 bytes): even rows on both sides of a tile
+    boundary, odd rows in the first and the last tile.  The first argmax is
+    then the lower of the two indices."""
+    ve = 8 if dtype == W.BF16 else 4
+    tile = 64 * 8 * ve
+    V = t.shape[-1]
+    assert V > 2 * tile
+    rows = t.reshape(-1, V)
+    vals = W.values(rows, dtype)
+    for r in range(rows.shape[0]):
+        top = rows[r, int(np.argmax(vals[r]))]
+        new = _next_above(top, dtype)
+        if r % 2 == 0:
+            bnd = tile * int(rng.integers(1, (V - 1) // tile + 1))
+            i1, i2 = bnd - 1, bnd
+        else:
+            i1, i2 = int(rng.integers(0, tile)), int(rng.integers((V - 1) // tile * tile, V))
+        rows[r, i1] = new
+        rows[r, i2] = new
+
+
+@pytest.mark.parametrize("dt", [W.BF16, W.F32])
+@pytest.mark.parametrize("V", [20000, 20001])
+def test_greedy_ties_across_tile_boundaries(svl, orc, dt, V):
+    inp = W.greedy_inputs(24, 4, V, dt, 2, match_p=0.7)
+    _plant_tile_ties(inp["target_logits"], dt, np.random.default_rng(0))
+    top = np.argmax(W.values(inp["target_logits"], dt), axis=-1)
+    inp["draft_tokens"][::2] = top[::2, :4]
+    got = run_greedy(svl, inp)
+    ref = orc.verify_greedy(inp)
+    np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+    np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+
+
+def test_temperature_zero_chain_matches_greedy_with_ties(svl, orc):
+    B, k, V = 16, 4, 20000
+    inp = W.chain_inputs(B, k, V, W.BF16, 4, target_sigma=2.0, draft_sigma=1.0, temperature=0.0)
+    _plant_tile_ties(inp["target_logits"], W.BF16, np.random.default_rng(1))
+    top = np.argmax(W.values(inp["target_logits"], W.BF16), axis=-1)
+    inp["draft_tokens"][::2] = top[::2, :k]
+    got, ref = _check_chain(svl, orc, inp, "T0 ties")
+    g = run_greedy(svl, dict(inp, kind="greedy"))
+    np.testing.assert_array_equal(got["emitted"], g["emitted"])
+
+
+def test_tree_per_sequence_parents_and_invalid_trees(svl, orc):
+    B, N, V = 6, 40, 3000
+    base = W.tree_inputs(B, N, V, W.BF16, 9, max_depth=6)
+    parents = np.stack([W.random_tree(N, 100 + b) for b in range(B)]).astype(np.int32)
+    parents[4, 7] = 9          # parent index not below the node: invalid
+    inp = dict(base, parent=parents)
+    depth = np.zeros(N, int)
+    for i in range(1, N):
+        depth[i] = depth[parents[5, i]] + 1
+    inp["max_depth"] = 6
+    got = run_tree(svl, inp)
+    ref = orc.verify_tree(inp)
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    assert got["accepted_len"][4] == -1
+
+
+def test_tree_linear_and_star_shapes(svl, orc):
+    V = 5000
+    for parent in (np.arange(-1, 11, dtype=np.int32), np.array([-1] + [0] * 30, np.int32)):
+        N = parent.size
+        inp = W.tree_inputs(8, N, V, W.F32, 3, parent=parent, match_p=0.8)
+        got = run_tree(svl, inp)
+        ref = orc.verify_tree(inp)
+        for key in ("accepted_len", "emitted", "accepted_nodes"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+
+
+# ------------------------------------------------------------ distribution on the GPU ---
+
+def test_gpu_emitted_distribution_chi_square(svl, orc):
+    """10^6 trials at V = 16, k = 4 through the GPU: bit-exact with the oracle
+    outside the band, and the emitted token at position j given j accepted
+    drafts is distributed as the target row j (chi-square)."""
+    from scipy import special, stats
+
+    rng = np.random.default_rng(2024)
+    t = (1.5 * rng.standard_normal((5, 16))).astype(np.float32)
+    d = (t[:4] + rng.standard_normal((4, 16))).astype(np.float32)
+    accs, ems = [], []
+    for blk in range(5):
+        inp = W.repeated_trials(t, d, 1.0, 200_000, seed=77, block=blk)
+        got, ref = _check_chain(svl, orc, inp, f"chi block{blk}")
+        accs.append(got["accepted_len"])
+        ems.append(got["emitted"])
+    acc, em = np.concatenate(accs), np.concatenate(ems)
+    for j in range(5):
+        sel = acc >= j
+        counts = np.bincount(em[sel, j], minlength=16)
+        p = special.softmax(t[j].astype(np.float64))
+        assert stats.chisquare(counts, p * sel.sum()).pvalue > 1e-4
