@@ -102,7 +102,9 @@ __device__ __forceinline__ void load_vec_masked(const void* base, int64_t row_el
 }
 
 // U vectors of lane `lane` of tile `tile`, unpacked into U*VE floats.
-template <int DT, bool VEC, int U>
+// FULL (only with VEC): the whole tile lies inside the row, so the loads need
+// no mask.  Otherwise elements past the row end read as -inf.
+template <int DT, bool VEC, int U, bool FULL = false>
 __device__ __forceinline__ void load_tile(const void* base, int64_t row_elem, int V, int64_t tile,
                                           int lane, float* v) {
     constexpr int VE = Elem<DT>::per_vec;
@@ -112,13 +114,28 @@ __device__ __forceinline__ void load_tile(const void* base, int64_t row_elem, in
         const char* row = static_cast<const char*>(base) + row_elem * Elem<DT>::bytes;
         uint4 raw[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) raw[i] = load_vec_aligned(row, v0 + i * 64, nv, Elem<DT>::neg_inf_word);
+        for (int i = 0; i < U; ++i) {
+            if constexpr (FULL)
+                raw[i] = *reinterpret_cast<const uint4*>(row + (v0 + i * 64) * 16);
+            else
+                raw[i] = load_vec_aligned(row, v0 + i * 64, nv, Elem<DT>::neg_inf_word);
+        }
 #pragma unroll
         for (int i = 0; i < U; ++i) unpack<DT>(raw[i], v + i * VE);
     } else {
+        static_assert(!FULL, "element loads are always masked");
 #pragma unroll
         for (int i = 0; i < U; ++i) load_vec_masked<DT>(base, row_elem, v0 + i * 64, V, v + i * VE);
     }
+}
+
+// Whether tile `tile` of U vectors per lane lies entirely inside a row of nv
+// vectors (and may take the unmasked path).
+template <bool VEC, int U>
+__device__ __forceinline__ bool tile_is_full(int64_t tile, int V, int ve) {
+    if constexpr (!VEC) return false;
+    const int64_t nv = (V + ve - 1) / ve;
+    return (tile + 1) * (64 * U) <= nv;
 }
 
 // ---------------------------------------------------------------- arithmetic ---
@@ -136,8 +153,16 @@ __device__ __forceinline__ float pairwise_sum(const float* x) {
 // exp2(l * c - r) with c = c_hi + c_lo (a double-float split of log2(e) / T)
 // and an integer-valued reference r: the product l * c_hi is exact inside the
 // fma, so the argument carries about one rounding of its own (small) value.
+// l must be finite (c_lo may be negative: -inf would give inf - inf).
 __device__ __forceinline__ float scaled_exp2(float l, float c_hi, float c_lo, float r) {
     return __builtin_amdgcn_exp2f(__builtin_fmaf(l, c_lo, __builtin_fmaf(l, c_hi, -r)));
+}
+
+// The same term for a possibly masked element: masked (-inf) elements weigh 0.
+template <bool FULL>
+__device__ __forceinline__ float exp_term(float l, float c_hi, float c_lo, float r) {
+    if constexpr (FULL) return scaled_exp2(l, c_hi, c_lo, r);
+    return l == -__builtin_inff() ? 0.f : scaled_exp2(l, c_hi, c_lo, r);
 }
 
 // ---------------------------------------------------------------- wave64 reductions ---

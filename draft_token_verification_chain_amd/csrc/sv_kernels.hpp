@@ -60,12 +60,12 @@ __device__ __forceinline__ void temperature_scale(float T, float& c_hi, float& c
 
 // Softmax partial of one tile: s = sum_v exp2(l_v c - r) with r = ceil(max l c)
 // taken over the whole tile, so exp2 never exceeds ~1 and never overflows.
-template <int DT, bool VEC, int U>
+template <int DT, bool VEC, int U, bool FULL>
 __device__ __forceinline__ Partial tile_softmax(const void* base, int64_t row_elem, int V, int64_t tile,
                                                 float c_hi, float c_lo) {
     constexpr int NE = U * Elem<DT>::per_vec;
     float v[NE];
-    load_tile<DT, VEC, U>(base, row_elem, V, tile, lane_id(), v);
+    load_tile<DT, VEC, U, FULL>(base, row_elem, V, tile, lane_id(), v);
     float mx = v[0];
 #pragma unroll
     for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
@@ -73,19 +73,19 @@ __device__ __forceinline__ Partial tile_softmax(const void* base, int64_t row_el
     const float r = ceilf(mx * c_hi);
     float e[NE];
 #pragma unroll
-    for (int j = 0; j < NE; ++j) e[j] = scaled_exp2(v[j], c_hi, c_lo, r);
+    for (int j = 0; j < NE; ++j) e[j] = exp_term<FULL>(v[j], c_hi, c_lo, r);
     const float s = wave_sum(pairwise_sum<NE>(e));
     return Partial{s, static_cast<int>(r)};
 }
 
 // (max, lowest index) of one tile of raw logits.
-template <int DT, bool VEC, int U>
+template <int DT, bool VEC, int U, bool FULL>
 __device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem, int V, int64_t tile) {
     constexpr int VE = Elem<DT>::per_vec;
     constexpr int NE = U * VE;
     const int lane = lane_id();
     float v[NE];
-    load_tile<DT, VEC, U>(base, row_elem, V, tile, lane, v);
+    load_tile<DT, VEC, U, FULL>(base, row_elem, V, tile, lane, v);
     ArgMax a{-__builtin_inff(), kNoIndex};
     const int64_t v0 = tile * (64 * U) + lane;
 #pragma unroll
@@ -100,6 +100,22 @@ __device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem
         }
     }
     return wave_argmax(a);
+}
+
+// Tile entry points that pick the unmasked path for tiles inside the row.
+template <int DT, bool VEC, int U>
+__device__ __forceinline__ Partial tile_softmax_any(const void* base, int64_t row_elem, int V, int64_t tile,
+                                                    float c_hi, float c_lo) {
+    if (tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec))
+        return tile_softmax<DT, VEC, U, VEC>(base, row_elem, V, tile, c_hi, c_lo);
+    return tile_softmax<DT, VEC, U, false>(base, row_elem, V, tile, c_hi, c_lo);
+}
+
+template <int DT, bool VEC, int U>
+__device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_elem, int V, int64_t tile) {
+    if (tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec))
+        return tile_argmax<DT, VEC, U, VEC>(base, row_elem, V, tile);
+    return tile_argmax<DT, VEC, U, false>(base, row_elem, V, tile);
 }
 
 // Combine the nT softmax partials of one row: R = max r_t, S = sum s_t 2^(r_t - R).
@@ -156,10 +172,10 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
     if (T > 0.f) {
         float c_hi, c_lo;
         temperature_scale(T, c_hi, c_lo);
-        p = tile_softmax<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
+        p = tile_softmax_any<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
     } else {
         if (!is_target) return;
-        const ArgMax a = tile_argmax<DT, VEC, U>(base, row_elem, V, tile);
+        const ArgMax a = tile_argmax_any<DT, VEC, U>(base, row_elem, V, tile);
         p = Partial{a.val, a.idx};
     }
     if (lane_id() == 0) part[r * nT + tile] = p;
@@ -241,20 +257,52 @@ __global__ __launch_bounds__(kWave) void chain_accept_kernel(
 // Weight of the final draw for the U*VE elements a lane holds.
 //   residual: w = max(0, p - q), p = exp2(l_t c - rt) / S_t, q likewise;
 //   bonus:    w = exp2(l c - ref), unnormalised (the draw is scale-free).
-template <int NE>
+template <int NE, bool FULL>
 __device__ __forceinline__ void residual_weights(const float* vt, const float* vd, const SeqInfo& s, float* w) {
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
-        const float p = scaled_exp2(vt[j], s.c_hi, s.c_lo, s.rt) * s.inv_st;
-        const float q = scaled_exp2(vd[j], s.c_hi, s.c_lo, s.rd) * s.inv_sd;
+        const float p = exp_term<FULL>(vt[j], s.c_hi, s.c_lo, s.rt) * s.inv_st;
+        const float q = exp_term<FULL>(vd[j], s.c_hi, s.c_lo, s.rd) * s.inv_sd;
         w[j] = fmaxf(p - q, 0.f);
     }
 }
 
-template <int NE>
+template <int NE, bool FULL>
 __device__ __forceinline__ void bonus_weights(const float* v, const SeqInfo& s, float ref, float* w) {
 #pragma unroll
-    for (int j = 0; j < NE; ++j) w[j] = scaled_exp2(v[j], s.c_hi, s.c_lo, ref);
+    for (int j = 0; j < NE; ++j) w[j] = exp_term<FULL>(v[j], s.c_hi, s.c_lo, ref);
+}
+
+// One tile of the final draw's weights: segment masses and the tile's
+// reference exponent (0 for the residual, whose weights are absolute).
+template <int DT, bool VEC, int U, bool FULL>
+__device__ __forceinline__ void final_part_tile(const void* draft, const void* target, int64_t trow, int64_t drow,
+                                                int V, int64_t tile, const SeqInfo& s, float* seg, Partial* ti) {
+    constexpr int VE = Elem<DT>::per_vec;
+    constexpr int NE = U * VE;
+    const int lane = lane_id();
+    float w[NE];
+    float ref = 0.f;
+    if (s.mode == kFinalResidual) {
+        float vt[NE], vd[NE];
+        load_tile<DT, VEC, U, FULL>(target, trow, V, tile, lane, vt);
+        load_tile<DT, VEC, U, FULL>(draft, drow, V, tile, lane, vd);
+        residual_weights<NE, FULL>(vt, vd, s, w);
+    } else {
+        float v[NE];
+        load_tile<DT, VEC, U, FULL>(target, trow, V, tile, lane, v);
+        float mx = v[0];
+#pragma unroll
+        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
+        ref = ceilf(wave_max(mx) * s.c_hi);
+        bonus_weights<NE, FULL>(v, s, ref, w);
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const float m = wave_sum(pairwise_sum<VE>(w + i * VE));
+        if (lane == 0) seg[i] = m;
+    }
+    if (lane == 0) *ti = Partial{0.f, static_cast<int>(ref)};
 }
 
 // Partial pass of the final draw: one wave per (sequence, tile) of the row(s)
@@ -266,7 +314,6 @@ __global__ __launch_bounds__(kBlock) void chain_final_part_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nT,
     const SeqInfo* __restrict__ info, float* __restrict__ segmass, Partial* __restrict__ tileinfo) {
     constexpr int VE = Elem<DT>::per_vec;
-    constexpr int NE = U * VE;
     const int64_t gw = global_wave();
     if (gw >= static_cast<int64_t>(B) * nT) return;
     const int64_t b = gw / nT;
@@ -276,51 +323,45 @@ __global__ __launch_bounds__(kBlock) void chain_final_part_kernel(
     const int lane = lane_id();
     const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
     if (s.mode == kFinalArgmax) {
-        const ArgMax a = tile_argmax<DT, VEC, U>(target, trow, V, tile);
+        const ArgMax a = tile_argmax_any<DT, VEC, U>(target, trow, V, tile);
         if (lane == 0) tileinfo[b * nT + tile] = Partial{a.val, a.idx};
         return;
     }
-    float w[NE];
-    float ref = 0.f;
-    if (s.mode == kFinalResidual) {
-        float vt[NE], vd[NE];
-        load_tile<DT, VEC, U>(target, trow, V, tile, lane, vt);
-        load_tile<DT, VEC, U>(draft, (b * k + s.a) * static_cast<int64_t>(V), V, tile, lane, vd);
-        residual_weights<NE>(vt, vd, s, w);
-    } else {
-        float v[NE];
-        load_tile<DT, VEC, U>(target, trow, V, tile, lane, v);
-        float mx = v[0];
-#pragma unroll
-        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
-        ref = ceilf(wave_max(mx) * s.c_hi);
-        bonus_weights<NE>(v, s, ref, w);
-    }
+    const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
     float* seg = segmass + (b * nT + tile) * U;
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-        const float m = wave_sum(pairwise_sum<VE>(w + i * VE));
-        if (lane == 0) seg[i] = m;
-    }
-    if (lane == 0) tileinfo[b * nT + tile] = Partial{0.f, static_cast<int>(ref)};
+    Partial* ti = tileinfo + b * nT + tile;
+    if (tile_is_full<VEC, U>(tile, V, VE))
+        final_part_tile<DT, VEC, U, VEC>(draft, target, trow, drow, V, tile, s, seg, ti);
+    else
+        final_part_tile<DT, VEC, U, false>(draft, target, trow, drow, V, tile, s, seg, ti);
 }
 
 // Weights of segment `seg` (one vector per lane) in the tile's scale.
+template <int DT, bool VEC, bool FULL>
+__device__ __forceinline__ void segment_weights_t(const void* draft, const void* target, int64_t trow,
+                                                  int64_t drow, int V, int64_t seg, const SeqInfo& s,
+                                                  bool residual, float ref, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    // a segment is tile seg/U's load seg%U, i.e. vectors 64*seg .. 64*seg+63
+    float vt[VE];
+    load_tile<DT, VEC, 1, FULL>(target, trow, V, seg, lane_id(), vt);
+    if (residual) {
+        float vd[VE];
+        load_tile<DT, VEC, 1, FULL>(draft, drow, V, seg, lane_id(), vd);
+        residual_weights<VE, FULL>(vt, vd, s, w);
+    } else {
+        bonus_weights<VE, FULL>(vt, s, ref, w);
+    }
+}
+
 template <int DT, bool VEC>
 __device__ __forceinline__ void segment_weights(const void* draft, const void* target, int64_t trow,
                                                 int64_t drow, int V, int64_t seg, const SeqInfo& s,
                                                 bool residual, float ref, float* w) {
-    constexpr int VE = Elem<DT>::per_vec;
-    // a segment is tile seg/U's load seg%U, i.e. vectors 64*seg .. 64*seg+63
-    float vt[VE];
-    load_tile<DT, VEC, 1>(target, trow, V, seg, lane_id(), vt);
-    if (residual) {
-        float vd[VE];
-        load_tile<DT, VEC, 1>(draft, drow, V, seg, lane_id(), vd);
-        residual_weights<VE>(vt, vd, s, w);
-    } else {
-        bonus_weights<VE>(vt, s, ref, w);
-    }
+    if (tile_is_full<VEC, 1>(seg, V, Elem<DT>::per_vec))
+        segment_weights_t<DT, VEC, VEC>(draft, target, trow, drow, V, seg, s, residual, ref, w);
+    else
+        segment_weights_t<DT, VEC, false>(draft, target, trow, drow, V, seg, s, residual, ref, w);
 }
 
 // Inverse CDF inside one segment.  `P` is the mass before the segment and
@@ -484,7 +525,7 @@ __global__ __launch_bounds__(kBlock) void argmax_rows_kernel(const void* __restr
     if (gw >= nrows * nT) return;
     const int64_t r = gw / nT;
     const int64_t tile = gw - r * nT;
-    const ArgMax a = tile_argmax<DT, VEC, U>(logits, r * static_cast<int64_t>(V), V, tile);
+    const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, r * static_cast<int64_t>(V), V, tile);
     if (lane_id() == 0) part[gw] = Partial{a.val, a.idx};
 }
 
