@@ -6,9 +6,11 @@
 // entry points correspond to its sections "Target-Draft" (chain
 // verification with sampling), "Speculative decoding" (greedy matching) and
 // "EAGLE" (tree verification).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -22,7 +24,7 @@ namespace {
 using sv::Partial;
 using sv::SeqInfo;
 
-// Vectors of 16 bytes per lane per tile.
+// Vectors of 16 bytes per lane per tile in the passes over every row.
 constexpr int kU = 8;
 
 constexpr size_t kAlign = 256;
@@ -33,11 +35,11 @@ int elem_bytes(sv_dtype dt) { return dt == SV_BF16 ? 2 : 4; }
 
 bool valid_dtype(sv_dtype dt) { return dt == SV_F32 || dt == SV_BF16; }
 
-// Tiles per row: NV = ceil(V / VE) vectors of 16 bytes, 64 * kU vectors per tile.
-int64_t tiles_per_row(int V, sv_dtype dt) {
+// Tiles per row: NV = ceil(V / VE) vectors of 16 bytes, 64 * u vectors per tile.
+int64_t tiles_per_row(int V, sv_dtype dt, int u = kU) {
     const int64_t ve = 16 / elem_bytes(dt);
     const int64_t nv = (V + ve - 1) / ve;
-    return (nv + 64 * kU - 1) / (64 * kU);
+    return (nv + 64 * u - 1) / (64 * u);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -49,18 +51,31 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 
 // ---------------------------------------------------------------- workspace layouts ---
 
+// Segments (64 vectors of 16 bytes) per row, and the final draw's chunks of
+// kSegPerChunk segments.
+int64_t segments_per_row(int V, sv_dtype dt) {
+    const int64_t ve = 16 / elem_bytes(dt);
+    return ((V + ve - 1) / ve + 63) / 64;
+}
+int64_t final_chunks(int V, sv_dtype dt) {
+    return (segments_per_row(V, dt) + sv::kSegPerChunk - 1) / sv::kSegPerChunk;
+}
+
+// The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
+// every sequence, their logits at the draft tokens, the final draw's
+// descriptors, segment masses and chunk argmaxes.
 struct ChainLayout {
-    size_t part, info, seg, tile, total;
+    size_t part, gathered, info, segs, chunkarg, total;
 };
 
 ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
-    const int64_t nT = tiles_per_row(V, dt);
     ChainLayout L{};
     L.part = 0;
-    L.info = align_up(L.part + sizeof(Partial) * static_cast<size_t>(2) * B * k * nT);
-    L.seg = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
-    L.tile = align_up(L.seg + sizeof(float) * static_cast<size_t>(B) * nT * kU);
-    L.total = align_up(L.tile + sizeof(Partial) * static_cast<size_t>(B) * nT);
+    L.gathered = align_up(L.part + sizeof(Partial) * static_cast<size_t>(2) * B * k * tiles_per_row(V, dt));
+    L.info = align_up(L.gathered + sizeof(float) * static_cast<size_t>(2) * B * k);
+    L.segs = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
+    L.chunkarg = align_up(L.segs + sizeof(Partial) * static_cast<size_t>(B) * segments_per_row(V, dt));
+    L.total = align_up(L.chunkarg + sizeof(Partial) * static_cast<size_t>(B) * final_chunks(V, dt));
     return L;
 }
 
@@ -79,19 +94,31 @@ struct Profiler {
     size_t next = 0;
 } g_prof;
 
-// Launch `fn` on `stream`, bracketing it with an event pair while profiling.
-template <typename F>
-sv_status timed_launch(const char* name, hipStream_t stream, F&& fn) {
+// Launch `kernel` on `stream`.  While profiling, the launch carries an event
+// pair that the runtime records at the dispatch's own start and end
+// (hipExtLaunchKernel), so the measured time is the kernel's execution alone.
+template <typename... KArgs, typename... Args>
+sv_status launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                 Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> params(static_cast<KArgs>(args)...);
+    void* argv[sizeof...(KArgs)];
+    std::apply([&argv](auto&... p) {
+        size_t i = 0;
+        ((argv[i++] = static_cast<void*>(&p)), ...);
+    }, params);
     ProfSlot* slot = nullptr;
     if (g_prof.on) {
         std::lock_guard<std::mutex> lk(g_prof.mu);
         if (g_prof.next < g_prof.slots.size()) slot = &g_prof.slots[g_prof.next++];
     }
-    if (slot && hipEventRecord(slot->start, stream) != hipSuccess) return SV_ERR_HIP;
-    fn();
-    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    const hipError_t err = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream,
+                                              slot ? slot->start : nullptr, slot ? slot->stop : nullptr, 0);
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return SV_ERR_HIP;
+    }
     if (slot) {
-        if (hipEventRecord(slot->stop, stream) != hipSuccess) return SV_ERR_HIP;
         slot->name = name;
         slot->used = true;
     }
@@ -103,45 +130,35 @@ sv_status timed_launch(const char* name, hipStream_t stream, F&& fn) {
 template <int DT, bool VEC>
 sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draft, const void* target,
                     const float* temperature, const float* uniforms, int32_t* accepted_len, int32_t* emitted,
-                    float* accept_prob, char* ws, const ChainLayout& L, int nT, hipStream_t stream) {
+                    float* accept_prob, char* ws, const ChainLayout& L, int nT, int nchunk, hipStream_t stream) {
     auto* part = reinterpret_cast<Partial*>(ws + L.part);
+    auto* gathered = reinterpret_cast<float*>(ws + L.gathered);
     auto* info = reinterpret_cast<SeqInfo*>(ws + L.info);
-    auto* seg = reinterpret_cast<float*>(ws + L.seg);
-    auto* tile = reinterpret_cast<Partial*>(ws + L.tile);
-    sv_status st = SV_OK;
+    auto* segs = reinterpret_cast<Partial*>(ws + L.segs);
+    auto* chunkarg = reinterpret_cast<Partial*>(ws + L.chunkarg);
+    sv_status st;
     if (k > 0) {
         const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * k * nT);
-        st = timed_launch("chain_rowstats", stream, [&] {
-            sv::chain_rowstats_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(blocks)), dim3(sv::kBlock), 0,
-                                                      stream>>>(target, draft, temperature, B, k, V, nT, part);
-        });
+        st = launch("chain_rowstats", sv::chain_rowstats_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
+                    dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, V, nT, part, gathered);
         if (st != SV_OK) return st;
     }
-    st = timed_launch("chain_accept", stream, [&] {
-        sv::chain_accept_kernel<DT><<<dim3(B), dim3(sv::kWave), 0, stream>>>(
-            tokens, draft, target, temperature, uniforms, B, k, V, nT, part, info, accepted_len, emitted,
-            accept_prob);
-    });
+    st = launch("chain_final_part", sv::chain_final_part_kernel<DT, VEC>,
+                dim3(static_cast<unsigned>(static_cast<int64_t>(B) * nchunk)), dim3(sv::kFinBlock), stream, tokens,
+                draft, target, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
+                static_cast<const float*>(gathered), nchunk,
+                accepted_len, emitted, accept_prob, info, segs, chunkarg);
     if (st != SV_OK) return st;
-    const int64_t fblocks = blocks_for_waves(static_cast<int64_t>(B) * nT);
-    st = timed_launch("chain_final_part", stream, [&] {
-        sv::chain_final_part_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(fblocks)), dim3(sv::kBlock), 0,
-                                                   stream>>>(draft, target, B, k, V, nT, info, seg, tile);
-    });
-    if (st != SV_OK) return st;
-    return timed_launch("chain_final_pick", stream, [&] {
-        sv::chain_final_pick_kernel<DT, VEC, kU><<<dim3(B), dim3(sv::kWave), 0, stream>>>(
-            draft, target, B, k, V, nT, info, seg, tile, emitted);
-    });
+    return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kWave), stream, draft,
+                  target, B, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),
+                  static_cast<const Partial*>(chunkarg), emitted);
 }
 
 template <int DT, bool VEC>
 sv_status run_argmax_rows(const void* logits, int64_t nrows, int V, int nT, Partial* part, hipStream_t stream) {
     const int64_t blocks = blocks_for_waves(nrows * nT);
-    return timed_launch("argmax_rows", stream, [&] {
-        sv::argmax_rows_kernel<DT, VEC, kU><<<dim3(static_cast<unsigned>(blocks)), dim3(sv::kBlock), 0, stream>>>(
-            logits, nrows, V, nT, part);
-    });
+    return launch("argmax_rows", sv::argmax_rows_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(sv::kBlock), stream, logits, nrows, V, nT, part);
 }
 
 sv_status argmax_rows(sv_dtype dt, bool vec, const void* logits, int64_t nrows, int V, int nT, Partial* part,
@@ -215,18 +232,20 @@ sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt, const int32_t* draft
     const ChainLayout L = chain_layout(B, k, V, dt);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK) return st;
     const int nT = static_cast<int>(tiles_per_row(V, dt));
+    const int nchunk = static_cast<int>(final_chunks(V, dt));
+    if (static_cast<int64_t>(B) * nchunk > kMaxGrid) return SV_ERR_UNSUPPORTED;
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits) &&
                      (k == 0 || aligned16(draft_logits));
     char* ws = static_cast<char*>(workspace);
     if (dt == SV_BF16)
         return vec ? run_chain<SV_BF16, true>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
-                                              uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream)
+                                              uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream)
                    : run_chain<SV_BF16, false>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
-                                               uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream);
+                                               uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream);
     return vec ? run_chain<SV_F32, true>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
-                                         uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream)
+                                         uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream)
                : run_chain<SV_F32, false>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
-                                          uniforms, accepted_len, emitted, accept_prob, ws, L, nT, stream);
+                                          uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream);
 }
 
 sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* target_logits,
@@ -245,10 +264,8 @@ sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draf
     auto* part = static_cast<Partial*>(workspace);
     if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * (k + 1), V, nT, part, stream)) != SV_OK)
         return st;
-    return timed_launch("greedy_finalize", stream, [&] {
-        sv::greedy_finalize_kernel<<<dim3(B), dim3(sv::kWave), 0, stream>>>(draft_tokens, k, nT, part,
-                                                                            accepted_len, emitted);
-    });
+    return launch("greedy_finalize", sv::greedy_finalize_kernel, dim3(B), dim3(sv::kWave), stream, draft_tokens, k,
+                  nT, part, accepted_len, emitted);
 }
 
 sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_tokens, const int32_t* parent,
@@ -270,10 +287,8 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
     if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) != SV_OK)
         return st;
     const int threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
-    return timed_launch("tree_finalize", stream, [&] {
-        sv::tree_finalize_kernel<<<dim3(B), dim3(threads), 0, stream>>>(
-            node_tokens, parent, parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
-    });
+    return launch("tree_finalize", sv::tree_finalize_kernel, dim3(B), dim3(threads), stream, node_tokens, parent,
+                  parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
 }
 
 sv_status sv_profile_begin(int max_launches) {

@@ -65,7 +65,7 @@ __device__ __forceinline__ Partial tile_softmax(const void* base, int64_t row_el
                                                 float c_hi, float c_lo) {
     constexpr int NE = U * Elem<DT>::per_vec;
     float v[NE];
-    load_tile<DT, VEC, U, FULL>(base, row_elem, V, tile, lane_id(), v);
+    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane_id(), v);
     float mx = v[0];
 #pragma unroll
     for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
@@ -85,7 +85,7 @@ __device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem
     constexpr int NE = U * VE;
     const int lane = lane_id();
     float v[NE];
-    load_tile<DT, VEC, U, FULL>(base, row_elem, V, tile, lane, v);
+    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane, v);
     ArgMax a{-__builtin_inff(), kNoIndex};
     const int64_t v0 = tile * (64 * U) + lane;
 #pragma unroll
@@ -118,12 +118,29 @@ __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_
     return tile_argmax<DT, VEC, U, false>(base, row_elem, V, tile);
 }
 
+// Partials are read kBatch at a time so that their loads are in flight
+// together rather than one round trip each.
+constexpr int kBatch = 8;
+
 // Combine the nT softmax partials of one row: R = max r_t, S = sum s_t 2^(r_t - R).
+// Single pass: when a larger reference appears the running sum is rescaled by
+// a power of two, which is exact, so the result equals the two-pass sum.
 __device__ inline void combine_softmax(const Partial* p, int nT, int& R, double& S) {
     int r = p[0].i;
-    for (int t = 1; t < nT; ++t) r = max(r, p[t].i);
-    double s = 0.0;
-    for (int t = 0; t < nT; ++t) s += ldexp(static_cast<double>(p[t].f), p[t].i - r);
+    double s = static_cast<double>(p[0].f);
+    for (int t0 = 1; t0 < nT; t0 += kBatch) {
+        Partial q[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) q[j] = (t0 + j < nT) ? p[t0 + j] : Partial{0.f, r};
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (q[j].i > r) {
+                s = ldexp(s, r - q[j].i);
+                r = q[j].i;
+            }
+            s += ldexp(static_cast<double>(q[j].f), q[j].i - r);
+        }
+    }
     R = r;
     S = s;
 }
@@ -131,7 +148,13 @@ __device__ inline void combine_softmax(const Partial* p, int nT, int& R, double&
 // Combine the nT argmax partials of one row (one lane, sequential).
 __device__ inline ArgMax combine_argmax(const Partial* p, int nT) {
     ArgMax a{p[0].f, p[0].i};
-    for (int t = 1; t < nT; ++t) a = better(a, ArgMax{p[t].f, p[t].i});
+    for (int t0 = 1; t0 < nT; t0 += kBatch) {
+        Partial q[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) q[j] = (t0 + j < nT) ? p[t0 + j] : Partial{-__builtin_inff(), kNoIndex};
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) a = better(a, ArgMax{q[j].f, q[j].i});
+    }
     return a;
 }
 
@@ -142,6 +165,72 @@ __device__ inline ArgMax wave_combine_argmax(const Partial* p, int nT) {
     return wave_argmax(a);
 }
 
+// Softmax partial merge: (r1, s1) + (r2, s2) over the larger reference.  The
+// rescaling is by powers of two (exact) and the one rounded addition is
+// commutative, so both lanes of a shuffle pair obtain identical bits.
+constexpr int kNoRef = -(1 << 30);
+
+__device__ __forceinline__ void merge_softmax(int& r, double& s, int r2, double s2) {
+    const int R = max(r, r2);
+    s = ldexp(s, r - R) + ldexp(s2, r2 - R);
+    r = R;
+}
+
+// The rows of one sequence are combined by groups of G lanes (G a power of
+// two): lane l works on row rho0 + l / G and reads that row's partials
+// t = l % G + j G.  group_load issues the first kBatch of them (so the loads
+// can be in flight before the caller knows how to combine them), and
+// group_reduce merges them, reads any further ones and then merges across
+// the group with a butterfly.
+__device__ __forceinline__ void group_load(const Partial* p, int nT, int G, bool valid, Partial* q) {
+    const int sl = lane_id() & (G - 1);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const int t = sl + j * G;
+        q[j] = (valid && t < nT) ? p[t] : Partial{0.f, 0};
+    }
+}
+
+template <bool SOFTMAX>
+__device__ __forceinline__ void group_reduce(const Partial* p, int nT, int G, bool valid, const Partial* q, int& r,
+                                             double& s, ArgMax& am) {
+    const int sl = lane_id() & (G - 1);
+    r = kNoRef;
+    s = 0.0;
+    am = ArgMax{-__builtin_inff(), kNoIndex};
+    auto merge = [&](const Partial& x) {
+        if constexpr (SOFTMAX)
+            merge_softmax(r, s, x.i, static_cast<double>(x.f));
+        else
+            am = better(am, ArgMax{x.f, x.i});
+    };
+    if (valid) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (sl + j * G < nT) merge(q[j]);
+        for (int t0 = sl + kBatch * G; t0 < nT; t0 += kBatch * G) {
+            Partial qq[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int t = t0 + j * G;
+                qq[j] = t < nT ? p[t] : Partial{0.f, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (t0 + j * G < nT) merge(qq[j]);
+        }
+    }
+    for (int m = G >> 1; m >= 1; m >>= 1) {
+        if constexpr (SOFTMAX) {
+            const int r2 = __shfl_xor(r, m, kWave);
+            const double s2 = __shfl_xor(s, m, kWave);
+            merge_softmax(r, s, r2, s2);
+        } else {
+            am = better(am, ArgMax{__shfl_xor(am.val, m, kWave), __shfl_xor(am.idx, m, kWave)});
+        }
+    }
+}
+
 __device__ __forceinline__ int64_t global_wave() {
     return static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
 }
@@ -150,13 +239,17 @@ __device__ __forceinline__ int64_t global_wave() {
 
 // Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
 // rows (b, i).  Draft rows of temperature-0 sequences are not needed (the
-// one-hot target decides alone) and are skipped.
+// one-hot target decides alone) and are skipped.  The wave streaming tile 0
+// of a sampled row also reads the row's logit at its draft token into
+// gathered[r], so that the acceptance needs no dependent gather.
 template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __restrict__ target,
                                                                 const void* __restrict__ draft,
                                                                 const float* __restrict__ temperature,
+                                                                const int32_t* __restrict__ tokens,
                                                                 int B, int k, int V, int nT,
-                                                                Partial* __restrict__ part) {
+                                                                Partial* __restrict__ part,
+                                                                float* __restrict__ gathered) {
     const int64_t gw = global_wave();
     const int64_t nbk = static_cast<int64_t>(B) * k;
     if (gw >= 2 * nbk * nT) return;
@@ -170,6 +263,11 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
     const int64_t row_elem = (is_target ? (b * (k + 1) + (rr - b * k)) : rr) * static_cast<int64_t>(V);
     Partial p;
     if (T > 0.f) {
+        if (tile == 0) {
+            const int x = tokens[rr];  // draft token scored by this row (rr = b * k + position)
+            if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
+                gathered[r] = load_elem<DT>(base, row_elem + x);
+        }
         float c_hi, c_lo;
         temperature_scale(T, c_hi, c_lo);
         p = tile_softmax_any<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
@@ -181,75 +279,125 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
     if (lane_id() == 0) part[r * nT + tile] = p;
 }
 
-// ---------------------------------------------------------------- chain: accept ---
+// ---------------------------------------------------------------- chain: acceptance ---
 
+// Acceptance of sequence b, computed by one wave (the first of its block):
+// the row statistics from the streaming partials (G lanes per row, one
+// round trip), the 2k logits at the draft tokens, tau_i in the log domain,
+// the first rejection by ballot.  Writes the final draw's descriptor into
+// *out and, when `publish`, accepted_len, the accepted prefix of emitted
+// (the rest -1; the final token is written later) and accept_prob.
 template <int DT>
-__global__ __launch_bounds__(kWave) void chain_accept_kernel(
-    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
-    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
-    const Partial* __restrict__ part, SeqInfo* __restrict__ info, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ emitted, float* __restrict__ accept_prob) {
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const float T = temperature[b];
+__device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ tokens,
+                                                const float* __restrict__ temperature,
+                                                const float* __restrict__ uniforms, int B, int k, int V, int nT,
+                                                const Partial* __restrict__ part, const float* __restrict__ gathered,
+                                                int64_t b, bool publish, int32_t* __restrict__ accepted_len,
+                                                int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+                                                int* s_r, double* s_s, SeqInfo* out) {
+    const int lane = lane_id();
     const int64_t nbk = static_cast<int64_t>(B) * k;
+    // every load first: none of them depends on another
+    const int rows = 2 * k;  // target rows 0..k-1, then draft rows
+    int G = kWave;
+    while (G > 1 && G * rows > kWave) G >>= 1;
+    const int per_pass = kWave / G;
+    auto row_of = [&](int rho) -> int64_t { return rho < k ? b * k + rho : nbk + b * k + (rho - k); };
+    Partial q[kBatch];
+    const int rho_first = lane / G;
+    group_load(part + (rho_first < rows ? row_of(rho_first) : 0) * nT, nT, G, rho_first < rows, q);
+    const float T = temperature[b];
+    const float uk = uniforms[b * (k + 1) + k];
+    int x = 0;
+    float ui = 0.f, lt = 0.f, ld = 0.f;
+    if (lane < k) {
+        x = tokens[b * k + lane];
+        ui = uniforms[b * (k + 1) + lane];
+        lt = gathered[b * k + lane];
+        ld = gathered[nbk + b * k + lane];
+    }
+    const bool sampled = T > 0.f;
+    const bool xok = static_cast<unsigned>(x) < static_cast<unsigned>(V);  // out-of-range ids are rejected
+    // row statistics (at temperature 0 only the target rows' argmax matters)
+    for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
+        const int rho = rho0 + lane / G;
+        const bool valid = rho < rows;
+        const Partial* p = part + (valid ? row_of(rho) : 0) * nT;
+        if (rho0 > 0) group_load(p, nT, G, valid, q);
+        int r;
+        double sum;
+        ArgMax am;
+        if (sampled) {
+            group_reduce<true>(p, nT, G, valid, q, r, sum, am);
+            if (valid && (lane & (G - 1)) == 0) {
+                s_r[rho] = r;
+                s_s[rho] = sum;
+            }
+        } else {
+            group_reduce<false>(p, nT, G, valid, q, r, sum, am);
+            if (valid && (lane & (G - 1)) == 0) s_r[rho] = am.idx;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     bool acc = true;
     double tau = 1.0;
-    int x = 0, g = -1, rt = 0, rd = 0;
+    int g = -1;
+    int rt = 0, rd = 0;
     double st = 1.0, sd = 1.0;
     if (lane < k) {
-        x = tokens[static_cast<int64_t>(b) * k + lane];
-        const Partial* pt = part + (static_cast<int64_t>(b) * k + lane) * nT;
-        if (static_cast<unsigned>(x) >= static_cast<unsigned>(V)) {
-            // a token id outside the vocabulary is never gathered: it is rejected
+        if (!sampled) g = s_r[lane];
+        if (!xok) {
             acc = false;
             tau = 0.0;
-        } else if (T > 0.f) {
-            const Partial* pd = part + (nbk + static_cast<int64_t>(b) * k + lane) * nT;
-            combine_softmax(pt, nT, rt, st);
-            combine_softmax(pd, nT, rd, sd);
+        } else if (sampled) {
+            rt = s_r[lane];
+            st = s_s[lane];
+            rd = s_r[k + lane];
+            sd = s_s[k + lane];
             const double c = kLog2e / static_cast<double>(T);
-            const double lt = load_elem<DT>(target, (static_cast<int64_t>(b) * (k + 1) + lane) * V + x);
-            const double ld = load_elem<DT>(draft, (static_cast<int64_t>(b) * k + lane) * V + x);
-            // log2 p - log2 q with log2 p = l c - R - log2 S (same for q)
-            const double l2ratio = (lt * c - rt - log2(st)) - (ld * c - rd - log2(sd));
+            // log2 p - log2 q with log2 p = l c - R - log2 S (the same for q)
+            const double l2ratio = (static_cast<double>(lt) * c - rt - log2(st)) -
+                                   (static_cast<double>(ld) * c - rd - log2(sd));
             tau = exp2(fmin(0.0, l2ratio));
-            acc = static_cast<double>(uniforms[static_cast<int64_t>(b) * (k + 1) + lane]) < tau;
+            acc = static_cast<double>(ui) < tau;
         } else {
-            g = combine_argmax(pt, nT).idx;
             acc = (x == g);
             tau = acc ? 1.0 : 0.0;
         }
     }
     int a = first_lane(lane < k && !acc);
     if (a < 0) a = k;
-    if (accept_prob != nullptr && lane < k) accept_prob[static_cast<int64_t>(b) * k + lane] = static_cast<float>(tau);
-    int32_t* out = emitted + static_cast<int64_t>(b) * (k + 1);
-    for (int j = lane; j <= k; j += kWave) out[j] = j < a ? tokens[static_cast<int64_t>(b) * k + j] : -1;
+    int32_t* em = emitted + b * (k + 1);
+    if (publish) {
+        if (accept_prob != nullptr && lane < k) accept_prob[b * k + lane] = static_cast<float>(tau);
+        for (int j = lane; j <= k; j += kWave) em[j] = j < a ? tokens[b * k + j] : -1;
+    }
     if (lane == (a < k ? a : 0)) {
-        SeqInfo s{};
-        s.a = a;
-        temperature_scale(T > 0.f ? T : 1.f, s.c_hi, s.c_lo);
-        s.u = uniforms[static_cast<int64_t>(b) * (k + 1) + k];
-        if (!(T > 0.f)) {
+        SeqInfo si{};
+        si.a = a;
+        temperature_scale(sampled ? T : 1.f, si.c_hi, si.c_lo);
+        si.u = uk;
+        if (!sampled) {
             if (a < k) {
-                out[a] = g;
-                s.mode = kFinalDone;
+                if (publish) em[a] = g;
+                si.mode = kFinalDone;
             } else {
-                s.mode = kFinalArgmax;
+                si.mode = kFinalArgmax;
             }
         } else if (a < k) {
-            s.mode = kFinalResidual;
-            s.rt = static_cast<float>(rt);
-            s.inv_st = static_cast<float>(1.0 / st);
-            s.rd = static_cast<float>(rd);
-            s.inv_sd = static_cast<float>(1.0 / sd);
+            si.mode = kFinalResidual;
+            si.rt = static_cast<float>(rt);
+            si.inv_st = static_cast<float>(1.0 / st);
+            si.rd = static_cast<float>(rd);
+            si.inv_sd = static_cast<float>(1.0 / sd);
         } else {
-            s.mode = kFinalBonus;
+            si.mode = kFinalBonus;
         }
-        info[b] = s;
+        *out = si;
     }
-    if (lane == 0) accepted_len[b] = a;
+    if (publish && lane == 0) accepted_len[b] = a;
 }
 
 // ---------------------------------------------------------------- chain: final draw ---
@@ -271,69 +419,6 @@ template <int NE, bool FULL>
 __device__ __forceinline__ void bonus_weights(const float* v, const SeqInfo& s, float ref, float* w) {
 #pragma unroll
     for (int j = 0; j < NE; ++j) w[j] = exp_term<FULL>(v[j], s.c_hi, s.c_lo, ref);
-}
-
-// One tile of the final draw's weights: segment masses and the tile's
-// reference exponent (0 for the residual, whose weights are absolute).
-template <int DT, bool VEC, int U, bool FULL>
-__device__ __forceinline__ void final_part_tile(const void* draft, const void* target, int64_t trow, int64_t drow,
-                                                int V, int64_t tile, const SeqInfo& s, float* seg, Partial* ti) {
-    constexpr int VE = Elem<DT>::per_vec;
-    constexpr int NE = U * VE;
-    const int lane = lane_id();
-    float w[NE];
-    float ref = 0.f;
-    if (s.mode == kFinalResidual) {
-        float vt[NE], vd[NE];
-        load_tile<DT, VEC, U, FULL>(target, trow, V, tile, lane, vt);
-        load_tile<DT, VEC, U, FULL>(draft, drow, V, tile, lane, vd);
-        residual_weights<NE, FULL>(vt, vd, s, w);
-    } else {
-        float v[NE];
-        load_tile<DT, VEC, U, FULL>(target, trow, V, tile, lane, v);
-        float mx = v[0];
-#pragma unroll
-        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
-        ref = ceilf(wave_max(mx) * s.c_hi);
-        bonus_weights<NE, FULL>(v, s, ref, w);
-    }
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-        const float m = wave_sum(pairwise_sum<VE>(w + i * VE));
-        if (lane == 0) seg[i] = m;
-    }
-    if (lane == 0) *ti = Partial{0.f, static_cast<int>(ref)};
-}
-
-// Partial pass of the final draw: one wave per (sequence, tile) of the row(s)
-// the draw needs.  Writes every segment's mass (segment = the 64 vectors of
-// one load instruction) and the tile's reference exponent; at temperature 0
-// it writes the tile's argmax instead.
-template <int DT, bool VEC, int U>
-__global__ __launch_bounds__(kBlock) void chain_final_part_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nT,
-    const SeqInfo* __restrict__ info, float* __restrict__ segmass, Partial* __restrict__ tileinfo) {
-    constexpr int VE = Elem<DT>::per_vec;
-    const int64_t gw = global_wave();
-    if (gw >= static_cast<int64_t>(B) * nT) return;
-    const int64_t b = gw / nT;
-    const int64_t tile = gw - b * nT;
-    const SeqInfo s = info[b];
-    if (s.mode == kFinalDone) return;
-    const int lane = lane_id();
-    const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
-    if (s.mode == kFinalArgmax) {
-        const ArgMax a = tile_argmax_any<DT, VEC, U>(target, trow, V, tile);
-        if (lane == 0) tileinfo[b * nT + tile] = Partial{a.val, a.idx};
-        return;
-    }
-    const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
-    float* seg = segmass + (b * nT + tile) * U;
-    Partial* ti = tileinfo + b * nT + tile;
-    if (tile_is_full<VEC, U>(tile, V, VE))
-        final_part_tile<DT, VEC, U, VEC>(draft, target, trow, drow, V, tile, s, seg, ti);
-    else
-        final_part_tile<DT, VEC, U, false>(draft, target, trow, drow, V, tile, s, seg, ti);
 }
 
 // Weights of segment `seg` (one vector per lane) in the tile's scale.
@@ -405,9 +490,102 @@ __device__ __forceinline__ int last_positive_in_segment(const float* w, int64_t 
     return static_cast<int>((seg * 64 + fl) * VE + e);
 }
 
-// Slow path, one wave: inverse CDF of the target row's own distribution, two
-// sequential sweeps over all segments.  Used only when the residual of a
-// rejection has no mass at all (the draft and target rows agree to rounding).
+// The final draw of sequence b is spread over `nchunk` workgroups, each
+// owning kSegPerChunk consecutive segments (a segment is the 64 vectors of
+// one wave load).  Every workgroup recomputes its sequence's acceptance (a
+// few KB of partials, cheaper than a separate launch), then streams its
+// chunk of the row(s) the draw needs and writes each segment's mass and
+// reference exponent -- or, at temperature 0, the chunk's argmax.  Chunk 0
+// also writes the acceptance outputs and the draw's descriptor.
+constexpr int kFinBlock = 256;
+constexpr int kFinWaves = kFinBlock / kWave;
+constexpr int kFinU = 4;  // segments per wave
+constexpr int kSegPerChunk = kFinWaves * kFinU;
+
+template <int DT, bool VEC, bool FULL>
+__device__ __forceinline__ void final_tile(const void* draft, const void* target, int64_t trow, int64_t drow,
+                                           int V, int64_t tile, int64_t nseg, const SeqInfo& si, int mode,
+                                           Partial* __restrict__ seg_out, ArgMax& best) {
+    constexpr int VE = Elem<DT>::per_vec;
+    constexpr int NE = kFinU * VE;
+    const int lane = lane_id();
+    if (mode == kFinalArgmax) {
+        best = better(best, tile_argmax<DT, VEC, kFinU, FULL>(target, trow, V, tile));
+        return;
+    }
+    float w[NE];  // the target's logits, then (in place) the weights
+    float ref = 0.f;
+    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
+    if (mode == kFinalResidual) {
+        float vd[NE];
+        load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
+        residual_weights<NE, FULL>(w, vd, si, w);
+    } else {
+        float mx = w[0];
+#pragma unroll
+        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, w[j]);
+        // a reference over the whole tile (which always holds an element of the row)
+        ref = ceilf(wave_max(mx) * si.c_hi);
+        bonus_weights<NE, FULL>(w, si, ref, w);
+    }
+#pragma unroll
+    for (int i = 0; i < kFinU; ++i) {
+        const float m = wave_sum(pairwise_sum<VE>(w + i * VE));
+        const int64_t g = tile * kFinU + i;
+        if (lane == 0 && g < nseg) seg_out[g] = Partial{m, static_cast<int>(ref)};
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
+    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
+    const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
+    int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ emitted, float* __restrict__ accept_prob, SeqInfo* __restrict__ info,
+    Partial* __restrict__ segs, Partial* __restrict__ chunkarg) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ int s_r[2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[2 * SV_MAX_DRAFTS];
+    __shared__ SeqInfo s_info;
+    __shared__ ArgMax s_arg[kFinWaves];
+    const int64_t b = blockIdx.x / nchunk;
+    const int c = static_cast<int>(blockIdx.x - b * nchunk);
+    if (threadIdx.x < kWave)
+        accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, c == 0, accepted_len,
+                            emitted, accept_prob, s_r, s_s, &s_info);
+    __syncthreads();
+    const SeqInfo si = s_info;
+    if (c == 0 && threadIdx.x == 0) info[b] = si;
+    if (si.mode == kFinalDone) return;
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
+    const int wave = threadIdx.x / kWave;
+    const int64_t tile = static_cast<int64_t>(c) * kFinWaves + wave;
+    ArgMax best{-__builtin_inff(), kNoIndex};
+    if (tile * kFinU < nseg) {
+        Partial* seg_out = segs + b * nseg;
+        if (tile_is_full<VEC, kFinU>(tile, V, VE))
+            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+        else
+            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+    }
+    if (si.mode == kFinalArgmax) {
+        if (lane_id() == 0) s_arg[wave] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            ArgMax r = s_arg[0];
+            for (int w = 1; w < kFinWaves; ++w) r = better(r, s_arg[w]);
+            chunkarg[b * nchunk + c] = Partial{r.val, r.idx};
+        }
+    }
+}
+
+// Slow path of the draw, one wave: inverse CDF of the target row's own
+// distribution with two sequential sweeps over its segments.  Used only when
+// the residual of a rejection has no mass at all (draft and target rows
+// agree to rounding).
 template <int DT, bool VEC>
 __device__ int pick_from_target_row(const void* target, int64_t trow, int V, int64_t nseg, const SeqInfo& s) {
     constexpr int VE = Elem<DT>::per_vec;
@@ -415,20 +593,14 @@ __device__ int pick_from_target_row(const void* target, int64_t trow, int V, int
     double W = 0.0;
     for (int64_t g = 0; g < nseg; ++g) {
         segment_weights<DT, VEC>(nullptr, target, trow, 0, V, g, s, false, s.rt, w);
-        float m = 0.f;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) m += w[e];
-        W += static_cast<double>(wave_sum(m));
+        W += static_cast<double>(wave_sum(pairwise_sum<VE>(w)));
     }
     const double target_mass = static_cast<double>(s.u) * W;
     double P = 0.0;
     int last = -1;
     for (int64_t g = 0; g < nseg; ++g) {
         segment_weights<DT, VEC>(nullptr, target, trow, 0, V, g, s, false, s.rt, w);
-        float m = 0.f;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) m += w[e];
-        const double mass = static_cast<double>(wave_sum(m));
+        const double mass = static_cast<double>(wave_sum(pairwise_sum<VE>(w)));
         if (mass > 0.0) {
             const int y = pick_in_segment<DT>(w, g, P, 1.0, target_mass);
             if (y >= 0) return y;
@@ -439,55 +611,92 @@ __device__ int pick_from_target_row(const void* target, int64_t trow, int V, int
     return last;
 }
 
-// Select pass of the final draw: one wave per sequence.
-template <int DT, bool VEC, int U>
+// Select pass of the final draw: one wave per sequence.  Lane l owns a
+// contiguous run of segments; a wave prefix over the run totals gives every
+// segment's starting mass, the segment holding u * W is found with a ballot,
+// and only that segment is read again to find the token.  The descriptor and
+// the lane's first kSegRun segments are loaded together.
+constexpr int kSegRun = 8;
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nT,
-    const SeqInfo* __restrict__ info, const float* __restrict__ segmass, const Partial* __restrict__ tileinfo,
+    const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nchunk,
+    const SeqInfo* __restrict__ info, const Partial* __restrict__ segs, const Partial* __restrict__ chunkarg,
     int32_t* __restrict__ emitted) {
     constexpr int VE = Elem<DT>::per_vec;
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x;
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const Partial* sg = segs + b * nseg;
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t g0 = min<int64_t>(nseg, lane * per), g1 = min<int64_t>(nseg, g0 + per);
+    Partial first[kSegRun];
+#pragma unroll
+    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : Partial{0.f, kNoRef};
     const SeqInfo s = info[b];
     if (s.mode == kFinalDone) return;
-    const Partial* ti = tileinfo + b * nT;
     int y;
     if (s.mode == kFinalArgmax) {
-        y = wave_combine_argmax(ti, nT).idx;
+        y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;
     } else {
         const bool residual = s.mode == kFinalResidual;
-        const int64_t nseg = static_cast<int64_t>(nT) * U;
-        const float* sm = segmass + b * nseg;
         const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
         const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
-        // global reference exponent (0 for the residual, whose masses are absolute)
-        int R = -0x7fffffff;
-        for (int t = lane; t < nT; t += kWave) R = max(R, ti[t].i);
-        R = wave_max(R);
-        // lane owns a contiguous run of segments; masses in the global scale
-        const int64_t per = (nseg + kWave - 1) / kWave;
-        const int64_t g0 = min<int64_t>(nseg, lane * per), g1 = min<int64_t>(nseg, g0 + per);
+        const int64_t nwin = (per + kSegRun - 1) / kSegRun;
+        // segment g of this lane's window w
+        auto seg_at = [&](int64_t w, int j) -> Partial {
+            const int64_t g = g0 + w * kSegRun + j;
+            return w == 0 ? first[j] : (g < g1 ? sg[g] : Partial{0.f, kNoRef});
+        };
+        // global reference exponent (residual masses are absolute: reference 0)
+        int R = 0;
+        if (!residual) {
+            R = kNoRef;
+            for (int64_t w = 0; w < nwin; ++w)
+#pragma unroll
+                for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).i);
+            R = wave_max(R);
+        }
+        // masses of this lane's window w in the global scale
+        auto window = [&](int64_t w, double* mg) {
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j) {
+                const Partial q = seg_at(w, j);
+                const bool in = g0 + w * kSegRun + j < g1;
+                mg[j] = !in ? 0.0 : residual ? static_cast<double>(q.f) : ldexp(static_cast<double>(q.f), q.i - R);
+            }
+        };
         double tot = 0.0;
-        for (int64_t g = g0; g < g1; ++g) tot += ldexp(static_cast<double>(sm[g]), ti[g / U].i - R);
+        for (int64_t w = 0; w < nwin; ++w) {
+            double mg[kSegRun];
+            window(w, mg);
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j) tot += mg[j];
+        }
         const double incl = wave_inclusive_scan(tot);
         const double W = __shfl(incl, kWave - 1, kWave);
-        double P = __shfl_up(incl, 1, kWave);
-        if (lane == 0) P = 0.0;
+        const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+        double P = lane == 0 ? 0.0 : excl;
         if (!(W > 0.0)) {
             y = residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0;
         } else {
             const double target_mass = static_cast<double>(s.u) * W;
-            int64_t found = -1;
+            int64_t found = -1, last_pos = -1;
             double Pfound = 0.0;
-            int64_t last_pos = -1;
-            for (int64_t g = g0; g < g1; ++g) {
-                const double m = ldexp(static_cast<double>(sm[g]), ti[g / U].i - R);
-                if (found < 0 && P + m > target_mass) {
-                    found = g;
-                    Pfound = P;
+            for (int64_t w = 0; w < nwin; ++w) {
+                double mg[kSegRun];
+                window(w, mg);
+#pragma unroll
+                for (int j = 0; j < kSegRun; ++j) {
+                    const int64_t g = g0 + w * kSegRun + j;
+                    if (g >= g1) break;
+                    if (found < 0 && P + mg[j] > target_mass) {
+                        found = g;
+                        Pfound = P;
+                    }
+                    if (mg[j] > 0.0) last_pos = g;
+                    P += mg[j];
                 }
-                if (m > 0.0) last_pos = g;
-                P += m;
             }
             int fl = first_lane(found >= 0);
             int64_t seg;
@@ -504,10 +713,10 @@ __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
                 Ps = 0.0;
                 fallback = true;
             }
-            const float ref = static_cast<float>(ti[seg / U].i);
-            const double scale = ldexp(1.0, ti[seg / U].i - R);
+            const int tref = residual ? 0 : sg[seg].i;
+            const double scale = ldexp(1.0, tref - R);
             float w[VE];
-            segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, ref, w);
+            segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, static_cast<float>(tref), w);
             y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, scale, target_mass);
             if (y < 0) y = last_positive_in_segment<DT>(w, seg);
         }

@@ -79,7 +79,7 @@ typedef enum {
  * tree nodes; V <= SV_MAX_VOCAB. */
 #define SV_MAX_DRAFTS 64
 #define SV_MAX_TREE_NODES 1024
-#define SV_MAX_VOCAB (1 << 30)
+#define SV_MAX_VOCAB (1 << 20)
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int sv_version(void);

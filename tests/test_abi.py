@@ -105,9 +105,10 @@ def test_chain_rejects_bad_arguments_on_the_host(lib):
 def test_chain_empty_batch_and_k0_pointer_rules(lib):
     # B == 0: nothing to do, no pointer is looked at
     assert _chain(lib, B=0, target=None, temp=None, u=None, acc=None, em=None, ws=None, ws_bytes=0) == OK
-    # k == 0 needs neither draft tokens nor draft logits: validation passes those checks
-    # and stops at the (deliberately) too-small workspace
-    assert _chain(lib, k=0, tokens=None, draft=None, ws_bytes=1) == WS_SMALL
+    # k == 0 still needs every other pointer (a k == 0 call that passes validation
+    # would launch, so only failing calls are made here; the GPU tests run k == 0)
+    assert _chain(lib, k=0, tokens=None, draft=None, em=None) == INVALID
+    assert _chain(lib, k=0, tokens=None, draft=None, temp=None) == INVALID
 
 
 def test_greedy_rejects_bad_arguments_on_the_host(lib):
