@@ -16,10 +16,11 @@
  *     kept and one more target token is appended;
  *   - section "MTP": logits row i predicts token i+1, hence target row j
  *     scores draft j and row k follows the last draft;
- *   - sections "Inference with speculative decoding" and "MTP schedule": the
- *     accepted lengths are what forces a device-to-host synchronisation, and a
- *     device kernel can place the next tokens without one -- so every result
- *     here stays in device memory and no call synchronises the host.
+ *   - sections "Inference with speculative decoding" and "MTP Schedule for a
+ *     Single Token": the accepted lengths are what forces a device-to-host
+ *     synchronisation, and a device kernel can place the next tokens without
+ *     one -- so every result here stays in device memory and no call
+ *     synchronises the host.
  * The acceptance rule (keep draft x with probability min(1, p(x)/q(x)); at
  * the first rejection draw from max(0, p - q) renormalised) is the
  * speculative sampling of Leviathan et al., "Fast Inference from
