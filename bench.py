@@ -103,7 +103,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -148,9 +148,10 @@ def main():
             t = dev[i % copies]
             svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
                              t["uniforms"], workspace=ws, out=out)
-        units = B * k                       # verified draft tokens per step
-        dominant = "chain_rowstats"
-        dominant_bytes = 2 * B * k * V * es  # every draft row and target rows 0..k-1, once
+        units = B * k if k > 0 else B       # verified draft tokens (sampled tokens when k == 0) per step
+        dominant = "chain_rowstats" if k > 0 else "chain_final_part"
+        # every draft row and target rows 0..k-1 once (k == 0: the sampled row)
+        dominant_bytes = 2 * B * k * V * es if k > 0 else B * V * es
     elif kind == "greedy":
         k = inp["k"]
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
@@ -178,6 +179,7 @@ def main():
         dominant = "argmax_rows"
         dominant_bytes = B * N * V * es
 
+    unit = "sampled tokens/s" if kind == "chain" and inp["k"] == 0 else "verified draft tokens/s"
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -233,7 +235,7 @@ def main():
     result = {
         "metric": METRIC if args.config == 2 else f"verified draft tokens/sec ({cfg['name']})",
         "value": units / s_per_step,
-        "unit": "verified draft tokens/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -261,7 +263,7 @@ def main():
 
     if not args.no_cpu:
         reps, el, threads = cpu_baseline(inp, args.cpu_seconds)
-        result["cpu_baseline"] = {"value": units * reps / el, "unit": "verified draft tokens/s", "cores": threads,
+        result["cpu_baseline"] = {"value": units * reps / el, "unit": unit, "cores": threads,
                                   "kind": "oracle",
                                   "sample": f"the full {cfg['name']} batch (B={B}) x {reps} repetitions, {el:.1f} s"}
     print(json.dumps(result), flush=True)

@@ -5,6 +5,7 @@ The Python names mirror the C entry points:
   verify_chain   -> sv_verify_chain   (acceptance test, first rejection, residual / bonus draw)
   verify_greedy  -> sv_verify_greedy  (temperature-0 argmax matching)
   verify_tree    -> sv_verify_tree    (EAGLE-style static tree, greedy)
+  commit_tokens  -> sv_commit_tokens  (append the step's tokens on the device)
 The shared library is loaded on first use; calls raise if it is missing.
 """
 
@@ -13,6 +14,7 @@ from ._binding import (  # noqa: F401
     SV_F32,
     SpecVerifyError,
     chain_workspace_bytes,
+    commit_tokens,
     greedy_workspace_bytes,
     load,
     profile_begin,

@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.sv_verify_greedy.argtypes = [i, i, i, i] + [p] * 5 + [sz, p]
     lib.sv_verify_tree.restype = i
     lib.sv_verify_tree.argtypes = [i, i, i, i, p, p, i, i, p, p, p, p, p, sz, p]
+    lib.sv_commit_tokens.restype = i
+    lib.sv_commit_tokens.argtypes = [i, i, p, p, p, p, i, p, p, p, p]
     lib.sv_profile_begin.restype = i
     lib.sv_profile_begin.argtypes = [i]
     lib.sv_profile_end.restype = i
@@ -204,6 +206,35 @@ def verify_tree(node_tokens, parent, max_depth: int, target_logits, *, accepted_
                             _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError("sv_verify_tree", st)
+    return out
+
+
+def commit_tokens(accepted_len, emitted, seq_len, history=None, *, packed: bool = True, status: bool = True,
+                  stream=None, out=None) -> dict:
+    """Appends each sequence's committed tokens to its history and advances
+    seq_len in place; see ``sv_commit_tokens``.  Returns packed_offsets
+    [B+1], packed [B*width] (only the first packed_offsets[B] are written)
+    and status [B] (or None for those not requested)."""
+    lib = load()
+    B, width = emitted.shape
+    dev = emitted.device
+    _check_dev("accepted_len", accepted_len, torch.int32, (B,))
+    _check_dev("emitted", emitted, torch.int32)
+    _check_dev("seq_len", seq_len, torch.int32, (B,))
+    stride = 0
+    if history is not None:
+        _check_dev("history", history, torch.int32)
+        if history.dim() != 2 or history.shape[0] != B:
+            raise ValueError("history must be [B, capacity]")
+        stride = history.shape[1]
+    if out is None:
+        out = dict(packed_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev) if packed else None,
+                   packed=torch.empty(max(B * width, 1), dtype=torch.int32, device=dev) if packed else None,
+                   status=torch.empty(B, dtype=torch.int32, device=dev) if status else None)
+    st = lib.sv_commit_tokens(B, width, _ptr(accepted_len), _ptr(emitted), _ptr(seq_len), _ptr(history), stride,
+                              _ptr(out["packed_offsets"]), _ptr(out["packed"]), _ptr(out["status"]), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError("sv_commit_tokens", st)
     return out
 
 

@@ -130,7 +130,8 @@ sv_status launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 blo
 template <int DT, bool VEC>
 sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draft, const void* target,
                     const float* temperature, const float* uniforms, int32_t* accepted_len, int32_t* emitted,
-                    float* accept_prob, char* ws, const ChainLayout& L, int nT, int nchunk, hipStream_t stream) {
+                    float* accept_prob, char* ws, const ChainLayout& L, int nT, int nchunk,
+                    hipStream_t stream) {
     auto* part = reinterpret_cast<Partial*>(ws + L.part);
     auto* gathered = reinterpret_cast<float*>(ws + L.gathered);
     auto* info = reinterpret_cast<SeqInfo*>(ws + L.info);
@@ -143,11 +144,10 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                     dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, V, nT, part, gathered);
         if (st != SV_OK) return st;
     }
-    st = launch("chain_final_part", sv::chain_final_part_kernel<DT, VEC>,
-                dim3(static_cast<unsigned>(static_cast<int64_t>(B) * nchunk)), dim3(sv::kFinBlock), stream, tokens,
-                draft, target, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
-                static_cast<const float*>(gathered), nchunk,
-                accepted_len, emitted, accept_prob, info, segs, chunkarg);
+    st = launch("chain_final_part", sv::chain_final_part_kernel<DT, VEC>, dim3(static_cast<unsigned>(static_cast<int64_t>(B) * nchunk)),
+                dim3(sv::kFinBlock), stream, tokens, draft, target, temperature, uniforms, B, k, V, nT,
+                static_cast<const Partial*>(part), static_cast<const float*>(gathered), nchunk, accepted_len,
+                emitted, accept_prob, info, segs, chunkarg);
     if (st != SV_OK) return st;
     return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kWave), stream, draft,
                   target, B, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),
@@ -289,6 +289,18 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
     const int threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
     return launch("tree_finalize", sv::tree_finalize_kernel, dim3(B), dim3(threads), stream, node_tokens, parent,
                   parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
+}
+
+sv_status sv_commit_tokens(int B, int width, const int32_t* accepted_len, const int32_t* emitted, int32_t* seq_len,
+                           int32_t* history, int history_stride, int32_t* packed_offsets, int32_t* packed,
+                           int32_t* status, hipStream_t stream) {
+    if (B < 0 || width < 1 || history_stride < 0) return SV_ERR_INVALID_ARGUMENT;
+    if (B > (1 << 24)) return SV_ERR_UNSUPPORTED;
+    if (B == 0) return SV_OK;
+    if (!accepted_len || !emitted || !seq_len) return SV_ERR_INVALID_ARGUMENT;
+    if (static_cast<int64_t>(B) * width > 0x7fffffff) return SV_ERR_UNSUPPORTED;
+    return launch("commit_tokens", sv::commit_tokens_kernel, dim3(1), dim3(sv::kCommitBlock), stream, B, width,
+                  accepted_len, emitted, seq_len, history, history_stride, packed_offsets, packed, status);
 }
 
 sv_status sv_profile_begin(int max_launches) {

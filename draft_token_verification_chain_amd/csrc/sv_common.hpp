@@ -178,11 +178,51 @@ __device__ __forceinline__ float exp_term(float l, float c_hi, float c_lo, float
 }
 
 // ---------------------------------------------------------------- wave64 reductions ---
+//
+// Reductions of 32-bit values use DPP row operations, which exchange registers
+// without going through the LDS crossbar: quad permutes (lane ^ 1, lane ^ 2),
+// half-row and row mirrors (which pair the groups of 4 and of 8 lanes once
+// their values agree), then row_bcast15 / row_bcast31 to fold the four rows of
+// 16 lanes into lane 63, read back as a wave-uniform value.  The order of the
+// operations is fixed, so results are deterministic.
 
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror
+constexpr int kMirror = 0x140;      // row_mirror
+constexpr int kBcast15 = 0x142;     // row_bcast:15 (rows 1 and 3 enabled below)
+constexpr int kBcast31 = 0x143;     // row_bcast:31 (rows 2 and 3 enabled below)
+}  // namespace dpp
+
+// DPP move of v; lanes of rows outside ROW_MASK receive `identity`.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_move(int identity, int v) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_move(float identity, float v) {
+    return __int_as_float(dpp_move<CTRL, ROW_MASK>(__float_as_int(identity), __float_as_int(v)));
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T dpp_reduce(T v, T identity, Op op) {
+    v = op(v, dpp_move<dpp::kXor1>(identity, v));
+    v = op(v, dpp_move<dpp::kXor2>(identity, v));
+    v = op(v, dpp_move<dpp::kHalfMirror>(identity, v));
+    v = op(v, dpp_move<dpp::kMirror>(identity, v));
+    v = op(v, dpp_move<dpp::kBcast15, 0xa>(identity, v));
+    v = op(v, dpp_move<dpp::kBcast31, 0xc>(identity, v));
+    return v;  // the reduction of all 64 lanes is in lane 63
+}
+
+__device__ __forceinline__ float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
+// Sum of the wave's values, returned to every lane.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-    return x;
+    return lane63(dpp_reduce(x, 0.f, [](float a, float b) { return a + b; }));
 }
 
 __device__ __forceinline__ double wave_sum(double x) {
@@ -192,15 +232,11 @@ __device__ __forceinline__ double wave_sum(double x) {
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-    return x;
+    return lane63(dpp_reduce(x, -__builtin_inff(), [](float a, float b) { return fmaxf(a, b); }));
 }
 
 __device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m, kWave));
-    return x;
+    return lane63(dpp_reduce(x, static_cast<int>(0x80000000), [](int a, int b) { return max(a, b); }));
 }
 
 // (value, index) maximum with ties resolved to the lowest index.
@@ -213,13 +249,21 @@ __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
     return (b.val > a.val || (b.val == a.val && b.idx < a.idx)) ? b : a;
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ ArgMax argmax_step(ArgMax a) {
+    const ArgMax o{dpp_move<CTRL, ROW_MASK>(-__builtin_inff(), a.val), dpp_move<CTRL, ROW_MASK>(kNoIndex, a.idx)};
+    return better(a, o);
+}
+
+// (max, lowest index) over the wave, returned to every lane.
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        ArgMax o{__shfl_xor(a.val, m, kWave), __shfl_xor(a.idx, m, kWave)};
-        a = better(a, o);
-    }
-    return a;
+    a = argmax_step<dpp::kXor1>(a);
+    a = argmax_step<dpp::kXor2>(a);
+    a = argmax_step<dpp::kHalfMirror>(a);
+    a = argmax_step<dpp::kMirror>(a);
+    a = argmax_step<dpp::kBcast15, 0xa>(a);
+    a = argmax_step<dpp::kBcast31, 0xc>(a);
+    return ArgMax{lane63(a.val), lane63(a.idx)};
 }
 
 // Inclusive prefix sum across the wave (Hillis-Steele, fixed order).

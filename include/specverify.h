@@ -175,6 +175,41 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Commit of one verification step on the device (section "MTP Schedule for
+ * a Single Token": after acceptance a kernel places the next tokens, so the
+ * host need not wait for the accepted lengths).
+ *
+ *   B             >= 0 sequences (0: no launch)
+ *   width         >= 1 columns of `emitted` (k+1 for chain and greedy outputs,
+ *                 max_depth+1 for tree outputs)
+ *   accepted_len  int32 [B]         a_b as written by a verify call; a_b < 0 (an invalid
+ *                                   tree) commits nothing
+ *   emitted       int32 [B][width]  the step's tokens; the first a_b + 1 are committed
+ *   seq_len       int32 [B]  in/out tokens already in each sequence's history; grows by
+ *                                   the committed count
+ *   history       int32 [B][history_stride] out  optional (NULL: no history, and no
+ *                                   capacity limit): committed tokens are written at
+ *                                   history[b][seq_len[b] + j], j = 0..a_b
+ *   packed_offsets int32 [B+1] out  optional (NULL): exclusive prefix sum of the committed
+ *                                   counts (where each sequence's new tokens start in a
+ *                                   packed buffer), the total in [B]
+ *   packed        int32 [>= B * width] out  optional (NULL): the committed tokens, packed
+ *                                   in sequence order at packed_offsets
+ *   status        int32 [B]   out  optional (NULL): 0 committed; 1 nothing committed because
+ *                                   a_b + 1 > width, seq_len[b] < 0 or (with a history)
+ *                                   seq_len[b] + a_b + 1 > history_stride; 2 nothing to
+ *                                   commit (a_b < 0)
+ *
+ * The history and packed writes of different sequences never overlap; seq_len
+ * is updated in place, so the call must not be repeated for the same step.
+ * Limits: B <= 2^24.
+ */
+sv_status sv_commit_tokens(int B, int width, const int32_t *accepted_len, const int32_t *emitted,
+                           int32_t *seq_len, int32_t *history, int history_stride,
+                           int32_t *packed_offsets, int32_t *packed, int32_t *status,
+                           hipStream_t stream);
+
+/*
  * Kernel timing, for benchmarks.  Between sv_profile_begin() and
  * sv_profile_end() every entry point records a HIP event pair around each of
  * its kernel launches (host memory for at most max_launches launches is

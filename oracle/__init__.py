@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
             [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 4)
         _lib.svo_row_logz.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
         _lib.svo_row_argmax.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
+        _lib.svo_commit_tokens.argtypes = ([ctypes.c_int] * 2 + [ctypes.c_void_p] * 4 + [ctypes.c_int] +
+                                           [ctypes.c_void_p] * 3)
     return _lib
 
 
@@ -148,3 +150,21 @@ def row_argmax(logits: np.ndarray, dtype: int) -> np.ndarray:
     if lib().svo_row_argmax(rows.shape[0], V, dtype, _ptr(rows), _ptr(out)) != 0:
         raise ValueError("svo_row_argmax failed")
     return out.reshape(logits.shape[:-1])
+
+
+def commit_tokens(accepted_len, emitted, seq_len, history=None) -> dict:
+    """Returns the updated seq_len and history and the packed layout."""
+    acc = _c(accepted_len, np.int32)
+    em = _c(emitted, np.int32)
+    B, width = em.shape
+    sl = np.array(seq_len, dtype=np.int32, copy=True)
+    hist = None if history is None else np.array(history, dtype=np.int32, copy=True)
+    stride = 0 if hist is None else hist.shape[1]
+    offs = np.empty(B + 1, np.int32)
+    packed = np.full(B * width, -7, np.int32)
+    status = np.empty(B, np.int32)
+    rc = lib().svo_commit_tokens(B, width, _ptr(acc), _ptr(em), _ptr(sl), _ptr(hist), stride, _ptr(offs),
+                                 _ptr(packed), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"svo_commit_tokens returned {rc}")
+    return dict(seq_len=sl, history=hist, packed_offsets=offs, packed=packed[:offs[B]], status=status)

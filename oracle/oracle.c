@@ -415,3 +415,46 @@ int svo_row_argmax(int nrows, int V, int dtype, const void *logits, int32_t *out
     for (int r = 0; r < nrows; ++r) out[r] = row_argmax(logits, dtype, (size_t)r * (size_t)V, V);
     return 0;
 }
+
+/*
+ * Commit of one verification step (section "MTP Schedule for a Single
+ * Token": once acceptance is known, the next tokens are placed without the
+ * host).  For each sequence in order: the first a_b + 1 entries of its
+ * emitted row are appended to its history at seq_len[b] and seq_len[b]
+ * grows by that count; packed_offsets[b] is the number of tokens committed
+ * by the sequences before b (the total in [B]) and packed holds the
+ * committed tokens in that order.  status: 0 committed, 1 refused (the row
+ * is too short for a_b + 1 tokens, the length is negative, or the history
+ * would overflow), 2 nothing to commit (a_b < 0).  history may be NULL (no
+ * history and no capacity limit).
+ */
+int svo_commit_tokens(int B, int width, const int32_t *accepted_len, const int32_t *emitted,
+                      int32_t *seq_len, int32_t *history, int history_stride,
+                      int32_t *packed_offsets, int32_t *packed, int32_t *status) {
+    if (B < 0 || width < 1 || history_stride < 0) return 1;
+    if (B == 0) return 0;
+    if (!accepted_len || !emitted || !seq_len) return 1;
+    int total = 0;
+    for (int b = 0; b < B; ++b) {
+        const int a = accepted_len[b];
+        const int len = seq_len[b];
+        int n = 0, st = 0;
+        if (a < 0)
+            st = 2;
+        else if (a + 1 > width || len < 0 || (history && (long long)len + a + 1 > (long long)history_stride))
+            st = 1;
+        else
+            n = a + 1;
+        if (packed_offsets) packed_offsets[b] = total;
+        for (int j = 0; j < n; ++j) {
+            const int32_t tok = emitted[(size_t)b * width + j];
+            if (history) history[(size_t)b * history_stride + len + j] = tok;
+            if (packed) packed[total + j] = tok;
+        }
+        seq_len[b] = len + n;
+        total += n;
+        if (status) status[b] = st;
+    }
+    if (packed_offsets) packed_offsets[B] = total;
+    return 0;
+}

@@ -147,3 +147,17 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(bnd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         bnd.load()
+
+
+def test_commit_rejects_bad_arguments_on_the_host(lib):
+    def c(B=4, width=3, acc=FAKE, em=FAKE, sl=FAKE, hist=FAKE, stride=8):
+        return lib.sv_commit_tokens(B, width, acc, em, sl, hist, stride, None, None, None, None)
+
+    assert c(B=-1) == INVALID
+    assert c(width=0) == INVALID
+    assert c(stride=-1) == INVALID
+    assert c(B=(1 << 24) + 1) == UNSUPPORTED
+    assert c(acc=None) == INVALID
+    assert c(em=None) == INVALID
+    assert c(sl=None) == INVALID
+    assert c(B=0, acc=None, em=None, sl=None, hist=None) == OK

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_common import compare_chain, dev, dev_logits, run_chain, run_greedy, run_tree
+from gpu_common import chain_tensors, compare_chain, dev, dev_logits, run_chain, run_greedy, run_tree
 
 pytestmark = pytest.mark.gpu
 
@@ -266,3 +266,77 @@ def test_gpu_emitted_distribution_chi_square(svl, orc):
         counts = np.bincount(em[sel, j], minlength=16)
         p = special.softmax(t[j].astype(np.float64))
         assert stats.chisquare(counts, p * sel.sum()).pvalue > 1e-4
+
+
+# ------------------------------------------------------------ NEXT rows ---
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("config", [6, 7])
+def test_full_mtp_and_sampling_configs(svl, orc, config, seed):
+    """Single-token MTP verification (k = 1, B = 256, V = 129280) and plain
+    temperature sampling (k = 0, B = 256)."""
+    inp = W.make_inputs(config, seed)
+    _check_chain(svl, orc, inp, f"config{config} seed{seed}")
+
+
+@pytest.mark.parametrize("with_history", [True, False])
+@pytest.mark.parametrize("B", [1, 37, 3000])
+def test_commit_tokens_parity(svl, orc, B, with_history):
+    import torch
+
+    rng = np.random.default_rng(B)
+    width, cap = 5, 64
+    acc = rng.integers(-1, width, B).astype(np.int32)
+    acc[::13] = width  # one more than the row holds: refused
+    em = rng.integers(0, 128256, (B, width)).astype(np.int32)
+    lens = rng.integers(0, cap, B).astype(np.int32)
+    hist = rng.integers(0, 9, (B, cap)).astype(np.int32)
+    ref = orc.commit_tokens(acc, em, lens, hist if with_history else None)
+    sl = dev(lens)
+    h = dev(hist) if with_history else None
+    out = svl.commit_tokens(dev(acc), dev(em), sl, h)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sl.cpu().numpy(), ref["seq_len"])
+    if with_history:
+        np.testing.assert_array_equal(h.cpu().numpy(), ref["history"])
+    offs = out["packed_offsets"].cpu().numpy()
+    np.testing.assert_array_equal(offs, ref["packed_offsets"])
+    np.testing.assert_array_equal(out["packed"].cpu().numpy()[:offs[B]], ref["packed"])
+    np.testing.assert_array_equal(out["status"].cpu().numpy(), ref["status"])
+
+
+def test_verify_then_commit_on_device(svl, orc):
+    """A decode step without host synchronisation: verification, then the commit
+    of its output into per-sequence histories, all on one stream."""
+    import torch
+
+    inp = W.make_inputs(2, 3)
+    B, k = inp["B"], inp["k"]
+    t = chain_tensors(inp)
+    lens = np.arange(B, dtype=np.int32) % 50
+    hist = np.zeros((B, 64), np.int32)
+    sl, h = dev(lens), dev(hist)
+    out = svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                           t["uniforms"])
+    com = svl.commit_tokens(out["accepted_len"], out["emitted"], sl, h)
+    torch.cuda.synchronize()
+    ref_v = orc.verify_chain(inp)
+    got_v = dict(accepted_len=out["accepted_len"].cpu().numpy(), emitted=out["emitted"].cpu().numpy(),
+                 accept_prob=out["accept_prob"].cpu().numpy())
+    compare_chain(inp, got_v, ref_v, "verify+commit")
+    ref_c = orc.commit_tokens(got_v["accepted_len"], got_v["emitted"], lens, hist)
+    np.testing.assert_array_equal(sl.cpu().numpy(), ref_c["seq_len"])
+    np.testing.assert_array_equal(h.cpu().numpy(), ref_c["history"])
+    np.testing.assert_array_equal(com["packed"].cpu().numpy()[:ref_c["packed_offsets"][B]], ref_c["packed"])
+
+
+@pytest.mark.parametrize("shape", [(600, 2, 9000, W.BF16), (700, 1, 9000, W.F32), (700, 1, 4097, W.BF16),
+                                   (1200, 0, 5000, W.BF16)],
+                         ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_pipelined_final_draw(svl, orc, shape):
+    """Batches large enough that each final-draw wave handles several tiles
+    (pipelined loads), with ragged row ends and an unaligned row length."""
+    B, k, V, dt = shape
+    inp = W.chain_inputs(B, k, V, dt, 11, target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0),
+                         temperature=(0.3, 1.3))
+    _check_chain(svl, orc, inp, f"pipelined B{B}k{k}V{V}dt{dt}")

@@ -424,3 +424,35 @@ def test_tree_invalid_parent_or_depth_marks_sequence(orc):
     r = orc.verify_tree(inp)
     assert r["accepted_len"].tolist() == [-1, -1]
     assert (r["emitted"] == -1).all() and (r["accepted_nodes"] == -1).all()
+
+
+# ------------------------------------------------------------ commit ---
+
+def test_commit_matches_list_semantics(orc):
+    """Appending each sequence's a+1 committed tokens, written as list
+    concatenation, against the oracle's index arithmetic."""
+    rng = np.random.default_rng(12)
+    B, width, cap = 300, 6, 40
+    acc = rng.integers(-1, width, B).astype(np.int32)
+    acc[::17] = width + 2  # more tokens than the row holds: refused
+    em = rng.integers(0, 1000, (B, width)).astype(np.int32)
+    lens = rng.integers(0, cap, B).astype(np.int32)
+    hist = rng.integers(0, 1000, (B, cap)).astype(np.int32)
+    r = orc.commit_tokens(acc, em, lens, hist)
+    packed, offs = [], [0]
+    for b in range(B):
+        old = list(hist[b, :lens[b]])
+        a = int(acc[b])
+        ok = 0 <= a < width and lens[b] + a + 1 <= cap
+        new = list(em[b, :a + 1]) if ok else []
+        assert list(r["history"][b, :lens[b] + len(new)]) == old + new
+        assert list(r["history"][b, lens[b] + len(new):]) == list(hist[b, lens[b] + len(new):])
+        assert r["seq_len"][b] == lens[b] + len(new)
+        assert r["status"][b] == (0 if ok else (2 if a < 0 else 1))
+        packed += new
+        offs.append(offs[-1] + len(new))
+    assert r["packed"].tolist() == packed
+    assert r["packed_offsets"].tolist() == offs
+    # without a history nothing limits the lengths
+    r2 = orc.commit_tokens(acc, em, lens)
+    assert (r2["seq_len"] == lens + np.where((acc >= 0) & (acc < width), acc + 1, 0)).all()

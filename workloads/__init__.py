@@ -277,6 +277,13 @@ CONFIGS = {
             target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=(0.3, 1.3)),
     5: dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
             target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6),
+    # one draft token per sequence, as in the single-token multi-token-prediction
+    # schedule (the target scores 2 tokens per sequence of the decode batch)
+    6: dict(name="MTP single-token verify", kind="chain", B=256, k=1, V=129280, dtype=BF16,
+            target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
+    # plain temperature sampling of one target row per sequence (no drafts)
+    7: dict(name="temperature sampling", kind="chain", B=256, k=0, V=128256, dtype=BF16,
+            target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
 }
 
 
