@@ -61,6 +61,10 @@ int64_t final_chunks(int V, sv_dtype dt) {
     return (segments_per_row(V, dt) + sv::kSegPerChunk - 1) / sv::kSegPerChunk;
 }
 
+// Largest final-draw grid for which every workgroup recomputes its
+// sequence's acceptance; beyond it one wave per sequence computes it once.
+constexpr int64_t kInlineAcceptMaxBlocks = 2048;
+
 // The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
 // every sequence, their logits at the draft tokens, the final draw's
 // descriptors, segment masses and chunk argmaxes.
@@ -138,16 +142,29 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
     auto* segs = reinterpret_cast<Partial*>(ws + L.segs);
     auto* chunkarg = reinterpret_cast<Partial*>(ws + L.chunkarg);
     sv_status st;
+    const int64_t fin_blocks = static_cast<int64_t>(B) * nchunk;
+    const int acc = k == 0 ? sv::kAcceptNone
+                           : (fin_blocks <= kInlineAcceptMaxBlocks ? sv::kAcceptInline : sv::kAcceptRead);
     if (k > 0) {
         const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * k * nT);
         st = launch("chain_rowstats", sv::chain_rowstats_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
                     dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, V, nT, part, gathered);
         if (st != SV_OK) return st;
     }
-    st = launch("chain_final_part", sv::chain_final_part_kernel<DT, VEC>, dim3(static_cast<unsigned>(static_cast<int64_t>(B) * nchunk)),
-                dim3(sv::kFinBlock), stream, tokens, draft, target, temperature, uniforms, B, k, V, nT,
-                static_cast<const Partial*>(part), static_cast<const float*>(gathered), nchunk, accepted_len,
-                emitted, accept_prob, info, segs, chunkarg);
+    if (acc == sv::kAcceptRead) {
+        const unsigned acc_blocks = static_cast<unsigned>((B + sv::kAccWaves - 1) / sv::kAccWaves);
+        st = launch("chain_accept", sv::chain_accept_kernel<DT>, dim3(acc_blocks), dim3(sv::kAccWaves * sv::kWave),
+                    stream, tokens, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
+                    static_cast<const float*>(gathered), accepted_len, emitted, accept_prob, info);
+        if (st != SV_OK) return st;
+    }
+    auto final_part = acc == sv::kAcceptNone     ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptNone>
+                      : acc == sv::kAcceptInline ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptInline>
+                                                 : sv::chain_final_part_kernel<DT, VEC, sv::kAcceptRead>;
+    st = launch("chain_final_part", final_part, dim3(static_cast<unsigned>(fin_blocks)), dim3(sv::kFinBlock), stream,
+                tokens, draft, target, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
+                static_cast<const float*>(gathered), nchunk, accepted_len, emitted, accept_prob, info, segs,
+                chunkarg);
     if (st != SV_OK) return st;
     return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kWave), stream, draft,
                   target, B, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),

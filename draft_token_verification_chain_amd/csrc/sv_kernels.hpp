@@ -78,14 +78,12 @@ __device__ __forceinline__ Partial tile_softmax(const void* base, int64_t row_el
     return Partial{s, static_cast<int>(r)};
 }
 
-// (max, lowest index) of one tile of raw logits.
-template <int DT, bool VEC, int U, bool FULL>
-__device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem, int V, int64_t tile) {
+// (max, lowest index) of one tile whose logits are already loaded (masked
+// elements hold -inf and never win).
+template <int DT, int U>
+__device__ __forceinline__ ArgMax argmax_of_tile(const float* v, int64_t tile) {
     constexpr int VE = Elem<DT>::per_vec;
-    constexpr int NE = U * VE;
     const int lane = lane_id();
-    float v[NE];
-    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane, v);
     ArgMax a{-__builtin_inff(), kNoIndex};
     const int64_t v0 = tile * (64 * U) + lane;
 #pragma unroll
@@ -100,6 +98,14 @@ __device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem
         }
     }
     return wave_argmax(a);
+}
+
+// (max, lowest index) of one tile of raw logits.
+template <int DT, bool VEC, int U, bool FULL>
+__device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem, int V, int64_t tile) {
+    float v[U * Elem<DT>::per_vec];
+    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane_id(), v);
+    return argmax_of_tile<DT, U>(v, tile);
 }
 
 // Tile entry points that pick the unmasked path for tiles inside the row.
@@ -400,6 +406,25 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
     if (publish && lane == 0) accepted_len[b] = a;
 }
 
+// One wave per sequence, kAccWaves sequences per workgroup: the acceptance
+// of every sequence, its outputs and the descriptor of its final draw.
+constexpr int kAccWaves = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kAccWaves * kWave) void chain_accept_kernel(
+    const int32_t* __restrict__ tokens, const float* __restrict__ temperature, const float* __restrict__ uniforms,
+    int B, int k, int V, int nT, const Partial* __restrict__ part, const float* __restrict__ gathered,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+    SeqInfo* __restrict__ info) {
+    __shared__ int s_r[kAccWaves][2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[kAccWaves][2 * SV_MAX_DRAFTS];
+    const int w = threadIdx.x / kWave;
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kAccWaves + w;
+    if (b >= B) return;  // whole waves only; the kernel has no workgroup barrier
+    accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, true, accepted_len, emitted,
+                        accept_prob, s_r[w], s_s[w], info + b);
+}
+
 // ---------------------------------------------------------------- chain: final draw ---
 
 // Weight of the final draw for the U*VE elements a lane holds.
@@ -492,11 +517,17 @@ __device__ __forceinline__ int last_positive_in_segment(const float* w, int64_t 
 
 // The final draw of sequence b is spread over `nchunk` workgroups, each
 // owning kSegPerChunk consecutive segments (a segment is the 64 vectors of
-// one wave load).  Every workgroup recomputes its sequence's acceptance (a
-// few KB of partials, cheaper than a separate launch), then streams its
-// chunk of the row(s) the draw needs and writes each segment's mass and
-// reference exponent -- or, at temperature 0, the chunk's argmax.  Chunk 0
-// also writes the acceptance outputs and the draw's descriptor.
+// one wave load).  A workgroup first needs the draw's descriptor, obtained
+// in one of three ways (FinalAccept): with no drafts it is formed from the
+// temperature alone, so the first loads are the row's; for a draw that fits
+// in one round of resident workgroups every workgroup recomputes its
+// sequence's acceptance (a few KB of partials: cheaper than another launch);
+// for larger draws chain_accept_kernel has written it once per sequence.
+// The workgroup then streams its chunk of the row(s) the draw needs and
+// writes each segment's mass and reference exponent, or, at temperature 0,
+// the chunk's argmax.
+enum FinalAccept : int { kAcceptNone = 0, kAcceptInline = 1, kAcceptRead = 2 };
+
 constexpr int kFinBlock = 256;
 constexpr int kFinWaves = kFinBlock / kWave;
 constexpr int kFinU = 4;  // segments per wave tile
@@ -509,13 +540,13 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     constexpr int VE = Elem<DT>::per_vec;
     constexpr int NE = kFinU * VE;
     const int lane = lane_id();
+    float w[NE];  // the target's logits, then (in place) the weights
+    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
     if (mode == kFinalArgmax) {
-        best = better(best, tile_argmax<DT, VEC, kFinU, FULL>(target, trow, V, tile));
+        best = better(best, argmax_of_tile<DT, kFinU>(w, tile));
         return;
     }
-    float w[NE];  // the target's logits, then (in place) the weights
     float ref = 0.f;
-    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
     if (mode == kFinalResidual) {
         float vd[NE];
         load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
@@ -536,28 +567,44 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int ACC>
 __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
     const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
-    int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ emitted, float* __restrict__ accept_prob, SeqInfo* __restrict__ info,
-    Partial* __restrict__ segs, Partial* __restrict__ chunkarg) {
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+    SeqInfo* __restrict__ info, Partial* __restrict__ segs, Partial* __restrict__ chunkarg) {
     constexpr int VE = Elem<DT>::per_vec;
-    __shared__ int s_r[2 * SV_MAX_DRAFTS];
-    __shared__ double s_s[2 * SV_MAX_DRAFTS];
-    __shared__ SeqInfo s_info;
     __shared__ ArgMax s_arg[kFinWaves];
     const int64_t b = blockIdx.x / nchunk;
     const int c = static_cast<int>(blockIdx.x - b * nchunk);
-    if (threadIdx.x < kWave)
-        accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, c == 0, accepted_len,
-                            emitted, accept_prob, s_r, s_s, &s_info);
-    __syncthreads();
-    const SeqInfo si = s_info;
-    if (c == 0 && threadIdx.x == 0) info[b] = si;
-    if (si.mode == kFinalDone) return;
+    SeqInfo si;
+    if constexpr (ACC == kAcceptInline) {
+        __shared__ int s_r[2 * SV_MAX_DRAFTS];
+        __shared__ double s_s[2 * SV_MAX_DRAFTS];
+        __shared__ SeqInfo s_info;
+        if (threadIdx.x < kWave)
+            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, c == 0, accepted_len,
+                                emitted, accept_prob, s_r, s_s, &s_info);
+        __syncthreads();
+        si = s_info;
+        if (c == 0 && threadIdx.x == 0) info[b] = si;
+        if (si.mode == kFinalDone) return;
+    } else if constexpr (ACC == kAcceptNone) {
+        // k == 0: draw from target row 0 (its argmax at temperature 0)
+        const float T = temperature[b];
+        si = SeqInfo{};
+        si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+        temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+        si.u = uniforms[b];
+        if (c == 0 && threadIdx.x == 0) {
+            info[b] = si;
+            accepted_len[b] = 0;
+        }
+    } else {
+        si = info[b];
+        if (si.mode == kFinalDone) return;
+    }
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
     const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);

@@ -331,11 +331,13 @@ def test_verify_then_commit_on_device(svl, orc):
 
 
 @pytest.mark.parametrize("shape", [(600, 2, 9000, W.BF16), (700, 1, 9000, W.F32), (700, 1, 4097, W.BF16),
-                                   (1200, 0, 5000, W.BF16)],
+                                   (1200, 0, 5000, W.BF16), (300, 2, 60000, W.F32), (300, 1, 64007, W.BF16),
+                                   (600, 0, 30001, W.F32), (2500, 0, 4097, W.BF16)],
                          ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
-def test_pipelined_final_draw(svl, orc, shape):
-    """Batches large enough that each final-draw wave handles several tiles
-    (pipelined loads), with ragged row ends and an unaligned row length."""
+def test_large_batch_final_draw(svl, orc, shape):
+    """Batches large enough that each final-draw wave handles several tiles,
+    with ragged row ends, a last chunk only partly inside the row and
+    unaligned row lengths."""
     B, k, V, dt = shape
     inp = W.chain_inputs(B, k, V, dt, 11, target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0),
                          temperature=(0.3, 1.3))

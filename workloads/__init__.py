@@ -288,7 +288,7 @@ CONFIGS = {
 
 
 def make_inputs(config: int, seed: int = 1, **override) -> dict:
-    """Inputs for one of the five named workloads (sizes may be overridden)."""
+    """Inputs for one of the named workloads in CONFIGS (sizes may be overridden)."""
     c = dict(CONFIGS[config])
     c.update(override)
     kind = c.pop("kind")
