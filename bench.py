@@ -201,7 +201,8 @@ def main():
                 final_bytes += (2 if a[b] < k else 1) * V * es
             elif a[b] == k:
                 final_bytes += V * es
-    step_bytes = dominant_bytes + final_bytes
+    # with no drafts the final draw is the dominant pass itself (its row counted once)
+    step_bytes = final_bytes if kind == "chain" and inp["k"] == 0 else dominant_bytes + final_bytes
 
     def timed(profiled: bool) -> float:
         """K steps back to back behind a ~20 ms spin kernel (so that host launch
@@ -233,7 +234,7 @@ def main():
     traffic = load_traffic(dominant, f"config{args.config}")
 
     result = {
-        "metric": METRIC if args.config == 2 else f"verified draft tokens/sec ({cfg['name']})",
+        "metric": METRIC if args.config == 2 else f"{unit[:-2]}/sec ({cfg['name']})",
         "value": units / s_per_step,
         "unit": unit,
         "n_gpus": 1,
