@@ -32,6 +32,7 @@ MUT_ROWS_SHIFTED = 3
 MUT_ACCEPT_INVERTED = 4
 MUT_ARGMAX_LAST = 5
 MUT_TREE_TIE_HIGHEST = 6
+MUT_TREE_STALE_RESIDUAL = 7
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
         _lib.svo_verify_greedy.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 4
         _lib.svo_verify_tree.argtypes = (
             [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 4)
+        _lib.svo_verify_tree_sampled.argtypes = (
+            [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 8 +
+            [ctypes.c_double])
         _lib.svo_row_logz.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
         _lib.svo_row_argmax.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
         _lib.svo_commit_tokens.argtypes = ([ctypes.c_int] * 2 + [ctypes.c_void_p] * 4 + [ctypes.c_int] +
@@ -129,6 +133,28 @@ def verify_tree(inp: dict) -> dict:
     if rc != 0:
         raise ValueError(f"svo_verify_tree returned {rc}")
     return dict(accepted_len=acc, emitted=em, accepted_nodes=nodes)
+
+
+def verify_tree_sampled(inp: dict, band_eps: float = BAND_EPS) -> dict:
+    """Multi-step speculative sampling over a draft tree (see oracle.c)."""
+    B, N, V, dt = inp["B"], inp["N"], inp["V"], inp["dtype"]
+    par = _c(inp["parent"], np.int32)
+    stride = 0 if par.ndim == 1 else par.shape[1]
+    md = int(inp["max_depth"])
+    tok = _c(inp["node_tokens"], np.int32)
+    d = _c(inp["draft_logits"])
+    t = _c(inp["target_logits"])
+    T = _c(inp["temperature"], np.float32)
+    u = _c(inp["uniforms"], np.float32)
+    acc = np.empty(B, np.int32)
+    em = np.empty((B, md + 1), np.int32)
+    nodes = np.empty((B, md + 1), np.int32)
+    band = np.empty(B, np.int32)
+    rc = lib().svo_verify_tree_sampled(B, N, V, dt, _ptr(tok), _ptr(par), stride, md, _ptr(d), _ptr(t), _ptr(T),
+                                       _ptr(u), _ptr(acc), _ptr(em), _ptr(nodes), _ptr(band), float(band_eps))
+    if rc != 0:
+        raise ValueError(f"svo_verify_tree_sampled returned {rc}")
+    return dict(accepted_len=acc, emitted=em, accepted_nodes=nodes, band=band.astype(bool))
 
 
 def row_logz(logits: np.ndarray, dtype: int, temperature) -> np.ndarray:

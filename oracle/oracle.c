@@ -39,6 +39,10 @@
  *   R-ties   every argmax is the lowest index among equal maxima.
  *   R-tree   a tree path starts at the root and may end at any node; the
  *            deepest fully accepted node wins, lowest index among equals.
+ *   R-mss    sampled trees: the pages give no rule, so the multi-step
+ *            speculative sampling of SpecInfer (Miao et al., 2023) -- the
+ *            multi-round rule the EAGLE work applies to its trees -- is used;
+ *            see svo_verify_tree_sampled.
  *
  * Band flag (sequences with T_b > 0 only): set when a tested uniform lies
  * within band_eps of its threshold tau_i, or u[b][k] lies within band_eps of
@@ -67,6 +71,8 @@
 #define MUT_ACCEPT_INVERTED 4           /* accept when u > tau              */
 #define MUT_ARGMAX_LAST 5               /* ties go to the highest index     */
 #define MUT_TREE_TIE_HIGHEST 6          /* tree: equal depth -> highest idx */
+#define MUT_TREE_STALE_RESIDUAL 7       /* sampled tree: later siblings tested
+                                           against p, not the updated residual */
 static int g_mutation = MUT_NONE;
 
 void svo_set_mutation(int m) { g_mutation = m; }
@@ -387,6 +393,154 @@ int svo_verify_tree(int B, int N, int V, int dtype, const int32_t *node_tokens,
             out[d] = g[m];
         }
         free(g); free(depth); free(acc);
+    }
+    return bad;
+}
+
+/*
+ * Sampled (stochastic) tree verification: multi-step speculative sampling
+ * (SpecInfer, Miao et al. 2023, the rule the EAGLE work uses for its draft
+ * trees).
+ *   node_tokens   [B][N]     node 0 is the root (its token is never tested)
+ *   parent        as for svo_verify_tree
+ *   draft_logits  [B][N][V]  row n: the draft distribution q_n from which the
+ *                            children of node n were drawn (rows of leaves unused)
+ *   target_logits [B][N][V]  row n: the target distribution p_n after node n
+ *   temperature   [B]        >= 0 (0: one-hot at the first argmax)
+ *   uniforms      [B][N]     u[b][i], i >= 1, tests node i; u[b][0] drives the
+ *                            final draw
+ * The walk starts at the root.  At node n the children are tested in
+ * ascending index order against a running distribution r, which starts as
+ * p_n: child i with token y is kept when u[b][i] < min(1, r(y) / q_n(y))
+ * (the q = 0 rule as for chains), and the walk moves to it.  A rejection
+ * replaces r by the normalised residual max(0, r - q_n).  When no child is
+ * kept (or n is a leaf), the final token is drawn from r by the inverse CDF
+ * with u[b][0].
+ * The residual after j rejections is max(0, p - c_j q) / Z(c_j) with
+ * Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0 and c_{j+1} = c_j + Z(c_j),
+ * because max(0, max(0, a) / Z - q) = max(0, a - Z q) / Z for Z > 0.  Only
+ * the scalar c is carried from one sibling to the next.  If a residual has no
+ * mass (rounding), r falls back to p_n (c = 0), as for chains.
+ * Outputs as for svo_verify_tree: accepted_len = depth of the last kept node,
+ * emitted = the kept tokens then the final token then -1, accepted_nodes the
+ * kept node ids then -1; an invalid tree gives -1 everywhere.  band[b] (T > 0
+ * only) flags a tested uniform within band_eps of its threshold or u[b][0]
+ * within band_eps of a CDF boundary of the final token.
+ */
+int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_tokens,
+                            const int32_t *parent, int parent_stride, int max_depth,
+                            const void *draft_logits, const void *target_logits,
+                            const float *temperature, const float *uniforms,
+                            int32_t *accepted_len, int32_t *emitted, int32_t *accepted_nodes,
+                            int32_t *band, double band_eps) {
+    if (B < 0 || N <= 0 || V <= 0 || max_depth < 0 || (dtype != SVO_F32 && dtype != SVO_BF16)) return 1;
+    if (parent_stride != 0 && parent_stride < N) return 1;
+    if (B == 0) return 0;
+    if (!node_tokens || !parent || !draft_logits || !target_logits || !temperature || !uniforms ||
+        !accepted_len || !emitted)
+        return 1;
+    const int width = max_depth + 1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parent + (size_t)b * (size_t)parent_stride;
+        const int32_t *tok = node_tokens + (size_t)b * N;
+        const float *u = uniforms + (size_t)b * N;
+        const double T = (double)temperature[b];
+        int32_t *out = emitted + (size_t)b * width;
+        int32_t *nodes = accepted_nodes ? accepted_nodes + (size_t)b * width : NULL;
+        for (int j = 0; j < width; ++j) {
+            out[j] = -1;
+            if (nodes) nodes[j] = -1;
+        }
+        int *depth = (int *)malloc(sizeof(int) * (size_t)N);
+        double *P = (double *)malloc(sizeof(double) * (size_t)V);
+        double *Q = (double *)malloc(sizeof(double) * (size_t)V);
+        double *w = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!depth || !P || !Q || !w) {
+            bad = 1;
+            free(depth); free(P); free(Q); free(w);
+            continue;
+        }
+        /* The same validity rule as the greedy tree. */
+        int valid = 1;
+        depth[0] = 0;
+        for (int i = 1; i < N; ++i) {
+            int p = par[i];
+            if (p < 0 || p >= i) { valid = 0; depth[i] = 0; continue; }
+            depth[i] = depth[p] + 1;
+            if (depth[i] > max_depth) valid = 0;
+        }
+        int flag = 0;
+        if (!valid) {
+            accepted_len[b] = -1;
+        } else {
+            int n = 0, d = 0;
+            double c = 0.0, Z = 1.0;
+            for (;;) {
+                size_t trow = ((size_t)b * N + n) * (size_t)V;
+                row_distribution(target_logits, dtype, trow, V, T, P);
+                int has_children = 0;
+                for (int i = n + 1; i < N; ++i)
+                    if (par[i] == n) has_children = 1;
+                if (has_children) row_distribution(draft_logits, dtype, trow, V, T, Q);
+                c = 0.0;
+                Z = 1.0;
+                int next = -1;
+                for (int i = n + 1; i < N && next < 0; ++i) {
+                    if (par[i] != n) continue;
+                    int y = tok[i];
+                    if (y < 0 || y >= V) { bad = 1; y = 0; }
+                    double cc = (g_mutation == MUT_TREE_STALE_RESIDUAL) ? 0.0 : c;
+                    double zz = (g_mutation == MUT_TREE_STALE_RESIDUAL) ? 1.0 : Z;
+                    double r = P[y] - cc * Q[y];
+                    r = (r > 0.0 ? r : 0.0) / zz;
+                    double tau = threshold(r, Q[y]);
+                    if (T > 0.0 && fabs((double)u[i] - tau) < band_eps) flag = 1;
+                    if ((double)u[i] < tau) {
+                        next = i;
+                        break;
+                    }
+                    /* rejected: the residual max(0, r - q) is max(0, p - (c + Z) q) / Z' */
+                    c += Z;
+                    Z = 0.0;
+                    for (int v = 0; v < V; ++v) {
+                        double e = P[v] - c * Q[v];
+                        Z += e > 0.0 ? e : 0.0;
+                    }
+                    if (Z == 0.0) { c = 0.0; Z = 1.0; }
+                }
+                if (next >= 0) {
+                    out[d] = tok[next];
+                    if (nodes) nodes[d] = next;
+                    ++d;
+                    n = next;
+                    continue;
+                }
+                /* No child kept: draw from max(0, p - c q) (p itself when c == 0). */
+                double W = 0.0;
+                for (int v = 0; v < V; ++v) {
+                    double e;
+                    if (c == 0.0 || g_mutation == MUT_SAMPLE_TARGET_AT_MISMATCH) e = P[v];
+                    else e = P[v] - c * Q[v];
+                    w[v] = e > 0.0 ? e : 0.0;
+                    W += w[v];
+                }
+                if (W == 0.0) {
+                    for (int v = 0; v < V; ++v) { w[v] = P[v]; W += w[v]; }
+                }
+                double c_lo = 0.0, c_hi = 0.0;
+                int y = inverse_cdf(w, V, W, (double)u[0], &c_lo, &c_hi);
+                if (T > 0.0 && (fabs((double)u[0] - c_lo / W) < band_eps ||
+                                fabs((double)u[0] - c_hi / W) < band_eps))
+                    flag = 1;
+                out[d] = y;
+                accepted_len[b] = d;
+                break;
+            }
+        }
+        if (band) band[b] = flag;
+        free(depth); free(P); free(Q); free(w);
     }
     return bad;
 }

@@ -456,3 +456,205 @@ def test_commit_matches_list_semantics(orc):
     # without a history nothing limits the lengths
     r2 = orc.commit_tokens(acc, em, lens)
     assert (r2["seq_len"] == lens + np.where((acc >= 0) & (acc < width), acc + 1, 0)).all()
+
+
+# ------------------------------------------------------------ sampled tree ---
+# Multi-step speculative sampling (SpecInfer, Miao et al. 2023; the rule the
+# EAGLE work applies to its trees): the pages give no rule for sampled trees.
+
+def _chain_as_tree(inp):
+    """A chain laid out as a linear tree: node i >= 1 carries draft i-1 and is
+    scored by rows i-1; u_tree[i] = u_chain[i-1], u_tree[0] = u_chain[k]."""
+    B, k, V = inp["B"], inp["k"], inp["V"]
+    N = k + 1
+    draft = np.zeros((B, N, V), dtype=inp["draft_logits"].dtype)
+    draft[:, :k] = inp["draft_logits"]
+    tok = np.zeros((B, N), np.int32)
+    tok[:, 1:] = inp["draft_tokens"]
+    u = np.empty((B, N), np.float32)
+    u[:, 1:] = inp["uniforms"][:, :k]
+    u[:, 0] = inp["uniforms"][:, k]
+    return dict(B=B, N=N, V=V, dtype=inp["dtype"], node_tokens=tok, parent=np.arange(-1, N - 1, dtype=np.int32),
+                max_depth=k, draft_logits=draft, target_logits=inp["target_logits"],
+                temperature=inp["temperature"], uniforms=u)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_sampled_linear_tree_is_chain(orc, seed, dtype):
+    """On a linear tree (one child per node) the walk is chain speculative
+    sampling: same accepted lengths, tokens and band flags, T = 0 included."""
+    B = 96
+    temps = np.random.default_rng(seed).uniform(0.3, 1.3, B).astype(np.float32)
+    temps[::4] = 0.0
+    inp = W.chain_inputs(B, 4, 3001, dtype, seed, target_sigma=2.0, zipf_s=1.1, draft_sigma=(0.2, 2.5),
+                         temperature=temps)
+    c = orc.verify_chain(inp)
+    t = orc.verify_tree_sampled(_chain_as_tree(inp))
+    np.testing.assert_array_equal(t["accepted_len"], c["accepted_len"])
+    np.testing.assert_array_equal(t["emitted"], c["emitted"])
+    np.testing.assert_array_equal(t["band"], c["band"])
+    for b in range(B):
+        a = c["accepted_len"][b]
+        np.testing.assert_array_equal(t["accepted_nodes"][b, :a], np.arange(1, a + 1))
+
+
+def _first_child_path(parent):
+    path, n = [], 0
+    while True:
+        kids = np.flatnonzero(parent == n)
+        kids = kids[kids > 0]
+        if kids.size == 0:
+            return path
+        n = int(kids[0])
+        path.append(n)
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+@pytest.mark.parametrize("T", [0.5, 1.0])
+def test_sampled_tree_identical_rows_keep_first_child(orc, dtype, T):
+    """Draft rows equal to target rows give tau = 1 for every tested child, so
+    the walk keeps the lowest-index child at every node down to a leaf."""
+    inp = W.sampled_tree_inputs(8, 40, 2000, dtype, 5, temperature=T)
+    inp["draft_logits"] = inp["target_logits"].copy()
+    r = orc.verify_tree_sampled(inp)
+    path = _first_child_path(inp["parent"])
+    assert (r["accepted_len"] == len(path)).all()
+    for b in range(inp["B"]):
+        np.testing.assert_array_equal(r["accepted_nodes"][b, :len(path)], path)
+        np.testing.assert_array_equal(r["emitted"][b, :len(path)], inp["node_tokens"][b, path])
+
+
+def _distinct_siblings(inp):
+    """Give equal-token siblings distinct tokens that miss the parent's argmax."""
+    tok = inp["node_tokens"].copy()
+    par = inp["parent"]
+    V = inp["V"]
+    top = np.argmax(W.values(inp["target_logits"], inp["dtype"]), axis=-1)
+    for b in range(inp["B"]):
+        for n in range(inp["N"]):
+            seen = set()
+            for i in np.flatnonzero(par == n):
+                if i == 0:
+                    continue
+                y = int(tok[b, i])
+                while y in seen:
+                    y = (y + 1) % V
+                    if y == top[b, n]:
+                        y = (y + 1) % V
+                seen.add(y)
+                tok[b, i] = y
+    inp["node_tokens"] = tok
+    return inp
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_sampled_tree_temperature_zero_is_greedy_tree(orc, seed):
+    """At T = 0 every distribution is one-hot at its first argmax: a child is
+    kept iff its token is the parent's target argmax, and the final token is
+    the last kept node's argmax -- the greedy tree, when siblings differ."""
+    inp = _distinct_siblings(W.tree_inputs(12, 48, 1500, W.BF16, seed, match_p=0.7))
+    rng = np.random.default_rng(seed)
+    inp["draft_logits"] = W.to_dtype(2.0 * rng.standard_normal(inp["target_logits"].shape, dtype=np.float32), W.BF16)
+    inp["temperature"] = np.zeros(inp["B"], np.float32)
+    inp["uniforms"] = rng.random((inp["B"], inp["N"]), dtype=np.float32)
+    g = orc.verify_tree(inp)
+    s = orc.verify_tree_sampled(inp)
+    np.testing.assert_array_equal(s["accepted_len"], g["accepted_len"])
+    np.testing.assert_array_equal(s["emitted"], g["emitted"])
+    np.testing.assert_array_equal(s["accepted_nodes"], g["accepted_nodes"])
+
+
+def test_sampled_tree_invalid_parent_or_depth_marks_sequence(orc):
+    inp = W.sampled_tree_inputs(3, 12, 500, W.F32, 2)
+    par = np.tile(inp["parent"], (3, 1))
+    par[1, 5] = 7            # a parent after its child
+    inp["parent"] = par
+    r = orc.verify_tree_sampled(inp)
+    assert r["accepted_len"][1] == -1 and (r["emitted"][1] == -1).all() and (r["accepted_nodes"][1] == -1).all()
+    assert (r["accepted_len"][[0, 2]] >= 0).all()
+    inp["parent"] = inp["parent"][0].copy()
+    inp["max_depth"] = 0
+    r = orc.verify_tree_sampled(inp)
+    assert (r["accepted_len"] == -1).all()
+
+
+V_TREE, N_TREE, TREE_BLOCKS = 8, 1_000_000, 5
+
+
+def _tree_tables():
+    rng = np.random.default_rng(4242)
+    V = V_TREE
+    root_t = (1.5 * rng.standard_normal(V)).astype(np.float32)
+    root_d = (root_t + rng.standard_normal(V)).astype(np.float32)
+    F = (1.5 * rng.standard_normal((V, V))).astype(np.float32)
+    G = (F + rng.standard_normal((V, V))).astype(np.float32)
+    H = (1.5 * rng.standard_normal((V, V))).astype(np.float32)
+    return root_t, root_d, F, G, H
+
+
+def _run_tree_trials(orc, tables, T=1.0):
+    acc, em, nodes = [], [], []
+    per = N_TREE // TREE_BLOCKS
+    for blk in range(TREE_BLOCKS):
+        r = orc.verify_tree_sampled(W.sampled_tree_trials(*tables, T, per, seed=91, block=blk))
+        acc.append(r["accepted_len"])
+        em.append(r["emitted"])
+        nodes.append(r["accepted_nodes"])
+    return np.concatenate(acc), np.concatenate(em), np.concatenate(nodes)
+
+
+def _tree_chi_pvalues(tables, acc, em, T=1.0):
+    """p-values of: y1 ~ p_root; y2 | y1 ~ F[y1]; y3 | y2 ~ H[y2]."""
+    root_t, root_d, F, G, H = tables
+    V = V_TREE
+    out = [stats.chisquare(np.bincount(em[:, 0], minlength=V), _softmax_rows(root_t, T) * len(acc)).pvalue]
+    for j, table in ((1, F), (2, H)):
+        sel = acc >= j
+        prev, cur = em[sel, j - 1], em[sel, j]
+        obs = np.bincount(prev * V + cur, minlength=V * V).reshape(V, V)
+        n_prev = obs.sum(axis=1)
+        exp = n_prev[:, None] * _softmax_rows(table, T)
+        keep = n_prev > 0
+        out.append(stats.chisquare(obs[keep].ravel(), exp[keep].ravel(), ddof=int(keep.sum()) - 1).pvalue)
+    return np.array(out)
+
+
+@pytest.fixture(scope="module")
+def tree_chi_trials(orc):
+    tables = _tree_tables()
+    return (tables,) + _run_tree_trials(orc, tables)
+
+
+def test_sampled_tree_tokens_follow_target_distribution(tree_chi_trials):
+    """10^6 seeded trials on a two-level tree (3 children, 2 grandchildren
+    each; V = 8; siblings drawn independently from the draft rows): the first
+    token follows the root's target row and each later token the target row
+    of the token before it (chi-square)."""
+    tables, acc, em, nodes = tree_chi_trials
+    pv = _tree_chi_pvalues(tables, acc, em)
+    assert (pv > 1e-4).all(), pv
+
+
+def test_sampled_tree_sibling_acceptance_rates(tree_chi_trials):
+    """At the root, child 1 is kept with probability sum min(p, q); given its
+    rejection, child 2 with probability sum min(r, q) where r is the
+    normalised residual max(0, p - q) (binomial z-scores)."""
+    tables, acc, em, nodes = tree_chi_trials
+    root_t, root_d = tables[0], tables[1]
+    p, q = _softmax_rows(root_t, 1.0), _softmax_rows(root_d, 1.0)
+    r = np.maximum(p - q, 0.0)
+    r /= r.sum()
+    first = nodes[:, 0]
+    for n, hits, alpha in ((len(first), (first == 1).sum(), np.minimum(p, q).sum()),
+                           ((first != 1).sum(), (first == 2).sum(), np.minimum(r, q).sum())):
+        z = (hits - n * alpha) / np.sqrt(n * alpha * (1 - alpha))
+        assert abs(z) < 5, (alpha, hits / n)
+
+
+@pytest.mark.parametrize("mutation", ["MUT_TREE_STALE_RESIDUAL", "MUT_SAMPLE_TARGET_AT_MISMATCH"])
+def test_sampled_tree_planted_mistakes_fail_the_distribution_test(orc, mutated, mutation):
+    tables = _tree_tables()
+    mutated(getattr(orc, mutation))
+    acc, em, nodes = _run_tree_trials(orc, tables)
+    assert _tree_chi_pvalues(tables, acc, em).min() < 1e-12

@@ -41,6 +41,7 @@ _PURPOSE = {
     "sigma": 8,
     "tree_tokens": 9,
     "greedy_tokens": 10,
+    "tree_uniforms": 11,
 }
 
 
@@ -264,7 +265,91 @@ def tree_inputs(B: int, N: int, V: int, dtype: int, seed: int, *,
                 target_logits=target)
 
 
-# ------------------------------------------------------------ the five workloads ---
+def sampled_tree_inputs(B: int, N: int, V: int, dtype: int, seed: int, *,
+                        target_sigma: float = 3.0, zipf_s: float | None = 1.1, draft_sigma=1.0,
+                        temperature=0.7, max_branch: int = 4, max_depth: int = 6,
+                        parent: np.ndarray | None = None) -> dict:
+    """Inputs for sampled (stochastic) tree verification.
+
+    One parent array shared by all B sequences.  For every node n:
+    target row t[b, n, :] = target_sigma * N(0,1) (+ Zipf bias) and draft row
+    d[b, n, :] = t[b, n, :] + sigma_b * N(0,1), both rounded to dtype (row n
+    predicts the children of node n).  The children of node n carry tokens
+    drawn independently from softmax(d[b, n, :] / T_b) (Gumbel-max), as a
+    drafter sampling its tree would.  uniforms u[b, :N] in [0, 1): u[b, i]
+    tests node i >= 1, u[b, 0] drives the final draw.
+    """
+    if parent is None:
+        parent = random_tree(N, seed, max_branch, max_depth)
+    temps = _per_seq(temperature, B, seed, "temperature")
+    sigmas = _per_seq(draft_sigma, B, seed, "sigma")
+    bias = zipf_bias(V, zipf_s, seed) if zipf_s else None
+    rt, rd, rx = rng_for(seed, "target"), rng_for(seed, "draft"), rng_for(seed, "tree_tokens")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, N, V), dtype=np_dt)
+    draft = np.empty((B, N, V), dtype=np_dt)
+    tokens = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        t = target_sigma * rt.standard_normal((N, V), dtype=np.float32)
+        if bias is not None:
+            t = t + bias
+        target[b] = to_dtype(t, dtype)
+        dv = values(target[b], dtype) + np.float32(sigmas[b]) * rd.standard_normal((N, V), dtype=np.float32)
+        draft[b] = to_dtype(dv, dtype)
+        tokens[b, 0] = int(rx.integers(0, V))
+        if N > 1:
+            rows = values(draft[b][parent[1:]], dtype)  # the draft row of each node's parent
+            tokens[b, 1:] = gumbel_max_tokens(rows, float(temps[b]), rx)
+    depth = np.zeros(N, dtype=np.int64)
+    for i in range(1, N):
+        depth[i] = depth[parent[i]] + 1
+    uniforms = rng_for(seed, "tree_uniforms").random((B, N), dtype=np.float32)
+    return dict(kind="tree_sampled", B=B, N=N, V=V, dtype=dtype, node_tokens=tokens,
+                parent=parent.astype(np.int32), max_depth=int(max(max_depth, depth.max())),
+                draft_logits=draft, target_logits=target, temperature=temps.astype(np.float32),
+                uniforms=uniforms, draft_sigma=sigmas.astype(np.float32))
+
+
+# Two-level tree of the sampled-tree trials: the root has three children, each
+# child two (N = 10).
+TRIAL_TREE = np.array([-1, 0, 0, 0, 1, 1, 2, 2, 3, 3], dtype=np.int32)
+
+
+def sampled_tree_trials(root_t: np.ndarray, root_d: np.ndarray, F: np.ndarray, G: np.ndarray,
+                        H: np.ndarray, temperature: float, n: int, seed: int, block: int = 0) -> dict:
+    """``n`` independent trials of sampled tree verification on TRIAL_TREE.
+
+    Logit tables (float32 values, used as F32 logits; V = len(root_t)): the
+    root has target row root_t and draft row root_d; a child with token y has
+    target row F[y] and draft row G[y]; a grandchild with token z has target
+    row H[z].  Children are drawn independently from softmax(root_d / T),
+    grandchildren of a child with token y from softmax(G[y] / T).  A target
+    that depends on the last token only then gives the first three emitted
+    tokens the laws softmax(root_t / T), softmax(F[y1] / T), softmax(H[y2] / T).
+    """
+    V = root_t.shape[0]
+    N = TRIAL_TREE.shape[0]
+    rx = np.random.Generator(np.random.Philox(key=[int(seed), 3000 + 2 * int(block)]))
+    ru = np.random.Generator(np.random.Philox(key=[int(seed), 3001 + 2 * int(block)]))
+    tok = np.zeros((n, N), dtype=np.int32)
+    tok[:, 1:4] = gumbel_max_tokens(np.broadcast_to(root_d, (n, 3, V)), temperature, rx)
+    for c in (1, 2, 3):
+        kids = [i for i in range(N) if TRIAL_TREE[i] == c]
+        tok[:, kids] = gumbel_max_tokens(G[tok[:, c]][:, None, :].repeat(len(kids), axis=1), temperature, rx)
+    target = np.zeros((n, N, V), dtype=np.float32)
+    draft = np.zeros((n, N, V), dtype=np.float32)
+    target[:, 0] = root_t
+    draft[:, 0] = root_d
+    target[:, 1:4] = F[tok[:, 1:4]]
+    draft[:, 1:4] = G[tok[:, 1:4]]
+    target[:, 4:] = H[tok[:, 4:]]
+    return dict(kind="tree_sampled", B=n, N=N, V=V, dtype=F32, node_tokens=tok, parent=TRIAL_TREE.copy(),
+                max_depth=2, draft_logits=draft, target_logits=target,
+                temperature=np.full(n, temperature, dtype=np.float32),
+                uniforms=ru.random((n, N), dtype=np.float32))
+
+
+# ------------------------------------------------------------ the named workloads ---
 
 CONFIGS = {
     1: dict(name="tiny chain verify", kind="chain", B=1, k=4, V=1024, dtype=F32,
@@ -284,6 +369,10 @@ CONFIGS = {
     # plain temperature sampling of one target row per sequence (no drafts)
     7: dict(name="temperature sampling", kind="chain", B=256, k=0, V=128256, dtype=BF16,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
+    # the tree of the EAGLE-style workload, verified by sampling (children drawn
+    # from the draft rows, logits generated like the Llama-scale chain)
+    8: dict(name="sampled tree verify", kind="tree_sampled", B=16, N=64, V=128256, dtype=BF16,
+            target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7, max_branch=4, max_depth=6),
 }
 
 
@@ -299,4 +388,6 @@ def make_inputs(config: int, seed: int = 1, **override) -> dict:
         return greedy_inputs(c.pop("B"), c.pop("k"), c.pop("V"), c.pop("dtype"), seed, **c)
     if kind == "tree":
         return tree_inputs(c.pop("B"), c.pop("N"), c.pop("V"), c.pop("dtype"), seed, **c)
+    if kind == "tree_sampled":
+        return sampled_tree_inputs(c.pop("B"), c.pop("N"), c.pop("V"), c.pop("dtype"), seed, **c)
     raise ValueError(kind)
