@@ -75,6 +75,12 @@ def to_device(inp, torch, W):
                  uniforms=torch.from_numpy(inp["uniforms"]).cuda())
     elif inp["kind"] == "greedy":
         t.update(draft_tokens=torch.from_numpy(inp["draft_tokens"]).cuda())
+    elif inp["kind"] == "tree_sampled":
+        t.update(draft_logits=logits(inp["draft_logits"]),
+                 node_tokens=torch.from_numpy(inp["node_tokens"]).cuda(),
+                 parent=torch.from_numpy(inp["parent"]).cuda(),
+                 temperature=torch.from_numpy(inp["temperature"]).cuda(),
+                 uniforms=torch.from_numpy(inp["uniforms"]).cuda())
     else:
         t.update(node_tokens=torch.from_numpy(inp["node_tokens"]).cuda(),
                  parent=torch.from_numpy(inp["parent"]).cuda())
@@ -86,7 +92,8 @@ def cpu_baseline(inp, seconds: float):
     batch for about `seconds`."""
     import oracle
 
-    fn = {"chain": oracle.verify_chain, "greedy": oracle.verify_greedy, "tree": oracle.verify_tree}[inp["kind"]]
+    fn = {"chain": oracle.verify_chain, "greedy": oracle.verify_greedy, "tree": oracle.verify_tree,
+          "tree_sampled": oracle.verify_tree_sampled}[inp["kind"]]
     fn(inp)  # warm-up (page faults, thread pool)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -103,7 +110,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -164,6 +171,24 @@ def main():
         units = B * k
         dominant = "argmax_rows"
         dominant_bytes = B * (k + 1) * V * es
+    elif kind == "tree_sampled":
+        N = inp["N"]
+        md = inp["max_depth"]
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                   emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
+                   accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
+        ws = torch.empty(svl.tree_sampled_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            t = dev[i % copies]
+            svl.verify_tree_sampled(t["node_tokens"], t["parent"], md, t["draft_logits"], t["target_logits"],
+                                    t["temperature"], t["uniforms"], workspace=ws, out=out)
+        units = B * (N - 1)                 # verified draft nodes per step
+        dominant = "tree_rowstats"
+        # every node's target row and the draft rows of inner nodes (the walk's
+        # passes over the rows of the nodes it visits come on top)
+        inner = int(np.count_nonzero(np.bincount(inp["parent"][1:], minlength=N)))
+        dominant_bytes = B * (N + inner) * V * es
     else:
         N = inp["N"]
         md = inp["max_depth"]

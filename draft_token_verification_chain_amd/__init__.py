@@ -5,6 +5,7 @@ The Python names mirror the C entry points:
   verify_chain   -> sv_verify_chain   (acceptance test, first rejection, residual / bonus draw)
   verify_greedy  -> sv_verify_greedy  (temperature-0 argmax matching)
   verify_tree    -> sv_verify_tree    (EAGLE-style static tree, greedy)
+  verify_tree_sampled -> sv_verify_tree_sampled (sampled tree, multi-step speculative sampling)
   commit_tokens  -> sv_commit_tokens  (append the step's tokens on the device)
 The shared library is loaded on first use; calls raise if it is missing.
 """
@@ -20,9 +21,11 @@ from ._binding import (  # noqa: F401
     profile_begin,
     profile_end,
     status_string,
+    tree_sampled_workspace_bytes,
     tree_workspace_bytes,
     verify_chain,
     verify_greedy,
     verify_tree,
+    verify_tree_sampled,
     version,
 )

@@ -46,7 +46,8 @@ def load() -> ctypes.CDLL:
     lib.sv_version.restype = i
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [i]
-    for fn in ("sv_chain_workspace_bytes", "sv_greedy_workspace_bytes", "sv_tree_workspace_bytes"):
+    for fn in ("sv_chain_workspace_bytes", "sv_greedy_workspace_bytes", "sv_tree_workspace_bytes",
+               "sv_tree_sampled_workspace_bytes"):
         getattr(lib, fn).restype = sz
         getattr(lib, fn).argtypes = [i, i, i, i]
     lib.sv_verify_chain.restype = i
@@ -55,6 +56,8 @@ def load() -> ctypes.CDLL:
     lib.sv_verify_greedy.argtypes = [i, i, i, i] + [p] * 5 + [sz, p]
     lib.sv_verify_tree.restype = i
     lib.sv_verify_tree.argtypes = [i, i, i, i, p, p, i, i, p, p, p, p, p, sz, p]
+    lib.sv_verify_tree_sampled.restype = i
+    lib.sv_verify_tree_sampled.argtypes = [i, i, i, i, p, p, i, i] + [p] * 8 + [sz, p]
     lib.sv_commit_tokens.restype = i
     lib.sv_commit_tokens.argtypes = [i, i, p, p, p, p, i, p, p, p, p]
     lib.sv_profile_begin.restype = i
@@ -111,6 +114,10 @@ def greedy_workspace_bytes(B: int, k: int, V: int, dtype: int) -> int:
 
 def tree_workspace_bytes(B: int, N: int, V: int, dtype: int) -> int:
     return int(load().sv_tree_workspace_bytes(B, N, V, dtype))
+
+
+def tree_sampled_workspace_bytes(B: int, N: int, V: int, dtype: int) -> int:
+    return int(load().sv_tree_sampled_workspace_bytes(B, N, V, dtype))
 
 
 def _workspace(nbytes: int, device, workspace):
@@ -206,6 +213,49 @@ def verify_tree(node_tokens, parent, max_depth: int, target_logits, *, accepted_
                             _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError("sv_verify_tree", st)
+    return out
+
+
+def verify_tree_sampled(node_tokens, parent, max_depth: int, draft_logits, target_logits, temperature, uniforms, *,
+                        accepted_nodes: bool = True, workspace=None, stream=None, out=None) -> dict:
+    """Sampled tree verification (multi-step speculative sampling); see
+    ``sv_verify_tree_sampled``.
+
+    node_tokens [B,N] int32, parent [N] (shared) or [B,N] int32, draft_logits
+    and target_logits [B,N,V] (same dtype), temperature [B] f32, uniforms
+    [B,N] f32.  Returns accepted_len [B], emitted [B,max_depth+1] and
+    accepted_nodes [B,max_depth+1] (or None).
+    """
+    lib = load()
+    B, N, V = target_logits.shape
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    _check_dev("target_logits", target_logits)
+    _check_dev("draft_logits", draft_logits, target_logits.dtype, (B, N, V))
+    _check_dev("node_tokens", node_tokens, torch.int32, (B, N))
+    _check_dev("parent", parent, torch.int32)
+    _check_dev("temperature", temperature, torch.float32, (B,))
+    _check_dev("uniforms", uniforms, torch.float32, (B, N))
+    if parent.dim() == 1:
+        if parent.shape[0] != N:
+            raise ValueError("parent must have N entries")
+        stride = 0
+    else:
+        if parent.shape[0] != B or parent.shape[1] < N:
+            raise ValueError("parent must be [N] or [B, >=N]")
+        stride = parent.shape[1]
+    w = max_depth + 1
+    if out is None:
+        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   emitted=torch.empty((B, w), dtype=torch.int32, device=dev),
+                   accepted_nodes=torch.empty((B, w), dtype=torch.int32, device=dev) if accepted_nodes else None)
+    ws = _workspace(lib.sv_tree_sampled_workspace_bytes(B, N, V, dt), dev, workspace)
+    st = lib.sv_verify_tree_sampled(B, N, V, dt, _ptr(node_tokens), _ptr(parent), stride, max_depth,
+                                    _ptr(draft_logits), _ptr(target_logits), _ptr(temperature), _ptr(uniforms),
+                                    _ptr(out["accepted_len"]), _ptr(out["emitted"]), _ptr(out["accepted_nodes"]),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError("sv_verify_tree_sampled", st)
     return out
 
 

@@ -235,6 +235,11 @@ size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt) {
     return align_up(sizeof(Partial) * static_cast<size_t>(B) * N * tiles_per_row(V, dt));
 }
 
+size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt) {
+    if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
+    return align_up(sizeof(Partial) * static_cast<size_t>(2) * B * N * tiles_per_row(V, dt));
+}
+
 sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* draft_logits,
                           const void* target_logits, const float* temperature, const float* uniforms,
                           int32_t* accepted_len, int32_t* emitted, float* accept_prob, void* workspace,
@@ -306,6 +311,41 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
     const int threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
     return launch("tree_finalize", sv::tree_finalize_kernel, dim3(B), dim3(threads), stream, node_tokens, parent,
                   parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
+}
+
+sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t* node_tokens,
+                                 const int32_t* parent, int parent_stride, int max_depth, const void* draft_logits,
+                                 const void* target_logits, const float* temperature, const float* uniforms,
+                                 int32_t* accepted_len, int32_t* emitted, int32_t* accepted_nodes, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || N < 1 || max_depth < 0 || parent_stride < 0 || (parent_stride != 0 && parent_stride < N))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
+    sv_status st = check_rows(static_cast<int64_t>(2) * B * N, V, dt);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!node_tokens || !parent || !draft_logits || !target_logits || !temperature || !uniforms || !accepted_len ||
+        !emitted)
+        return SV_ERR_INVALID_ARGUMENT;
+    if ((st = check_workspace(workspace, workspace_bytes, sv_tree_sampled_workspace_bytes(B, N, V, dt))) != SV_OK)
+        return st;
+    const int nT = static_cast<int>(tiles_per_row(V, dt));
+    const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits) &&
+                     aligned16(draft_logits);
+    auto* part = static_cast<Partial*>(workspace);
+    const unsigned blocks = static_cast<unsigned>(blocks_for_waves(static_cast<int64_t>(2) * B * N * nT));
+    auto rowstats = dt == SV_BF16 ? (vec ? sv::tree_rowstats_kernel<SV_BF16, true, kU>
+                                         : sv::tree_rowstats_kernel<SV_BF16, false, kU>)
+                                  : (vec ? sv::tree_rowstats_kernel<SV_F32, true, kU>
+                                         : sv::tree_rowstats_kernel<SV_F32, false, kU>);
+    st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits, draft_logits, parent,
+                parent_stride, temperature, B, N, V, nT, part);
+    if (st != SV_OK) return st;
+    auto walk = dt == SV_BF16 ? (vec ? sv::tree_sample_kernel<SV_BF16, true> : sv::tree_sample_kernel<SV_BF16, false>)
+                              : (vec ? sv::tree_sample_kernel<SV_F32, true> : sv::tree_sample_kernel<SV_F32, false>);
+    return launch("tree_sample", walk, dim3(B), dim3(sv::kWalkBlock), stream, node_tokens, parent, parent_stride, N,
+                  max_depth, draft_logits, target_logits, temperature, uniforms, B, V, nT,
+                  static_cast<const Partial*>(part), accepted_len, emitted, accepted_nodes);
 }
 
 sv_status sv_commit_tokens(int B, int width, const int32_t* accepted_len, const int32_t* emitted, int32_t* seq_len,

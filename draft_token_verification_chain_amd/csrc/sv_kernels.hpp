@@ -915,6 +915,420 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_finalize_kernel(
     }
 }
 
+// ---------------------------------------------------------------- tree: sampled ---
+//
+// Multi-step speculative sampling over a draft tree (SpecInfer, Miao et al.
+// 2023, the rule the EAGLE work applies to sampled trees; the pages, section
+// "EAGLE", keep the longest path that passes).  At node n the children are
+// tested in index order against a running distribution r that starts as the
+// target row p_n; a rejection replaces r by the normalised residual
+// max(0, r - q_n).  That residual after j rejections is max(0, p - c_j q) /
+// Z(c_j), Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0, c_{j+1} = c_j + Z(c_j),
+// so a sibling's test needs only the scalars (c, Z) and each rejection one
+// pass over the node's two rows.
+
+// Rows 0 .. B*N-1 are target rows (b, n), rows B*N .. 2*B*N-1 draft rows.
+// The draft row of a leaf is never needed and is skipped.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __restrict__ target,
+                                                               const void* __restrict__ draft,
+                                                               const int32_t* __restrict__ parent, int parent_stride,
+                                                               const float* __restrict__ temperature, int B, int N,
+                                                               int V, int nT, Partial* __restrict__ part) {
+    const int64_t gw = global_wave();
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    if (gw >= 2 * nbn * nT) return;
+    const int64_t r = gw / nT;
+    const int64_t tile = gw - r * nT;
+    const bool is_target = r < nbn;
+    const int64_t rr = is_target ? r : r - nbn;
+    const int64_t b = rr / N;
+    const int n = static_cast<int>(rr - b * N);
+    if (!is_target) {
+        const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+        bool kid = false;
+        for (int i = n + 1 + lane_id(); i < N; i += kWave) kid |= par[i] == n;
+        if (!__ballot(kid)) return;
+    }
+    const float T = temperature[b];
+    const void* base = is_target ? target : draft;
+    const int64_t row_elem = rr * static_cast<int64_t>(V);
+    Partial p;
+    if (T > 0.f) {
+        float c_hi, c_lo;
+        temperature_scale(T, c_hi, c_lo);
+        p = tile_softmax_any<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
+    } else {
+        const ArgMax a = tile_argmax_any<DT, VEC, U>(base, row_elem, V, tile);
+        p = Partial{a.val, a.idx};
+    }
+    if (lane_id() == 0) part[r * nT + tile] = p;
+}
+
+// One workgroup per sequence walks its tree; each thread holds kWalkSlots
+// node slots (t, t + kWalkBlock, ...).
+constexpr int kWalkBlock = 512;
+constexpr int kWalkWaves = kWalkBlock / kWave;
+constexpr int kWalkSlots = SV_MAX_TREE_NODES / kWalkBlock;
+constexpr int kWalkMaxSegs = SV_MAX_VOCAB / (4 * 64);  // f32 rows have the most segments
+constexpr int kWalkUnroll = 8;                          // segments in flight per wave
+
+// Normalised weights of segment g of the running distribution: p when the
+// residual scale c is 0, else max(0, p - c q) (s.inv_sd carries c / S_d).
+template <int DT, bool VEC>
+__device__ __forceinline__ void walk_weights(const void* draft, const void* target, int64_t row, int V, int64_t g,
+                                             const SeqInfo& s, bool residual, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    segment_weights<DT, VEC>(draft, target, row, row, V, g, s, residual, s.rt, w);
+    if (!residual) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
+    }
+}
+
+// Weights of one full segment from its raw 16-byte vectors (the same
+// arithmetic as walk_weights on an unmasked segment).
+template <int DT, bool RESIDUAL>
+__device__ __forceinline__ void walk_weights_raw(const uint4& rt, const uint4& rd, const SeqInfo& s, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    float vt[VE];
+    unpack<DT>(rt, vt);
+    if constexpr (RESIDUAL) {
+        float vd[VE];
+        unpack<DT>(rd, vd);
+        residual_weights<VE, true>(vt, vd, s, w);
+    } else {
+        bonus_weights<VE, true>(vt, s, s.rt, w);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
+    }
+}
+
+// Every thread of the workgroup: the mass of every segment of the running
+// distribution into s_mass, and their total (ascending order, fp64) as the
+// return value (identical in every thread).  Segments that lie wholly inside
+// the row are read kWalkUnroll per wave at a time with straight-line 16-byte
+// loads (indices clamped rather than branched on, so that all loads are in
+// flight together); the row's tail takes the masked path.
+template <int DT, bool VEC, bool RESIDUAL>
+__device__ double walk_masses(const void* draft, const void* target, int64_t row, int V, int64_t nseg,
+                              const SeqInfo& s, float* s_mass, double* s_sum) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int64_t nfull = VEC ? ((V + VE - 1) / VE) / 64 : 0;
+    const char* tr = static_cast<const char*>(target) + row * Elem<DT>::bytes;
+    const char* dr = static_cast<const char*>(draft) + row * Elem<DT>::bytes;
+    for (int64_t g0 = wave; g0 < nfull; g0 += kWalkWaves * kWalkUnroll) {
+        uint4 rt[kWalkUnroll], rd[kWalkUnroll];
+#pragma unroll
+        for (int j = 0; j < kWalkUnroll; ++j) {
+            const int64_t g = min<int64_t>(g0 + j * kWalkWaves, nfull - 1);
+            rt[j] = *reinterpret_cast<const uint4*>(tr + (g * 64 + lane) * 16);
+            if constexpr (RESIDUAL) rd[j] = *reinterpret_cast<const uint4*>(dr + (g * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kWalkUnroll; ++j) {
+            const int64_t g = g0 + j * kWalkWaves;
+            float w[VE];
+            walk_weights_raw<DT, RESIDUAL>(rt[j], rd[j], s, w);
+            const float m = wave_sum(pairwise_sum<VE>(w));
+            if (lane == 0 && g < nfull) s_mass[g] = m;
+        }
+    }
+    for (int64_t g = nfull + wave; g < nseg; g += kWalkWaves) {
+        float w[VE];
+        walk_weights<DT, VEC>(draft, target, row, V, g, s, RESIDUAL, w);
+        const float m = wave_sum(pairwise_sum<VE>(w));
+        if (lane == 0) s_mass[g] = m;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int64_t per = (nseg + kWave - 1) / kWave;
+        const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+        double run = 0.0;
+        for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
+        const double tot = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+        if (lane == 0) *s_sum = tot;
+    }
+    __syncthreads();
+    return *s_sum;
+}
+
+// Inverse CDF of the running distribution whose segment masses are in
+// s_mass (wave 0; returns the token in every lane).
+template <int DT, bool VEC>
+__device__ int walk_pick(const void* draft, const void* target, int64_t row, int V, int64_t nseg, const SeqInfo& s,
+                         bool residual, const float* s_mass, double W, double u) {
+    const int lane = lane_id();
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+    double run = 0.0;
+    for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
+    const double incl = wave_inclusive_scan(run);
+    const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+    double P = lane == 0 ? 0.0 : excl;
+    const double target_mass = u * W;
+    int64_t found = -1, last_pos = -1;
+    double Pfound = 0.0;
+    for (int64_t g = a; g < e; ++g) {
+        const double m = static_cast<double>(s_mass[g]);
+        if (found < 0 && P + m > target_mass) {
+            found = g;
+            Pfound = P;
+        }
+        if (m > 0.0) last_pos = g;
+        P += m;
+    }
+    int fl = first_lane(found >= 0);
+    int64_t seg;
+    double Ps = 0.0;
+    bool fallback = false;
+    if (fl >= 0) {
+        seg = __shfl(found, fl, kWave);
+        Ps = __shfl(Pfound, fl, kWave);
+    } else {
+        const uint64_t m = __ballot(last_pos >= 0);
+        fl = m ? 63 - __builtin_clzll(m) : 0;
+        seg = m ? __shfl(last_pos, fl, kWave) : 0;
+        fallback = true;
+    }
+    float w[Elem<DT>::per_vec];
+    walk_weights<DT, VEC>(draft, target, row, V, seg, s, residual, w);
+    int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, 1.0, target_mass);
+    if (y < 0) y = last_positive_in_segment<DT>(w, seg);
+    return y;
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
+    const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
+    int max_depth, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
+    const Partial* __restrict__ part, int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted,
+    int32_t* __restrict__ accepted_nodes) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ int s_par[SV_MAX_TREE_NODES];
+    __shared__ int s_anc[SV_MAX_TREE_NODES];
+    __shared__ int s_len[SV_MAX_TREE_NODES];
+    __shared__ uint64_t s_kids[SV_MAX_TREE_NODES / kWave];
+    __shared__ float s_mass[kWalkMaxSegs];
+    // the current node's children in index order: node id, uniform, and the
+    // target and draft logits at the child's token
+    __shared__ int s_cid[SV_MAX_TREE_NODES];
+    __shared__ float s_cu[SV_MAX_TREE_NODES];
+    __shared__ float s_clt[SV_MAX_TREE_NODES];
+    __shared__ float s_cld[SV_MAX_TREE_NODES];
+    __shared__ double s_sum;
+    __shared__ double s_norm[2];  // S_t, S_d of the current node
+    __shared__ int s_ref[2];      // R_t, R_d (at temperature 0: the two argmaxes)
+    __shared__ int s_bad, s_accept;
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = t / kWave;
+    const int width = max_depth + 1;
+    const float T = temperature[b];
+    const bool sampled = T > 0.f;
+    int32_t* out = emitted + b * width;
+    int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
+
+    // validity and depths (pointer jumping), as for the greedy tree
+    if (t == 0) s_bad = 0;
+    __syncthreads();
+    const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+    int anc[kWalkSlots], len[kWalkSlots];
+#pragma unroll
+    for (int q = 0; q < kWalkSlots; ++q) {
+        const int i = t + q * kWalkBlock;
+        anc[q] = 0;
+        len[q] = 0;
+        if (i < N) {
+            const int p = i == 0 ? 0 : par[i];
+            if (i > 0 && (p < 0 || p >= i)) s_bad = 1;
+            s_par[i] = i == 0 ? -1 : p;
+            anc[q] = p;
+            len[q] = i == 0 ? 0 : 1;
+        }
+    }
+    __syncthreads();
+    if (!s_bad) {
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            if (i < N) {
+                s_anc[i] = anc[q];
+                s_len[i] = len[q];
+            }
+        }
+        __syncthreads();
+        for (int step = 1; step < N; step <<= 1) {
+            int a2[kWalkSlots], l2[kWalkSlots];
+#pragma unroll
+            for (int q = 0; q < kWalkSlots; ++q) {
+                const bool in = t + q * kWalkBlock < N;
+                a2[q] = in ? s_anc[anc[q]] : 0;
+                l2[q] = in ? s_len[anc[q]] : 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kWalkSlots; ++q) {
+                const int i = t + q * kWalkBlock;
+                if (i < N) {
+                    len[q] += l2[q];
+                    anc[q] = a2[q];
+                    s_anc[i] = anc[q];
+                    s_len[i] = len[q];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q)
+            if (t + q * kWalkBlock < N && len[q] > max_depth) s_bad = 1;
+    }
+    __syncthreads();
+    for (int j = t; j < width; j += kWalkBlock) {
+        out[j] = -1;
+        if (nodes) nodes[j] = -1;
+    }
+    if (s_bad) {
+        if (t == 0) accepted_len[b] = -1;
+        return;
+    }
+
+    SeqInfo s{};
+    temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
+    const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int nmask = (N + kWave - 1) / kWave;
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    int n = 0, d = 0;
+    for (;;) {
+        const int64_t row = (b * N + n) * static_cast<int64_t>(V);
+        // children of n, and the statistics of its target and draft rows
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            const uint64_t km = __ballot(i < N && s_par[i] == n);
+            if (lane == 0 && wave + q * kWalkWaves < nmask) s_kids[wave + q * kWalkWaves] = km;
+        }
+        __syncthreads();
+        // every child reads its own token, uniform and the two logits at that token
+        int nkids = 0;
+        for (int m = 0; m < nmask; ++m) nkids += __popcll(s_kids[m]);
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            const int m = i / kWave;
+            if (i < N && ((s_kids[m] >> (i % kWave)) & 1)) {
+                int rank = __popcll(s_kids[m] & ((uint64_t{1} << (i % kWave)) - 1));
+                for (int m2 = 0; m2 < m; ++m2) rank += __popcll(s_kids[m2]);
+                const int y = node_tokens[b * N + i];
+                const bool yok = static_cast<unsigned>(y) < static_cast<unsigned>(V);
+                s_cid[rank] = yok ? i : -1 - i;  // an id outside [0, V) is rejected
+                s_cu[rank] = uniforms[b * N + i];
+                s_clt[rank] = yok ? load_elem<DT>(target, row + y) : 0.f;
+                s_cld[rank] = yok ? load_elem<DT>(draft, row + y) : 0.f;
+            }
+        }
+        if (wave == 0) {
+            const bool is_draft = lane >= 32;
+            const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+            Partial q[kBatch];
+            group_load(pr, nT, 32, true, q);
+            int r;
+            double sum;
+            ArgMax am;
+            if (sampled) {
+                group_reduce<true>(pr, nT, 32, true, q, r, sum, am);
+            } else {
+                group_reduce<false>(pr, nT, 32, true, q, r, sum, am);
+                r = am.idx;
+            }
+            if ((lane & 31) == 0) {
+                s_ref[is_draft] = r;
+                s_norm[is_draft] = sum;
+            }
+        }
+        __syncthreads();
+        const int Rt = s_ref[0], Rd = s_ref[1];
+        const double St = s_norm[0], Sd = s_norm[1];
+        s.rt = static_cast<float>(Rt);
+        s.inv_st = static_cast<float>(1.0 / St);
+        s.rd = static_cast<float>(Rd);
+        double c = 0.0, Z = 1.0;
+        int next = -1;
+        // log2 of the two normalisers' mantissas, once per node (thread 0 tests)
+        const double lsum = t == 0 && sampled && nkids > 0 ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
+        for (int k = 0; k < nkids && next < 0; ++k) {
+            if (t == 0) {
+                const int id = s_cid[k];
+                double tau = 0.0;
+                if (id >= 0) {
+                    if (sampled) {
+                        // p/q = exp2((l_t - l_d) c - (R_t + log2 S_t) + (R_d + log2 S_d))
+                        const double lt = s_clt[k], ld = s_cld[k];
+                        const double l2ratio = (lt * cT - ld * cT) - lsum;
+                        tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
+                    } else {
+                        const int y = node_tokens[b * N + id];
+                        const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
+                        const double rv = fmax(0.0, pv - c * qv) / Z;
+                        tau = qv > 0.0 ? fmin(1.0, rv / qv) : (rv > 0.0 ? 1.0 : 0.0);
+                    }
+                }
+                s_accept = static_cast<double>(s_cu[k]) < tau;
+            }
+            __syncthreads();
+            if (s_accept) {
+                next = s_cid[k];
+            } else {
+                // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
+                c += Z;
+                if (sampled) {
+                    s.inv_sd = static_cast<float>(c / Sd);
+                    Z = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+                } else {
+                    Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
+                }
+                if (!(Z > 0.0)) {
+                    c = 0.0;
+                    Z = 1.0;
+                }
+            }
+            __syncthreads();
+        }
+        if (next >= 0) {
+            if (t == 0) {
+                out[d] = node_tokens[b * N + next];
+                if (nodes) nodes[d] = next;
+            }
+            ++d;
+            n = next;
+            continue;
+        }
+        // no child kept: the final token from max(0, p - c q) (p when c == 0)
+        int y;
+        if (!sampled) {
+            y = Rt;  // one-hot p; with c > 0 the residual is p itself or empty (then p)
+        } else {
+            const bool residual = c > 0.0;
+            double W = Z;
+            if (!residual) W = walk_masses<DT, VEC, false>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+            y = 0;
+            if (wave == 0)
+                y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, residual, s_mass, W,
+                                       static_cast<double>(uniforms[b * N]));
+        }
+        if (t == 0) {
+            out[d] = y;
+            accepted_len[b] = d;
+        }
+        return;
+    }
+}
+
 // ---------------------------------------------------------------- commit ---
 
 // One workgroup: thread t handles sequences t, t + 1024, ... in rounds of

@@ -93,6 +93,7 @@ const char *sv_status_string(sv_status s);
 size_t sv_chain_workspace_bytes(int B, int k, int V, sv_dtype dt);
 size_t sv_greedy_workspace_bytes(int B, int k, int V, sv_dtype dt);
 size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt);
+size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt);
 
 /*
  * Chain verification with sampling (sections "Speculative decoding" and
@@ -173,6 +174,43 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
                          int max_depth, const void *target_logits,
                          int32_t *accepted_len, int32_t *emitted, int32_t *accepted_nodes,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sampled (stochastic) tree verification.  The pages (section "EAGLE") keep
+ * the longest path of the draft tree that passes but give no rule for a
+ * sampled tree; the rule is the multi-step speculative sampling of SpecInfer
+ * (Miao et al., 2023), the one the EAGLE work uses.
+ *
+ *   node_tokens, parent, parent_stride, max_depth   as for sv_verify_tree;
+ *                 the children of node n are expected to be independent draws
+ *                 from node n's draft distribution (the output then follows the
+ *                 target distribution)
+ *   draft_logits  dt    [B][N][V]  row n: the draft distribution the children of n
+ *                                  were drawn from (rows of leaves are not read)
+ *   target_logits dt    [B][N][V]  row n: the target's prediction after node n
+ *   temperature   f32   [B]        >= 0; 0 means one-hot rows at the lowest-index argmax
+ *   uniforms      f32   [B][N]     in [0,1): u[b][i] tests node i >= 1, u[b][0] drives
+ *                                  the final draw
+ *   accepted_len, emitted, accepted_nodes   out, as for sv_verify_tree: the depth of
+ *                 the last kept node (-1 for an invalid tree), the kept tokens then the
+ *                 final token then -1, the kept node ids then -1
+ *
+ * From the root, the children of the current node n are tested in ascending
+ * index order against a running distribution r that starts as P_target,n:
+ * child i with token y is kept when u[b][i] < min(1, r(y) / P_draft,n(y)) and
+ * the walk moves to it; a rejection replaces r by max(0, r - P_draft,n)
+ * renormalised (by P_target,n itself if that is empty).  When no child is kept
+ * (or n is a leaf) the final token is drawn from r by the inverse CDF over
+ * ascending token ids with u[b][0].  Token ids outside [0,V) are rejected.
+ * One workgroup per sequence walks the tree after a streaming pass over all
+ * target rows and the draft rows of inner nodes.
+ */
+sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt,
+                                 const int32_t *node_tokens, const int32_t *parent, int parent_stride,
+                                 int max_depth, const void *draft_logits, const void *target_logits,
+                                 const float *temperature, const float *uniforms,
+                                 int32_t *accepted_len, int32_t *emitted, int32_t *accepted_nodes,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Commit of one verification step on the device (section "MTP Schedule for

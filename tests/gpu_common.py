@@ -64,3 +64,35 @@ def compare_chain(inp, got, ref, label=""):
         err = np.abs(got["accept_prob"].astype(np.float64) - ref["accept_prob"])
         assert err.max() <= PROB_TOL, f"{label}: accept_prob error {err.max():.3g}"
     return dict(n=int(band.size), banded=int(band.sum()), banded_mismatch=int((mism & band).sum()))
+
+
+def tree_sampled_tensors(inp, device="cuda"):
+    return dict(node_tokens=dev(inp["node_tokens"].astype(np.int32), device),
+                parent=dev(inp["parent"].astype(np.int32), device),
+                draft_logits=dev_logits(inp["draft_logits"], inp["dtype"], device),
+                target_logits=dev_logits(inp["target_logits"], inp["dtype"], device),
+                temperature=dev(inp["temperature"].astype(np.float32), device),
+                uniforms=dev(inp["uniforms"].astype(np.float32), device))
+
+
+def run_tree_sampled(svl, inp, **kw):
+    t = tree_sampled_tensors(inp)
+    out = svl.verify_tree_sampled(t["node_tokens"], t["parent"], int(inp["max_depth"]), t["draft_logits"],
+                                  t["target_logits"], t["temperature"], t["uniforms"], **kw)
+    torch.cuda.synchronize()
+    return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+
+
+def compare_tree_sampled(got, ref, label=""):
+    """Bit-exact accepted_len / emitted / accepted_nodes outside the oracle's
+    band.  Returns the band statistics."""
+    band = ref["band"]
+    mism = ((got["accepted_len"] != ref["accepted_len"]) | (got["emitted"] != ref["emitted"]).any(axis=1) |
+            (got["accepted_nodes"] != ref["accepted_nodes"]).any(axis=1))
+    bad = np.flatnonzero(mism & ~band)
+    assert bad.size == 0, (
+        f"{label}: {bad.size} sequences differ outside the band, e.g. b={bad[0]}: "
+        f"gpu a={got['accepted_len'][bad[0]]} em={got['emitted'][bad[0]].tolist()} "
+        f"nodes={got['accepted_nodes'][bad[0]].tolist()} oracle a={ref['accepted_len'][bad[0]]} "
+        f"em={ref['emitted'][bad[0]].tolist()} nodes={ref['accepted_nodes'][bad[0]].tolist()}")
+    return dict(n=int(band.size), banded=int(band.sum()), banded_mismatch=int((mism & band).sum()))

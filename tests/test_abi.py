@@ -161,3 +161,28 @@ def test_commit_rejects_bad_arguments_on_the_host(lib):
     assert c(em=None) == INVALID
     assert c(sl=None) == INVALID
     assert c(B=0, acc=None, em=None, sl=None, hist=None) == OK
+
+
+def test_tree_sampled_rejects_bad_arguments_on_the_host(lib):
+    def t(B=2, N=8, V=50, dt=F32, tok=FAKE, par=FAKE, stride=0, md=3, draft=FAKE, target=FAKE, temp=FAKE, u=FAKE,
+          acc=FAKE, em=FAKE, nodes=None, ws=FAKE, ws_bytes=1 << 20):
+        return lib.sv_verify_tree_sampled(B, N, V, dt, tok, par, stride, md, draft, target, temp, u, acc, em, nodes,
+                                          ws, ws_bytes, None)
+
+    assert lib.sv_tree_sampled_workspace_bytes(16, 64, 128256, BF16) == 2 * lib.sv_tree_workspace_bytes(
+        16, 64, 128256, BF16)
+    assert lib.sv_tree_sampled_workspace_bytes(16, 1025, 128256, BF16) == 0
+    assert t(B=-1) == INVALID
+    assert t(N=0) == INVALID
+    assert t(md=-1) == INVALID
+    assert t(stride=4) == INVALID
+    assert t(V=0) == INVALID
+    assert t(dt=3) == INVALID
+    assert t(N=1025) == UNSUPPORTED
+    assert t(V=(1 << 20) + 1) == UNSUPPORTED
+    for key in ("tok", "par", "draft", "target", "temp", "u", "acc", "em"):
+        assert t(**{key: None}) == INVALID, key
+    assert t(ws_bytes=8) == WS_SMALL
+    assert t(ws=ctypes.c_void_p(0x1008)) == INVALID
+    assert t(B=0, tok=None, par=None, draft=None, target=None, temp=None, u=None, acc=None, em=None, ws=None,
+             ws_bytes=0) == OK

@@ -1,0 +1,163 @@
+"""Parity of sampled tree verification (sv_verify_tree_sampled, through the C
+ABI) with the fp64 CPU oracle.
+
+accepted_len, emitted and accepted_nodes must match bit-exactly, except for
+sequences the oracle flags as lying within 1e-5 of an acceptance threshold or
+CDF boundary (counted and reported).  Rule: multi-step speculative sampling
+(SpecInfer, Miao et al. 2023), the rule the EAGLE work uses for sampled
+trees; the pages' section "EAGLE" keeps the longest path that passes.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_common import compare_tree_sampled, run_tree_sampled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def svl():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_token_verification_chain_amd as svl
+
+    svl.load()
+    return svl
+
+
+def _record(label, stats):
+    path = os.environ.get("SV_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(dict(kind="tree_sampled", case=label, **stats)) + "\n")
+    print(f"[parity] tree_sampled {label} {stats}", flush=True)
+
+
+def _check(svl, orc, inp, label):
+    print(f"[case] {label}", flush=True)
+    got = run_tree_sampled(svl, inp)
+    ref = orc.verify_tree_sampled(inp)
+    _record(label, compare_tree_sampled(got, ref, label))
+    return got, ref
+
+
+SHAPES = [
+    # B, N, V, dtype, temperature (None: mixed, a quarter of the rows at 0)
+    (8, 20, 3001, W.F32, 0.8),
+    (6, 64, 5000, W.BF16, 0.7),
+    (5, 33, 4097, W.BF16, None),
+    (3, 100, 1000, W.F32, 1.2),
+    (4, 1, 2000, W.BF16, 0.9),       # the root alone: a plain draw from its target row
+    (3, 64, 128257, W.BF16, 0.6),    # odd V: element loads, many segments
+    (2, 40, 65536, W.F32, 0.5),
+]
+
+
+def _temps(B, T, seed):
+    if T is not None:
+        return T
+    t = np.random.default_rng(seed).uniform(0.3, 1.3, B).astype(np.float32)
+    t[::4] = 0.0
+    return t
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}N{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_small_shapes(svl, orc, shape, seed):
+    B, N, V, dt, T = shape
+    inp = W.sampled_tree_inputs(B, N, V, dt, seed, temperature=_temps(B, T, seed), draft_sigma=(0.3, 2.5))
+    _check(svl, orc, inp, f"B{B}N{N}V{V}dt{dt}s{seed}")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_full_sampled_tree_config(svl, orc, seed):
+    inp = W.make_inputs(8, seed)
+    got, ref = _check(svl, orc, inp, f"config8 s{seed}")
+    assert (got["accepted_len"] >= 0).all()
+
+
+def test_linear_deep_and_wide_star_trees(svl, orc):
+    """A chain-shaped tree of depth 63 and a one-level tree of 300 children
+    (up to 300 sequential rejections at the root)."""
+    lin = np.arange(-1, 63, dtype=np.int32)
+    inp = W.sampled_tree_inputs(4, 64, 3000, W.BF16, 4, parent=lin, max_depth=63, draft_sigma=0.3)
+    _check(svl, orc, inp, "linear64")
+    star = np.zeros(301, dtype=np.int32)
+    star[0] = -1
+    inp = W.sampled_tree_inputs(3, 301, 2000, W.F32, 5, parent=star, max_depth=1, draft_sigma=3.0)
+    _check(svl, orc, inp, "star300")
+
+
+def test_max_nodes(svl, orc):
+    inp = W.sampled_tree_inputs(2, 1024, 600, W.BF16, 6, max_branch=8, max_depth=12, draft_sigma=(0.5, 2.0))
+    _check(svl, orc, inp, "N1024")
+
+
+def test_identical_rows_keep_first_children(svl, orc):
+    inp = W.sampled_tree_inputs(6, 48, 4000, W.BF16, 7)
+    inp["draft_logits"] = inp["target_logits"].copy()
+    got, ref = _check(svl, orc, inp, "identical")
+    assert (got["accepted_len"] == ref["accepted_len"]).all()
+
+
+def test_per_sequence_parents_and_invalid_trees(svl, orc):
+    inp = W.sampled_tree_inputs(4, 24, 1500, W.F32, 8)
+    par = np.stack([W.random_tree(24, s) for s in (11, 12, 13, 14)]).astype(np.int32)
+    par[2, 9] = 15  # a parent after its child: sequence 2 is invalid
+    inp["parent"] = par
+    inp["max_depth"] = 23
+    got, ref = _check(svl, orc, inp, "per-sequence")
+    assert got["accepted_len"][2] == -1 and (got["emitted"][2] == -1).all()
+    inp["max_depth"] = 1  # now deeper nodes make every sequence with depth > 1 invalid
+    _check(svl, orc, inp, "too-deep")
+
+
+def test_determinism(svl, orc):
+    inp = W.sampled_tree_inputs(6, 64, 20000, W.BF16, 9)
+    a = run_tree_sampled(svl, inp)
+    for _ in range(3):
+        b = run_tree_sampled(svl, inp)
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_gpu_sampled_tree_distribution_chi_square(svl, orc):
+    """The chi-square of the oracle's pin, through the GPU: 5 * 10^5 trials on
+    the two-level tree (V = 8); each emitted token follows the target row of
+    the token before it."""
+    from scipy import special, stats
+
+    rng = np.random.default_rng(4242)
+    V = 8
+    root_t = (1.5 * rng.standard_normal(V)).astype(np.float32)
+    root_d = (root_t + rng.standard_normal(V)).astype(np.float32)
+    F = (1.5 * rng.standard_normal((V, V))).astype(np.float32)
+    G = (F + rng.standard_normal((V, V))).astype(np.float32)
+    H = (1.5 * rng.standard_normal((V, V))).astype(np.float32)
+    acc, em = [], []
+    for blk in range(2):
+        inp = W.sampled_tree_trials(root_t, root_d, F, G, H, 1.0, 250_000, seed=93, block=blk)
+        r = run_tree_sampled(svl, inp)
+        if blk == 0:  # element by element too: every trial sequence of the first block
+            _record("chi-square trials", compare_tree_sampled(r, orc.verify_tree_sampled(inp), "trials"))
+        acc.append(r["accepted_len"])
+        em.append(r["emitted"])
+    acc, em = np.concatenate(acc), np.concatenate(em)
+    sm = lambda x: special.softmax(np.asarray(x, np.float64), axis=-1)  # noqa: E731
+    pv = [stats.chisquare(np.bincount(em[:, 0], minlength=V), sm(root_t) * len(acc)).pvalue]
+    for j, table in ((1, F), (2, H)):
+        sel = acc >= j
+        obs = np.bincount(em[sel, j - 1] * V + em[sel, j], minlength=V * V).reshape(V, V)
+        n_prev = obs.sum(axis=1)
+        keep = n_prev > 0
+        exp = n_prev[:, None] * sm(table)
+        pv.append(stats.chisquare(obs[keep].ravel(), exp[keep].ravel(), ddof=int(keep.sum()) - 1).pvalue)
+    print(f"[chi2] sampled tree p-values {pv}", flush=True)
+    assert min(pv) > 1e-4, pv
