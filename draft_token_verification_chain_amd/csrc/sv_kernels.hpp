@@ -58,14 +58,11 @@ __device__ __forceinline__ void temperature_scale(float T, float& c_hi, float& c
 
 // ---------------------------------------------------------------- wave tiles ---
 
-// Softmax partial of one tile: s = sum_v exp2(l_v c - r) with r = ceil(max l c)
-// taken over the whole tile, so exp2 never exceeds ~1 and never overflows.
-template <int DT, bool VEC, int U, bool FULL>
-__device__ __forceinline__ Partial tile_softmax(const void* base, int64_t row_elem, int V, int64_t tile,
-                                                float c_hi, float c_lo) {
-    constexpr int NE = U * Elem<DT>::per_vec;
-    float v[NE];
-    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane_id(), v);
+// Softmax partial of one tile whose logits are loaded: s = sum_v exp2(l_v c - r)
+// with r = ceil(max l c) taken over the whole tile, so exp2 never exceeds ~1
+// and never overflows.
+template <int NE, bool FULL>
+__device__ __forceinline__ Partial softmax_of_tile(const float* v, float c_hi, float c_lo) {
     float mx = v[0];
 #pragma unroll
     for (int j = 1; j < NE; ++j) mx = fmaxf(mx, v[j]);
@@ -108,15 +105,7 @@ __device__ __forceinline__ ArgMax tile_argmax(const void* base, int64_t row_elem
     return argmax_of_tile<DT, U>(v, tile);
 }
 
-// Tile entry points that pick the unmasked path for tiles inside the row.
-template <int DT, bool VEC, int U>
-__device__ __forceinline__ Partial tile_softmax_any(const void* base, int64_t row_elem, int V, int64_t tile,
-                                                    float c_hi, float c_lo) {
-    if (tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec))
-        return tile_softmax<DT, VEC, U, VEC>(base, row_elem, V, tile, c_hi, c_lo);
-    return tile_softmax<DT, VEC, U, false>(base, row_elem, V, tile, c_hi, c_lo);
-}
-
+// Tile entry point that picks the unmasked path for tiles inside the row.
 template <int DT, bool VEC, int U>
 __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_elem, int V, int64_t tile) {
     if (tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec))
@@ -243,11 +232,28 @@ __device__ __forceinline__ int64_t global_wave() {
 
 // ---------------------------------------------------------------- chain: rowstats ---
 
+// The partial of one tile of a row of sequence b: the tile's loads are issued
+// before the temperature is known, which then selects softmax or argmax.
+template <int DT, bool VEC, int U, bool FULL>
+__device__ __forceinline__ Partial rowstats_tile(const void* base, int64_t row_elem, int V, int64_t tile, float T) {
+    constexpr int NE = U * Elem<DT>::per_vec;
+    float v[NE];
+    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane_id(), v);
+    if (T > 0.f) {
+        float c_hi, c_lo;
+        temperature_scale(T, c_hi, c_lo);
+        return softmax_of_tile<NE, FULL>(v, c_hi, c_lo);
+    }
+    const ArgMax a = argmax_of_tile<DT, U>(v, tile);
+    return Partial{a.val, a.idx};
+}
+
 // Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
-// rows (b, i).  Draft rows of temperature-0 sequences are not needed (the
-// one-hot target decides alone) and are skipped.  The wave streaming tile 0
-// of a sampled row also reads the row's logit at its draft token into
-// gathered[r], so that the acceptance needs no dependent gather.
+// rows (b, i).  The wave streaming tile 0 of a row also reads the row's logit
+// at its draft token into gathered[r], so that the acceptance needs no
+// dependent gather.  Draft rows of temperature-0 sequences are streamed too,
+// and their partials go unused: deciding to skip them would put the
+// temperature's load in front of every wave's tile loads.
 template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __restrict__ target,
                                                                 const void* __restrict__ draft,
@@ -264,24 +270,17 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
     const bool is_target = r < nbk;
     const int64_t rr = is_target ? r : r - nbk;
     const int64_t b = rr / k;
-    const float T = temperature[b];
     const void* base = is_target ? target : draft;
     const int64_t row_elem = (is_target ? (b * (k + 1) + (rr - b * k)) : rr) * static_cast<int64_t>(V);
-    Partial p;
-    if (T > 0.f) {
-        if (tile == 0) {
-            const int x = tokens[rr];  // draft token scored by this row (rr = b * k + position)
-            if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
-                gathered[r] = load_elem<DT>(base, row_elem + x);
-        }
-        float c_hi, c_lo;
-        temperature_scale(T, c_hi, c_lo);
-        p = tile_softmax_any<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
-    } else {
-        if (!is_target) return;
-        const ArgMax a = tile_argmax_any<DT, VEC, U>(base, row_elem, V, tile);
-        p = Partial{a.val, a.idx};
+    if (tile == 0) {
+        const int x = tokens[rr];  // draft token scored by this row (rr = b * k + position)
+        if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
+            gathered[r] = load_elem<DT>(base, row_elem + x);
     }
+    const float T = temperature[b];
+    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
+                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
     if (lane_id() == 0) part[r * nT + tile] = p;
 }
 
@@ -950,18 +949,12 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
         for (int i = n + 1 + lane_id(); i < N; i += kWave) kid |= par[i] == n;
         if (!__ballot(kid)) return;
     }
-    const float T = temperature[b];
     const void* base = is_target ? target : draft;
     const int64_t row_elem = rr * static_cast<int64_t>(V);
-    Partial p;
-    if (T > 0.f) {
-        float c_hi, c_lo;
-        temperature_scale(T, c_hi, c_lo);
-        p = tile_softmax_any<DT, VEC, U>(base, row_elem, V, tile, c_hi, c_lo);
-    } else {
-        const ArgMax a = tile_argmax_any<DT, VEC, U>(base, row_elem, V, tile);
-        p = Partial{a.val, a.idx};
-    }
+    const float T = temperature[b];
+    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
+                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
     if (lane_id() == 0) part[r * nT + tile] = p;
 }
 
