@@ -50,6 +50,15 @@ struct SeqInfo {
     int pad[3];
 };
 
+// log2 of a positive double with an exact exponent and an fp32 log2 of the
+// mantissa in [0.5, 1): absolute error about 1.5e-7, far below the 1e-5 band
+// within which acceptance decisions are allowed to differ.
+__device__ __forceinline__ double log2_of_sum(double x) {
+    int e;
+    const double m = frexp(x, &e);
+    return static_cast<double>(e) + static_cast<double>(log2f(static_cast<float>(m)));
+}
+
 __device__ __forceinline__ void temperature_scale(float T, float& c_hi, float& c_lo) {
     const double c = kLog2e / static_cast<double>(T);
     c_hi = static_cast<float>(c);
@@ -363,9 +372,10 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
             sd = s_s[k + lane];
             const double c = kLog2e / static_cast<double>(T);
             // log2 p - log2 q with log2 p = l c - R - log2 S (the same for q)
-            const double l2ratio = (static_cast<double>(lt) * c - rt - log2(st)) -
-                                   (static_cast<double>(ld) * c - rd - log2(sd));
-            tau = exp2(fmin(0.0, l2ratio));
+            const double l2ratio = (static_cast<double>(lt) * c - rt - log2_of_sum(st)) -
+                                   (static_cast<double>(ld) * c - rd - log2_of_sum(sd));
+            // exp2 of a non-positive argument in fp32: relative error about 1e-7
+            tau = static_cast<double>(exp2f(static_cast<float>(fmin(0.0, l2ratio))));
             acc = static_cast<double>(ui) < tau;
         } else {
             acc = (x == g);
