@@ -186,3 +186,46 @@ def test_tree_sampled_rejects_bad_arguments_on_the_host(lib):
     assert t(ws=ctypes.c_void_p(0x1008)) == INVALID
     assert t(B=0, tok=None, par=None, draft=None, target=None, temp=None, u=None, acc=None, em=None, ws=None,
              ws_bytes=0) == OK
+
+
+C_CONSUMER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "specverify.h"
+
+int main(void) {
+    if (sv_version() < 100) return 1;
+    if (strncmp(sv_status_string(SV_ERR_INVALID_ARGUMENT), "SV_", 3) != 0) return 2;
+    if (sv_chain_workspace_bytes(64, 4, 128256, SV_BF16) == 0) return 3;
+    if (sv_tree_sampled_workspace_bytes(16, 64, 128256, SV_BF16) == 0) return 4;
+    /* rejected on the host: no launch */
+    if (sv_verify_chain(-1, 4, 100, SV_F32, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL)
+        != SV_ERR_INVALID_ARGUMENT) return 5;
+    if (sv_verify_greedy(2, SV_MAX_DRAFTS + 1, 100, SV_BF16, NULL, NULL, NULL, NULL, NULL, 0, NULL)
+        != SV_ERR_UNSUPPORTED) return 6;
+    /* an empty batch is a no-op */
+    if (sv_verify_tree(0, 4, 100, SV_F32, NULL, NULL, 0, 3, NULL, NULL, NULL, NULL, NULL, 0, NULL) != SV_OK) return 7;
+    if (sv_commit_tokens(0, 5, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL) != SV_OK) return 8;
+    puts("ok");
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """A C11 program includes include/specverify.h, links against the shared
+    library and calls it (only calls that return before any launch)."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(bnd.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", str(src), "-o", str(exe),
+                           "-L", libdir, "-lspecverify", f"-Wl,-rpath,{libdir}"])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr)
