@@ -116,8 +116,11 @@ sv_status launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 blo
         std::lock_guard<std::mutex> lk(g_prof.mu);
         if (g_prof.next < g_prof.slots.size()) slot = &g_prof.slots[g_prof.next++];
     }
-    const hipError_t err = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream,
-                                              slot ? slot->start : nullptr, slot ? slot->stop : nullptr, 0);
+    // without profiling, the plain launch (the form HIP graph capture records)
+    const hipError_t err =
+        slot ? hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream, slot->start,
+                                  slot->stop, 0)
+             : hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
     if (err != hipSuccess) {
         (void)hipGetLastError();
         return SV_ERR_HIP;
