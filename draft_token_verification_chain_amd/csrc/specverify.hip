@@ -83,6 +83,31 @@ ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
     return L;
 }
 
+// The sampled-tree workspace: partials of every node's two rows, the
+// children's gathered logits, the walk's double-buffered state and pass
+// partial sums (P slices per sequence), and the final draw's segment masses.
+struct TreeSampledLayout {
+    int P;
+    size_t part, tg, dg, state, z, tsegs, total;
+};
+
+TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
+    TreeSampledLayout L{};
+    const int64_t nseg = segments_per_row(V, dt);
+    // slices of at least four segments, about 1024 workgroups per round
+    const int64_t want = (1024 + std::max(B, 1) - 1) / std::max(B, 1);
+    L.P = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, (nseg + 3) / 4)));
+    const size_t bn = static_cast<size_t>(B) * N;
+    L.part = 0;
+    L.tg = align_up(sizeof(Partial) * 2 * bn * tiles_per_row(V, dt));
+    L.dg = align_up(L.tg + sizeof(float) * bn);
+    L.state = align_up(L.dg + sizeof(float) * bn);
+    L.z = align_up(L.state + sizeof(sv::WalkState) * 2 * static_cast<size_t>(B));
+    L.tsegs = align_up(L.z + sizeof(double) * 2 * static_cast<size_t>(B) * L.P);
+    L.total = align_up(L.tsegs + sizeof(float) * static_cast<size_t>(B) * nseg);
+    return L;
+}
+
 // ---------------------------------------------------------------- kernel timing ---
 
 struct ProfSlot {
@@ -240,7 +265,7 @@ size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt) {
 
 size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt) {
     if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
-    return align_up(sizeof(Partial) * static_cast<size_t>(2) * B * N * tiles_per_row(V, dt));
+    return tree_sampled_layout(B, N, V, dt).total;
 }
 
 sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* draft_logits,
@@ -335,20 +360,46 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
     const int nT = static_cast<int>(tiles_per_row(V, dt));
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits) &&
                      aligned16(draft_logits);
-    auto* part = static_cast<Partial*>(workspace);
+    const TreeSampledLayout L = tree_sampled_layout(B, N, V, dt);
+    if (static_cast<int64_t>(B) * L.P > kMaxGrid) return SV_ERR_UNSUPPORTED;
+    char* ws = static_cast<char*>(workspace);
+    auto* part = reinterpret_cast<Partial*>(ws + L.part);
+    auto* tg = reinterpret_cast<float*>(ws + L.tg);
+    auto* dg = reinterpret_cast<float*>(ws + L.dg);
+    auto* state = reinterpret_cast<sv::WalkState*>(ws + L.state);
+    auto* z = reinterpret_cast<double*>(ws + L.z);
+    auto* tsegs = reinterpret_cast<float*>(ws + L.tsegs);
     const unsigned blocks = static_cast<unsigned>(blocks_for_waves(static_cast<int64_t>(2) * B * N * nT));
     auto rowstats = dt == SV_BF16 ? (vec ? sv::tree_rowstats_kernel<SV_BF16, true, kU>
                                          : sv::tree_rowstats_kernel<SV_BF16, false, kU>)
                                   : (vec ? sv::tree_rowstats_kernel<SV_F32, true, kU>
                                          : sv::tree_rowstats_kernel<SV_F32, false, kU>);
-    st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits, draft_logits, parent,
-                parent_stride, temperature, B, N, V, nT, part);
+    st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits,
+                          draft_logits, parent, parent_stride, node_tokens, temperature, B, N, V, nT, part, tg, dg);
     if (st != SV_OK) return st;
+    st = launch("tree_walk_init", sv::tree_walk_init_kernel, dim3(B), dim3(sv::kWalkBlock), stream, parent,
+                parent_stride, N, max_depth, state, accepted_len, emitted, accepted_nodes);
+    if (st != SV_OK) return st;
+    auto round = dt == SV_BF16 ? (vec ? sv::tree_round_kernel<SV_BF16, true> : sv::tree_round_kernel<SV_BF16, false>)
+                               : (vec ? sv::tree_round_kernel<SV_F32, true> : sv::tree_round_kernel<SV_F32, false>);
+    for (int r = 0; r < sv::kWalkRounds; ++r) {
+        st = launch("tree_round", round, dim3(static_cast<unsigned>(static_cast<int64_t>(B) * L.P)),
+                    dim3(sv::kRoundBlock), stream, node_tokens, parent, parent_stride, N, max_depth, draft_logits,
+                    target_logits, temperature, uniforms, B, V, nT, static_cast<const Partial*>(part),
+                    static_cast<const float*>(tg), static_cast<const float*>(dg),
+                    static_cast<const sv::WalkState*>(state + (r & 1) * B), state + ((r + 1) & 1) * B,
+                    static_cast<const double*>(z + static_cast<size_t>(r & 1) * B * L.P),
+                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, L.P, accepted_len, emitted,
+                    accepted_nodes);
+        if (st != SV_OK) return st;
+    }
+    // sequences the rounds have not finished: the one-workgroup walk, from the start
     auto walk = dt == SV_BF16 ? (vec ? sv::tree_sample_kernel<SV_BF16, true> : sv::tree_sample_kernel<SV_BF16, false>)
                               : (vec ? sv::tree_sample_kernel<SV_F32, true> : sv::tree_sample_kernel<SV_F32, false>);
     return launch("tree_sample", walk, dim3(B), dim3(sv::kWalkBlock), stream, node_tokens, parent, parent_stride, N,
                   max_depth, draft_logits, target_logits, temperature, uniforms, B, V, nT,
-                  static_cast<const Partial*>(part), accepted_len, emitted, accepted_nodes);
+                  static_cast<const Partial*>(part), static_cast<const sv::WalkState*>(state + (sv::kWalkRounds & 1) * B),
+                  accepted_len, emitted, accepted_nodes);
 }
 
 sv_status sv_commit_tokens(int B, int width, const int32_t* accepted_len, const int32_t* emitted, int32_t* seq_len,

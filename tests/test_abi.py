@@ -169,7 +169,7 @@ def test_tree_sampled_rejects_bad_arguments_on_the_host(lib):
         return lib.sv_verify_tree_sampled(B, N, V, dt, tok, par, stride, md, draft, target, temp, u, acc, em, nodes,
                                           ws, ws_bytes, None)
 
-    assert lib.sv_tree_sampled_workspace_bytes(16, 64, 128256, BF16) == 2 * lib.sv_tree_workspace_bytes(
+    assert lib.sv_tree_sampled_workspace_bytes(16, 64, 128256, BF16) > 2 * lib.sv_tree_workspace_bytes(
         16, 64, 128256, BF16)
     assert lib.sv_tree_sampled_workspace_bytes(16, 1025, 128256, BF16) == 0
     assert t(B=-1) == INVALID
