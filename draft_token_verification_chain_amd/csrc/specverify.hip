@@ -377,9 +377,6 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
     st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits,
                           draft_logits, parent, parent_stride, node_tokens, temperature, B, N, V, nT, part, tg, dg);
     if (st != SV_OK) return st;
-    st = launch("tree_walk_init", sv::tree_walk_init_kernel, dim3(B), dim3(sv::kWalkBlock), stream, parent,
-                parent_stride, N, max_depth, state, accepted_len, emitted, accepted_nodes);
-    if (st != SV_OK) return st;
     auto round = dt == SV_BF16 ? (vec ? sv::tree_round_kernel<SV_BF16, true> : sv::tree_round_kernel<SV_BF16, false>)
                                : (vec ? sv::tree_round_kernel<SV_F32, true> : sv::tree_round_kernel<SV_F32, false>);
     for (int r = 0; r < sv::kWalkRounds; ++r) {
@@ -389,8 +386,8 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                     static_cast<const float*>(tg), static_cast<const float*>(dg),
                     static_cast<const sv::WalkState*>(state + (r & 1) * B), state + ((r + 1) & 1) * B,
                     static_cast<const double*>(z + static_cast<size_t>(r & 1) * B * L.P),
-                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, L.P, accepted_len, emitted,
-                    accepted_nodes);
+                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, L.P, r == 0 ? 1 : 0, accepted_len,
+                    emitted, accepted_nodes);
         if (st != SV_OK) return st;
     }
     // sequences the rounds have not finished: the one-workgroup walk, from the start

@@ -1119,11 +1119,14 @@ __device__ int walk_pick(const void* draft, const void* target, int64_t row, int
 }
 
 // Validity of a tree and the depth of every node (pointer jumping over the
-// parent links), as for the greedy tree: kWalkBlock threads with kWalkSlots
-// node slots each.  Fills s_par (parent ids, -1 for the root) and returns
-// whether the tree is invalid, in every thread.
+// parent links), as for the greedy tree: BLOCK threads with
+// SV_MAX_TREE_NODES / BLOCK node slots each.  Fills s_par (parent ids, -1 for
+// the root) and returns whether the tree is invalid, in every thread.
+template <int BLOCK>
 __device__ bool walk_validate(const int32_t* __restrict__ par, int N, int max_depth, int* s_par, int* s_anc,
                               int* s_len, int* s_bad) {
+    constexpr int kWalkSlots = SV_MAX_TREE_NODES / BLOCK;
+    constexpr int kWalkBlock = BLOCK;
     const int t = threadIdx.x;
     if (t == 0) *s_bad = 0;
     __syncthreads();
@@ -1232,8 +1235,8 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
 
     // validity and depths (pointer jumping), as for the greedy tree
-    const bool bad =
-        walk_validate(parent + b * static_cast<int64_t>(parent_stride), N, max_depth, s_par, s_anc, s_len, &s_bad);
+    const bool bad = walk_validate<kWalkBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth, s_par,
+                                               s_anc, s_len, &s_bad);
     for (int j = t; j < width; j += kWalkBlock) {
         out[j] = -1;
         if (nodes) nodes[j] = -1;
@@ -1386,40 +1389,14 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
 // round later the slices are summed (in a fixed order) and the tests go on.
 // When no child is kept, each workgroup writes its slice's segment masses of
 // the final distribution and the next round's chunk 0 picks the token.
-// Chunk 0 writes the outputs and the next state.  A sequence not finished
-// after the launched rounds is walked again from the start by tree_sample.
+// Chunk 0 writes the outputs and the next state.  Round 0 also checks each
+// tree (invalid trees give -1 outputs) and sets the outputs to -1.  A
+// sequence not finished after the launched rounds is walked again from the
+// start by tree_sample.
 constexpr int kRoundBlock = 256;
 constexpr int kRoundWaves = kRoundBlock / kWave;
 constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;
 constexpr int kWalkRounds = 8;
-
-// One workgroup per sequence: validity, outputs set to -1, the first state.
-__global__ __launch_bounds__(kWalkBlock) void tree_walk_init_kernel(const int32_t* __restrict__ parent,
-                                                                    int parent_stride, int N, int max_depth,
-                                                                    WalkState* __restrict__ state,
-                                                                    int32_t* __restrict__ accepted_len,
-                                                                    int32_t* __restrict__ emitted,
-                                                                    int32_t* __restrict__ accepted_nodes) {
-    __shared__ int s_par[SV_MAX_TREE_NODES];
-    __shared__ int s_anc[SV_MAX_TREE_NODES];
-    __shared__ int s_len[SV_MAX_TREE_NODES];
-    __shared__ int s_bad;
-    const int64_t b = blockIdx.x;
-    const int width = max_depth + 1;
-    const bool bad =
-        walk_validate(parent + b * static_cast<int64_t>(parent_stride), N, max_depth, s_par, s_anc, s_len, &s_bad);
-    for (int j = threadIdx.x; j < width; j += kWalkBlock) {
-        emitted[b * width + j] = -1;
-        if (accepted_nodes) accepted_nodes[b * width + j] = -1;
-    }
-    if (threadIdx.x == 0) {
-        WalkState st{};
-        st.phase = bad ? kWalkDone : kWalkEnter;
-        st.Z = 1.0;
-        state[b] = st;
-        if (bad) accepted_len[b] = -1;
-    }
-}
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
@@ -1428,10 +1405,13 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ tg, const float* __restrict__ dg,
     const WalkState* __restrict__ st_in, WalkState* __restrict__ st_out, const double* __restrict__ z_in,
-    double* __restrict__ z_out, float* __restrict__ tsegs, int P, int32_t* __restrict__ accepted_len,
+    double* __restrict__ z_out, float* __restrict__ tsegs, int P, int first, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
     constexpr int VE = Elem<DT>::per_vec;
     __shared__ int s_par[SV_MAX_TREE_NODES];
+    __shared__ int s_anc[SV_MAX_TREE_NODES];
+    __shared__ int s_len[SV_MAX_TREE_NODES];
+    __shared__ int s_bad;
     __shared__ int s_tok[SV_MAX_TREE_NODES];
     __shared__ float s_u[SV_MAX_TREE_NODES];
     __shared__ float s_tg[SV_MAX_TREE_NODES];
@@ -1448,14 +1428,30 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const int lane = lane_id();
     const int wave = t / kWave;
     const bool lead = j == 0;  // chunk 0 writes the outputs and the next state
-    WalkState st = st_in[b];
+    const int width = max_depth + 1;
+    int32_t* out = emitted + b * width;
+    int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
+    WalkState st{};
+    if (first) {
+        const bool bad = walk_validate<kRoundBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth,
+                                                    s_par, s_anc, s_len, &s_bad);
+        if (lead) {
+            for (int q = t; q < width; q += kRoundBlock) {
+                out[q] = -1;
+                if (nodes) nodes[q] = -1;
+            }
+        }
+        __syncthreads();  // the -1s before any path write of this workgroup
+        st.phase = bad ? kWalkDone : kWalkEnter;
+        st.Z = 1.0;
+        if (bad && lead && t == 0) accepted_len[b] = -1;
+    } else {
+        st = st_in[b];
+    }
     if (st.phase == kWalkDone || st.phase == kWalkStuck) {
         if (lead && t == 0) st_out[b] = st;
         return;
     }
-    const int width = max_depth + 1;
-    int32_t* out = emitted + b * width;
-    int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
     const float T = temperature[b];
     const bool sampled = T > 0.f;
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
