@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -39,10 +40,15 @@ KERNEL_SOURCES = ["draft_token_verification_chain_amd/csrc/sv_common.hpp",
 
 
 def kernel_source_digest() -> str:
+    """Digest of the kernel sources' code: comments and whitespace are
+    dropped, so that only a change of code marks stored counters stale."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,8 +4,9 @@
 //
 // Scheme: "Accelerating Sonar through speculation" (Perplexity, 2025); the
 // entry points correspond to its sections "Target-Draft" (chain
-// verification with sampling), "Speculative decoding" (greedy matching) and
-// "EAGLE" (tree verification).
+// verification with sampling), "Speculative decoding" (greedy matching),
+// "EAGLE" (tree verification, greedy and sampled) and "MTP Schedule for a
+// Single Token" (the device-side commit).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

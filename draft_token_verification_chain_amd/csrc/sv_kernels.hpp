@@ -8,7 +8,9 @@
 //   accept     one wave per sequence: combines the row partials, gathers the
 //              2k logits at the draft tokens, forms tau_i in the log domain,
 //              takes the first rejection with a ballot, writes the accepted
-//              prefix and a descriptor of the final draw;
+//              prefix and a descriptor of the final draw -- inside every
+//              final_part workgroup for small draws, as its own kernel for
+//              large ones, not at all without drafts;
 //   final_part streams only the row(s) the final draw needs (target and draft
 //              row a at a rejection, target row k after full acceptance) and
 //              writes the residual mass of every 64-vector segment;
@@ -16,11 +18,15 @@
 //              the segment holding u * W and rescans only that segment to find
 //              the token.
 // sv_verify_greedy and sv_verify_tree use argmax_rows (the streaming argmax)
-// followed by a per-sequence finaliser.
+// followed by a per-sequence finaliser.  sv_verify_tree_sampled streams the
+// tree's rows (tree_rowstats), then walks every tree in rounds of launches
+// (tree_round), with a one-workgroup walk (tree_sample) for what the rounds
+// leave.  sv_commit_tokens is one workgroup (commit_tokens).
 //
 // Scheme: "Accelerating Sonar through speculation" (Perplexity, 2025),
 // sections "Speculative decoding", "Target-Draft" and "EAGLE"; acceptance
-// and residual rule of Leviathan et al., first in that page's references.
+// and residual rule of Leviathan et al., first in that page's references;
+// sampled trees: multi-step speculative sampling (SpecInfer, Miao et al.).
 #pragma once
 
 #include "sv_common.hpp"
@@ -125,29 +131,6 @@ __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_
 // Partials are read kBatch at a time so that their loads are in flight
 // together rather than one round trip each.
 constexpr int kBatch = 8;
-
-// Combine the nT softmax partials of one row: R = max r_t, S = sum s_t 2^(r_t - R).
-// Single pass: when a larger reference appears the running sum is rescaled by
-// a power of two, which is exact, so the result equals the two-pass sum.
-__device__ inline void combine_softmax(const Partial* p, int nT, int& R, double& S) {
-    int r = p[0].i;
-    double s = static_cast<double>(p[0].f);
-    for (int t0 = 1; t0 < nT; t0 += kBatch) {
-        Partial q[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) q[j] = (t0 + j < nT) ? p[t0 + j] : Partial{0.f, r};
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (q[j].i > r) {
-                s = ldexp(s, r - q[j].i);
-                r = q[j].i;
-            }
-            s += ldexp(static_cast<double>(q[j].f), q[j].i - r);
-        }
-    }
-    R = r;
-    S = s;
-}
 
 // Combine the nT argmax partials of one row (one lane, sequential).
 __device__ inline ArgMax combine_argmax(const Partial* p, int nT) {
