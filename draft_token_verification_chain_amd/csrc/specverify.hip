@@ -50,6 +50,11 @@ int64_t blocks_for_waves(int64_t waves) { return (waves + sv::kWavesPerBlock - 1
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
+// Largest accepted max_depth of the tree entry points (output rows of
+// max_depth + 1 entries; no tree of SV_MAX_TREE_NODES nodes is deeper than
+// SV_MAX_TREE_NODES - 1, so this only guards the arithmetic).
+constexpr int kMaxDepth = 1 << 24;
+
 // ---------------------------------------------------------------- workspace layouts ---
 
 // Segments (64 vectors of 16 bytes) per row, and the final draw's chunks of
@@ -325,7 +330,7 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
                          hipStream_t stream) {
     if (B < 0 || N < 1 || max_depth < 0 || parent_stride < 0 || (parent_stride != 0 && parent_stride < N))
         return SV_ERR_INVALID_ARGUMENT;
-    if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
+    if (N > SV_MAX_TREE_NODES || max_depth > kMaxDepth) return SV_ERR_UNSUPPORTED;
     sv_status st = check_rows(static_cast<int64_t>(B) * N, V, dt);
     if (st != SV_OK) return st;
     if (B == 0) return SV_OK;
@@ -349,7 +354,7 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                                  size_t workspace_bytes, hipStream_t stream) {
     if (B < 0 || N < 1 || max_depth < 0 || parent_stride < 0 || (parent_stride != 0 && parent_stride < N))
         return SV_ERR_INVALID_ARGUMENT;
-    if (N > SV_MAX_TREE_NODES) return SV_ERR_UNSUPPORTED;
+    if (N > SV_MAX_TREE_NODES || max_depth > kMaxDepth) return SV_ERR_UNSUPPORTED;
     sv_status st = check_rows(static_cast<int64_t>(2) * B * N, V, dt);
     if (st != SV_OK) return st;
     if (B == 0) return SV_OK;

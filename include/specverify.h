@@ -77,7 +77,8 @@ typedef enum {
 } sv_dtype;
 
 /* Limits: k <= SV_MAX_DRAFTS draft tokens per sequence; N <= SV_MAX_TREE_NODES
- * tree nodes; V <= SV_MAX_VOCAB. */
+ * tree nodes and max_depth <= 2^24 for the tree entry points; V <= SV_MAX_VOCAB.
+ * Larger sizes return SV_ERR_UNSUPPORTED. */
 #define SV_MAX_DRAFTS 64
 #define SV_MAX_TREE_NODES 1024
 #define SV_MAX_VOCAB (1 << 20)

@@ -136,6 +136,7 @@ def test_tree_rejects_bad_arguments_on_the_host(lib):
     assert t(stride=4) == INVALID  # a per-sequence parent stride shorter than N
     assert t(stride=-1) == INVALID
     assert t(N=1025) == UNSUPPORTED
+    assert t(md=(1 << 24) + 1) == UNSUPPORTED
     assert t(par=None) == INVALID
     assert t(tok=None) == INVALID
     assert t(ws_bytes=8) == WS_SMALL
@@ -179,6 +180,7 @@ def test_tree_sampled_rejects_bad_arguments_on_the_host(lib):
     assert t(V=0) == INVALID
     assert t(dt=3) == INVALID
     assert t(N=1025) == UNSUPPORTED
+    assert t(md=(1 << 30)) == UNSUPPORTED
     assert t(V=(1 << 20) + 1) == UNSUPPORTED
     for key in ("tok", "par", "draft", "target", "temp", "u", "acc", "em"):
         assert t(**{key: None}) == INVALID, key
