@@ -551,12 +551,14 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
         ref = ceilf(wave_max(mx) * si.c_hi);
         bonus_weights<NE, FULL>(w, si, ref, w);
     }
+    static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
+    float a[kFinU];
 #pragma unroll
-    for (int i = 0; i < kFinU; ++i) {
-        const float m = wave_sum(pairwise_sum<VE>(w + i * VE));
-        const int64_t g = tile * kFinU + i;
-        if (lane == 0 && g < nseg) seg_out[g] = Partial{m, static_cast<int>(ref)};
-    }
+    for (int i = 0; i < kFinU; ++i) a[i] = pairwise_sum<VE>(w + i * VE);
+    int i_own;
+    const float m = wave_sum4(a, i_own);
+    const int64_t g = tile * kFinU + i_own;
+    if (lane < kFinU && g < nseg) seg_out[g] = Partial{m, static_cast<int>(ref)};
 }
 
 template <int DT, bool VEC, int ACC>
