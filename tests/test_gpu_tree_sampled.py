@@ -161,3 +161,38 @@ def test_gpu_sampled_tree_distribution_chi_square(svl, orc):
         pv.append(stats.chisquare(obs[keep].ravel(), exp[keep].ravel(), ddof=int(keep.sum()) - 1).pvalue)
     print(f"[chi2] sampled tree p-values {pv}", flush=True)
     assert min(pv) > 1e-4, pv
+
+
+def test_hand_derived_golden_examples_on_gpu(svl):
+    """The hand-derived examples of tests/golden, through the GPU (chain and
+    sampled tree): the GPU reproduces the values derived by hand."""
+    from gpu_common import run_chain
+
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    g = json.load(open(os.path.join(here, "tree_sampled_v3_hand.json")))
+    cases, B, N, V = g["cases"], len(g["cases"]), g["N"], g["V"]
+    lg = lambda key: np.log(np.array([c[key] for c in cases], np.float64)).astype(np.float32)  # noqa: E731
+    inp = dict(B=B, N=N, V=V, dtype=W.F32, node_tokens=np.array([c["node_tokens"] for c in cases], np.int32),
+               parent=np.array([c["parent"] for c in cases], np.int32), max_depth=g["max_depth"],
+               target_logits=lg("target_probs"), draft_logits=lg("draft_probs"),
+               temperature=np.full(B, g["temperature"], np.float32),
+               uniforms=np.array([c["uniforms"] for c in cases], np.float32))
+    got = run_tree_sampled(svl, inp)
+    for i, c in enumerate(cases):
+        assert got["accepted_len"][i] == c["accepted_len"], c["why"]
+        assert got["emitted"][i].tolist() == c["emitted"], c["why"]
+        assert got["accepted_nodes"][i].tolist() == c["accepted_nodes"], c["why"]
+    g = json.load(open(os.path.join(here, "chain_v4_hand.json")))
+    cases, B, k, V = g["cases"], len(g["cases"]), g["k"], g["V"]
+    t = np.log(np.array(g["target_probs"], np.float64)).astype(np.float32)
+    d = np.log(np.array(g["draft_probs"], np.float64)).astype(np.float32)
+    inp = dict(B=B, k=k, V=V, dtype=W.F32, draft_tokens=np.array([c["draft_tokens"] for c in cases], np.int32),
+               draft_logits=np.broadcast_to(d, (B, k, V)).copy(),
+               target_logits=np.broadcast_to(t, (B, k + 1, V)).copy(),
+               temperature=np.full(B, g["temperature"], np.float32),
+               uniforms=np.array([c["uniforms"] for c in cases], np.float32))
+    got = run_chain(svl, inp)
+    for i, c in enumerate(cases):
+        assert got["accepted_len"][i] == c["accepted_len"], c["why"]
+        assert got["emitted"][i].tolist() == c["emitted"], c["why"]
+        np.testing.assert_allclose(got["accept_prob"][i], c["accept_prob"], atol=1e-6, err_msg=c["why"])

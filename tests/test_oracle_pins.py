@@ -658,3 +658,21 @@ def test_sampled_tree_planted_mistakes_fail_the_distribution_test(orc, mutated, 
     mutated(getattr(orc, mutation))
     acc, em, nodes = _run_tree_trials(orc, tables)
     assert _tree_chi_pvalues(tables, acc, em).min() < 1e-12
+
+
+def test_sampled_tree_hand_derived_golden_example(orc):
+    g = json.load(open(os.path.join(GOLDEN, "tree_sampled_v3_hand.json")))
+    V, N, cases = g["V"], g["N"], g["cases"]
+    B = len(cases)
+    lg = lambda key: np.log(np.array([c[key] for c in cases], np.float64)).astype(np.float32)  # noqa: E731
+    inp = dict(B=B, N=N, V=V, dtype=W.F32, node_tokens=np.array([c["node_tokens"] for c in cases], np.int32),
+               parent=np.array([c["parent"] for c in cases], np.int32), max_depth=g["max_depth"],
+               target_logits=lg("target_probs"), draft_logits=lg("draft_probs"),
+               temperature=np.full(B, g["temperature"], np.float32),
+               uniforms=np.array([c["uniforms"] for c in cases], np.float32))
+    r = orc.verify_tree_sampled(inp)
+    for i, c in enumerate(cases):
+        assert r["accepted_len"][i] == c["accepted_len"], c["why"]
+        assert r["emitted"][i].tolist() == c["emitted"], c["why"]
+        assert r["accepted_nodes"][i].tolist() == c["accepted_nodes"], c["why"]
+    assert not r["band"].any()
