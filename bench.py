@@ -15,8 +15,9 @@ kernel dispatch on its launch stream, which gives every kernel's duration
 (the roofline of the dominant kernel uses these).
 
 Prints one JSON line (see the metric, roofline and cpu_baseline fields).
-Other workloads (--config 3 greedy, 5 tree, 4 DeepSeek-scale chain) are for
-exploration; the default line is the Llama-scale chain.
+Other workloads (--workload greedy_chain, deepseek_chain, eagle_tree, mtp_chain,
+sampling, sampled_tree) print the same line for their own step; the default
+line is the Llama-scale chain.
 """
 
 import argparse
@@ -34,9 +35,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
 METRIC = "verified draft tokens/sec and HBM GB/s (% of peak) at B=64,k=4,V=128256 bf16"
-KERNEL_SOURCES = ["draft_token_verification_chain_amd/csrc/sv_common.hpp",
-                  "draft_token_verification_chain_amd/csrc/sv_kernels.hpp",
-                  "draft_token_verification_chain_amd/csrc/specverify.hip"]
+KERNEL_SOURCES = ["draft_token_verification_chain_amd/csrc/" + f for f in (
+    "sv_common.hpp", "sv_tiles.hpp", "sv_chain.hpp", "sv_greedy_tree.hpp", "sv_tree_sampled.hpp", "sv_commit.hpp",
+    "sv_kernels.hpp", "specverify.hip")]
 
 
 def kernel_source_digest() -> str:
@@ -116,7 +117,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8])
+    ap.add_argument("--workload", default="llama_chain",
+                    choices=["llama_chain", "greedy_chain", "deepseek_chain", "eagle_tree", "mtp_chain",
+                             "sampling", "sampled_tree"])
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -141,8 +144,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     svl.load()
-    cfg = W.CONFIGS[args.config]
-    inp = W.make_inputs(args.config, args.seed)
+    cfg = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(args.workload, args.seed)
     kind = inp["kind"]
     es = 2 if inp["dtype"] == W.BF16 else 4
     in_bytes = sum(v.nbytes for k, v in inp.items() if isinstance(v, np.ndarray))
@@ -265,10 +268,10 @@ def main():
     kernels = {name: dict(launches=n, avg_us=1e3 * tot / max(n, 1)) for name, (n, tot) in prof.items()}
     dom_us = kernels[dominant]["avg_us"]
     achieved = dominant_bytes / (dom_us * 1e-6) / 1e9
-    traffic = load_traffic(dominant, f"config{args.config}")
+    traffic = load_traffic(dominant, args.workload)
 
     result = {
-        "metric": METRIC if args.config == 2 else f"{unit[:-2]}/sec ({cfg['name']})",
+        "metric": METRIC if args.workload == "llama_chain" else f"{unit[:-2]}/sec ({cfg['name']})",
         "value": units / s_per_step,
         "unit": unit,
         "n_gpus": 1,

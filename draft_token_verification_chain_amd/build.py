@@ -7,6 +7,7 @@ binding loads it from.
 
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
@@ -17,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
 SOURCES = [os.path.join(CSRC, "specverify.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("sv_common.hpp", "sv_kernels.hpp")] + [os.path.join(INCLUDE, "specverify.h")]
+HEADERS = sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) + [os.path.join(INCLUDE, "specverify.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1,0 +1,551 @@
+// sv_chain.hpp -- sv_verify_chain: rowstats, acceptance, final draw and pick
+// (part of sv_kernels.hpp).
+#pragma once
+
+#include "sv_tiles.hpp"
+
+namespace sv {
+// ---------------------------------------------------------------- chain: rowstats ---
+
+// The partial of one tile of a row of sequence b: the tile's loads are issued
+// before the temperature is known, which then selects softmax or argmax.
+template <int DT, bool VEC, int U, bool FULL>
+__device__ __forceinline__ Partial rowstats_tile(const void* base, int64_t row_elem, int V, int64_t tile, float T) {
+    constexpr int NE = U * Elem<DT>::per_vec;
+    float v[NE];
+    load_tile<DT, VEC, U, FULL, true>(base, row_elem, V, tile, lane_id(), v);
+    if (T > 0.f) {
+        float c_hi, c_lo;
+        temperature_scale(T, c_hi, c_lo);
+        return softmax_of_tile<NE, FULL>(v, c_hi, c_lo);
+    }
+    const ArgMax a = argmax_of_tile<DT, U>(v, tile);
+    return Partial{a.val, a.idx};
+}
+
+// Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
+// rows (b, i).  The wave streaming tile 0 of a row also reads the row's logit
+// at its draft token into gathered[r], so that the acceptance needs no
+// dependent gather.  Draft rows of temperature-0 sequences are streamed too,
+// and their partials go unused: deciding to skip them would put the
+// temperature's load in front of every wave's tile loads.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __restrict__ target,
+                                                                const void* __restrict__ draft,
+                                                                const float* __restrict__ temperature,
+                                                                const int32_t* __restrict__ tokens,
+                                                                int B, int k, int V, int nT,
+                                                                Partial* __restrict__ part,
+                                                                float* __restrict__ gathered) {
+    const int64_t gw = global_wave();
+    const int64_t nbk = static_cast<int64_t>(B) * k;
+    if (gw >= 2 * nbk * nT) return;
+    const int64_t r = gw / nT;
+    const int64_t tile = gw - r * nT;
+    const bool is_target = r < nbk;
+    const int64_t rr = is_target ? r : r - nbk;
+    const int64_t b = rr / k;
+    const void* base = is_target ? target : draft;
+    const int64_t row_elem = (is_target ? (b * (k + 1) + (rr - b * k)) : rr) * static_cast<int64_t>(V);
+    if (tile == 0) {
+        const int x = tokens[rr];  // draft token scored by this row (rr = b * k + position)
+        if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
+            gathered[r] = load_elem<DT>(base, row_elem + x);
+    }
+    const float T = temperature[b];
+    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
+                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
+    if (lane_id() == 0) part[r * nT + tile] = p;
+}
+
+// ---------------------------------------------------------------- chain: acceptance ---
+
+// Acceptance of sequence b, computed by one wave (the first of its block):
+// the row statistics from the streaming partials (G lanes per row, one
+// round trip), the 2k logits at the draft tokens, tau_i in the log domain,
+// the first rejection by ballot.  Writes the final draw's descriptor into
+// *out and, when `publish`, accepted_len, the accepted prefix of emitted
+// (the rest -1; the final token is written later) and accept_prob.
+template <int DT>
+__device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ tokens,
+                                                const float* __restrict__ temperature,
+                                                const float* __restrict__ uniforms, int B, int k, int V, int nT,
+                                                const Partial* __restrict__ part, const float* __restrict__ gathered,
+                                                int64_t b, bool publish, int32_t* __restrict__ accepted_len,
+                                                int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+                                                int* s_r, double* s_s, SeqInfo* out) {
+    const int lane = lane_id();
+    const int64_t nbk = static_cast<int64_t>(B) * k;
+    // every load first: none of them depends on another
+    const int rows = 2 * k;  // target rows 0..k-1, then draft rows
+    int G = kWave;
+    while (G > 1 && G * rows > kWave) G >>= 1;
+    const int per_pass = kWave / G;
+    auto row_of = [&](int rho) -> int64_t { return rho < k ? b * k + rho : nbk + b * k + (rho - k); };
+    Partial q[kBatch];
+    const int rho_first = lane / G;
+    group_load(part + (rho_first < rows ? row_of(rho_first) : 0) * nT, nT, G, rho_first < rows, q);
+    const float T = temperature[b];
+    const float uk = uniforms[b * (k + 1) + k];
+    int x = 0;
+    float ui = 0.f, lt = 0.f, ld = 0.f;
+    if (lane < k) {
+        x = tokens[b * k + lane];
+        ui = uniforms[b * (k + 1) + lane];
+        lt = gathered[b * k + lane];
+        ld = gathered[nbk + b * k + lane];
+    }
+    const bool sampled = T > 0.f;
+    const bool xok = static_cast<unsigned>(x) < static_cast<unsigned>(V);  // out-of-range ids are rejected
+    // row statistics (at temperature 0 only the target rows' argmax matters)
+    for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
+        const int rho = rho0 + lane / G;
+        const bool valid = rho < rows;
+        const Partial* p = part + (valid ? row_of(rho) : 0) * nT;
+        if (rho0 > 0) group_load(p, nT, G, valid, q);
+        int r;
+        double sum;
+        ArgMax am;
+        if (sampled) {
+            group_reduce<true>(p, nT, G, valid, q, r, sum, am);
+            if (valid && (lane & (G - 1)) == 0) {
+                s_r[rho] = r;
+                s_s[rho] = sum;
+            }
+        } else {
+            group_reduce<false>(p, nT, G, valid, q, r, sum, am);
+            if (valid && (lane & (G - 1)) == 0) s_r[rho] = am.idx;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    bool acc = true;
+    double tau = 1.0;
+    int g = -1;
+    int rt = 0, rd = 0;
+    double st = 1.0, sd = 1.0;
+    if (lane < k) {
+        if (!sampled) g = s_r[lane];
+        if (!xok) {
+            acc = false;
+            tau = 0.0;
+        } else if (sampled) {
+            rt = s_r[lane];
+            st = s_s[lane];
+            rd = s_r[k + lane];
+            sd = s_s[k + lane];
+            const double c = kLog2e / static_cast<double>(T);
+            // log2 p - log2 q with log2 p = l c - R - log2 S (the same for q)
+            const double l2ratio = (static_cast<double>(lt) * c - rt - log2_of_sum(st)) -
+                                   (static_cast<double>(ld) * c - rd - log2_of_sum(sd));
+            // exp2 of a non-positive argument in fp32: relative error about 1e-7
+            tau = static_cast<double>(exp2f(static_cast<float>(fmin(0.0, l2ratio))));
+            acc = static_cast<double>(ui) < tau;
+        } else {
+            acc = (x == g);
+            tau = acc ? 1.0 : 0.0;
+        }
+    }
+    int a = first_lane(lane < k && !acc);
+    if (a < 0) a = k;
+    int32_t* em = emitted + b * (k + 1);
+    if (publish) {
+        if (accept_prob != nullptr && lane < k) accept_prob[b * k + lane] = static_cast<float>(tau);
+        for (int j = lane; j <= k; j += kWave) em[j] = j < a ? tokens[b * k + j] : -1;
+    }
+    if (lane == (a < k ? a : 0)) {
+        SeqInfo si{};
+        si.a = a;
+        temperature_scale(sampled ? T : 1.f, si.c_hi, si.c_lo);
+        si.u = uk;
+        if (!sampled) {
+            if (a < k) {
+                if (publish) em[a] = g;
+                si.mode = kFinalDone;
+            } else {
+                si.mode = kFinalArgmax;
+            }
+        } else if (a < k) {
+            si.mode = kFinalResidual;
+            si.rt = static_cast<float>(rt);
+            si.inv_st = static_cast<float>(1.0 / st);
+            si.rd = static_cast<float>(rd);
+            si.inv_sd = static_cast<float>(1.0 / sd);
+        } else {
+            si.mode = kFinalBonus;
+        }
+        *out = si;
+    }
+    if (publish && lane == 0) accepted_len[b] = a;
+}
+
+// One wave per sequence, kAccWaves sequences per workgroup: the acceptance
+// of every sequence, its outputs and the descriptor of its final draw.
+constexpr int kAccWaves = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kAccWaves * kWave) void chain_accept_kernel(
+    const int32_t* __restrict__ tokens, const float* __restrict__ temperature, const float* __restrict__ uniforms,
+    int B, int k, int V, int nT, const Partial* __restrict__ part, const float* __restrict__ gathered,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+    SeqInfo* __restrict__ info) {
+    __shared__ int s_r[kAccWaves][2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[kAccWaves][2 * SV_MAX_DRAFTS];
+    const int w = threadIdx.x / kWave;
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kAccWaves + w;
+    if (b >= B) return;  // whole waves only; the kernel has no workgroup barrier
+    accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, true, accepted_len, emitted,
+                        accept_prob, s_r[w], s_s[w], info + b);
+}
+
+// ---------------------------------------------------------------- chain: final draw ---
+
+// Weight of the final draw for the U*VE elements a lane holds.
+//   residual: w = max(0, p - q), p = exp2(l_t c - rt) / S_t, q likewise;
+//   bonus:    w = exp2(l c - ref), unnormalised (the draw is scale-free).
+template <int NE, bool FULL>
+__device__ __forceinline__ void residual_weights(const float* vt, const float* vd, const SeqInfo& s, float* w) {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        const float p = exp_term<FULL>(vt[j], s.c_hi, s.c_lo, s.rt) * s.inv_st;
+        const float q = exp_term<FULL>(vd[j], s.c_hi, s.c_lo, s.rd) * s.inv_sd;
+        w[j] = fmaxf(p - q, 0.f);
+    }
+}
+
+template <int NE, bool FULL>
+__device__ __forceinline__ void bonus_weights(const float* v, const SeqInfo& s, float ref, float* w) {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) w[j] = exp_term<FULL>(v[j], s.c_hi, s.c_lo, ref);
+}
+
+// Weights of segment `seg` (one vector per lane) in the tile's scale.
+template <int DT, bool VEC, bool FULL>
+__device__ __forceinline__ void segment_weights_t(const void* draft, const void* target, int64_t trow,
+                                                  int64_t drow, int V, int64_t seg, const SeqInfo& s,
+                                                  bool residual, float ref, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    // a segment is tile seg/U's load seg%U, i.e. vectors 64*seg .. 64*seg+63
+    float vt[VE];
+    load_tile<DT, VEC, 1, FULL>(target, trow, V, seg, lane_id(), vt);
+    if (residual) {
+        float vd[VE];
+        load_tile<DT, VEC, 1, FULL>(draft, drow, V, seg, lane_id(), vd);
+        residual_weights<VE, FULL>(vt, vd, s, w);
+    } else {
+        bonus_weights<VE, FULL>(vt, s, ref, w);
+    }
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void segment_weights(const void* draft, const void* target, int64_t trow,
+                                                int64_t drow, int V, int64_t seg, const SeqInfo& s,
+                                                bool residual, float ref, float* w) {
+    if (tile_is_full<VEC, 1>(seg, V, Elem<DT>::per_vec))
+        segment_weights_t<DT, VEC, VEC>(draft, target, trow, drow, V, seg, s, residual, ref, w);
+    else
+        segment_weights_t<DT, VEC, false>(draft, target, trow, drow, V, seg, s, residual, ref, w);
+}
+
+// Inverse CDF inside one segment.  `P` is the mass before the segment and
+// `scale` maps the segment's weights to the global scale (a power of two).
+// Returns the token, or -1 when rounding leaves C <= target everywhere.
+template <int DT>
+__device__ __forceinline__ int pick_in_segment(const float* w, int64_t seg, double P, double scale,
+                                               double target_mass) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int lane = lane_id();
+    double lane_sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) lane_sum += static_cast<double>(w[e]) * scale;
+    const double incl = wave_inclusive_scan(lane_sum);
+    const double excl = __shfl_up(incl, 1, kWave);
+    double C = P + (lane == 0 ? 0.0 : excl);
+    int hit = -1;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        C += static_cast<double>(w[e]) * scale;
+        if (hit < 0 && C > target_mass) hit = e;
+    }
+    const int fl = first_lane(hit >= 0);
+    if (fl < 0) return -1;
+    const int e = __shfl(hit, fl, kWave);
+    return static_cast<int>((seg * 64 + fl) * VE + e);
+}
+
+// Last token of the segment whose weight is positive, or -1.
+template <int DT>
+__device__ __forceinline__ int last_positive_in_segment(const float* w, int64_t seg) {
+    constexpr int VE = Elem<DT>::per_vec;
+    int last = -1;
+#pragma unroll
+    for (int e = 0; e < VE; ++e)
+        if (w[e] > 0.f) last = e;
+    const uint64_t m = __ballot(last >= 0);
+    if (!m) return -1;
+    const int fl = 63 - __builtin_clzll(m);
+    const int e = __shfl(last, fl, kWave);
+    return static_cast<int>((seg * 64 + fl) * VE + e);
+}
+
+// The final draw of sequence b is spread over `nchunk` workgroups, each
+// owning kSegPerChunk consecutive segments (a segment is the 64 vectors of
+// one wave load).  A workgroup first needs the draw's descriptor, obtained
+// in one of three ways (FinalAccept): with no drafts it is formed from the
+// temperature alone, so the first loads are the row's; for a draw that fits
+// in one round of resident workgroups every workgroup recomputes its
+// sequence's acceptance (a few KB of partials: cheaper than another launch);
+// for larger draws chain_accept_kernel has written it once per sequence.
+// The workgroup then streams its chunk of the row(s) the draw needs and
+// writes each segment's mass and reference exponent, or, at temperature 0,
+// the chunk's argmax.
+enum FinalAccept : int { kAcceptNone = 0, kAcceptInline = 1, kAcceptRead = 2 };
+
+constexpr int kFinBlock = 256;
+constexpr int kFinWaves = kFinBlock / kWave;
+constexpr int kFinU = 4;  // segments per wave tile
+constexpr int kSegPerChunk = kFinWaves * kFinU;  // segments per workgroup and tile round
+
+template <int DT, bool VEC, bool FULL>
+__device__ __forceinline__ void final_tile(const void* draft, const void* target, int64_t trow, int64_t drow,
+                                           int V, int64_t tile, int64_t nseg, const SeqInfo& si, int mode,
+                                           Partial* __restrict__ seg_out, ArgMax& best) {
+    constexpr int VE = Elem<DT>::per_vec;
+    constexpr int NE = kFinU * VE;
+    const int lane = lane_id();
+    float w[NE];  // the target's logits, then (in place) the weights
+    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
+    if (mode == kFinalArgmax) {
+        best = better(best, argmax_of_tile<DT, kFinU>(w, tile));
+        return;
+    }
+    float ref = 0.f;
+    if (mode == kFinalResidual) {
+        float vd[NE];
+        load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
+        residual_weights<NE, FULL>(w, vd, si, w);
+    } else {
+        float mx = w[0];
+#pragma unroll
+        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, w[j]);
+        // a reference over the whole tile (which always holds an element of the row)
+        ref = ceilf(wave_max(mx) * si.c_hi);
+        bonus_weights<NE, FULL>(w, si, ref, w);
+    }
+    static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
+    float a[kFinU];
+#pragma unroll
+    for (int i = 0; i < kFinU; ++i) a[i] = pairwise_sum<VE>(w + i * VE);
+    int i_own;
+    const float m = wave_sum4(a, i_own);
+    const int64_t g = tile * kFinU + i_own;
+    if (lane < kFinU && g < nseg) seg_out[g] = Partial{m, static_cast<int>(ref)};
+}
+
+template <int DT, bool VEC, int ACC>
+__global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
+    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
+    const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+    SeqInfo* __restrict__ info, Partial* __restrict__ segs, Partial* __restrict__ chunkarg) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ ArgMax s_arg[kFinWaves];
+    const int64_t b = blockIdx.x / nchunk;
+    const int c = static_cast<int>(blockIdx.x - b * nchunk);
+    SeqInfo si;
+    if constexpr (ACC == kAcceptInline) {
+        __shared__ int s_r[2 * SV_MAX_DRAFTS];
+        __shared__ double s_s[2 * SV_MAX_DRAFTS];
+        __shared__ SeqInfo s_info;
+        if (threadIdx.x < kWave)
+            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, c == 0, accepted_len,
+                                emitted, accept_prob, s_r, s_s, &s_info);
+        __syncthreads();
+        si = s_info;
+        if (c == 0 && threadIdx.x == 0) info[b] = si;
+        if (si.mode == kFinalDone) return;
+    } else if constexpr (ACC == kAcceptNone) {
+        // k == 0: draw from target row 0 (its argmax at temperature 0)
+        const float T = temperature[b];
+        si = SeqInfo{};
+        si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+        temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+        si.u = uniforms[b];
+        if (c == 0 && threadIdx.x == 0) {
+            info[b] = si;
+            accepted_len[b] = 0;
+        }
+    } else {
+        si = info[b];
+        if (si.mode == kFinalDone) return;
+    }
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
+    const int wave = threadIdx.x / kWave;
+    const int64_t tile = static_cast<int64_t>(c) * kFinWaves + wave;  // the workgroup's waves read adjacent tiles
+    Partial* seg_out = segs + b * nseg;
+    ArgMax best{-__builtin_inff(), kNoIndex};
+    if (tile * kFinU < nseg) {
+        if (tile_is_full<VEC, kFinU>(tile, V, VE))
+            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+        else
+            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+    }
+    if (si.mode == kFinalArgmax) {
+        if (lane_id() == 0) s_arg[wave] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            ArgMax r = s_arg[0];
+            for (int w = 1; w < kFinWaves; ++w) r = better(r, s_arg[w]);
+            chunkarg[b * nchunk + c] = Partial{r.val, r.idx};
+        }
+    }
+}
+
+// Slow path of the draw, one wave: inverse CDF of the target row's own
+// distribution with two sequential sweeps over its segments.  Used only when
+// the residual of a rejection has no mass at all (draft and target rows
+// agree to rounding).
+template <int DT, bool VEC>
+__device__ int pick_from_target_row(const void* target, int64_t trow, int V, int64_t nseg, const SeqInfo& s) {
+    constexpr int VE = Elem<DT>::per_vec;
+    float w[VE];
+    double W = 0.0;
+    for (int64_t g = 0; g < nseg; ++g) {
+        segment_weights<DT, VEC>(nullptr, target, trow, 0, V, g, s, false, s.rt, w);
+        W += static_cast<double>(wave_sum(pairwise_sum<VE>(w)));
+    }
+    const double target_mass = static_cast<double>(s.u) * W;
+    double P = 0.0;
+    int last = -1;
+    for (int64_t g = 0; g < nseg; ++g) {
+        segment_weights<DT, VEC>(nullptr, target, trow, 0, V, g, s, false, s.rt, w);
+        const double mass = static_cast<double>(wave_sum(pairwise_sum<VE>(w)));
+        if (mass > 0.0) {
+            const int y = pick_in_segment<DT>(w, g, P, 1.0, target_mass);
+            if (y >= 0) return y;
+            last = last_positive_in_segment<DT>(w, g);
+        }
+        P += mass;
+    }
+    return last;
+}
+
+// Select pass of the final draw: one wave per sequence.  Lane l owns a
+// contiguous run of segments; a wave prefix over the run totals gives every
+// segment's starting mass, the segment holding u * W is found with a ballot,
+// and only that segment is read again to find the token.  The descriptor and
+// the lane's first kSegRun segments are loaded together.
+constexpr int kSegRun = 8;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
+    const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nchunk,
+    const SeqInfo* __restrict__ info, const Partial* __restrict__ segs, const Partial* __restrict__ chunkarg,
+    int32_t* __restrict__ emitted) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int64_t b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const Partial* sg = segs + b * nseg;
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t g0 = min<int64_t>(nseg, lane * per), g1 = min<int64_t>(nseg, g0 + per);
+    Partial first[kSegRun];
+#pragma unroll
+    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : Partial{0.f, kNoRef};
+    const SeqInfo s = info[b];
+    if (s.mode == kFinalDone) return;
+    int y;
+    if (s.mode == kFinalArgmax) {
+        y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;
+    } else {
+        const bool residual = s.mode == kFinalResidual;
+        const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
+        const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
+        const int64_t nwin = (per + kSegRun - 1) / kSegRun;
+        // segment g of this lane's window w
+        auto seg_at = [&](int64_t w, int j) -> Partial {
+            const int64_t g = g0 + w * kSegRun + j;
+            return w == 0 ? first[j] : (g < g1 ? sg[g] : Partial{0.f, kNoRef});
+        };
+        // global reference exponent (residual masses are absolute: reference 0)
+        int R = 0;
+        if (!residual) {
+            R = kNoRef;
+            for (int64_t w = 0; w < nwin; ++w)
+#pragma unroll
+                for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).i);
+            R = wave_max(R);
+        }
+        // masses of this lane's window w in the global scale
+        auto window = [&](int64_t w, double* mg) {
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j) {
+                const Partial q = seg_at(w, j);
+                const bool in = g0 + w * kSegRun + j < g1;
+                mg[j] = !in ? 0.0 : residual ? static_cast<double>(q.f) : ldexp(static_cast<double>(q.f), q.i - R);
+            }
+        };
+        double tot = 0.0;
+        for (int64_t w = 0; w < nwin; ++w) {
+            double mg[kSegRun];
+            window(w, mg);
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j) tot += mg[j];
+        }
+        const double incl = wave_inclusive_scan(tot);
+        const double W = __shfl(incl, kWave - 1, kWave);
+        const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+        double P = lane == 0 ? 0.0 : excl;
+        if (!(W > 0.0)) {
+            y = residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0;
+        } else {
+            const double target_mass = static_cast<double>(s.u) * W;
+            int64_t found = -1, last_pos = -1;
+            double Pfound = 0.0;
+            for (int64_t w = 0; w < nwin; ++w) {
+                double mg[kSegRun];
+                window(w, mg);
+#pragma unroll
+                for (int j = 0; j < kSegRun; ++j) {
+                    const int64_t g = g0 + w * kSegRun + j;
+                    if (g >= g1) break;
+                    if (found < 0 && P + mg[j] > target_mass) {
+                        found = g;
+                        Pfound = P;
+                    }
+                    if (mg[j] > 0.0) last_pos = g;
+                    P += mg[j];
+                }
+            }
+            int fl = first_lane(found >= 0);
+            int64_t seg;
+            double Ps;
+            bool fallback = false;
+            if (fl >= 0) {
+                seg = __shfl(found, fl, kWave);
+                Ps = __shfl(Pfound, fl, kWave);
+            } else {
+                // rounding put u * W at or past the total: the last segment with mass
+                const uint64_t m = __ballot(last_pos >= 0);
+                fl = m ? 63 - __builtin_clzll(m) : 0;
+                seg = m ? __shfl(last_pos, fl, kWave) : 0;
+                Ps = 0.0;
+                fallback = true;
+            }
+            const int tref = residual ? 0 : sg[seg].i;
+            const double scale = ldexp(1.0, tref - R);
+            float w[VE];
+            segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, static_cast<float>(tref), w);
+            y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, scale, target_mass);
+            if (y < 0) y = last_positive_in_segment<DT>(w, seg);
+        }
+    }
+    if (lane == 0) emitted[b * (k + 1) + s.a] = y;
+}
+
+}  // namespace sv

@@ -1,0 +1,762 @@
+// sv_tree_sampled.hpp -- sv_verify_tree_sampled: the tree rowstats, the walk in rounds and
+// the one-workgroup walk (part of sv_kernels.hpp).
+#pragma once
+
+#include "sv_chain.hpp"
+
+namespace sv {
+// ---------------------------------------------------------------- tree: sampled ---
+//
+// Multi-step speculative sampling over a draft tree (SpecInfer, Miao et al.
+// 2023, the rule the EAGLE work applies to sampled trees; the pages, section
+// "EAGLE", keep the longest path that passes).  At node n the children are
+// tested in index order against a running distribution r that starts as the
+// target row p_n; a rejection replaces r by the normalised residual
+// max(0, r - q_n).  That residual after j rejections is max(0, p - c_j q) /
+// Z(c_j), Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0, c_{j+1} = c_j + Z(c_j),
+// so a sibling's test needs only the scalars (c, Z) and each rejection one
+// pass over the node's two rows.
+
+// Rows 0 .. B*N-1 are target rows (b, n), rows B*N .. 2*B*N-1 draft rows.
+// The draft row of a leaf is never needed and is skipped.
+// The wave streaming tile 0 of inner node n's draft row also gathers, for
+// every child i of n, the target and draft logits of row n at i's token into
+// tg[b][i] and dg[b][i] (0 for a token outside [0, V)), so that the walk's
+// sibling tests need no dependent loads.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __restrict__ target,
+                                                               const void* __restrict__ draft,
+                                                               const int32_t* __restrict__ parent, int parent_stride,
+                                                               const int32_t* __restrict__ node_tokens,
+                                                               const float* __restrict__ temperature, int B, int N,
+                                                               int V, int nT, Partial* __restrict__ part,
+                                                               float* __restrict__ tg, float* __restrict__ dg) {
+    const int64_t gw = global_wave();
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    if (gw >= 2 * nbn * nT) return;
+    const int64_t r = gw / nT;
+    const int64_t tile = gw - r * nT;
+    const bool is_target = r < nbn;
+    const int64_t rr = is_target ? r : r - nbn;
+    const int64_t b = rr / N;
+    const int n = static_cast<int>(rr - b * N);
+    if (!is_target) {
+        const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+        bool kid = false;
+        for (int i = n + 1 + lane_id(); i < N; i += kWave) {
+            const bool child = par[i] == n;
+            kid |= child;
+            if (child && tile == 0) {
+                const int y = node_tokens[b * N + i];
+                const bool yok = static_cast<unsigned>(y) < static_cast<unsigned>(V);
+                tg[b * N + i] = yok ? load_elem<DT>(target, rr * static_cast<int64_t>(V) + y) : 0.f;
+                dg[b * N + i] = yok ? load_elem<DT>(draft, rr * static_cast<int64_t>(V) + y) : 0.f;
+            }
+        }
+        if (!__ballot(kid)) return;
+    }
+    const void* base = is_target ? target : draft;
+    const int64_t row_elem = rr * static_cast<int64_t>(V);
+    const float T = temperature[b];
+    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
+                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
+    if (lane_id() == 0) part[r * nT + tile] = p;
+}
+
+// One workgroup per sequence walks its tree; each thread holds kWalkSlots
+// node slots (t, t + kWalkBlock, ...).
+constexpr int kWalkBlock = 512;
+constexpr int kWalkWaves = kWalkBlock / kWave;
+constexpr int kWalkSlots = SV_MAX_TREE_NODES / kWalkBlock;
+constexpr int kWalkMaxSegs = SV_MAX_VOCAB / (4 * 64);  // f32 rows have the most segments
+constexpr int kWalkUnroll = 8;                          // segments in flight per wave
+
+// Normalised weights of segment g of the running distribution: p when the
+// residual scale c is 0, else max(0, p - c q) (s.inv_sd carries c / S_d).
+template <int DT, bool VEC>
+__device__ __forceinline__ void walk_weights(const void* draft, const void* target, int64_t row, int V, int64_t g,
+                                             const SeqInfo& s, bool residual, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    segment_weights<DT, VEC>(draft, target, row, row, V, g, s, residual, s.rt, w);
+    if (!residual) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
+    }
+}
+
+// Weights of one full segment from its raw 16-byte vectors (the same
+// arithmetic as walk_weights on an unmasked segment).
+template <int DT, bool RESIDUAL>
+__device__ __forceinline__ void walk_weights_raw(const uint4& rt, const uint4& rd, const SeqInfo& s, float* w) {
+    constexpr int VE = Elem<DT>::per_vec;
+    float vt[VE];
+    unpack<DT>(rt, vt);
+    if constexpr (RESIDUAL) {
+        float vd[VE];
+        unpack<DT>(rd, vd);
+        residual_weights<VE, true>(vt, vd, s, w);
+    } else {
+        bonus_weights<VE, true>(vt, s, s.rt, w);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
+    }
+}
+
+// Every thread of the workgroup: the mass of every segment of the running
+// distribution into s_mass, and their total (ascending order, fp64) as the
+// return value (identical in every thread).  Segments that lie wholly inside
+// the row are read kWalkUnroll per wave at a time with straight-line 16-byte
+// loads (indices clamped rather than branched on, so that all loads are in
+// flight together); the row's tail takes the masked path.
+template <int DT, bool VEC, bool RESIDUAL>
+__device__ double walk_masses(const void* draft, const void* target, int64_t row, int V, int64_t nseg,
+                              const SeqInfo& s, float* s_mass, double* s_sum) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int wave = threadIdx.x / kWave;
+    const int lane = lane_id();
+    const int64_t nfull = VEC ? ((V + VE - 1) / VE) / 64 : 0;
+    const char* tr = static_cast<const char*>(target) + row * Elem<DT>::bytes;
+    const char* dr = static_cast<const char*>(draft) + row * Elem<DT>::bytes;
+    for (int64_t g0 = wave; g0 < nfull; g0 += kWalkWaves * kWalkUnroll) {
+        uint4 rt[kWalkUnroll], rd[kWalkUnroll];
+#pragma unroll
+        for (int j = 0; j < kWalkUnroll; ++j) {
+            const int64_t g = min<int64_t>(g0 + j * kWalkWaves, nfull - 1);
+            rt[j] = *reinterpret_cast<const uint4*>(tr + (g * 64 + lane) * 16);
+            if constexpr (RESIDUAL) rd[j] = *reinterpret_cast<const uint4*>(dr + (g * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < kWalkUnroll; ++j) {
+            const int64_t g = g0 + j * kWalkWaves;
+            float w[VE];
+            walk_weights_raw<DT, RESIDUAL>(rt[j], rd[j], s, w);
+            const float m = wave_sum(pairwise_sum<VE>(w));
+            if (lane == 0 && g < nfull) s_mass[g] = m;
+        }
+    }
+    for (int64_t g = nfull + wave; g < nseg; g += kWalkWaves) {
+        float w[VE];
+        walk_weights<DT, VEC>(draft, target, row, V, g, s, RESIDUAL, w);
+        const float m = wave_sum(pairwise_sum<VE>(w));
+        if (lane == 0) s_mass[g] = m;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const int64_t per = (nseg + kWave - 1) / kWave;
+        const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+        double run = 0.0;
+        for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
+        const double tot = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+        if (lane == 0) *s_sum = tot;
+    }
+    __syncthreads();
+    return *s_sum;
+}
+
+// Inverse CDF of the running distribution whose segment masses are in
+// s_mass (wave 0; returns the token in every lane).
+template <int DT, bool VEC>
+__device__ int walk_pick(const void* draft, const void* target, int64_t row, int V, int64_t nseg, const SeqInfo& s,
+                         bool residual, const float* s_mass, double W, double u) {
+    const int lane = lane_id();
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+    double run = 0.0;
+    for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
+    const double incl = wave_inclusive_scan(run);
+    const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+    double P = lane == 0 ? 0.0 : excl;
+    const double target_mass = u * W;
+    int64_t found = -1, last_pos = -1;
+    double Pfound = 0.0;
+    for (int64_t g = a; g < e; ++g) {
+        const double m = static_cast<double>(s_mass[g]);
+        if (found < 0 && P + m > target_mass) {
+            found = g;
+            Pfound = P;
+        }
+        if (m > 0.0) last_pos = g;
+        P += m;
+    }
+    int fl = first_lane(found >= 0);
+    int64_t seg;
+    double Ps = 0.0;
+    bool fallback = false;
+    if (fl >= 0) {
+        seg = __shfl(found, fl, kWave);
+        Ps = __shfl(Pfound, fl, kWave);
+    } else {
+        const uint64_t m = __ballot(last_pos >= 0);
+        fl = m ? 63 - __builtin_clzll(m) : 0;
+        seg = m ? __shfl(last_pos, fl, kWave) : 0;
+        fallback = true;
+    }
+    float w[Elem<DT>::per_vec];
+    walk_weights<DT, VEC>(draft, target, row, V, seg, s, residual, w);
+    int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, 1.0, target_mass);
+    if (y < 0) y = last_positive_in_segment<DT>(w, seg);
+    return y;
+}
+
+// Validity of a tree and the depth of every node (pointer jumping over the
+// parent links), as for the greedy tree: BLOCK threads with
+// SV_MAX_TREE_NODES / BLOCK node slots each.  Fills s_par (parent ids, -1 for
+// the root) and returns whether the tree is invalid, in every thread.
+template <int BLOCK>
+__device__ bool walk_validate(const int32_t* __restrict__ par, int N, int max_depth, int* s_par, int* s_anc,
+                              int* s_len, int* s_bad) {
+    constexpr int kWalkSlots = SV_MAX_TREE_NODES / BLOCK;
+    constexpr int kWalkBlock = BLOCK;
+    const int t = threadIdx.x;
+    if (t == 0) *s_bad = 0;
+    __syncthreads();
+    int anc[kWalkSlots], len[kWalkSlots];
+#pragma unroll
+    for (int q = 0; q < kWalkSlots; ++q) {
+        const int i = t + q * kWalkBlock;
+        anc[q] = 0;
+        len[q] = 0;
+        if (i < N) {
+            const int p = i == 0 ? 0 : par[i];
+            if (i > 0 && (p < 0 || p >= i)) *s_bad = 1;
+            s_par[i] = i == 0 ? -1 : p;
+            anc[q] = p;
+            len[q] = i == 0 ? 0 : 1;
+        }
+    }
+    __syncthreads();
+    if (!*s_bad) {
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            if (i < N) {
+                s_anc[i] = anc[q];
+                s_len[i] = len[q];
+            }
+        }
+        __syncthreads();
+        for (int step = 1; step < N; step <<= 1) {
+            int a2[kWalkSlots], l2[kWalkSlots];
+#pragma unroll
+            for (int q = 0; q < kWalkSlots; ++q) {
+                const bool in = t + q * kWalkBlock < N;
+                a2[q] = in ? s_anc[anc[q]] : 0;
+                l2[q] = in ? s_len[anc[q]] : 0;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kWalkSlots; ++q) {
+                const int i = t + q * kWalkBlock;
+                if (i < N) {
+                    len[q] += l2[q];
+                    anc[q] = a2[q];
+                    s_anc[i] = anc[q];
+                    s_len[i] = len[q];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q)
+            if (t + q * kWalkBlock < N && len[q] > max_depth) *s_bad = 1;
+    }
+    __syncthreads();
+    return *s_bad != 0;
+}
+
+// State of one sequence's walk between the round launches (double-buffered).
+enum WalkPhase : int {
+    kWalkEnter = 0,  // at the start of `node`: its statistics are still to be combined
+    kWalkTest = 1,   // testing `node`'s children from rank kidx on (only inside a round)
+    kWalkPass = 2,   // a rejection advanced c; the partial sums of Z(c) are in z
+    kWalkPick = 3,   // the final distribution's segment masses are written; the pick remains
+    kWalkDone = 4,
+    kWalkStuck = 5   // a case the rounds leave to the one-workgroup walk (an empty final residual)
+};
+
+struct alignas(16) WalkState {
+    int phase, node, depth, kidx;  // kidx: children of `node` already rejected
+    int Rt, Rd, pad0, pad1;        // node statistics (at temperature 0: the two argmaxes)
+    double St, Sd, c, Z;
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
+    const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
+    int max_depth, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
+    const Partial* __restrict__ part, const WalkState* __restrict__ state, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
+    constexpr int VE = Elem<DT>::per_vec;
+    if (state != nullptr && state[blockIdx.x].phase == kWalkDone) return;  // finished by the rounds
+    __shared__ int s_par[SV_MAX_TREE_NODES];
+    __shared__ int s_anc[SV_MAX_TREE_NODES];
+    __shared__ int s_len[SV_MAX_TREE_NODES];
+    __shared__ uint64_t s_kids[SV_MAX_TREE_NODES / kWave];
+    __shared__ float s_mass[kWalkMaxSegs];
+    // the current node's children in index order: node id, uniform, and the
+    // target and draft logits at the child's token
+    __shared__ int s_cid[SV_MAX_TREE_NODES];
+    __shared__ float s_cu[SV_MAX_TREE_NODES];
+    __shared__ float s_clt[SV_MAX_TREE_NODES];
+    __shared__ float s_cld[SV_MAX_TREE_NODES];
+    __shared__ double s_sum;
+    __shared__ double s_norm[2];  // S_t, S_d of the current node
+    __shared__ int s_ref[2];      // R_t, R_d (at temperature 0: the two argmaxes)
+    __shared__ int s_bad, s_accept;
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = t / kWave;
+    const int width = max_depth + 1;
+    const float T = temperature[b];
+    const bool sampled = T > 0.f;
+    int32_t* out = emitted + b * width;
+    int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
+
+    // validity and depths (pointer jumping), as for the greedy tree
+    const bool bad = walk_validate<kWalkBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth, s_par,
+                                               s_anc, s_len, &s_bad);
+    for (int j = t; j < width; j += kWalkBlock) {
+        out[j] = -1;
+        if (nodes) nodes[j] = -1;
+    }
+    if (bad) {
+        if (t == 0) accepted_len[b] = -1;
+        return;
+    }
+
+    SeqInfo s{};
+    temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
+    const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int nmask = (N + kWave - 1) / kWave;
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    int n = 0, d = 0;
+    for (;;) {
+        const int64_t row = (b * N + n) * static_cast<int64_t>(V);
+        // children of n, and the statistics of its target and draft rows
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            const uint64_t km = __ballot(i < N && s_par[i] == n);
+            if (lane == 0 && wave + q * kWalkWaves < nmask) s_kids[wave + q * kWalkWaves] = km;
+        }
+        __syncthreads();
+        // every child reads its own token, uniform and the two logits at that token
+        int nkids = 0;
+        for (int m = 0; m < nmask; ++m) nkids += __popcll(s_kids[m]);
+#pragma unroll
+        for (int q = 0; q < kWalkSlots; ++q) {
+            const int i = t + q * kWalkBlock;
+            const int m = i / kWave;
+            if (i < N && ((s_kids[m] >> (i % kWave)) & 1)) {
+                int rank = __popcll(s_kids[m] & ((uint64_t{1} << (i % kWave)) - 1));
+                for (int m2 = 0; m2 < m; ++m2) rank += __popcll(s_kids[m2]);
+                const int y = node_tokens[b * N + i];
+                const bool yok = static_cast<unsigned>(y) < static_cast<unsigned>(V);
+                s_cid[rank] = yok ? i : -1 - i;  // an id outside [0, V) is rejected
+                s_cu[rank] = uniforms[b * N + i];
+                s_clt[rank] = yok ? load_elem<DT>(target, row + y) : 0.f;
+                s_cld[rank] = yok ? load_elem<DT>(draft, row + y) : 0.f;
+            }
+        }
+        if (wave == 0) {
+            const bool is_draft = lane >= 32;
+            const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+            Partial q[kBatch];
+            group_load(pr, nT, 32, true, q);
+            int r;
+            double sum;
+            ArgMax am;
+            if (sampled) {
+                group_reduce<true>(pr, nT, 32, true, q, r, sum, am);
+            } else {
+                group_reduce<false>(pr, nT, 32, true, q, r, sum, am);
+                r = am.idx;
+            }
+            if ((lane & 31) == 0) {
+                s_ref[is_draft] = r;
+                s_norm[is_draft] = sum;
+            }
+        }
+        __syncthreads();
+        const int Rt = s_ref[0], Rd = s_ref[1];
+        const double St = s_norm[0], Sd = s_norm[1];
+        s.rt = static_cast<float>(Rt);
+        s.inv_st = static_cast<float>(1.0 / St);
+        s.rd = static_cast<float>(Rd);
+        double c = 0.0, Z = 1.0;
+        int next = -1;
+        // log2 of the two normalisers' mantissas, once per node (thread 0 tests)
+        const double lsum = t == 0 && sampled && nkids > 0 ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
+        for (int k = 0; k < nkids && next < 0; ++k) {
+            if (t == 0) {
+                const int id = s_cid[k];
+                double tau = 0.0;
+                if (id >= 0) {
+                    if (sampled) {
+                        // p/q = exp2((l_t - l_d) c - (R_t + log2 S_t) + (R_d + log2 S_d))
+                        const double lt = s_clt[k], ld = s_cld[k];
+                        const double l2ratio = (lt * cT - ld * cT) - lsum;
+                        tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
+                    } else {
+                        const int y = node_tokens[b * N + id];
+                        const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
+                        const double rv = fmax(0.0, pv - c * qv) / Z;
+                        tau = qv > 0.0 ? fmin(1.0, rv / qv) : (rv > 0.0 ? 1.0 : 0.0);
+                    }
+                }
+                s_accept = static_cast<double>(s_cu[k]) < tau;
+            }
+            __syncthreads();
+            if (s_accept) {
+                next = s_cid[k];
+            } else {
+                // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
+                c += Z;
+                if (sampled) {
+                    s.inv_sd = static_cast<float>(c / Sd);
+                    Z = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+                } else {
+                    Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
+                }
+                if (!(Z > 0.0)) {
+                    c = 0.0;
+                    Z = 1.0;
+                }
+            }
+            __syncthreads();
+        }
+        if (next >= 0) {
+            if (t == 0) {
+                out[d] = node_tokens[b * N + next];
+                if (nodes) nodes[d] = next;
+            }
+            ++d;
+            n = next;
+            continue;
+        }
+        // no child kept: the final token from max(0, p - c q) (p when c == 0)
+        int y;
+        if (!sampled) {
+            y = Rt;  // one-hot p; with c > 0 the residual is p itself or empty (then p)
+        } else {
+            const bool residual = c > 0.0;
+            double W = Z;
+            if (!residual) W = walk_masses<DT, VEC, false>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+            y = 0;
+            if (wave == 0)
+                y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, residual, s_mass, W,
+                                       static_cast<double>(uniforms[b * N]));
+        }
+        if (t == 0) {
+            out[d] = y;
+            accepted_len[b] = d;
+        }
+        return;
+    }
+}
+
+// The walk in rounds.  tree_sample runs each sequence's rejection passes on
+// one CU, where a pass over two rows is VALU-bound (two exps and about ten
+// more operations per element).  The rounds spread every pass over P
+// workgroups per sequence and use the kernel boundaries between launches as
+// the synchronisation: in every round each of a sequence's workgroups
+// replays the same deterministic tests from the round's input state (the
+// children's logits were gathered by tree_rowstats), up to the next
+// rejection, and computes its slice of Z(c) = sum_v max(0, p - c q); one
+// round later the slices are summed (in a fixed order) and the tests go on.
+// When no child is kept, each workgroup writes its slice's segment masses of
+// the final distribution and the next round's chunk 0 picks the token.
+// Chunk 0 writes the outputs and the next state.  Round 0 also checks each
+// tree (invalid trees give -1 outputs) and sets the outputs to -1.  A
+// sequence not finished after the launched rounds is walked again from the
+// start by tree_sample.
+constexpr int kRoundBlock = 256;
+constexpr int kRoundWaves = kRoundBlock / kWave;
+constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;
+constexpr int kWalkRounds = 8;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
+    const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
+    int max_depth, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
+    const Partial* __restrict__ part, const float* __restrict__ tg, const float* __restrict__ dg,
+    const WalkState* __restrict__ st_in, WalkState* __restrict__ st_out, const double* __restrict__ z_in,
+    double* __restrict__ z_out, float* __restrict__ tsegs, int P, int first, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ int s_par[SV_MAX_TREE_NODES];
+    __shared__ int s_anc[SV_MAX_TREE_NODES];
+    __shared__ int s_len[SV_MAX_TREE_NODES];
+    __shared__ int s_bad;
+    __shared__ int s_tok[SV_MAX_TREE_NODES];
+    __shared__ float s_u[SV_MAX_TREE_NODES];
+    __shared__ float s_tg[SV_MAX_TREE_NODES];
+    __shared__ float s_dg[SV_MAX_TREE_NODES];
+    __shared__ uint64_t s_kids[SV_MAX_TREE_NODES / kWave];
+    __shared__ double s_norm[2];
+    __shared__ int s_ref[2];
+    __shared__ double s_wsum[kRoundWaves];
+    __shared__ double s_z;
+    __shared__ int s_accept;
+    const int64_t b = blockIdx.x / P;
+    const int j = static_cast<int>(blockIdx.x - b * P);
+    const int t = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = t / kWave;
+    const bool lead = j == 0;  // chunk 0 writes the outputs and the next state
+    const int width = max_depth + 1;
+    int32_t* out = emitted + b * width;
+    int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
+    WalkState st{};
+    if (first) {
+        const bool bad = walk_validate<kRoundBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth,
+                                                    s_par, s_anc, s_len, &s_bad);
+        if (lead) {
+            for (int q = t; q < width; q += kRoundBlock) {
+                out[q] = -1;
+                if (nodes) nodes[q] = -1;
+            }
+        }
+        __syncthreads();  // the -1s before any path write of this workgroup
+        st.phase = bad ? kWalkDone : kWalkEnter;
+        st.Z = 1.0;
+        if (bad && lead && t == 0) accepted_len[b] = -1;
+    } else {
+        st = st_in[b];
+    }
+    if (st.phase == kWalkDone || st.phase == kWalkStuck) {
+        if (lead && t == 0) st_out[b] = st;
+        return;
+    }
+    const float T = temperature[b];
+    const bool sampled = T > 0.f;
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    SeqInfo s{};
+    temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
+
+    if (st.phase == kWalkPick) {
+        // the final distribution's masses were written last round: wave 0 of chunk 0 draws the token
+        if (lead && wave == 0) {
+            const int64_t row = (b * N + st.node) * static_cast<int64_t>(V);
+            s.rt = static_cast<float>(st.Rt);
+            s.inv_st = static_cast<float>(1.0 / st.St);
+            s.rd = static_cast<float>(st.Rd);
+            s.inv_sd = static_cast<float>(st.c / st.Sd);
+            const float* m = tsegs + b * nseg;
+            const int64_t per = (nseg + kWave - 1) / kWave;
+            const int64_t a0 = min<int64_t>(nseg, lane * per), a1 = min<int64_t>(nseg, a0 + per);
+            double run = 0.0;
+            for (int64_t g = a0; g < a1; ++g) run += static_cast<double>(m[g]);
+            const double W = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+            if (W > 0.0) {
+                const int y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, st.c > 0.0, m, W,
+                                                 static_cast<double>(uniforms[b * N]));
+                if (lane == 0) {
+                    out[st.depth] = y;
+                    accepted_len[b] = st.depth;
+                }
+                st.phase = kWalkDone;
+            } else {
+                st.phase = kWalkStuck;  // an empty residual: the one-workgroup walk falls back to p
+            }
+            if (lane == 0) st_out[b] = st;
+        }
+        return;
+    }
+
+    // the tree, the tokens, uniforms and gathered logits of every node, and
+    // the partial sums of a pending pass
+    const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+#pragma unroll
+    for (int q = 0; q < kRoundSlots; ++q) {
+        const int i = t + q * kRoundBlock;
+        if (i < N) {
+            s_par[i] = i == 0 ? -1 : par[i];
+            s_tok[i] = node_tokens[b * N + i];
+            s_u[i] = uniforms[b * N + i];
+            s_tg[i] = tg[b * N + i];
+            s_dg[i] = dg[b * N + i];
+        }
+    }
+    if (st.phase == kWalkPass && wave == 0) {
+        double zz = 0.0;
+        for (int q = lane; q < P; q += kWave) zz += z_in[b * P + q];
+        zz = wave_sum(zz);
+        if (lane == 0) s_z = zz;
+    }
+    __syncthreads();
+    int n = st.node, d = st.depth, kidx = st.kidx, Rt = st.Rt, Rd = st.Rd;
+    double St = st.St, Sd = st.Sd, c = st.c, Z = st.Z;
+    int phase = st.phase;
+    if (phase == kWalkPass) {
+        Z = s_z;
+        if (!(Z > 0.0)) {
+            c = 0.0;
+            Z = 1.0;
+        }
+        phase = kWalkTest;
+    }
+    const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
+    const int nmask = (N + kWave - 1) / kWave;
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    for (;;) {
+        if (phase == kWalkEnter) {
+            if (wave == 0) {
+                const bool is_draft = lane >= 32;
+                const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+                Partial qv[kBatch];
+                group_load(pr, nT, 32, true, qv);
+                int r;
+                double sum;
+                ArgMax am;
+                if (sampled) {
+                    group_reduce<true>(pr, nT, 32, true, qv, r, sum, am);
+                } else {
+                    group_reduce<false>(pr, nT, 32, true, qv, r, sum, am);
+                    r = am.idx;
+                }
+                if ((lane & 31) == 0) {
+                    s_ref[is_draft] = r;
+                    s_norm[is_draft] = sum;
+                }
+            }
+            __syncthreads();
+            Rt = s_ref[0];
+            Rd = s_ref[1];
+            St = s_norm[0];
+            Sd = s_norm[1];
+            c = 0.0;
+            Z = 1.0;
+            kidx = 0;
+            phase = kWalkTest;
+            __syncthreads();  // s_ref and s_norm are reused at the next node
+        }
+#pragma unroll
+        for (int q = 0; q < kRoundSlots; ++q) {
+            const int i = t + q * kRoundBlock;
+            const uint64_t km = __ballot(i < N && s_par[i] == n);
+            if (lane == 0 && wave + q * kRoundWaves < nmask) s_kids[wave + q * kRoundWaves] = km;
+        }
+        __syncthreads();
+        const double lsum = t == 0 && sampled ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
+        int next = -1, rank = 0;
+        bool pass = false;
+        for (int m = 0; m < nmask && next < 0 && !pass; ++m) {
+            uint64_t kids = s_kids[m];
+            while (kids && next < 0 && !pass) {
+                const int i = m * kWave + __builtin_ctzll(kids);
+                kids &= kids - 1;
+                if (rank++ < kidx) continue;  // rejected in an earlier round
+                if (t == 0) {
+                    const int y = s_tok[i];
+                    double tau = 0.0;
+                    if (static_cast<unsigned>(y) < static_cast<unsigned>(V)) {
+                        if (sampled) {
+                            const double l2ratio = (static_cast<double>(s_tg[i]) * cT -
+                                                    static_cast<double>(s_dg[i]) * cT) - lsum;
+                            tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
+                        } else {
+                            const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
+                            const double rv = fmax(0.0, pv - c * qv) / Z;
+                            tau = qv > 0.0 ? fmin(1.0, rv / qv) : (rv > 0.0 ? 1.0 : 0.0);
+                        }
+                    }
+                    s_accept = static_cast<double>(s_u[i]) < tau;
+                }
+                __syncthreads();
+                const bool accepted = s_accept;
+                __syncthreads();  // s_accept is reused by the next test
+                if (accepted) {
+                    next = i;
+                } else {
+                    // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
+                    c += Z;
+                    kidx = rank;
+                    if (sampled) {
+                        pass = true;
+                    } else {
+                        Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
+                        if (!(Z > 0.0)) {
+                            c = 0.0;
+                            Z = 1.0;
+                        }
+                    }
+                }
+            }
+        }
+        if (next >= 0) {
+            if (lead && t == 0) {
+                out[d] = s_tok[next];
+                if (nodes) nodes[d] = next;
+            }
+            ++d;
+            n = next;
+            phase = kWalkEnter;
+            continue;
+        }
+        if (pass) {
+            phase = kWalkPass;
+        } else if (!sampled) {
+            // one-hot p: the final token is its argmax
+            if (lead && t == 0) {
+                out[d] = Rt;
+                accepted_len[b] = d;
+            }
+            phase = kWalkDone;
+        } else {
+            phase = kWalkPick;  // the masses are written below, the pick comes next round
+        }
+        break;
+    }
+    if (phase == kWalkPass || phase == kWalkPick) {
+        // this workgroup's slice of the segments of node n's rows
+        const int64_t row = (b * N + n) * static_cast<int64_t>(V);
+        s.rt = static_cast<float>(Rt);
+        s.inv_st = static_cast<float>(1.0 / St);
+        s.rd = static_cast<float>(Rd);
+        s.inv_sd = static_cast<float>(c / Sd);
+        const bool residual = c > 0.0;
+        const int64_t spc = (nseg + P - 1) / P;
+        const int64_t g0 = j * spc, g1 = min<int64_t>(nseg, g0 + spc);
+        double acc = 0.0;
+        for (int64_t g = g0 + wave; g < g1; g += kRoundWaves) {
+            float w[VE];
+            walk_weights<DT, VEC>(draft, target, row, V, g, s, residual, w);
+            const float m = wave_sum(pairwise_sum<VE>(w));
+            if (phase == kWalkPick) {
+                if (lane == 0) tsegs[b * nseg + g] = m;
+            } else {
+                acc += static_cast<double>(m);
+            }
+        }
+        if (phase == kWalkPass) {
+            if (lane == 0) s_wsum[wave] = acc;
+            __syncthreads();
+            if (t == 0) {
+                double z = 0.0;
+                for (int w = 0; w < kRoundWaves; ++w) z += s_wsum[w];
+                z_out[b * P + j] = z;
+            }
+        }
+    }
+    if (lead && t == 0) {
+        st.phase = phase;
+        st.node = n;
+        st.depth = d;
+        st.kidx = kidx;
+        st.Rt = Rt;
+        st.Rd = Rd;
+        st.St = St;
+        st.Sd = Sd;
+        st.c = c;
+        st.Z = Z;
+        st_out[b] = st;
+    }
+}
+
+}  // namespace sv

@@ -52,8 +52,8 @@ def main():
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calibrate-mib", type=int, default=256)
-    ap.add_argument("--workload", default="config2")
-    ap.add_argument("--prefix", default="chain_config2")
+    ap.add_argument("--workload", default="llama_chain")
+    ap.add_argument("--prefix", default="llama_chain")
     ap.add_argument("--command", required=True, help="the bench command of the kernel-trace run")
     ap.add_argument("--pmc-command", help="the bench command of the counter runs (default: --command)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))

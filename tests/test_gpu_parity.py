@@ -124,34 +124,34 @@ def test_empty_batch_is_a_no_op(svl):
 # ------------------------------------------------------------ full workloads ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("config", [1, 2, 4])
-def test_full_chain_configs(svl, orc, config, seed):
-    inp = W.make_inputs(config, seed)
-    _check_chain(svl, orc, inp, f"config{config} seed{seed}")
+@pytest.mark.parametrize("workload", ["tiny_chain", "llama_chain", "deepseek_chain"])
+def test_full_chain_workloads(svl, orc, workload, seed):
+    inp = W.make_inputs(workload, seed)
+    _check_chain(svl, orc, inp, f"{workload} seed{seed}")
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
-def test_full_greedy_config(svl, orc, seed):
-    inp = W.make_inputs(3, seed)
+def test_full_greedy_workload(svl, orc, seed):
+    inp = W.make_inputs("greedy_chain", seed)
     got = run_greedy(svl, inp)
     ref = orc.verify_greedy(inp)
     np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
     np.testing.assert_array_equal(got["emitted"], ref["emitted"])
-    _record("greedy", f"config3 seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
+    _record("greedy", f"greedy_chain seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
-def test_full_tree_config(svl, orc, seed):
-    inp = W.make_inputs(5, seed)
+def test_full_tree_workload(svl, orc, seed):
+    inp = W.make_inputs("eagle_tree", seed)
     got = run_tree(svl, inp)
     ref = orc.verify_tree(inp)
     for key in ("accepted_len", "emitted", "accepted_nodes"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
-    _record("tree", f"config5 seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
+    _record("tree", f"eagle_tree seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
 
 
 def test_determinism(svl):
-    inp = W.make_inputs(2, 1)
+    inp = W.make_inputs("llama_chain", 1)
     a = run_chain(svl, inp)
     b = run_chain(svl, inp)
     for key in a:
@@ -271,12 +271,12 @@ def test_gpu_emitted_distribution_chi_square(svl, orc):
 # ------------------------------------------------------------ NEXT rows ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
-@pytest.mark.parametrize("config", [6, 7])
-def test_full_mtp_and_sampling_configs(svl, orc, config, seed):
+@pytest.mark.parametrize("workload", ["mtp_chain", "sampling"])
+def test_full_mtp_and_sampling_workloads(svl, orc, workload, seed):
     """Single-token MTP verification (k = 1, B = 256, V = 129280) and plain
     temperature sampling (k = 0, B = 256)."""
-    inp = W.make_inputs(config, seed)
-    _check_chain(svl, orc, inp, f"config{config} seed{seed}")
+    inp = W.make_inputs(workload, seed)
+    _check_chain(svl, orc, inp, f"{workload} seed{seed}")
 
 
 @pytest.mark.parametrize("with_history", [True, False])
@@ -310,7 +310,7 @@ def test_verify_then_commit_on_device(svl, orc):
     of its output into per-sequence histories, all on one stream."""
     import torch
 
-    inp = W.make_inputs(2, 3)
+    inp = W.make_inputs("llama_chain", 3)
     B, k = inp["B"], inp["k"]
     t = chain_tensors(inp)
     lens = np.arange(B, dtype=np.int32) % 50

@@ -77,9 +77,9 @@ def test_small_shapes(svl, orc, shape, seed):
 
 
 @pytest.mark.parametrize("seed", [1, 2])
-def test_full_sampled_tree_config(svl, orc, seed):
-    inp = W.make_inputs(8, seed)
-    got, ref = _check(svl, orc, inp, f"config8 s{seed}")
+def test_full_sampled_tree_workload(svl, orc, seed):
+    inp = W.make_inputs("sampled_tree", seed)
+    got, ref = _check(svl, orc, inp, f"sampled_tree s{seed}")
     assert (got["accepted_len"] >= 0).all()
 
 

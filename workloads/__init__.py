@@ -351,34 +351,34 @@ def sampled_tree_trials(root_t: np.ndarray, root_d: np.ndarray, F: np.ndarray, G
 
 # ------------------------------------------------------------ the named workloads ---
 
-CONFIGS = {
-    1: dict(name="tiny chain verify", kind="chain", B=1, k=4, V=1024, dtype=F32,
+WORKLOADS = {
+    "tiny_chain": dict(name="tiny chain verify", kind="chain", B=1, k=4, V=1024, dtype=F32,
             target_sigma=2.0, zipf_s=None, draft_sigma=0.5, temperature=1.0),
-    2: dict(name="Llama-scale chain verify", kind="chain", B=64, k=4, V=128256, dtype=BF16,
+    "llama_chain": dict(name="Llama-scale chain verify", kind="chain", B=64, k=4, V=128256, dtype=BF16,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
-    3: dict(name="greedy chain verify", kind="greedy", B=256, k=5, V=128256, dtype=BF16,
+    "greedy_chain": dict(name="greedy chain verify", kind="greedy", B=256, k=5, V=128256, dtype=BF16,
             target_sigma=2.0, match_p=0.8),
-    4: dict(name="DeepSeek-scale chain verify", kind="chain", B=32, k=8, V=129280, dtype=F32,
+    "deepseek_chain": dict(name="DeepSeek-scale chain verify", kind="chain", B=32, k=8, V=129280, dtype=F32,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=(0.3, 1.3)),
-    5: dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
+    "eagle_tree": dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
             target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6),
     # one draft token per sequence, as in the single-token multi-token-prediction
     # schedule (the target scores 2 tokens per sequence of the decode batch)
-    6: dict(name="MTP single-token verify", kind="chain", B=256, k=1, V=129280, dtype=BF16,
+    "mtp_chain": dict(name="MTP single-token verify", kind="chain", B=256, k=1, V=129280, dtype=BF16,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
     # plain temperature sampling of one target row per sequence (no drafts)
-    7: dict(name="temperature sampling", kind="chain", B=256, k=0, V=128256, dtype=BF16,
+    "sampling": dict(name="temperature sampling", kind="chain", B=256, k=0, V=128256, dtype=BF16,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7),
     # the tree of the EAGLE-style workload, verified by sampling (children drawn
     # from the draft rows, logits generated like the Llama-scale chain)
-    8: dict(name="sampled tree verify", kind="tree_sampled", B=16, N=64, V=128256, dtype=BF16,
+    "sampled_tree": dict(name="sampled tree verify", kind="tree_sampled", B=16, N=64, V=128256, dtype=BF16,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=1.0, temperature=0.7, max_branch=4, max_depth=6),
 }
 
 
-def make_inputs(config: int, seed: int = 1, **override) -> dict:
-    """Inputs for one of the named workloads in CONFIGS (sizes may be overridden)."""
-    c = dict(CONFIGS[config])
+def make_inputs(workload: str, seed: int = 1, **override) -> dict:
+    """Inputs for one of the named workloads in WORKLOADS (sizes may be overridden)."""
+    c = dict(WORKLOADS[workload])
     c.update(override)
     kind = c.pop("kind")
     c.pop("name")
