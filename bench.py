@@ -94,22 +94,40 @@ def to_device(inp, torch, W):
     return t
 
 
-def cpu_baseline(inp, seconds: float):
-    """The oracle as it stands, on this host's cores, repeated on the same
-    batch for about `seconds`."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, seconds: float, threads: int = 0):
+    """The oracle as it stands, on this host's cores (or on `threads` of
+    them), repeated on the same batch for about `seconds`."""
     import oracle
 
     fn = {"chain": oracle.verify_chain, "greedy": oracle.verify_greedy, "tree": oracle.verify_tree,
           "tree_sampled": oracle.verify_tree_sampled}[inp["kind"]]
-    fn(inp)  # warm-up (page faults, thread pool)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        fn(inp)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return reps, el, oracle.max_threads()
+    default = oracle.max_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        fn(inp)  # warm-up (page faults, thread pool)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn(inp)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        used = oracle.max_threads()
+    finally:
+        oracle.set_num_threads(default)
+    return reps, el, used
 
 
 def main():
@@ -302,9 +320,13 @@ def main():
 
     if not args.no_cpu:
         reps, el, threads = cpu_baseline(inp, args.cpu_seconds)
+        reps1, el1, _ = cpu_baseline(inp, args.cpu_seconds / 2, threads=1)
         result["cpu_baseline"] = {"value": units * reps / el, "unit": unit, "cores": threads,
                                   "kind": "oracle",
-                                  "sample": f"the full {cfg['name']} batch (B={B}) x {reps} repetitions, {el:.1f} s"}
+                                  "sample": f"the full {cfg['name']} batch (B={B}) x {reps} repetitions, {el:.1f} s",
+                                  "value_1thread": units * reps1 / el1,
+                                  "sample_1thread": f"the same batch x {reps1} repetitions on one thread, {el1:.1f} s",
+                                  "cpu_model": cpu_model()}
     print(json.dumps(result), flush=True)
 
 
