@@ -275,6 +275,15 @@ enum WalkPhase : int {
     kWalkStuck = 5   // a case the rounds leave to the one-workgroup walk (an empty final residual)
 };
 
+// Normalisers of a node's target and draft rows, as the walk combines them
+// from the row partials: reference exponent and sum of each softmax (at
+// temperature 0 the two argmax indices).  A leaf's draft row is never
+// streamed; its entries are rd = 0, sd = 1 and go unused.
+struct alignas(8) NodeNorm {
+    int rt, rd;
+    double st, sd;
+};
+
 struct alignas(16) WalkState {
     int phase, node, depth, kidx;  // kidx: children of `node` already rejected
     int Rt, Rd, pad0, pad1;        // node statistics (at temperature 0: the two argmaxes)
@@ -471,9 +480,11 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
 // When no child is kept, each workgroup writes its slice's segment masses of
 // the final distribution and the next round's chunk 0 picks the token.
 // Chunk 0 writes the outputs and the next state.  Round 0 also checks each
-// tree (invalid trees give -1 outputs) and sets the outputs to -1.  A
-// sequence not finished after the launched rounds is walked again from the
-// start by tree_sample.
+// tree (invalid trees give -1 outputs), sets the outputs to -1 and combines
+// the normalisers of every node, each workgroup a share of the nodes, so
+// that from round 1 on a round reads all its inputs in one round trip and
+// entering a child needs no dependent load.  A sequence not finished after
+// the launched rounds is walked again from the start by tree_sample.
 constexpr int kRoundBlock = 256;
 constexpr int kRoundWaves = kRoundBlock / kWave;
 constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;
@@ -486,8 +497,8 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ tg, const float* __restrict__ dg,
     const WalkState* __restrict__ st_in, WalkState* __restrict__ st_out, const double* __restrict__ z_in,
-    double* __restrict__ z_out, float* __restrict__ tsegs, int P, int first, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
+    double* __restrict__ z_out, float* __restrict__ tsegs, NodeNorm* __restrict__ norm, int P, int first,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
     constexpr int VE = Elem<DT>::per_vec;
     __shared__ int s_par[SV_MAX_TREE_NODES];
     __shared__ int s_anc[SV_MAX_TREE_NODES];
@@ -512,10 +523,66 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const int width = max_depth + 1;
     int32_t* out = emitted + b * width;
     int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
+    const int64_t nbn = static_cast<int64_t>(B) * N;
+    const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+    // every input of the round first (none depends on another): the tree, the
+    // tokens, uniforms and gathered logits of every node, the pending pass's
+    // partial sums and, after round 0, the node normalisers
+    int r_par[kRoundSlots], r_tok[kRoundSlots];
+    float r_u[kRoundSlots], r_tg[kRoundSlots], r_dg[kRoundSlots];
+    NodeNorm r_nrm[kRoundSlots];
+#pragma unroll
+    for (int q = 0; q < kRoundSlots; ++q) {
+        const int i = t + q * kRoundBlock;
+        if (i < N) {
+            r_par[q] = i == 0 ? -1 : par[i];
+            r_tok[q] = node_tokens[b * N + i];
+            r_u[q] = uniforms[b * N + i];
+            r_tg[q] = tg[b * N + i];
+            r_dg[q] = dg[b * N + i];
+            if (!first) r_nrm[q] = norm[b * N + i];
+        }
+    }
+    double zz = 0.0;
+    if (!first && wave == 0)
+        for (int q = lane; q < P; q += kWave) zz += z_in[b * P + q];
+    const float T = temperature[b];
+    const bool sampled = T > 0.f;
     WalkState st{};
     if (first) {
-        const bool bad = walk_validate<kRoundBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth,
-                                                    s_par, s_anc, s_len, &s_bad);
+        // this workgroup's nodes j, j + P, ...: the last wave combines their
+        // normalisers (lanes 0-31 the target row, 32-63 the draft row), the
+        // first node's partials in flight while the tree is checked
+        const bool nw = wave == kRoundWaves - 1;
+        const bool is_draft = lane >= 32;
+        auto rows_of = [&](int i) { return part + ((is_draft ? nbn : 0) + b * N + i) * nT; };
+        Partial qv[kBatch];
+        if (nw && j < N) group_load(rows_of(j), nT, 32, true, qv);
+        const bool bad = walk_validate<kRoundBlock>(par, N, max_depth, s_par, s_anc, s_len, &s_bad);
+        if (nw && !bad) {
+            for (int i = j; i < N; i += P) {
+                if (i != j) group_load(rows_of(i), nT, 32, true, qv);
+                int r;
+                double sum;
+                ArgMax am;
+                if (sampled) {
+                    group_reduce<true>(rows_of(i), nT, 32, true, qv, r, sum, am);
+                } else {
+                    group_reduce<false>(rows_of(i), nT, 32, true, qv, r, sum, am);
+                    r = am.idx;
+                }
+                bool kid = false;
+                for (int m = lane & 31; m < N; m += 32) kid |= s_par[m] == i;
+                const bool inner = (__ballot(kid) >> 32) != 0;
+                if (lane == 0) {
+                    norm[b * N + i].rt = r;
+                    norm[b * N + i].st = sum;
+                } else if (lane == 32) {
+                    norm[b * N + i].rd = inner ? r : 0;
+                    norm[b * N + i].sd = inner ? sum : 1.0;
+                }
+            }
+        }
         if (lead) {
             for (int q = t; q < width; q += kRoundBlock) {
                 out[q] = -1;
@@ -533,8 +600,6 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         if (lead && t == 0) st_out[b] = st;
         return;
     }
-    const float T = temperature[b];
-    const bool sampled = T > 0.f;
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     SeqInfo s{};
     temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
@@ -569,23 +634,18 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         return;
     }
 
-    // the tree, the tokens, uniforms and gathered logits of every node, and
-    // the partial sums of a pending pass
-    const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
 #pragma unroll
     for (int q = 0; q < kRoundSlots; ++q) {
         const int i = t + q * kRoundBlock;
         if (i < N) {
-            s_par[i] = i == 0 ? -1 : par[i];
-            s_tok[i] = node_tokens[b * N + i];
-            s_u[i] = uniforms[b * N + i];
-            s_tg[i] = tg[b * N + i];
-            s_dg[i] = dg[b * N + i];
+            if (!first) s_par[i] = r_par[q];  // round 0: filled by the tree check
+            s_tok[i] = r_tok[q];
+            s_u[i] = r_u[q];
+            s_tg[i] = r_tg[q];
+            s_dg[i] = r_dg[q];
         }
     }
     if (st.phase == kWalkPass && wave == 0) {
-        double zz = 0.0;
-        for (int q = lane; q < P; q += kWave) zz += z_in[b * P + q];
         zz = wave_sum(zz);
         if (lane == 0) s_z = zz;
     }
@@ -603,10 +663,20 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     }
     const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
     const int nmask = (N + kWave - 1) / kWave;
-    const int64_t nbn = static_cast<int64_t>(B) * N;
     for (;;) {
         if (phase == kWalkEnter) {
-            if (wave == 0) {
+            if (!first) {
+                // combined in round 0; the thread holding node n shares them
+#pragma unroll
+                for (int q = 0; q < kRoundSlots; ++q) {
+                    if (t + q * kRoundBlock == n) {
+                        s_ref[0] = r_nrm[q].rt;
+                        s_ref[1] = r_nrm[q].rd;
+                        s_norm[0] = r_nrm[q].st;
+                        s_norm[1] = r_nrm[q].sd;
+                    }
+                }
+            } else if (wave == 0) {
                 const bool is_draft = lane >= 32;
                 const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
                 Partial qv[kBatch];
