@@ -480,11 +480,13 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
 // When no child is kept, each workgroup writes its slice's segment masses of
 // the final distribution and the next round's chunk 0 picks the token.
 // Chunk 0 writes the outputs and the next state.  Round 0 also checks each
-// tree (invalid trees give -1 outputs), sets the outputs to -1 and combines
-// the normalisers of every node, each workgroup a share of the nodes, so
-// that from round 1 on a round reads all its inputs in one round trip and
-// entering a child needs no dependent load.  A sequence not finished after
-// the launched rounds is walked again from the start by tree_sample.
+// tree (invalid trees give -1 outputs) and sets the outputs to -1.  When a
+// sequence has at most one node per wave of its workgroups (N <= 4 P), round
+// 0 also combines the normalisers of every node, one node per wave, so that
+// from round 1 on a round reads all its inputs in one round trip and entering
+// a child needs no dependent load; otherwise every entry combines the node's
+// partials.  A sequence not finished after the launched rounds is walked
+// again from the start by tree_sample.
 constexpr int kRoundBlock = 256;
 constexpr int kRoundWaves = kRoundBlock / kWave;
 constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;
@@ -531,6 +533,7 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     int r_par[kRoundSlots], r_tok[kRoundSlots];
     float r_u[kRoundSlots], r_tg[kRoundSlots], r_dg[kRoundSlots];
     NodeNorm r_nrm[kRoundSlots];
+    const bool cached = N <= kRoundWaves * P;  // node normalisers combined in round 0
 #pragma unroll
     for (int q = 0; q < kRoundSlots; ++q) {
         const int i = t + q * kRoundBlock;
@@ -540,7 +543,7 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
             r_u[q] = uniforms[b * N + i];
             r_tg[q] = tg[b * N + i];
             r_dg[q] = dg[b * N + i];
-            if (!first) r_nrm[q] = norm[b * N + i];
+            if (cached && !first) r_nrm[q] = norm[b * N + i];
         }
     }
     double zz = 0.0;
@@ -550,37 +553,35 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const bool sampled = T > 0.f;
     WalkState st{};
     if (first) {
-        // this workgroup's nodes j, j + P, ...: the last wave combines their
-        // normalisers (lanes 0-31 the target row, 32-63 the draft row), the
-        // first node's partials in flight while the tree is checked
-        const bool nw = wave == kRoundWaves - 1;
+        // with the cache: node j + (3 - wave) P of this workgroup, if any, is
+        // combined by this wave (lanes 0-31 the target row, 32-63 the draft
+        // row), its partials in flight while the tree is checked
+        const int i = j + (kRoundWaves - 1 - wave) * P;
+        const bool mine = cached && i < N;
         const bool is_draft = lane >= 32;
-        auto rows_of = [&](int i) { return part + ((is_draft ? nbn : 0) + b * N + i) * nT; };
+        const Partial* rows = part + ((is_draft ? nbn : 0) + b * N + (mine ? i : 0)) * nT;
         Partial qv[kBatch];
-        if (nw && j < N) group_load(rows_of(j), nT, 32, true, qv);
+        if (mine) group_load(rows, nT, 32, true, qv);
         const bool bad = walk_validate<kRoundBlock>(par, N, max_depth, s_par, s_anc, s_len, &s_bad);
-        if (nw && !bad) {
-            for (int i = j; i < N; i += P) {
-                if (i != j) group_load(rows_of(i), nT, 32, true, qv);
-                int r;
-                double sum;
-                ArgMax am;
-                if (sampled) {
-                    group_reduce<true>(rows_of(i), nT, 32, true, qv, r, sum, am);
-                } else {
-                    group_reduce<false>(rows_of(i), nT, 32, true, qv, r, sum, am);
-                    r = am.idx;
-                }
-                bool kid = false;
-                for (int m = lane & 31; m < N; m += 32) kid |= s_par[m] == i;
-                const bool inner = (__ballot(kid) >> 32) != 0;
-                if (lane == 0) {
-                    norm[b * N + i].rt = r;
-                    norm[b * N + i].st = sum;
-                } else if (lane == 32) {
-                    norm[b * N + i].rd = inner ? r : 0;
-                    norm[b * N + i].sd = inner ? sum : 1.0;
-                }
+        if (mine && !bad) {
+            int r;
+            double sum;
+            ArgMax am;
+            if (sampled) {
+                group_reduce<true>(rows, nT, 32, true, qv, r, sum, am);
+            } else {
+                group_reduce<false>(rows, nT, 32, true, qv, r, sum, am);
+                r = am.idx;
+            }
+            bool kid = false;
+            for (int m = lane & 31; m < N; m += 32) kid |= s_par[m] == i;
+            const bool inner = (__ballot(kid) >> 32) != 0;
+            if (lane == 0) {
+                norm[b * N + i].rt = r;
+                norm[b * N + i].st = sum;
+            } else if (lane == 32) {
+                norm[b * N + i].rd = inner ? r : 0;
+                norm[b * N + i].sd = inner ? sum : 1.0;
             }
         }
         if (lead) {
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const int nmask = (N + kWave - 1) / kWave;
     for (;;) {
         if (phase == kWalkEnter) {
-            if (!first) {
+            if (cached && !first) {
                 // combined in round 0; the thread holding node n shares them
 #pragma unroll
                 for (int q = 0; q < kRoundSlots; ++q) {

@@ -76,6 +76,24 @@ def test_small_shapes(svl, orc, shape, seed):
     _check(svl, orc, inp, f"B{B}N{N}V{V}dt{dt}s{seed}")
 
 
+# Batches on both sides of the normaliser cache's bound.  With P workgroups
+# per sequence (about 1024 / B, at most a quarter of the segments), round 0
+# combines every node's normalisers when N <= 4 P, one node per wave; above
+# that every entry into a node combines its partials.
+BATCHES = [
+    (128, 24, 8200, W.F32),   # P = 8: cached, three nodes per workgroup
+    (300, 16, 5000, W.F32),   # P = 4: N = 4 P exactly, one node on every wave
+    (200, 24, 6000, W.BF16),  # P = 3: not cached
+]
+
+
+@pytest.mark.parametrize("shape", BATCHES, ids=lambda s: f"B{s[0]}N{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_batch_sizes_around_the_normaliser_cache(svl, orc, shape):
+    B, N, V, dt = shape
+    inp = W.sampled_tree_inputs(B, N, V, dt, 11, temperature=_temps(B, None, 11), draft_sigma=(0.3, 2.5))
+    _check(svl, orc, inp, f"batch B{B}N{N}V{V}dt{dt}")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_full_sampled_tree_workload(svl, orc, seed):
     inp = W.make_inputs("sampled_tree", seed)
