@@ -1,7 +1,9 @@
-"""Serving-loop use of the C ABI on the GPU: a verification step and the
-device-side commit captured once in a HIP graph and replayed on new inputs,
-and independent batches verified concurrently on two streams.  Results are
-checked against the fp64 oracle (bit-exact outside the 1e-5 band)."""
+"""Serving-loop use of the C ABI on the GPU: every verification entry point
+(the sampled chain together with the device-side commit, greedy, the greedy
+tree, the sampled tree) captured once in a HIP graph and replayed on new
+inputs with eager calls in between, and independent batches verified
+concurrently on two streams.  Results are checked against the fp64 oracle
+(bit-exact outside the 1e-5 band)."""
 
 import numpy as np
 import pytest
@@ -115,3 +117,146 @@ def test_two_streams_concurrently(svl, orc):
     for i, (oa, ob) in enumerate(outs):
         compare_chain(a_inp, _np(oa), ra, f"stream 1 round {i}")
         compare_chain(b_inp, _np(ob), rb, f"stream 2 round {i}")
+
+
+def _capture(step):
+    """A HIP graph of step(), after one warm-up call on a side stream."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
+def _replay_each(g, static, sets, to_tensors, check, eager):
+    """Replays g once per input set (copied into the captured tensors), with
+    an eager call on other buffers between replays; checks every result."""
+    import torch
+
+    for rep, inp in enumerate(sets):
+        fresh = to_tensors(inp)
+        for key in static:
+            static[key].copy_(fresh[key])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(inp, rep)
+        other = sets[(rep + 1) % len(sets)]
+        eager(other, rep)
+
+
+def test_graph_replay_greedy_and_tree(svl, orc):
+    """sv_verify_greedy and sv_verify_tree captured once each and replayed on
+    new inputs; every replay matches the oracle exactly."""
+    import torch
+
+    from gpu_common import dev_logits, run_greedy, run_tree
+
+    gsets = [W.greedy_inputs(48, 5, 20011, W.BF16, s, match_p=0.7) for s in (51, 52, 53)]
+    B, k, V = 48, 5, 20011
+    to_g = lambda inp: dict(draft_tokens=dev(inp["draft_tokens"].astype(np.int32)),
+                            target_logits=dev_logits(inp["target_logits"], inp["dtype"]))
+    gs = to_g(gsets[0])
+    gws = torch.zeros(svl.greedy_workspace_bytes(B, k, V, W.BF16), dtype=torch.uint8, device="cuda")
+    gout = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"))
+    g = _capture(lambda: svl.verify_greedy(gs["draft_tokens"], gs["target_logits"], workspace=gws, out=gout))
+
+    def check_g(inp, rep):
+        ref = orc.verify_greedy(inp)
+        np.testing.assert_array_equal(gout["accepted_len"].cpu().numpy(), ref["accepted_len"], f"replay {rep}")
+        np.testing.assert_array_equal(gout["emitted"].cpu().numpy(), ref["emitted"], f"replay {rep}")
+
+    def eager_g(inp, rep):
+        np.testing.assert_array_equal(run_greedy(svl, inp)["emitted"], orc.verify_greedy(inp)["emitted"])
+
+    _replay_each(g, gs, gsets + gsets[:1], to_g, check_g, eager_g)
+
+    tsets = [W.tree_inputs(12, 40, 9001, W.F32, s, match_p=0.6) for s in (61, 62, 63)]
+    B, N, V, md = 12, 40, 9001, int(tsets[0]["max_depth"])
+    to_t = lambda inp: dict(node_tokens=dev(inp["node_tokens"].astype(np.int32)),
+                            parent=dev(inp["parent"].astype(np.int32)),
+                            target_logits=dev_logits(inp["target_logits"], inp["dtype"]))
+    ts = to_t(tsets[0])
+    tws = torch.zeros(svl.tree_workspace_bytes(B, N, V, W.F32), dtype=torch.uint8, device="cuda")
+    tout = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
+                accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
+    g = _capture(lambda: svl.verify_tree(ts["node_tokens"], ts["parent"], md, ts["target_logits"], workspace=tws,
+                                         out=tout))
+
+    def check_t(inp, rep):
+        ref = orc.verify_tree(inp)
+        for key in ("accepted_len", "emitted", "accepted_nodes"):
+            np.testing.assert_array_equal(tout[key].cpu().numpy(), ref[key], f"replay {rep} {key}")
+
+    def eager_t(inp, rep):
+        np.testing.assert_array_equal(run_tree(svl, inp)["emitted"], orc.verify_tree(inp)["emitted"])
+
+    _replay_each(g, ts, tsets + tsets[:1], to_t, check_t, eager_t)
+
+
+def test_graph_replay_sampled_tree(svl, orc):
+    """sv_verify_tree_sampled (rowstats, the walk rounds with their
+    double-buffered state, the finisher) captured once and replayed on new
+    inputs, with eager sampled-tree calls in between."""
+    import torch
+
+    from gpu_common import compare_tree_sampled, run_tree_sampled, tree_sampled_tensors
+
+    temps = np.array([0.7, 1.1, 0.0, 0.5, 0.9, 1.3, 0.0, 0.8, 0.6, 1.0], np.float32)
+    sets = [W.sampled_tree_inputs(10, 48, 12007, W.BF16, s, temperature=temps, draft_sigma=(0.3, 2.5))
+            for s in (71, 72, 73)]
+    B, N, V, md = 10, 48, 12007, int(sets[0]["max_depth"])
+    static = tree_sampled_tensors(sets[0])
+    ws = torch.zeros(svl.tree_sampled_workspace_bytes(B, N, V, W.BF16), dtype=torch.uint8, device="cuda")
+    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+               emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
+               accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
+    g = _capture(lambda: svl.verify_tree_sampled(static["node_tokens"], static["parent"], md,
+                                                 static["draft_logits"], static["target_logits"],
+                                                 static["temperature"], static["uniforms"], workspace=ws, out=out))
+
+    def check(inp, rep):
+        compare_tree_sampled(_np(out), orc.verify_tree_sampled(inp), f"graph replay {rep}")
+
+    def eager(inp, rep):
+        compare_tree_sampled(run_tree_sampled(svl, inp), orc.verify_tree_sampled(inp), f"eager {rep}")
+
+    _replay_each(g, static, sets + sets[:2], tree_sampled_tensors, check, eager)
+
+
+def test_sampled_trees_on_two_streams(svl, orc):
+    """Two sampled-tree batches in flight together on two streams, each with
+    its own workspace."""
+    import torch
+
+    from gpu_common import compare_tree_sampled, tree_sampled_tensors
+
+    a_inp = W.sampled_tree_inputs(12, 40, 9001, W.F32, 81, draft_sigma=(0.3, 2.0))
+    b_inp = W.sampled_tree_inputs(7, 64, 20000, W.BF16, 82, draft_sigma=(0.3, 2.0))
+    ta, tb = tree_sampled_tensors(a_inp), tree_sampled_tensors(b_inp)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa = svl.verify_tree_sampled(ta["node_tokens"], ta["parent"], int(a_inp["max_depth"]),
+                                         ta["draft_logits"], ta["target_logits"], ta["temperature"], ta["uniforms"])
+        with torch.cuda.stream(s2):
+            ob = svl.verify_tree_sampled(tb["node_tokens"], tb["parent"], int(b_inp["max_depth"]),
+                                         tb["draft_logits"], tb["target_logits"], tb["temperature"], tb["uniforms"])
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    ra, rb = orc.verify_tree_sampled(a_inp), orc.verify_tree_sampled(b_inp)
+    for i, (oa, ob) in enumerate(outs):
+        compare_tree_sampled(_np(oa), ra, f"stream 1 round {i}")
+        compare_tree_sampled(_np(ob), rb, f"stream 2 round {i}")
