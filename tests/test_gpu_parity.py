@@ -342,3 +342,48 @@ def test_large_batch_final_draw(svl, orc, shape):
     inp = W.chain_inputs(B, k, V, dt, 11, target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0),
                          temperature=(0.3, 1.3))
     _check_chain(svl, orc, inp, f"pipelined B{B}k{k}V{V}dt{dt}")
+
+
+@pytest.mark.parametrize("fill", [0xFF, 0x7F], ids=["ff", "7f"])
+def test_workspace_needs_no_initialisation(svl, orc, fill):
+    """Every entry point on a workspace whose bytes all hold `fill` (0xFF: NaN
+    floats and -1 integers; 0x7F: huge values) gives the oracle's results, as
+    the header promises: no call reads workspace memory it has not written."""
+    import torch
+
+    from gpu_common import compare_tree_sampled, tree_sampled_tensors
+
+    def ws(nbytes):
+        return torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+
+    temps = np.array([0.7, 0.0, 1.2, 0.5, 0.9, 0.0], np.float32)
+    chains = [W.chain_inputs(6, 3, 5000, W.BF16, 91, draft_sigma=(0.3, 2.0), temperature=temps),   # inline acceptance
+              W.chain_inputs(700, 1, 20000, W.BF16, 92, draft_sigma=(0.3, 2.0)),                 # acceptance kernel
+              W.chain_inputs(9, 0, 3001, W.F32, 93, temperature=np.linspace(0, 1.5, 9, dtype=np.float32))]
+    for i, inp in enumerate(chains):
+        got = run_chain(svl, inp, workspace=ws(svl.chain_workspace_bytes(inp["B"], inp["k"], inp["V"], inp["dtype"])))
+        compare_chain(inp, got, orc.verify_chain(inp), f"chain {i} fill {fill:#x}")
+    g = W.greedy_inputs(20, 4, 7000, W.F32, 94)
+    out = svl.verify_greedy(dev(g["draft_tokens"].astype(np.int32)), dev_logits(g["target_logits"], g["dtype"]),
+                            workspace=ws(svl.greedy_workspace_bytes(20, 4, 7000, W.F32)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["emitted"].cpu().numpy(), orc.verify_greedy(g)["emitted"])
+    t = W.tree_inputs(8, 30, 6000, W.BF16, 95)
+    out = svl.verify_tree(dev(t["node_tokens"].astype(np.int32)), dev(t["parent"].astype(np.int32)),
+                          int(t["max_depth"]), dev_logits(t["target_logits"], t["dtype"]),
+                          workspace=ws(svl.tree_workspace_bytes(8, 30, 6000, W.BF16)))
+    torch.cuda.synchronize()
+    ref = orc.verify_tree(t)
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], key)
+    # the sampled tree with and without the round-0 normaliser cache
+    for inp in (W.sampled_tree_inputs(6, 40, 9000, W.BF16, 96, draft_sigma=(0.3, 2.0)),
+                W.sampled_tree_inputs(200, 24, 6000, W.BF16, 97, draft_sigma=(0.3, 2.0))):
+        ts = tree_sampled_tensors(inp)
+        B, N, V = inp["B"], inp["N"], inp["V"]
+        out = svl.verify_tree_sampled(ts["node_tokens"], ts["parent"], int(inp["max_depth"]), ts["draft_logits"],
+                                      ts["target_logits"], ts["temperature"], ts["uniforms"],
+                                      workspace=ws(svl.tree_sampled_workspace_bytes(B, N, V, inp["dtype"])))
+        torch.cuda.synchronize()
+        got = {key: (v.cpu().numpy() if v is not None else None) for key, v in out.items()}
+        compare_tree_sampled(got, orc.verify_tree_sampled(inp), f"sampled tree B{B} fill {fill:#x}")
