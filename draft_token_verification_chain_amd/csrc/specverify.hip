@@ -399,12 +399,14 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                     emitted, accepted_nodes);
         if (st != SV_OK) return st;
     }
-    // sequences the rounds have not finished: the one-workgroup walk, from the start
+    // what the rounds leave: the final draw from masses the last round wrote, or the
+    // one-workgroup walk from the start
     auto walk = dt == SV_BF16 ? (vec ? sv::tree_sample_kernel<SV_BF16, true> : sv::tree_sample_kernel<SV_BF16, false>)
                               : (vec ? sv::tree_sample_kernel<SV_F32, true> : sv::tree_sample_kernel<SV_F32, false>);
     return launch("tree_sample", walk, dim3(B), dim3(sv::kWalkBlock), stream, node_tokens, parent, parent_stride, N,
                   max_depth, draft_logits, target_logits, temperature, uniforms, B, V, nT,
                   static_cast<const Partial*>(part), static_cast<const sv::WalkState*>(state + (sv::kWalkRounds & 1) * B),
+                  static_cast<const float*>(tsegs),
                   accepted_len, emitted, accepted_nodes);
 }
 

@@ -290,15 +290,64 @@ struct alignas(16) WalkState {
     double St, Sd, c, Z;
 };
 
+// The final draw of a walk that stopped at st.node, from the segment masses m
+// of its final distribution (written by the last round): one wave.  Returns
+// false, with y untouched, when the masses sum to zero (an empty residual).
+template <int DT, bool VEC>
+__device__ bool pick_from_masses(const void* draft, const void* target, int64_t b, int N, int V, float T,
+                                 const WalkState& st, const float* m, float u, int& y) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int lane = lane_id();
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    SeqInfo s{};
+    temperature_scale(T > 0.f ? T : 1.f, s.c_hi, s.c_lo);
+    s.rt = static_cast<float>(st.Rt);
+    s.inv_st = static_cast<float>(1.0 / st.St);
+    s.rd = static_cast<float>(st.Rd);
+    s.inv_sd = static_cast<float>(st.c / st.Sd);
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t a0 = min<int64_t>(nseg, lane * per), a1 = min<int64_t>(nseg, a0 + per);
+    double run = 0.0;
+    for (int64_t g = a0; g < a1; ++g) run += static_cast<double>(m[g]);
+    const double W = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+    if (!(W > 0.0)) return false;
+    const int64_t row = (b * N + st.node) * static_cast<int64_t>(V);
+    y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, st.c > 0.0, m, W, static_cast<double>(u));
+    return true;
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
     int max_depth, const void* __restrict__ draft, const void* __restrict__ target,
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
-    const Partial* __restrict__ part, const WalkState* __restrict__ state, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
+    const Partial* __restrict__ part, const WalkState* __restrict__ state, const float* __restrict__ tsegs,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
     constexpr int VE = Elem<DT>::per_vec;
-    if (state != nullptr && state[blockIdx.x].phase == kWalkDone) return;  // finished by the rounds
+    if (state != nullptr) {
+        const WalkState st = state[blockIdx.x];
+        if (st.phase == kWalkDone) return;  // finished by the rounds
+        if (st.phase == kWalkPick) {
+            // the rounds left only the final draw: its segment masses are written
+            __shared__ int s_picked;
+            const int64_t b = blockIdx.x;
+            if (threadIdx.x < kWave) {
+                const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+                int y = -1;
+                const bool ok = pick_from_masses<DT, VEC>(draft, target, b, N, V, temperature[b], st,
+                                                          tsegs + b * nseg, uniforms[b * N], y);
+                if (lane_id() == 0) {
+                    s_picked = ok;
+                    if (ok) {
+                        emitted[b * (max_depth + 1) + st.depth] = y;
+                        accepted_len[b] = st.depth;
+                    }
+                }
+            }
+            __syncthreads();
+            if (s_picked) return;  // else (an empty residual) the walk below starts over
+        }
+    }
     __shared__ int s_par[SV_MAX_TREE_NODES];
     __shared__ int s_anc[SV_MAX_TREE_NODES];
     __shared__ int s_len[SV_MAX_TREE_NODES];
@@ -485,12 +534,13 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
 // 0 also combines the normalisers of every node, one node per wave, so that
 // from round 1 on a round reads all its inputs in one round trip and entering
 // a child needs no dependent load; otherwise every entry combines the node's
-// partials.  A sequence not finished after the launched rounds is walked
-// again from the start by tree_sample.
+// partials.  After the launched rounds, tree_sample draws the final token of
+// a sequence whose last round wrote its final masses, and walks any other
+// unfinished sequence again from the start.
 constexpr int kRoundBlock = 256;
 constexpr int kRoundWaves = kRoundBlock / kWave;
 constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;
-constexpr int kWalkRounds = 8;
+constexpr int kWalkRounds = 7;
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
@@ -608,20 +658,9 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     if (st.phase == kWalkPick) {
         // the final distribution's masses were written last round: wave 0 of chunk 0 draws the token
         if (lead && wave == 0) {
-            const int64_t row = (b * N + st.node) * static_cast<int64_t>(V);
-            s.rt = static_cast<float>(st.Rt);
-            s.inv_st = static_cast<float>(1.0 / st.St);
-            s.rd = static_cast<float>(st.Rd);
-            s.inv_sd = static_cast<float>(st.c / st.Sd);
-            const float* m = tsegs + b * nseg;
-            const int64_t per = (nseg + kWave - 1) / kWave;
-            const int64_t a0 = min<int64_t>(nseg, lane * per), a1 = min<int64_t>(nseg, a0 + per);
-            double run = 0.0;
-            for (int64_t g = a0; g < a1; ++g) run += static_cast<double>(m[g]);
-            const double W = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
-            if (W > 0.0) {
-                const int y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, st.c > 0.0, m, W,
-                                                 static_cast<double>(uniforms[b * N]));
+            int y = -1;
+            if (pick_from_masses<DT, VEC>(draft, target, b, N, V, T, st, tsegs + b * nseg,
+                                          uniforms[b * N], y)) {
                 if (lane == 0) {
                     out[st.depth] = y;
                     accepted_len[b] = st.depth;

@@ -214,3 +214,23 @@ def test_hand_derived_golden_examples_on_gpu(svl):
         assert got["accepted_len"][i] == c["accepted_len"], c["why"]
         assert got["emitted"][i].tolist() == c["emitted"], c["why"]
         np.testing.assert_allclose(got["accept_prob"][i], c["accept_prob"], atol=1e-6, err_msg=c["why"])
+
+
+@pytest.mark.parametrize("kids", [5, 6, 7, 12])
+def test_walks_ending_around_the_last_round(svl, orc, kids):
+    """A root whose `kids` children all carry tokens the target row gives
+    almost no mass: every child is rejected, so the walk needs `kids` passes
+    over the root's rows and then the final draw.  With seven rounds the
+    draw then falls in the last round (5), in the finisher from the masses
+    the last round wrote (6), or the finisher walks the sequence again from
+    the start (7, 12)."""
+    B, V = 8, 3000
+    star = np.full(kids + 1, 0, dtype=np.int32)
+    star[0] = -1
+    inp = W.sampled_tree_inputs(B, kids + 1, V, W.F32, 40 + kids, parent=star, max_depth=1, draft_sigma=0.5)
+    for b in range(B):
+        toks = inp["node_tokens"][b, 1:]
+        inp["target_logits"][b, 0, toks] = -30.0  # p(x) ~ 1e-13 relative: certain rejection
+        inp["draft_logits"][b, 0, toks] = 8.0
+    got, ref = _check(svl, orc, inp, f"star{kids}")
+    assert (ref["accepted_len"] == 0).all()  # the oracle rejected every child
