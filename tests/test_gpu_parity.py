@@ -387,3 +387,27 @@ def test_workspace_needs_no_initialisation(svl, orc, fill):
         torch.cuda.synchronize()
         got = {key: (v.cpu().numpy() if v is not None else None) for key, v in out.items()}
         compare_tree_sampled(got, orc.verify_tree_sampled(inp), f"sampled tree B{B} fill {fill:#x}")
+
+
+# Vocabulary sizes at the edges of the work units: a 16-byte vector (8 bf16 or
+# 4 f32), a segment (64 vectors), the draw's wave tile (4 segments) and the
+# streaming tile (8 segments), one below and one above each, and V = 1.
+EDGE_V = [1, 2, 7, 8, 9, 63, 64, 65, 255, 256, 257, 511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097]
+
+
+@pytest.mark.parametrize("V", EDGE_V)
+def test_vocabulary_sizes_at_tile_and_segment_edges(svl, orc, V):
+    temps = np.array([0.7, 0.0, 1.2, 0.4, 1.0], np.float32)
+    for dt in (W.BF16, W.F32):
+        inp = W.chain_inputs(5, 2, V, dt, V, draft_sigma=(0.3, 2.0), temperature=temps)
+        _check_chain(svl, orc, inp, f"edge V{V} dt{dt}")
+        k0 = W.chain_inputs(5, 0, V, dt, V + 1, temperature=temps)
+        _check_chain(svl, orc, k0, f"edge k0 V{V} dt{dt}")
+        g = W.greedy_inputs(5, 2, V, dt, V)
+        got, ref = run_greedy(svl, g), orc.verify_greedy(g)
+        np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+        np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+        t = W.tree_inputs(4, 9, V, dt, V)
+        got, ref = run_tree(svl, t), orc.verify_tree(t)
+        for key in ("accepted_len", "emitted", "accepted_nodes"):
+            np.testing.assert_array_equal(got[key], ref[key], key)

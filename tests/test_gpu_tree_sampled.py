@@ -234,3 +234,10 @@ def test_walks_ending_around_the_last_round(svl, orc, kids):
         inp["draft_logits"][b, 0, toks] = 8.0
     got, ref = _check(svl, orc, inp, f"star{kids}")
     assert (ref["accepted_len"] == 0).all()  # the oracle rejected every child
+
+
+@pytest.mark.parametrize("V", [1, 2, 9, 64, 257, 512, 2049, 4096])
+def test_vocabulary_sizes_at_segment_edges(svl, orc, V):
+    for dt in (W.BF16, W.F32):
+        inp = W.sampled_tree_inputs(4, 9, V, dt, V, temperature=_temps(4, None, V), draft_sigma=(0.3, 2.0))
+        _check(svl, orc, inp, f"edge V{V} dt{dt}")

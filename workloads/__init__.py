@@ -96,7 +96,10 @@ def zipf_bias(V: int, s: float, seed: int) -> np.ndarray:
 
 
 def _other_token(rng: np.random.Generator, avoid: int, V: int) -> int:
-    """Uniform over the V-1 tokens different from ``avoid``."""
+    """Uniform over the V-1 tokens different from ``avoid`` (``avoid`` itself
+    when V = 1, where there is no other token)."""
+    if V < 2:
+        return avoid
     r = int(rng.integers(0, V - 1))
     return r if r < avoid else r + 1
 
