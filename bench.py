@@ -310,8 +310,8 @@ def main():
         "hbm_frac_of_peak": step_bytes / s_per_step / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": step_bytes,
         "bytes_per_verified_token": step_bytes / units,
-        "emitted_tokens_per_s": (float(out["accepted_len"].sum().item() + B) / s_per_step
-                                 if kind != "tree" else float(out["accepted_len"].sum().item() + B) / s_per_step),
+        # every sequence emits its accepted tokens plus one final token
+        "emitted_tokens_per_s": float(out["accepted_len"].sum().item() + B) / s_per_step,
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
