@@ -383,8 +383,8 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                                          : sv::tree_rowstats_kernel<SV_BF16, false, kU>)
                                   : (vec ? sv::tree_rowstats_kernel<SV_F32, true, kU>
                                          : sv::tree_rowstats_kernel<SV_F32, false, kU>);
-    st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits,
-                          draft_logits, parent, parent_stride, node_tokens, temperature, B, N, V, nT, part, tg, dg);
+    st = launch("tree_rowstats", rowstats, dim3(blocks), dim3(sv::kBlock), stream, target_logits, draft_logits,
+                parent, parent_stride, node_tokens, temperature, B, N, V, nT, part, tg, dg);
     if (st != SV_OK) return st;
     auto round = dt == SV_BF16 ? (vec ? sv::tree_round_kernel<SV_BF16, true> : sv::tree_round_kernel<SV_BF16, false>)
                                : (vec ? sv::tree_round_kernel<SV_F32, true> : sv::tree_round_kernel<SV_F32, false>);
@@ -406,8 +406,7 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
     return launch("tree_sample", walk, dim3(B), dim3(sv::kWalkBlock), stream, node_tokens, parent, parent_stride, N,
                   max_depth, draft_logits, target_logits, temperature, uniforms, B, V, nT,
                   static_cast<const Partial*>(part), static_cast<const sv::WalkState*>(state + (sv::kWalkRounds & 1) * B),
-                  static_cast<const float*>(tsegs),
-                  accepted_len, emitted, accepted_nodes);
+                  static_cast<const float*>(tsegs), accepted_len, emitted, accepted_nodes);
 }
 
 sv_status sv_commit_tokens(int B, int width, const int32_t* accepted_len, const int32_t* emitted, int32_t* seq_len,
