@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Summarise rocprofv3 output of bench.py runs into profiles/.
 
-Inputs (rocprofv3 CSV directories written on the GPU machine):
+Inputs (rocprofv3 CSV output directories):
   --trace DIR   from  rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o bench -- python3 bench.py ...
   --fetch DIR   from  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
   --write DIR   from  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
