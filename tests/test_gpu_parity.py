@@ -268,6 +268,21 @@ def test_gpu_emitted_distribution_chi_square(svl, orc):
         assert stats.chisquare(counts, p * sel.sum()).pvalue > 1e-4
 
 
+def test_gpu_plain_sampling_chi_square(svl, orc):
+    """k = 0 through the GPU: 10^6 trials at V = 16 and T = 0.8, bit-exact
+    with the oracle outside the band, and the sampled token distributed as
+    softmax(t / T) (chi-square)."""
+    from scipy import special, stats
+
+    rng = np.random.default_rng(2024)
+    t = (1.5 * rng.standard_normal((1, 16))).astype(np.float32)
+    inp = W.repeated_trials(t, np.zeros((0, 16), np.float32), 0.8, 1_000_000, seed=92)
+    got, ref = _check_chain(svl, orc, inp, "chi k0")
+    counts = np.bincount(got["emitted"][:, 0], minlength=16)
+    p = special.softmax(t[0].astype(np.float64) / np.float64(np.float32(0.8)))
+    assert stats.chisquare(counts, p * 1_000_000).pvalue > 1e-4
+
+
 # ------------------------------------------------------------ NEXT rows ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3])

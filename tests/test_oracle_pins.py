@@ -275,6 +275,20 @@ def test_acceptance_rate_is_overlap(chi_trials):
         assert abs(z) < 5, (j, alpha, hits / n)
 
 
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.5])
+def test_plain_sampling_follows_target_distribution(orc, T):
+    """k = 0 (no drafts): over 10^6 seeded trials at V = 16 the sampled token
+    is distributed as softmax(t / T) (chi-square), and the same counts reject
+    a softmax at a wrong temperature, so the test has the power to see one."""
+    t, _ = _chi_rows()
+    inp = W.repeated_trials(t[:1], np.zeros((0, V_CHI), np.float32), T, N_CHI, seed=91)
+    r = orc.verify_chain(inp)
+    assert (r["accepted_len"] == 0).all()
+    counts = np.bincount(r["emitted"][:, 0], minlength=V_CHI)
+    assert stats.chisquare(counts, _softmax_rows(t[0], T) * N_CHI).pvalue > 1e-4
+    assert stats.chisquare(counts, _softmax_rows(t[0], 1.7) * N_CHI).pvalue < 1e-12
+
+
 @pytest.mark.parametrize("mutation", ["MUT_SAMPLE_TARGET_AT_MISMATCH", "MUT_RESIDUAL_SWAPPED",
                                       "MUT_ROWS_SHIFTED", "MUT_ACCEPT_INVERTED"])
 def test_planted_mistakes_fail_the_distribution_test(orc, mutated, mutation):
