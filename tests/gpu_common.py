@@ -10,14 +10,19 @@ BAND_EPS = 1e-5
 PROB_TOL = 1e-5
 
 
+def _host(arr, dtype=None):
+    """A C-contiguous, writable array (copied only when needed) for torch.from_numpy."""
+    return np.require(arr, dtype=dtype, requirements=["C", "W"])
+
+
 def dev_logits(arr, dtype, device="cuda"):
     if dtype == W.BF16:
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+        return torch.from_numpy(_host(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(_host(arr, np.float32)).to(device)
 
 
 def dev(arr, device="cuda"):
-    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    return torch.from_numpy(_host(arr)).to(device)
 
 
 def chain_tensors(inp, device="cuda"):
