@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kCommitBlock) void commit_tokens_kernel(
             len = seq_len[b];
             if (a < 0) {
                 st = 2;
-            } else if (a + 1 > width || len < 0 ||
+            } else if (a >= width || len < 0 || static_cast<int64_t>(len) + a + 1 > INT32_MAX ||
                        (history != nullptr &&
                         static_cast<int64_t>(len) + a + 1 > static_cast<int64_t>(history_stride))) {
                 st = 1;

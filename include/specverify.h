@@ -235,9 +235,9 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt,
  *   packed        int32 [>= B * width] out  optional (NULL): the committed tokens, packed
  *                                   in sequence order at packed_offsets
  *   status        int32 [B]   out  optional (NULL): 0 committed; 1 nothing committed because
- *                                   a_b + 1 > width, seq_len[b] < 0 or (with a history)
- *                                   seq_len[b] + a_b + 1 > history_stride; 2 nothing to
- *                                   commit (a_b < 0)
+ *                                   a_b >= width, seq_len[b] < 0, seq_len[b] + a_b + 1 >
+ *                                   INT32_MAX or (with a history) seq_len[b] + a_b + 1 >
+ *                                   history_stride; 2 nothing to commit (a_b < 0)
  *
  * The history and packed writes of different sequences never overlap; seq_len
  * is updated in place, so the call must not be repeated for the same step.

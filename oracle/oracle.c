@@ -595,7 +595,8 @@ int svo_commit_tokens(int B, int width, const int32_t *accepted_len, const int32
         int n = 0, st = 0;
         if (a < 0)
             st = 2;
-        else if (a + 1 > width || len < 0 || (history && (long long)len + a + 1 > (long long)history_stride))
+        else if (a >= width || len < 0 || (long long)len + a + 1 > 2147483647LL ||
+                 (history && (long long)len + a + 1 > (long long)history_stride))
             st = 1;
         else
             n = a + 1;

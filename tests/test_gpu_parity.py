@@ -320,6 +320,31 @@ def test_commit_tokens_parity(svl, orc, B, with_history):
     np.testing.assert_array_equal(out["status"].cpu().numpy(), ref["status"])
 
 
+@pytest.mark.parametrize("with_history", [True, False])
+def test_commit_tokens_rows_that_would_overflow(svl, orc, with_history):
+    """Counts and lengths at the int32 limit: the GPU refuses and commits the
+    same rows as the oracle, with no wrap-around."""
+    import torch
+
+    imax = int(np.iinfo(np.int32).max)
+    acc = np.array([imax, 1, 2, 0, 2, imax - 1], np.int32)
+    em = np.arange(18, dtype=np.int32).reshape(6, 3)
+    lens = np.array([5, imax - 2, imax - 2, imax, 3, 0], np.int32)
+    hist = np.zeros((6, 8), np.int32) if with_history else None
+    ref = orc.commit_tokens(acc, em, lens, hist)
+    sl = dev(lens)
+    h = dev(hist) if with_history else None
+    out = svl.commit_tokens(dev(acc), dev(em), sl, h)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["status"].cpu().numpy(), ref["status"])
+    np.testing.assert_array_equal(sl.cpu().numpy(), ref["seq_len"])
+    offs = out["packed_offsets"].cpu().numpy()
+    np.testing.assert_array_equal(offs, ref["packed_offsets"])
+    np.testing.assert_array_equal(out["packed"].cpu().numpy()[:offs[-1]], ref["packed"])
+    if with_history:
+        np.testing.assert_array_equal(h.cpu().numpy(), ref["history"])
+
+
 def test_verify_then_commit_on_device(svl, orc):
     """A decode step without host synchronisation: verification, then the commit
     of its output into per-sequence histories, all on one stream."""

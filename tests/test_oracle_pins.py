@@ -472,6 +472,21 @@ def test_commit_matches_list_semantics(orc):
     assert (r2["seq_len"] == lens + np.where((acc >= 0) & (acc < width), acc + 1, 0)).all()
 
 
+def test_commit_refuses_rows_that_would_overflow(orc):
+    """A count of INT32_MAX, or (without a history, which has no capacity) a
+    length that would pass INT32_MAX, is refused with status 1 and leaves the
+    sequence untouched; a length that reaches INT32_MAX exactly is committed."""
+    imax = int(np.iinfo(np.int32).max)
+    acc = np.array([imax, 1, 2, 0], np.int32)
+    em = np.arange(12, dtype=np.int32).reshape(4, 3)
+    lens = np.array([5, imax - 2, imax - 2, imax], np.int32)
+    r = orc.commit_tokens(acc, em, lens)
+    assert r["status"].tolist() == [1, 0, 1, 1]
+    assert r["seq_len"].tolist() == [5, imax, imax - 2, imax]
+    assert r["packed"].tolist() == [3, 4]
+    assert r["packed_offsets"].tolist() == [0, 0, 2, 2, 2]
+
+
 # ------------------------------------------------------------ sampled tree ---
 # Multi-step speculative sampling (SpecInfer, Miao et al. 2023; the rule the
 # EAGLE work applies to its trees): the pages give no rule for sampled trees.
