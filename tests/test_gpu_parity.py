@@ -451,3 +451,29 @@ def test_vocabulary_sizes_at_tile_and_segment_edges(svl, orc, V):
         got, ref = run_tree(svl, t), orc.verify_tree(t)
         for key in ("accepted_len", "emitted", "accepted_nodes"):
             np.testing.assert_array_equal(got[key], ref[key], key)
+
+
+# Logits at the edges of the header's preconditions (|l| / T < 10^6, and
+# |l_v - max l| / T < 700 within a row): large common offsets (the
+# distributions do not change, but the integer references and the split
+# temperature scale work at large magnitudes), a very small and a very large
+# temperature.  The drafts drawn before the shift remain samples of the
+# shifted draft rows.
+EXTREMES = [
+    (5000.0, 0.7, W.BF16, 3.0),
+    (-5000.0, 0.7, W.BF16, 3.0),
+    (1.0e5, 1.0, W.F32, 3.0),
+    (-1.0e5, 1.0, W.F32, 3.0),
+    (0.0, 0.05, W.F32, 1.0),
+    (0.0, 100.0, W.BF16, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", EXTREMES, ids=lambda c: f"off{c[0]:g}-T{c[1]:g}-{W.DTYPE_NAMES[c[2]]}")
+def test_logits_at_the_edges_of_the_declared_range(svl, orc, case):
+    offset, T, dt, sigma = case
+    inp = W.chain_inputs(16, 3, 5000, dt, 31, target_sigma=sigma, draft_sigma=(0.2, 1.5),
+                         temperature=np.float32(T))
+    for key in ("target_logits", "draft_logits"):
+        inp[key] = W.to_dtype(W.values(inp[key], dt) + np.float32(offset), dt)
+    _check_chain(svl, orc, inp, f"extreme off{offset:g} T{T:g} dt{dt}")
