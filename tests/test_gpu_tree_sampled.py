@@ -241,3 +241,16 @@ def test_vocabulary_sizes_at_segment_edges(svl, orc, V):
     for dt in (W.BF16, W.F32):
         inp = W.sampled_tree_inputs(4, 9, V, dt, V, temperature=_temps(4, None, V), draft_sigma=(0.3, 2.0))
         _check(svl, orc, inp, f"edge V{V} dt{dt}")
+
+
+@pytest.mark.parametrize("case", [(5000.0, 0.7, W.BF16), (-1.0e5, 1.0, W.F32), (0.0, 0.05, W.F32), (0.0, 100.0, W.BF16)],
+                         ids=lambda c: f"off{c[0]:g}-T{c[1]:g}-{W.DTYPE_NAMES[c[2]]}")
+def test_logits_at_the_edges_of_the_declared_range(svl, orc, case):
+    """Large common offsets and extreme temperatures, inside the header's
+    preconditions (|l| / T < 10^6, |l_v - max l| / T < 700)."""
+    offset, T, dt = case
+    inp = W.sampled_tree_inputs(8, 24, 5000, dt, 33, target_sigma=1.0 if T < 0.1 else 3.0, zipf_s=None,
+                                draft_sigma=(0.2, 1.5), temperature=np.float32(T))
+    for key in ("target_logits", "draft_logits"):
+        inp[key] = W.to_dtype(W.values(inp[key], dt) + np.float32(offset), dt)
+    _check(svl, orc, inp, f"extreme off{offset:g} T{T:g} dt{dt}")
