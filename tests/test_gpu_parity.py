@@ -477,3 +477,46 @@ def test_logits_at_the_edges_of_the_declared_range(svl, orc, case):
     for key in ("target_logits", "draft_logits"):
         inp[key] = W.to_dtype(W.values(inp[key], dt) + np.float32(offset), dt)
     _check_chain(svl, orc, inp, f"extreme off{offset:g} T{T:g} dt{dt}")
+
+
+def test_out_of_range_draft_tokens_are_rejected(svl, orc):
+    """The header's rule for a draft token outside [0, V): it is rejected
+    (tau = 0) and never used as an index.  The oracle refuses such inputs, so
+    the check is by properties: acceptance stops at or before the bad
+    position, its accept_prob is 0 and the final token is a valid id; the
+    other sequences still match the oracle exactly."""
+    V = 3001
+    temps = np.array([0.8, 1.1, 0.0, 0.6] * 4, np.float32)
+    inp = W.chain_inputs(16, 4, V, W.F32, 41, draft_sigma=0.05, temperature=temps)  # near-copy drafts: long prefixes
+    bad = {1: (1, V), 5: (2, -7), 9: (0, V + 1000), 14: (3, -1)}  # sequence: (position, token)
+    for b, (j, tok) in bad.items():
+        inp["draft_tokens"][b, j] = tok
+    got = run_chain(svl, inp)
+    for b, (j, tok) in bad.items():
+        a = int(got["accepted_len"][b])
+        assert a <= j, (b, a, j)
+        if a == j:
+            assert got["accept_prob"][b, j] == 0.0
+        assert 0 <= got["emitted"][b, a] < V
+        assert (got["emitted"][b, :a] == inp["draft_tokens"][b, :a]).all()
+        assert (got["emitted"][b, a + 1:] == -1).all()
+    keep = np.array([b for b in range(16) if b not in bad])
+    sub = {key: (val[keep] if isinstance(val, np.ndarray) and val.ndim and val.shape[0] == 16 else val)
+           for key, val in inp.items()}
+    sub["B"] = keep.size
+    ref = orc.verify_chain(sub)
+    compare_chain(sub, {key: (v[keep] if v is not None else None) for key, v in got.items()}, ref, "valid rows")
+    # greedy: an out-of-range id never equals the argmax
+    g = W.greedy_inputs(8, 4, V, W.BF16, 42, match_p=1.0)
+    g["draft_tokens"][3, 2] = V + 3
+    g["draft_tokens"][6, 0] = -2
+    gg = run_greedy(svl, g)
+    assert gg["accepted_len"][3] == 2 and gg["accepted_len"][6] == 0
+    assert ((gg["emitted"] >= 0) | (gg["emitted"] == -1)).all() and (gg["emitted"] < V).all()
+    # greedy tree: a node with an out-of-range token is never accepted
+    t = W.tree_inputs(4, 16, V, W.F32, 43, match_p=1.0)
+    t["node_tokens"][:, 1:] = np.where(np.arange(1, 16) % 3 == 0, V + 9, t["node_tokens"][:, 1:])
+    tt = run_tree(svl, t)
+    for b in range(4):
+        path = [n for n in tt["accepted_nodes"][b] if n >= 0]
+        assert all(n % 3 != 0 for n in path), path
