@@ -520,3 +520,14 @@ def test_out_of_range_draft_tokens_are_rejected(svl, orc):
     for b in range(4):
         path = [n for n in tt["accepted_nodes"][b] if n >= 0]
         assert all(n % 3 != 0 for n in path), path
+
+
+@pytest.mark.parametrize("workload", ["llama_chain", "deepseek_chain", "mtp_chain"])
+def test_accept_prob_precision(svl, orc, workload):
+    """A guard on the precision of the row normalisers, ten times tighter than
+    the 1e-5 the results are held to: accept_prob = min(1, p/q) is within
+    1e-6 of the oracle's fp64 value (measured maxima are about 3e-7)."""
+    inp = W.make_inputs(workload, 3)
+    got, ref = run_chain(svl, inp), orc.verify_chain(inp)
+    err = np.abs(got["accept_prob"].astype(np.float64) - ref["accept_prob"])
+    assert err.max() < 1e-6, err.max()
