@@ -203,7 +203,7 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                 chunkarg);
     if (st != SV_OK) return st;
     return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kWave), stream, draft,
-                  target, B, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),
+                  target, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),
                   static_cast<const Partial*>(chunkarg), emitted);
 }
 

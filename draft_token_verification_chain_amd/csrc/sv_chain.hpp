@@ -444,7 +444,7 @@ constexpr int kSegRun = 8;
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target, int B, int k, int V, int nchunk,
+    const void* __restrict__ draft, const void* __restrict__ target, int k, int V, int nchunk,
     const SeqInfo* __restrict__ info, const Partial* __restrict__ segs, const Partial* __restrict__ chunkarg,
     int32_t* __restrict__ emitted) {
     constexpr int VE = Elem<DT>::per_vec;
