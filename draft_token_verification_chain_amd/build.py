@@ -34,6 +34,7 @@ FLAGS = [
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Wextra",
 ]
 
 
