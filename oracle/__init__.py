@@ -39,7 +39,7 @@ def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (no fast-math)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                                "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
