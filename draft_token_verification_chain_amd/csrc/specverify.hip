@@ -10,6 +10,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <tuple>
 #include <cstring>
@@ -344,7 +345,8 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
     auto* part = static_cast<Partial*>(workspace);
     if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) != SV_OK)
         return st;
-    const int threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
+    // one thread per node, and at least 256 so that each node's argmax partials are spread over several lanes
+    const int threads = std::max(256, (N + sv::kWave - 1) / sv::kWave * sv::kWave);
     return launch("tree_finalize", sv::tree_finalize_kernel, dim3(B), dim3(threads), stream, node_tokens, parent,
                   parent_stride, N, max_depth, nT, part, accepted_len, emitted, accepted_nodes);
 }

@@ -21,27 +21,41 @@ __global__ __launch_bounds__(kBlock) void argmax_rows_kernel(const void* __restr
 
 // ---------------------------------------------------------------- greedy ---
 
-// One wave per sequence: lane j combines row j's tiles into g_j; the first
-// lane with x_j != g_j is the rejection; g_a is the emitted target token.
+// One wave per sequence.  The argmax g_j of each of the k + 1 rows is
+// combined by a group of G lanes (the first partials of every row and the
+// draft tokens in flight together); the first position with x_j != g_j is the
+// rejection, and g_a is the emitted target token.
 __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* __restrict__ tokens, int k,
                                                                 int nT, const Partial* __restrict__ part,
                                                                 int32_t* __restrict__ accepted_len,
                                                                 int32_t* __restrict__ emitted) {
+    __shared__ int s_g[SV_MAX_DRAFTS + 1];
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x;
-    int g = -1, x = 0;
-    if (lane < k) {
-        x = tokens[b * k + lane];
-        g = combine_argmax(part + (b * (k + 1) + lane) * nT, nT).idx;
+    const int rows = k + 1;
+    int G = kWave;
+    while (G > 1 && G * rows > kWave) G >>= 1;
+    const int per_pass = kWave / G;
+    const Partial* rows_base = part + b * rows * static_cast<int64_t>(nT);
+    Partial q[kBatch];
+    group_load(rows_base + (lane / G < rows ? lane / G : 0) * static_cast<int64_t>(nT), nT, G, lane / G < rows, q);
+    const int x = lane < k ? tokens[b * k + lane] : 0;
+    for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
+        const int rho = rho0 + lane / G;
+        const bool valid = rho < rows;
+        const Partial* p = rows_base + (valid ? rho : 0) * static_cast<int64_t>(nT);
+        if (rho0 > 0) group_load(p, nT, G, valid, q);
+        int r;
+        double sum;
+        ArgMax am;
+        group_reduce<false>(p, nT, G, valid, q, r, sum, am);
+        if (valid && (lane & (G - 1)) == 0) s_g[rho] = am.idx;
     }
+    __syncthreads();
+    const int g = lane < k ? s_g[lane] : -1;
     int a = first_lane(lane < k && x != g);
-    int y;
-    if (a < 0) {
-        a = k;
-        y = wave_combine_argmax(part + (b * (k + 1) + k) * nT, nT).idx;
-    } else {
-        y = __shfl(g, a, kWave);
-    }
+    if (a < 0) a = k;
+    const int y = s_g[a];
     int32_t* out = emitted + b * (k + 1);
     for (int j = lane; j <= k; j += kWave) out[j] = j < a ? tokens[b * k + j] : (j == a ? y : -1);
     if (lane == 0) accepted_len[b] = a;
@@ -50,9 +64,12 @@ __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* _
 // ---------------------------------------------------------------- tree ---
 
 // One workgroup per sequence, one thread per node (N <= blockDim.x <= 1024).
-// Pointer jumping over the parent links gives every node its depth and
-// whether every edge on its root path matches; the deepest accepted node
-// (lowest index among equals) is chosen and its path written out.
+// The argmax of each node's row is combined by a group of G lanes (G as large
+// as the block allows; the first partials of every row, the tokens and the
+// parent links in flight together).  Pointer jumping over the parent links
+// gives every node its depth and whether every edge on its root path
+// matches; the deepest accepted node (lowest index among equals) is chosen
+// and its path written out.
 __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_finalize_kernel(
     const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
     int max_depth, int nT, const Partial* __restrict__ part, int32_t* __restrict__ accepted_len,
@@ -74,13 +91,30 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_finalize_kernel(
     }
     __syncthreads();
     const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
+    const int nthreads = blockDim.x;
+    int G = kWave;
+    while (G > 1 && G * N > nthreads) G >>= 1;
+    const int per_pass = nthreads / G;
+    const Partial* rows_base = part + b * N * static_cast<int64_t>(nT);
+    Partial q[kBatch];
+    group_load(rows_base + (n / G < N ? n / G : 0) * static_cast<int64_t>(nT), nT, G, n / G < N, q);
     int p = 0;
     if (n < N) {
-        s_g[n] = combine_argmax(part + (b * N + n) * nT, nT).idx;
         s_tok[n] = node_tokens[b * N + n];
         p = n == 0 ? 0 : par[n];
         if (n > 0 && (p < 0 || p >= n)) s_bad = 1;
         s_par[n] = p;
+    }
+    for (int m0 = 0; m0 < N; m0 += per_pass) {
+        const int m = m0 + n / G;
+        const bool valid = m < N;
+        const Partial* pr = rows_base + (valid ? m : 0) * static_cast<int64_t>(nT);
+        if (m0 > 0) group_load(pr, nT, G, valid, q);
+        int r;
+        double sum;
+        ArgMax am;
+        group_reduce<false>(pr, nT, G, valid, q, r, sum, am);
+        if (valid && (n & (G - 1)) == 0) s_g[m] = am.idx;
     }
     __syncthreads();
     int anc = 0, len = 0, ok = 0;

@@ -105,20 +105,7 @@ __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_
 // together rather than one round trip each.
 constexpr int kBatch = 8;
 
-// Combine the nT argmax partials of one row (one lane, sequential).
-__device__ inline ArgMax combine_argmax(const Partial* p, int nT) {
-    ArgMax a{p[0].f, p[0].i};
-    for (int t0 = 1; t0 < nT; t0 += kBatch) {
-        Partial q[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) q[j] = (t0 + j < nT) ? p[t0 + j] : Partial{-__builtin_inff(), kNoIndex};
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) a = better(a, ArgMax{q[j].f, q[j].i});
-    }
-    return a;
-}
-
-// The same, with the whole wave striding over the tiles.
+// The argmax of a row from its nT partials, the whole wave striding over them.
 __device__ inline ArgMax wave_combine_argmax(const Partial* p, int nT) {
     ArgMax a{-__builtin_inff(), kNoIndex};
     for (int t = lane_id(); t < nT; t += kWave) a = better(a, ArgMax{p[t].f, p[t].i});
