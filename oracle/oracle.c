@@ -43,6 +43,13 @@
  *            speculative sampling of SpecInfer (Miao et al., 2023) -- the
  *            multi-round rule the EAGLE work applies to its trees -- is used;
  *            see svo_verify_tree_sampled.
+ *   R-commit the device-side commit (section "MTP Schedule for a Single
+ *            Token": a kernel places the next tokens, so the host need not
+ *            read the accepted counts) appends a_b + 1 tokens to sequence b's
+ *            history and advances its length; a row is refused whole when
+ *            a_b < 0 (an invalid tree), a_b >= width, the length is negative,
+ *            the new length would pass INT32_MAX or (with a history) its
+ *            capacity; see svo_commit_tokens.
  *
  * Band flag (sequences with T_b > 0 only): set when a tested uniform lies
  * within band_eps of its threshold tau_i, or u[b][k] lies within band_eps of
