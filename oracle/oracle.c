@@ -585,9 +585,9 @@ int svo_row_argmax(int nrows, int V, int dtype, const void *logits, int32_t *out
  * grows by that count; packed_offsets[b] is the number of tokens committed
  * by the sequences before b (the total in [B]) and packed holds the
  * committed tokens in that order.  status: 0 committed, 1 refused (the row
- * is too short for a_b + 1 tokens, the length is negative, or the history
- * would overflow), 2 nothing to commit (a_b < 0).  history may be NULL (no
- * history and no capacity limit).
+ * is too short for a_b + 1 tokens, the length is negative, the new length
+ * would pass INT32_MAX, or the history would overflow), 2 nothing to commit
+ * (a_b < 0).  history may be NULL (no history and no capacity limit).
  */
 int svo_commit_tokens(int B, int width, const int32_t *accepted_len, const int32_t *emitted,
                       int32_t *seq_len, int32_t *history, int history_stride,
