@@ -94,6 +94,23 @@ def to_device(inp, torch, W):
     return t
 
 
+def check_against_oracle(inp, got: dict) -> dict:
+    """The timed steps' outputs (every step verifies the same batch) against
+    the oracle's: bit-exact outside the oracle's band."""
+    import numpy as np
+
+    import oracle
+
+    ref = {"chain": oracle.verify_chain, "greedy": oracle.verify_greedy, "tree": oracle.verify_tree,
+           "tree_sampled": oracle.verify_tree_sampled}[inp["kind"]](inp)
+    mism = (got["accepted_len"] != ref["accepted_len"]) | (got["emitted"] != ref["emitted"]).any(axis=1)
+    if got.get("accepted_nodes") is not None and ref.get("accepted_nodes") is not None:
+        mism |= (got["accepted_nodes"] != ref["accepted_nodes"]).any(axis=1)
+    band = ref.get("band", np.zeros(mism.shape, bool))
+    return {"sequences": int(mism.size), "banded": int(band.sum()),
+            "banded_differing": int((mism & band).sum()), "differing_outside_band": int((mism & ~band).sum())}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -315,7 +332,8 @@ def main():
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "bytes_per_launch": dominant_bytes, "avg_launch_us": dom_us},
+                     "bytes_per_launch": dominant_bytes, "avg_launch_us": dom_us,
+                     "traffic_gbs": traffic / (dom_us * 1e-6) / 1e9 if traffic else None},
     }
 
     if not args.no_cpu:
@@ -327,6 +345,8 @@ def main():
                                   "value_1thread": units * reps1 / el1,
                                   "sample_1thread": f"the same batch x {reps1} repetitions on one thread, {el1:.1f} s",
                                   "cpu_model": cpu_model()}
+        result["parity"] = check_against_oracle(inp, {key: (v.cpu().numpy() if v is not None else None)
+                                                      for key, v in out.items()})
     print(json.dumps(result), flush=True)
 
 
