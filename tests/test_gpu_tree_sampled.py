@@ -84,6 +84,8 @@ BATCHES = [
     (128, 24, 8200, W.F32),   # P = 8: cached, three nodes per workgroup
     (300, 16, 5000, W.F32),   # P = 4: N = 4 P exactly, one node on every wave
     (200, 24, 6000, W.BF16),  # P = 3: not cached
+    (1100, 8, 600, W.BF16),   # P = 1 (one workgroup per sequence and round): not cached
+    (1500, 3, 1000, W.F32),   # P = 1, cached (three nodes on three waves)
 ]
 
 
