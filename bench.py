@@ -165,8 +165,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library runs on a single MI355X and the "
-              "workload is one GPU's batch; multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs on a single MI355X and the workload is "
+              "one GPU's batch (sequences are independent, so a batch splits across GPUs with no exchange).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
