@@ -291,7 +291,7 @@ def main():
 
     # timed region 1: the throughput (no per-kernel events), K steps timed three
     # times; the median is reported (the spread between back-to-back runs on one
-    # box is about 1 us per step, mostly in the gaps between kernels)
+    # machine is about 1 us per step, mostly in the gaps between kernels)
     ms_repeats = [timed(False) for _ in range(3)]
     ms_per_step = sorted(ms_repeats)[1]
     # timed region 2: the same steps, each kernel's own dispatch timed by HIP events
