@@ -214,8 +214,11 @@ def main():
             t = dev[i % copies]
             svl.verify_greedy(t["draft_tokens"], t["target_logits"], workspace=ws, out=out)
         units = B * k
-        dominant = "argmax_rows"
-        dominant_bytes = B * (k + 1) * V * es
+        # rows 0..s-1 of every sequence; at 256 MiB of rows and more the library
+        # reads rows s..k only for sequences accepting their first s drafts
+        s_first = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1
+        dominant = "greedy_rows"
+        dominant_bytes = B * s_first * V * es
     elif kind == "tree_sampled":
         N = inp["N"]
         md = inp["max_depth"]
@@ -260,7 +263,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # bytes the final draw reads, from this batch's outcome (identical in every copy)
+    # bytes the final draw (greedy: the second phase's rows) reads, from this
+    # batch's outcome (identical in every copy)
     final_bytes = 0
     if kind == "chain":
         a = out["accepted_len"].cpu().numpy()
@@ -271,6 +275,9 @@ def main():
                 final_bytes += (2 if a[b] < k else 1) * V * es
             elif a[b] == k:
                 final_bytes += V * es
+    elif kind == "greedy" and s_first <= inp["k"]:
+        a = out["accepted_len"].cpu().numpy()
+        final_bytes = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es
     # with no drafts the final draw is the dominant pass itself (its row counted once)
     step_bytes = final_bytes if kind == "chain" and inp["k"] == 0 else dominant_bytes + final_bytes
 

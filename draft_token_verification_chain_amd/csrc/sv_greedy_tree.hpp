@@ -21,10 +21,69 @@ __global__ __launch_bounds__(kBlock) void argmax_rows_kernel(const void* __restr
 
 // ---------------------------------------------------------------- greedy ---
 
+// The argmax partials of rows j0 .. j0 + nrows - 1 of every sequence of a
+// greedy chain (rows b * (k + 1) + j).  Rows after a sequence's first
+// mismatch never reach its outputs, so the rows are streamed in two phases:
+// CHECK = false streams rows 0 .. s - 1 of every sequence; CHECK = true
+// streams rows s .. k only for sequences whose first s drafts all equal their
+// rows' argmax, which wave 0 of each workgroup finds from the first phase's
+// partials (G lanes per row, one round trip).  Each wave takes TPW tiles, a
+// workgroup kWavesPerBlock * TPW consecutive ones (`groups` workgroups per
+// row).  The one-dimensional grid runs over (sequence, row, group) with the
+// group fastest: the dispatcher deals consecutive workgroups out to the XCDs
+// in turn, so every sequence's work is spread over the XCDs and each gets an
+// even share of the second phase however its sequences fall.
+template <int DT, bool VEC, int U, bool CHECK, int TPW>
+__global__ __launch_bounds__(kBlock) void greedy_rows_kernel(const void* __restrict__ logits,
+                                                             const int32_t* __restrict__ tokens, int k, int V,
+                                                             int nT, int groups, int nrows, int j0,
+                                                             Partial* __restrict__ part) {
+    const int per_seq = groups * nrows;
+    const int64_t b = blockIdx.x / per_seq;
+    const int rem = static_cast<int>(blockIdx.x - b * per_seq);
+    const int z = rem / groups;
+    const int group = rem - z * groups;
+    const int rows = k + 1;
+    if constexpr (CHECK) {
+        __shared__ int s_go;
+        if (threadIdx.x < kWave) {
+            const int lane = lane_id();
+            const int s = j0;  // rows 0 .. s - 1 were streamed by the first phase
+            int G = kWave;
+            while (G > 1 && G * s > kWave) G >>= 1;
+            const int rho = lane / G;
+            const bool valid = rho < s;
+            const Partial* p = part + (b * rows + (valid ? rho : 0)) * static_cast<int64_t>(nT);
+            Partial q[kBatch];
+            group_load(p, nT, G, valid, q);
+            const int x = valid ? tokens[b * k + rho] : 0;
+            int r;
+            double sum;
+            ArgMax am;
+            group_reduce<false>(p, nT, G, valid, q, r, sum, am);
+            const bool mismatch = __ballot(valid && (lane & (G - 1)) == 0 && x != am.idx) != 0;
+            if (lane == 0) s_go = !mismatch;
+        }
+        __syncthreads();
+        if (!s_go) return;
+    }
+    const int64_t row = b * rows + j0 + z;
+    const int wave = threadIdx.x / kWave;
+#pragma unroll 1
+    for (int i = 0; i < TPW; ++i) {
+        const int64_t tile = (static_cast<int64_t>(group) * TPW + i) * kWavesPerBlock + wave;
+        if (tile >= nT) break;
+        const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, row * static_cast<int64_t>(V), V, tile);
+        if (lane_id() == 0) part[row * nT + tile] = Partial{a.val, a.idx};
+    }
+}
+
 // One wave per sequence.  The argmax g_j of each of the k + 1 rows is
 // combined by a group of G lanes (the first partials of every row and the
 // draft tokens in flight together); the first position with x_j != g_j is the
-// rejection, and g_a is the emitted target token.
+// rejection, and g_a is the emitted target token.  The partials of rows a
+// second phase skipped hold stale values; they only yield g_j for j past a
+// mismatch in the first phase's rows, which are never used.
 __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* __restrict__ tokens, int k,
                                                                 int nT, const Partial* __restrict__ part,
                                                                 int32_t* __restrict__ accepted_len,

@@ -140,6 +140,10 @@ sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
  *   accepted_len  int32 [B]      out  a_b = first i with x_i != g_i, else k, where g_j is
  *                                     the lowest-index argmax of target row j
  *   emitted       int32 [B][k+1] out  x_0..x_{a-1}, g_a, then -1
+ *
+ * When the target rows reach 256 MiB they are read in two phases: rows
+ * 0..(k+1)/2-1 of every sequence, then the rest only for the sequences whose
+ * drafts match in all of those rows.
  */
 sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt,
                            const int32_t *draft_tokens, const void *target_logits,

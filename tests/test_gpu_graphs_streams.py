@@ -204,6 +204,36 @@ def test_graph_replay_greedy_and_tree(svl, orc):
     _replay_each(g, ts, tsets + tsets[:1], to_t, check_t, eager_t)
 
 
+def test_graph_replay_greedy_two_phase(svl, orc):
+    """sv_verify_greedy at a size that reads its rows in two phases, captured
+    once and replayed on inputs with other match patterns: which sequences the
+    second phase streams is decided on the device at every replay."""
+    import torch
+
+    from gpu_common import dev_logits, run_greedy
+
+    B, k, V = 72, 5, 156000
+    assert B * (k + 1) * V * 4 >= 256 << 20
+    gsets = [W.greedy_inputs(B, k, V, W.F32, s, match_p=p) for s, p in ((71, 0.8), (72, 1.0), (73, 0.5))]
+    to_g = lambda inp: dict(draft_tokens=dev(inp["draft_tokens"].astype(np.int32)),
+                            target_logits=dev_logits(inp["target_logits"], inp["dtype"]))
+    gs = to_g(gsets[0])
+    gws = torch.zeros(svl.greedy_workspace_bytes(B, k, V, W.F32), dtype=torch.uint8, device="cuda")
+    gout = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+                emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"))
+    g = _capture(lambda: svl.verify_greedy(gs["draft_tokens"], gs["target_logits"], workspace=gws, out=gout))
+
+    def check_g(inp, rep):
+        ref = orc.verify_greedy(inp)
+        np.testing.assert_array_equal(gout["accepted_len"].cpu().numpy(), ref["accepted_len"], f"replay {rep}")
+        np.testing.assert_array_equal(gout["emitted"].cpu().numpy(), ref["emitted"], f"replay {rep}")
+
+    def eager_g(inp, rep):
+        np.testing.assert_array_equal(run_greedy(svl, inp)["emitted"], orc.verify_greedy(inp)["emitted"])
+
+    _replay_each(g, gs, gsets + gsets[:1], to_g, check_g, eager_g)
+
+
 def test_graph_replay_sampled_tree(svl, orc):
     """sv_verify_tree_sampled (rowstats, the walk rounds with their
     double-buffered state, the finisher) captured once and replayed on new

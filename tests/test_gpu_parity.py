@@ -140,6 +140,55 @@ def test_full_greedy_workload(svl, orc, seed):
     _record("greedy", f"greedy_chain seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
 
 
+# Calls whose target rows reach 256 MiB stream them in two phases: the first
+# half of each sequence's rows, then the rest only for sequences whose drafts
+# all match in the first half.
+TWO_PHASE = [
+    # B, k, V, dtype, match_p -- rows per phase: (k+1)//2 then the rest (the
+    # bf16 vector path takes two phases in the full greedy workload above)
+    (64, 4, 262144, W.F32, 0.8),
+    (96, 1, 350000, W.F32, 0.8),
+    (40, 15, 211111, W.BF16, 0.9),   # odd V: element loads
+    (128, 5, 100000, W.F32, 1.0),    # every sequence takes the second phase
+    (128, 5, 100000, W.F32, 0.0),    # none does
+    (20, 63, 60001, W.F32, 0.95),    # V * 4 not a multiple of 16: element loads
+]
+
+
+@pytest.fixture(scope="module")
+def two_phase_ws(svl):
+    """One workspace for every two-phase case, 0xFF bytes at first and then
+    whatever the earlier cases left in it."""
+    import torch
+
+    nbytes = max(svl.greedy_workspace_bytes(B, k, V, dt) for B, k, V, dt, _ in TWO_PHASE)
+    return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("case", list(range(len(TWO_PHASE))) + [0],
+                         ids=[f"case{i}" for i in range(len(TWO_PHASE))] + ["case0-again"])
+def test_greedy_two_phase(svl, orc, two_phase_ws, case):
+    """Parity on sizes that take the two phases.  Rows a call skips keep the
+    partials of earlier calls in the shared workspace, which must never reach
+    its results; the first case runs again last, over the others' partials."""
+    import torch
+
+    B, k, V, dt, mp = TWO_PHASE[case]
+    assert B * (k + 1) * V * (2 if dt == W.BF16 else 4) >= 256 << 20
+    inp = W.greedy_inputs(B, k, V, dt, 60 + case, match_p=mp)
+    out = svl.verify_greedy(dev(inp["draft_tokens"].astype(np.int32)), dev_logits(inp["target_logits"], dt),
+                            workspace=two_phase_ws)
+    torch.cuda.synchronize()
+    ref = orc.verify_greedy(inp)
+    got = {key: v.cpu().numpy() for key, v in out.items()}
+    np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+    np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+    s = (k + 1) // 2
+    _record("greedy", f"two-phase B{B} k{k} V{V} p{mp}",
+            dict(n=B, second_phase=int((ref["accepted_len"] >= s).sum()),
+                 mean_accepted=float(ref["accepted_len"].mean())))
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
 def test_full_tree_workload(svl, orc, seed):
     inp = W.make_inputs("eagle_tree", seed)
