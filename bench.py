@@ -201,7 +201,11 @@ def main():
             svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
                              t["uniforms"], workspace=ws, out=out)
         units = B * k if k > 0 else B       # verified draft tokens (sampled tokens when k == 0) per step
-        dominant = "chain_rowstats" if k > 0 else "chain_final_part"
+        # k == 0: one workgroup per row from 256 rows of at most 256 segments
+        # (64 vectors of 16 bytes each)
+        nseg = -(-(-(-V // (16 // es))) // 64)  # ceil(ceil(V / (16 / es)) / 64)
+        dominant = ("chain_rowstats" if k > 0 else
+                    "chain_sample" if B >= 256 and nseg <= 256 else "chain_final_part")
         # every draft row and target rows 0..k-1 once (k == 0: the sampled row)
         dominant_bytes = 2 * B * k * V * es if k > 0 else B * V * es
     elif kind == "greedy":

@@ -72,6 +72,12 @@ int64_t final_chunks(int V, sv_dtype dt) {
 // sequence's acceptance; beyond it one wave per sequence computes it once.
 constexpr int64_t kInlineAcceptMaxBlocks = 2048;
 
+// Plain sampling (k = 0) runs one workgroup per row (chain_sample_kernel)
+// from this many rows on, for rows of at most kSampleMaxSegs segments: one
+// row per CU fills the chip.  Below it a row alone on a CU streams too slowly
+// and the two-kernel draw (rows split over many workgroups) is faster.
+constexpr int kSampleMinRows = 256;
+
 // The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
 // every sequence, their logits at the draft tokens, the final draw's
 // descriptors, segment masses and chunk argmaxes.
@@ -195,6 +201,9 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                     static_cast<const float*>(gathered), accepted_len, emitted, accept_prob, info);
         if (st != SV_OK) return st;
     }
+    if (k == 0 && B >= kSampleMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kSampleMaxSegs)
+        return launch("chain_sample", sv::chain_sample_kernel<DT, VEC>, dim3(static_cast<unsigned>(B)),
+                      dim3(sv::kSampleBlock), stream, target, temperature, uniforms, V, accepted_len, emitted);
     auto final_part = acc == sv::kAcceptNone     ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptNone>
                       : acc == sv::kAcceptInline ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptInline>
                                                  : sv::chain_final_part_kernel<DT, VEC, sv::kAcceptRead>;

@@ -435,13 +435,110 @@ __device__ int pick_from_target_row(const void* target, int64_t trow, int V, int
     return last;
 }
 
-// Select pass of the final draw: one wave per sequence.  Lane l owns a
-// contiguous run of segments; a wave prefix over the run totals gives every
-// segment's starting mass, the segment holding u * W is found with a ballot,
-// and only that segment is read again to find the token.  The descriptor and
-// the lane's first kSegRun segments are loaded together.
+// The token of a residual or bonus draw from its segment masses `sg` (in
+// global or LDS memory), one wave.  Lane l owns a contiguous run of
+// segments; a wave prefix over the run totals gives every segment's starting
+// mass, the segment holding u * W is found with a ballot, and only that
+// segment is read again to find the token.  `first` holds the lane's first
+// kSegRun segments, loaded by the caller (ahead of the descriptor).
 constexpr int kSegRun = 8;
 
+template <int DT, bool VEC>
+__device__ int draw_from_segments(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
+                                  int64_t nseg, const SeqInfo& s, const Partial* sg, const Partial* first) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int lane = lane_id();
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t g0 = min<int64_t>(nseg, lane * per), g1 = min<int64_t>(nseg, g0 + per);
+    const bool residual = s.mode == kFinalResidual;
+    const int64_t nwin = (per + kSegRun - 1) / kSegRun;
+    // segment g of this lane's window w
+    auto seg_at = [&](int64_t w, int j) -> Partial {
+        const int64_t g = g0 + w * kSegRun + j;
+        return w == 0 ? first[j] : (g < g1 ? sg[g] : Partial{0.f, kNoRef});
+    };
+    // global reference exponent (residual masses are absolute: reference 0)
+    int R = 0;
+    if (!residual) {
+        R = kNoRef;
+        for (int64_t w = 0; w < nwin; ++w)
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).i);
+        R = wave_max(R);
+    }
+    // masses of this lane's window w in the global scale
+    auto window = [&](int64_t w, double* mg) {
+#pragma unroll
+        for (int j = 0; j < kSegRun; ++j) {
+            const Partial q = seg_at(w, j);
+            const bool in = g0 + w * kSegRun + j < g1;
+            mg[j] = !in ? 0.0 : residual ? static_cast<double>(q.f) : ldexp(static_cast<double>(q.f), q.i - R);
+        }
+    };
+    double tot = 0.0;
+    for (int64_t w = 0; w < nwin; ++w) {
+        double mg[kSegRun];
+        window(w, mg);
+#pragma unroll
+        for (int j = 0; j < kSegRun; ++j) tot += mg[j];
+    }
+    const double incl = wave_inclusive_scan(tot);
+    const double W = __shfl(incl, kWave - 1, kWave);
+    const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+    double P = lane == 0 ? 0.0 : excl;
+    if (!(W > 0.0)) return residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0;
+    const double target_mass = static_cast<double>(s.u) * W;
+    int64_t found = -1, last_pos = -1;
+    double Pfound = 0.0;
+    for (int64_t w = 0; w < nwin; ++w) {
+        double mg[kSegRun];
+        window(w, mg);
+#pragma unroll
+        for (int j = 0; j < kSegRun; ++j) {
+            const int64_t g = g0 + w * kSegRun + j;
+            if (g >= g1) break;
+            if (found < 0 && P + mg[j] > target_mass) {
+                found = g;
+                Pfound = P;
+            }
+            if (mg[j] > 0.0) last_pos = g;
+            P += mg[j];
+        }
+    }
+    int fl = first_lane(found >= 0);
+    int64_t seg;
+    double Ps;
+    bool fallback = false;
+    if (fl >= 0) {
+        seg = __shfl(found, fl, kWave);
+        Ps = __shfl(Pfound, fl, kWave);
+    } else {
+        // rounding put u * W at or past the total: the last segment with mass
+        const uint64_t m = __ballot(last_pos >= 0);
+        fl = m ? 63 - __builtin_clzll(m) : 0;
+        seg = m ? __shfl(last_pos, fl, kWave) : 0;
+        Ps = 0.0;
+        fallback = true;
+    }
+    const int tref = residual ? 0 : sg[seg].i;
+    const double scale = ldexp(1.0, tref - R);
+    float w[VE];
+    segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, static_cast<float>(tref), w);
+    int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, scale, target_mass);
+    if (y < 0) y = last_positive_in_segment<DT>(w, seg);
+    return y;
+}
+
+// The lane's first kSegRun segments of draw_from_segments.
+__device__ __forceinline__ void first_segments(const Partial* sg, int64_t nseg, Partial* first) {
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t g0 = min<int64_t>(nseg, lane_id() * per), g1 = min<int64_t>(nseg, g0 + per);
+#pragma unroll
+    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : Partial{0.f, kNoRef};
+}
+
+// Select pass of the final draw: one wave per sequence.  The descriptor and
+// the lane's first segments are loaded together.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int k, int V, int nchunk,
@@ -449,103 +546,78 @@ __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
     int32_t* __restrict__ emitted) {
     constexpr int VE = Elem<DT>::per_vec;
     const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const Partial* sg = segs + b * nseg;
-    const int64_t per = (nseg + kWave - 1) / kWave;
-    const int64_t g0 = min<int64_t>(nseg, lane * per), g1 = min<int64_t>(nseg, g0 + per);
     Partial first[kSegRun];
-#pragma unroll
-    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : Partial{0.f, kNoRef};
+    first_segments(sg, nseg, first);
     const SeqInfo s = info[b];
     if (s.mode == kFinalDone) return;
     int y;
     if (s.mode == kFinalArgmax) {
         y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;
     } else {
-        const bool residual = s.mode == kFinalResidual;
         const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
         const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
-        const int64_t nwin = (per + kSegRun - 1) / kSegRun;
-        // segment g of this lane's window w
-        auto seg_at = [&](int64_t w, int j) -> Partial {
-            const int64_t g = g0 + w * kSegRun + j;
-            return w == 0 ? first[j] : (g < g1 ? sg[g] : Partial{0.f, kNoRef});
-        };
-        // global reference exponent (residual masses are absolute: reference 0)
-        int R = 0;
-        if (!residual) {
-            R = kNoRef;
-            for (int64_t w = 0; w < nwin; ++w)
-#pragma unroll
-                for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).i);
-            R = wave_max(R);
-        }
-        // masses of this lane's window w in the global scale
-        auto window = [&](int64_t w, double* mg) {
-#pragma unroll
-            for (int j = 0; j < kSegRun; ++j) {
-                const Partial q = seg_at(w, j);
-                const bool in = g0 + w * kSegRun + j < g1;
-                mg[j] = !in ? 0.0 : residual ? static_cast<double>(q.f) : ldexp(static_cast<double>(q.f), q.i - R);
-            }
-        };
-        double tot = 0.0;
-        for (int64_t w = 0; w < nwin; ++w) {
-            double mg[kSegRun];
-            window(w, mg);
-#pragma unroll
-            for (int j = 0; j < kSegRun; ++j) tot += mg[j];
-        }
-        const double incl = wave_inclusive_scan(tot);
-        const double W = __shfl(incl, kWave - 1, kWave);
-        const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
-        double P = lane == 0 ? 0.0 : excl;
-        if (!(W > 0.0)) {
-            y = residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0;
-        } else {
-            const double target_mass = static_cast<double>(s.u) * W;
-            int64_t found = -1, last_pos = -1;
-            double Pfound = 0.0;
-            for (int64_t w = 0; w < nwin; ++w) {
-                double mg[kSegRun];
-                window(w, mg);
-#pragma unroll
-                for (int j = 0; j < kSegRun; ++j) {
-                    const int64_t g = g0 + w * kSegRun + j;
-                    if (g >= g1) break;
-                    if (found < 0 && P + mg[j] > target_mass) {
-                        found = g;
-                        Pfound = P;
-                    }
-                    if (mg[j] > 0.0) last_pos = g;
-                    P += mg[j];
-                }
-            }
-            int fl = first_lane(found >= 0);
-            int64_t seg;
-            double Ps;
-            bool fallback = false;
-            if (fl >= 0) {
-                seg = __shfl(found, fl, kWave);
-                Ps = __shfl(Pfound, fl, kWave);
-            } else {
-                // rounding put u * W at or past the total: the last segment with mass
-                const uint64_t m = __ballot(last_pos >= 0);
-                fl = m ? 63 - __builtin_clzll(m) : 0;
-                seg = m ? __shfl(last_pos, fl, kWave) : 0;
-                Ps = 0.0;
-                fallback = true;
-            }
-            const int tref = residual ? 0 : sg[seg].i;
-            const double scale = ldexp(1.0, tref - R);
-            float w[VE];
-            segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, static_cast<float>(tref), w);
-            y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, scale, target_mass);
-            if (y < 0) y = last_positive_in_segment<DT>(w, seg);
-        }
+        y = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, s, sg, first);
     }
-    if (lane == 0) emitted[b * (k + 1) + s.a] = y;
+    if (threadIdx.x == 0) emitted[b * (k + 1) + s.a] = y;
+}
+
+// ---------------------------------------------------------------- sampling (k = 0), one workgroup per row ---
+
+// With no drafts the draw needs no descriptor beyond the temperature, and a
+// row of at most kSampleMaxSegs segments is one workgroup's work: its 16
+// waves stream the row's tiles (the same tiles, weights and segment masses
+// as chain_final_part, into LDS), then wave 0 draws the token exactly as
+// chain_final_pick does.  One launch instead of two, and no segment masses
+// through HBM.
+constexpr int kSampleBlock = 1024;
+constexpr int kSampleWaves = kSampleBlock / kWave;
+constexpr int kSampleMaxSegs = 256;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kSampleBlock) void chain_sample_kernel(const void* __restrict__ target,
+                                                                     const float* __restrict__ temperature,
+                                                                     const float* __restrict__ uniforms, int V,
+                                                                     int32_t* __restrict__ accepted_len,
+                                                                     int32_t* __restrict__ emitted) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ Partial s_seg[kSampleMaxSegs];
+    __shared__ ArgMax s_arg[kSampleWaves];
+    const int64_t b = blockIdx.x;
+    const float T = temperature[b];
+    SeqInfo si{};
+    si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+    temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+    si.u = uniforms[b];
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int64_t ntile = (nseg + kFinU - 1) / kFinU;
+    const int64_t trow = b * static_cast<int64_t>(V);
+    const int wave = threadIdx.x / kWave;
+    ArgMax best{-__builtin_inff(), kNoIndex};
+    for (int64_t tile = wave; tile < ntile; tile += kSampleWaves) {
+        if (tile_is_full<VEC, kFinU>(tile, V, VE))
+            final_tile<DT, VEC, VEC>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
+        else
+            final_tile<DT, VEC, false>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
+    }
+    if (lane_id() == 0) s_arg[wave] = best;
+    __syncthreads();
+    if (wave != 0) return;
+    int y;
+    if (si.mode == kFinalArgmax) {
+        ArgMax r = s_arg[0];
+        for (int w = 1; w < kSampleWaves; ++w) r = better(r, s_arg[w]);
+        y = r.idx;
+    } else {
+        Partial first[kSegRun];
+        first_segments(s_seg, nseg, first);
+        y = draw_from_segments<DT, VEC>(nullptr, target, trow, 0, V, nseg, si, s_seg, first);
+    }
+    if (threadIdx.x == 0) {
+        emitted[b] = y;
+        accepted_len[b] = 0;
+    }
 }
 
 }  // namespace sv

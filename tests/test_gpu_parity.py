@@ -332,6 +332,32 @@ def test_gpu_plain_sampling_chi_square(svl, orc):
     assert stats.chisquare(counts, p * 1_000_000).pvalue > 1e-4
 
 
+def _rows(inp, lo, hi):
+    """Sequences lo..hi-1 of a chain batch."""
+    out = dict(inp, B=hi - lo)
+    for key, v in inp.items():
+        if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == inp["B"]:
+            out[key] = v[lo:hi]
+    return out
+
+
+@pytest.mark.parametrize("V,dt", [(128256, W.BF16), (131072, W.BF16), (131073, W.BF16), (65536, W.F32),
+                                  (30001, W.F32), (70001, W.BF16), (1, W.BF16), (700, W.F32)])
+def test_sampling_one_workgroup_per_row_matches_split_batches(svl, orc, V, dt):
+    """k = 0 from 256 rows on draws each row in one workgroup (rows of at most
+    256 segments); smaller batches take the two-kernel draw.  Both compute the
+    same tiles, weights, segment masses and pick: one batch of 256 rows and
+    the same rows as four batches of 64 give bit-identical outputs, which
+    match the oracle outside the band.  Temperature 0 rows take the argmax."""
+    B = 256
+    temps = np.where(np.arange(B) % 7 == 3, 0.0, np.linspace(0.3, 1.6, B)).astype(np.float32)
+    inp = W.chain_inputs(B, 0, V, dt, 77, target_sigma=3.0, temperature=temps)
+    whole, ref = _check_chain(svl, orc, inp, f"k0 one workgroup per row V{V}")
+    parts = [run_chain(svl, _rows(inp, lo, lo + 64)) for lo in range(0, B, 64)]
+    for key in ("accepted_len", "emitted"):
+        np.testing.assert_array_equal(whole[key], np.concatenate([p[key] for p in parts]), err_msg=key)
+
+
 # ------------------------------------------------------------ NEXT rows ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
