@@ -205,7 +205,7 @@ def main():
         # (64 vectors of 16 bytes each)
         nseg = -(-(-(-V // (16 // es))) // 64)  # ceil(ceil(V / (16 / es)) / 64)
         dominant = ("chain_rowstats" if k > 0 else
-                    "chain_sample" if B >= 256 and nseg <= 256 else "chain_final_part")
+                    "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part")
         # every draft row and target rows 0..k-1 once (k == 0: the sampled row)
         dominant_bytes = 2 * B * k * V * es if k > 0 else B * V * es
     elif kind == "greedy":

@@ -72,11 +72,11 @@ int64_t final_chunks(int V, sv_dtype dt) {
 // sequence's acceptance; beyond it one wave per sequence computes it once.
 constexpr int64_t kInlineAcceptMaxBlocks = 2048;
 
-// Plain sampling (k = 0) runs one workgroup per row (chain_sample_kernel)
-// from this many rows on, for rows of at most kSampleMaxSegs segments: one
+// The final draw runs one workgroup per sequence (chain_row_draw_kernel) from
+// this many sequences on, for rows of at most kRowDrawMaxSegs segments: one
 // row per CU fills the chip.  Below it a row alone on a CU streams too slowly
 // and the two-kernel draw (rows split over many workgroups) is faster.
-constexpr int kSampleMinRows = 256;
+constexpr int kRowDrawMinRows = 256;
 
 // The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
 // every sequence, their logits at the draft tokens, the final draw's
@@ -194,6 +194,13 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                     dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, V, nT, part, gathered);
         if (st != SV_OK) return st;
     }
+    if (B >= kRowDrawMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kRowDrawMaxSegs) {
+        auto row_draw = k == 0 ? sv::chain_row_draw_kernel<DT, VEC, sv::kAcceptNone>
+                               : sv::chain_row_draw_kernel<DT, VEC, sv::kAcceptInline>;
+        return launch("chain_row_draw", row_draw, dim3(static_cast<unsigned>(B)), dim3(sv::kRowDrawBlock), stream,
+                      tokens, draft, target, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
+                      static_cast<const float*>(gathered), accepted_len, emitted, accept_prob);
+    }
     if (acc == sv::kAcceptRead) {
         const unsigned acc_blocks = static_cast<unsigned>((B + sv::kAccWaves - 1) / sv::kAccWaves);
         st = launch("chain_accept", sv::chain_accept_kernel<DT>, dim3(acc_blocks), dim3(sv::kAccWaves * sv::kWave),
@@ -201,9 +208,6 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                     static_cast<const float*>(gathered), accepted_len, emitted, accept_prob, info);
         if (st != SV_OK) return st;
     }
-    if (k == 0 && B >= kSampleMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kSampleMaxSegs)
-        return launch("chain_sample", sv::chain_sample_kernel<DT, VEC>, dim3(static_cast<unsigned>(B)),
-                      dim3(sv::kSampleBlock), stream, target, temperature, uniforms, V, accepted_len, emitted);
     auto final_part = acc == sv::kAcceptNone     ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptNone>
                       : acc == sv::kAcceptInline ? sv::chain_final_part_kernel<DT, VEC, sv::kAcceptInline>
                                                  : sv::chain_final_part_kernel<DT, VEC, sv::kAcceptRead>;

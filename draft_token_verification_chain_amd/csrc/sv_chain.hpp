@@ -563,43 +563,61 @@ __global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
     if (threadIdx.x == 0) emitted[b * (k + 1) + s.a] = y;
 }
 
-// ---------------------------------------------------------------- sampling (k = 0), one workgroup per row ---
+// ---------------------------------------------------------------- final draw, one workgroup per row ---
 
-// With no drafts the draw needs no descriptor beyond the temperature, and a
-// row of at most kSampleMaxSegs segments is one workgroup's work: its 16
-// waves stream the row's tiles (the same tiles, weights and segment masses
-// as chain_final_part, into LDS), then wave 0 draws the token exactly as
-// chain_final_pick does.  One launch instead of two, and no segment masses
-// through HBM.
-constexpr int kSampleBlock = 1024;
-constexpr int kSampleWaves = kSampleBlock / kWave;
-constexpr int kSampleMaxSegs = 256;
+// When one row per CU fills the chip, a sequence's whole final draw is one
+// workgroup's work (rows of at most kRowDrawMaxSegs segments).  Wave 0 first
+// forms the draw's descriptor: from the temperature alone with no drafts
+// (kAcceptNone), else by running accept_sequence (kAcceptInline).  The 16
+// waves then stream the draw's row or rows with final_tile, the segment
+// masses going to LDS instead of HBM, and wave 0 draws the token with
+// draw_from_segments.  It computes exactly what chain_final_part and
+// chain_final_pick compute, in one launch.
+constexpr int kRowDrawBlock = 1024;
+constexpr int kRowDrawWaves = kRowDrawBlock / kWave;
+constexpr int kRowDrawMaxSegs = 256;
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kSampleBlock) void chain_sample_kernel(const void* __restrict__ target,
-                                                                     const float* __restrict__ temperature,
-                                                                     const float* __restrict__ uniforms, int V,
-                                                                     int32_t* __restrict__ accepted_len,
-                                                                     int32_t* __restrict__ emitted) {
+template <int DT, bool VEC, int ACC>
+__global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
+    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
+    const Partial* __restrict__ part, const float* __restrict__ gathered, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ emitted, float* __restrict__ accept_prob) {
+    static_assert(ACC == kAcceptNone || ACC == kAcceptInline, "descriptor from the temperature or inline");
     constexpr int VE = Elem<DT>::per_vec;
-    __shared__ Partial s_seg[kSampleMaxSegs];
-    __shared__ ArgMax s_arg[kSampleWaves];
+    __shared__ Partial s_seg[kRowDrawMaxSegs];
+    __shared__ ArgMax s_arg[kRowDrawWaves];
     const int64_t b = blockIdx.x;
-    const float T = temperature[b];
-    SeqInfo si{};
-    si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
-    temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
-    si.u = uniforms[b];
+    SeqInfo si;
+    if constexpr (ACC == kAcceptInline) {
+        __shared__ int s_r[2 * SV_MAX_DRAFTS];
+        __shared__ double s_s[2 * SV_MAX_DRAFTS];
+        __shared__ SeqInfo s_info;
+        if (threadIdx.x < kWave)
+            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, true, accepted_len,
+                                emitted, accept_prob, s_r, s_s, &s_info);
+        __syncthreads();
+        si = s_info;
+        if (si.mode == kFinalDone) return;
+    } else {
+        // k == 0: draw from target row 0 (its argmax at temperature 0)
+        const float T = temperature[b];
+        si = SeqInfo{};
+        si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+        temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+        si.u = uniforms[b];
+    }
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const int64_t ntile = (nseg + kFinU - 1) / kFinU;
-    const int64_t trow = b * static_cast<int64_t>(V);
+    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
     const int wave = threadIdx.x / kWave;
     ArgMax best{-__builtin_inff(), kNoIndex};
-    for (int64_t tile = wave; tile < ntile; tile += kSampleWaves) {
+    for (int64_t tile = wave; tile < ntile; tile += kRowDrawWaves) {
         if (tile_is_full<VEC, kFinU>(tile, V, VE))
-            final_tile<DT, VEC, VEC>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
+            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
         else
-            final_tile<DT, VEC, false>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
+            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
     }
     if (lane_id() == 0) s_arg[wave] = best;
     __syncthreads();
@@ -607,16 +625,16 @@ __global__ __launch_bounds__(kSampleBlock) void chain_sample_kernel(const void* 
     int y;
     if (si.mode == kFinalArgmax) {
         ArgMax r = s_arg[0];
-        for (int w = 1; w < kSampleWaves; ++w) r = better(r, s_arg[w]);
+        for (int w = 1; w < kRowDrawWaves; ++w) r = better(r, s_arg[w]);
         y = r.idx;
     } else {
         Partial first[kSegRun];
         first_segments(s_seg, nseg, first);
-        y = draw_from_segments<DT, VEC>(nullptr, target, trow, 0, V, nseg, si, s_seg, first);
+        y = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_seg, first);
     }
     if (threadIdx.x == 0) {
-        emitted[b] = y;
-        accepted_len[b] = 0;
+        emitted[b * (k + 1) + si.a] = y;
+        if constexpr (ACC == kAcceptNone) accepted_len[b] = 0;
     }
 }
 

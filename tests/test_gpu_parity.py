@@ -341,21 +341,28 @@ def _rows(inp, lo, hi):
     return out
 
 
-@pytest.mark.parametrize("V,dt", [(128256, W.BF16), (131072, W.BF16), (131073, W.BF16), (65536, W.F32),
-                                  (30001, W.F32), (70001, W.BF16), (1, W.BF16), (700, W.F32)])
-def test_sampling_one_workgroup_per_row_matches_split_batches(svl, orc, V, dt):
-    """k = 0 from 256 rows on draws each row in one workgroup (rows of at most
-    256 segments); smaller batches take the two-kernel draw.  Both compute the
-    same tiles, weights, segment masses and pick: one batch of 256 rows and
-    the same rows as four batches of 64 give bit-identical outputs, which
-    match the oracle outside the band.  Temperature 0 rows take the argmax."""
+ROW_DRAW = [(0, V, dt) for V, dt in [(128256, W.BF16), (131072, W.BF16), (131073, W.BF16), (65536, W.F32),
+                                      (30001, W.F32), (70001, W.BF16), (1, W.BF16), (700, W.F32)]] + \
+           [(1, 129280, W.BF16), (3, 65536, W.F32), (2, 70001, W.BF16), (4, 131073, W.BF16), (1, 2, W.F32)]
+
+
+@pytest.mark.parametrize("k,V,dt", ROW_DRAW)
+def test_row_draw_matches_split_batches(svl, orc, k, V, dt):
+    """From 256 sequences on, the final draw of a sequence whose rows have at
+    most 256 segments runs in one workgroup (with no drafts, or after the
+    sequence's acceptance computed inline); smaller batches take the
+    two-kernel draw.  Both compute the same tiles, weights, segment masses and
+    pick: one batch of 256 sequences and the same sequences as four batches
+    of 64 give bit-identical outputs, which match the oracle outside the
+    band.  Temperature 0 sequences take the argmax."""
     B = 256
     temps = np.where(np.arange(B) % 7 == 3, 0.0, np.linspace(0.3, 1.6, B)).astype(np.float32)
-    inp = W.chain_inputs(B, 0, V, dt, 77, target_sigma=3.0, temperature=temps)
-    whole, ref = _check_chain(svl, orc, inp, f"k0 one workgroup per row V{V}")
+    inp = W.chain_inputs(B, k, V, dt, 77 + k, target_sigma=3.0, draft_sigma=(0.2, 1.5), temperature=temps)
+    whole, ref = _check_chain(svl, orc, inp, f"row draw k{k} V{V}")
     parts = [run_chain(svl, _rows(inp, lo, lo + 64)) for lo in range(0, B, 64)]
-    for key in ("accepted_len", "emitted"):
-        np.testing.assert_array_equal(whole[key], np.concatenate([p[key] for p in parts]), err_msg=key)
+    for key in ("accepted_len", "emitted", "accept_prob"):
+        if whole[key] is not None:
+            np.testing.assert_array_equal(whole[key], np.concatenate([p[key] for p in parts]), err_msg=key)
 
 
 # ------------------------------------------------------------ NEXT rows ---
