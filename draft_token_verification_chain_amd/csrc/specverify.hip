@@ -249,8 +249,12 @@ sv_status run_greedy_rows(const void* logits, const int32_t* tokens, int B, int 
     constexpr int tpw = CHECK ? kGreedyRestTilesPerWave : 1;
     const int groups = (nT + sv::kWavesPerBlock * tpw - 1) / (sv::kWavesPerBlock * tpw);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * nrows * groups));
-    return launch(CHECK ? "greedy_rows_rest" : "greedy_rows", sv::greedy_rows_kernel<DT, VEC, kU, CHECK, tpw>, grid,
-                  dim3(sv::kBlock), stream, logits, tokens, k, V, nT, groups, nrows, j0, part);
+    if constexpr (CHECK)
+        return launch("greedy_rows_rest", sv::greedy_rows_rest_kernel<DT, VEC, kU, tpw>, grid, dim3(sv::kBlock),
+                      stream, logits, tokens, k, V, nT, groups, nrows, j0, part);
+    else
+        return launch("greedy_rows", sv::greedy_rows_kernel<DT, VEC, kU>, grid, dim3(sv::kBlock), stream, logits,
+                      tokens, k, V, nT, groups, nrows, j0, part);
 }
 
 sv_status greedy_rows(sv_dtype dt, bool vec, bool check, const void* logits, const int32_t* tokens, int B, int k, int V,

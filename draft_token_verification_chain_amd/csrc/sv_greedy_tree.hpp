@@ -34,10 +34,9 @@ __global__ __launch_bounds__(kBlock) void argmax_rows_kernel(const void* __restr
 // in turn, so every sequence's work is spread over the XCDs and each gets an
 // even share of the second phase however its sequences fall.
 template <int DT, bool VEC, int U, bool CHECK, int TPW>
-__global__ __launch_bounds__(kBlock) void greedy_rows_kernel(const void* __restrict__ logits,
-                                                             const int32_t* __restrict__ tokens, int k, int V,
-                                                             int nT, int groups, int nrows, int j0,
-                                                             Partial* __restrict__ part) {
+__device__ __forceinline__ void greedy_rows(const void* __restrict__ logits, const int32_t* __restrict__ tokens,
+                                            int k, int V, int nT, int groups, int nrows, int j0,
+                                            Partial* __restrict__ part) {
     const int per_seq = groups * nrows;
     const int64_t b = blockIdx.x / per_seq;
     const int rem = static_cast<int>(blockIdx.x - b * per_seq);
@@ -76,6 +75,24 @@ __global__ __launch_bounds__(kBlock) void greedy_rows_kernel(const void* __restr
         const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, row * static_cast<int64_t>(V), V, tile);
         if (lane_id() == 0) part[row * nT + tile] = Partial{a.val, a.idx};
     }
+}
+
+// The first phase (or the only one).
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void greedy_rows_kernel(const void* __restrict__ logits,
+                                                             const int32_t* __restrict__ tokens, int k, int V,
+                                                             int nT, int groups, int nrows, int j0,
+                                                             Partial* __restrict__ part) {
+    greedy_rows<DT, VEC, U, false, 1>(logits, tokens, k, V, nT, groups, nrows, j0, part);
+}
+
+// The second phase.
+template <int DT, bool VEC, int U, int TPW>
+__global__ __launch_bounds__(kBlock) void greedy_rows_rest_kernel(const void* __restrict__ logits,
+                                                                  const int32_t* __restrict__ tokens, int k, int V,
+                                                                  int nT, int groups, int nrows, int j0,
+                                                                  Partial* __restrict__ part) {
+    greedy_rows<DT, VEC, U, true, TPW>(logits, tokens, k, V, nT, groups, nrows, j0, part);
 }
 
 // One wave per sequence.  The argmax g_j of each of the k + 1 rows is
