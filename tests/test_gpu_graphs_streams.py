@@ -35,13 +35,15 @@ def _np(out):
     return {key: (v.cpu().numpy() if v is not None else None) for key, v in out.items()}
 
 
-def test_graph_capture_and_replay(svl, orc):
+@pytest.mark.parametrize("B,k", [(32, 4), (256, 1), (256, 0)])
+def test_graph_capture_and_replay(svl, orc, B, k):
     """verify_chain + commit_tokens captured once; every replay, on freshly
-    copied inputs and with eager work in between, matches the oracle."""
+    copied inputs and with eager work in between, matches the oracle.  From
+    256 sequences the final draw runs one workgroup per sequence."""
     import torch
 
-    sets = [_inputs(s) for s in (31, 32, 33, 34)]
-    B, k, V = sets[0]["B"], sets[0]["k"], sets[0]["V"]
+    sets = [_inputs(s, B=B, k=k) for s in (31, 32, 33, 34)]
+    V = sets[0]["V"]
     static = chain_tensors(sets[0])
     ws = torch.zeros(svl.chain_workspace_bytes(B, k, V, W.BF16), dtype=torch.uint8, device="cuda")
     out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
