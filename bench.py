@@ -253,7 +253,10 @@ def main():
             t = dev[i % copies]
             svl.verify_tree(t["node_tokens"], t["parent"], md, t["target_logits"], workspace=ws, out=out)
         units = B * (N - 1)                 # verified draft nodes per step
-        dominant = "argmax_rows"
+        # from 96 MiB of rows the library streams the root rows, then only the
+        # rows below a depth-1 node carrying the root's argmax (counted below)
+        tree_two_phase = N > 1 and B * N * V * es >= 96 << 20
+        dominant = "tree_rows_rest" if tree_two_phase else "argmax_rows"
         dominant_bytes = B * N * V * es
 
     unit = "sampled tokens/s" if kind == "chain" and inp["k"] == 0 else "verified draft tokens/s"
@@ -267,8 +270,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # bytes the final draw (greedy: the second phase's rows) reads, from this
-    # batch's outcome (identical in every copy)
+    # bytes read beyond the dominant kernel's, from this batch's outcome
+    # (identical in every copy): the chain's final draw, the greedy chain's
+    # second phase, the greedy tree's root rows (its second phase is then the
+    # dominant kernel, whose bytes also depend on the outcome)
     final_bytes = 0
     if kind == "chain":
         a = out["accepted_len"].cpu().numpy()
@@ -279,6 +284,18 @@ def main():
                 final_bytes += (2 if a[b] < k else 1) * V * es
             elif a[b] == k:
                 final_bytes += V * es
+    elif kind == "tree" and tree_two_phase:
+        # the second phase's rows: nodes whose depth-1 ancestor carries the root
+        # row's argmax, which is emitted[b][0] whatever the outcome
+        par = inp["parent"]
+        anc = np.arange(N)
+        for n in range(1, N):
+            anc[n] = n if par[n] == 0 else anc[par[n]]
+        g0 = out["emitted"][:, 0].cpu().numpy()
+        tok = inp["node_tokens"]
+        rest_rows = int(sum(np.count_nonzero(tok[b, anc[1:]] == g0[b]) for b in range(B)))
+        dominant_bytes = rest_rows * V * es
+        final_bytes = B * V * es          # the root rows
     elif kind == "greedy" and s_first <= inp["k"]:
         a = out["accepted_len"].cpu().numpy()
         final_bytes = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es

@@ -123,6 +123,21 @@ TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
     return L;
 }
 
+// The greedy-tree workspace: the partials of every node's row, then the
+// second phase's node lists and their lengths.
+struct TreeLayout {
+    size_t part, list, count, total;
+};
+
+TreeLayout tree_layout(int B, int N, int V, sv_dtype dt) {
+    TreeLayout L{};
+    L.part = 0;
+    L.list = align_up(sizeof(Partial) * static_cast<size_t>(B) * N * tiles_per_row(V, dt));
+    L.count = align_up(L.list + sizeof(int32_t) * static_cast<size_t>(B) * N);
+    L.total = align_up(L.count + sizeof(int32_t) * static_cast<size_t>(B));
+    return L;
+}
+
 // ---------------------------------------------------------------- kernel timing ---
 
 struct ProfSlot {
@@ -273,6 +288,43 @@ sv_status greedy_rows(sv_dtype dt, bool vec, bool check, const void* logits, con
                  : run_greedy_rows<SV_F32, false, false>(logits, tokens, B, k, V, nT, nrows, j0, part, stream);
 }
 
+// Greedy trees are streamed in two phases (root rows, then the rows below
+// an accepted depth-1 node) from this size on.  The two extra launches cost
+// about 8 us: on random trees of 64 nodes at a 0.6 match rate the two phases
+// lose 2.8 us at 66 MB of rows and gain 6.2 us at 131 MB.
+constexpr int64_t kTreeTwoPhaseMinBytes = int64_t(96) << 20;
+
+template <int DT, bool VEC>
+sv_status run_tree_two_phase(const void* logits, const int32_t* tokens, const int32_t* parent, int parent_stride,
+                             int B, int N, int V, int nT, Partial* part, int32_t* list, int32_t* count,
+                             hipStream_t stream) {
+    const int groups = static_cast<int>(blocks_for_waves(nT));
+    sv_status st = launch("tree_root_rows", sv::tree_root_rows_kernel<DT, VEC, kU>,
+                          dim3(static_cast<unsigned>(static_cast<int64_t>(B) * groups)), dim3(sv::kBlock), stream,
+                          logits, N, V, nT, groups, part);
+    if (st != SV_OK) return st;
+    st = launch("tree_plan", sv::tree_plan_kernel, dim3(B), dim3((N + sv::kWave - 1) / sv::kWave * sv::kWave), stream,
+                tokens, parent, parent_stride, N, nT, static_cast<const Partial*>(part), list, count);
+    if (st != SV_OK) return st;
+    return launch("tree_rows_rest", sv::tree_rows_rest_kernel<DT, VEC, kU>,
+                  dim3(static_cast<unsigned>(static_cast<int64_t>(B) * (N - 1) * groups)), dim3(sv::kBlock), stream,
+                  logits, N, V, nT, groups, static_cast<const int32_t*>(list), static_cast<const int32_t*>(count), part);
+}
+
+sv_status tree_two_phase(sv_dtype dt, bool vec, const void* logits, const int32_t* tokens, const int32_t* parent,
+                         int parent_stride, int B, int N, int V, int nT, Partial* part, int32_t* list, int32_t* count,
+                         hipStream_t stream) {
+    if (dt == SV_BF16)
+        return vec ? run_tree_two_phase<SV_BF16, true>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
+                                                       count, stream)
+                   : run_tree_two_phase<SV_BF16, false>(logits, tokens, parent, parent_stride, B, N, V, nT, part,
+                                                        list, count, stream);
+    return vec ? run_tree_two_phase<SV_F32, true>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
+                                                  count, stream)
+               : run_tree_two_phase<SV_F32, false>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
+                                                   count, stream);
+}
+
 // Greedy verification streams its rows in two phases only from this size on.
 // The second phase costs about 5 us beyond the rows it streams (a dependent
 // launch, the check's round trip, workgroups that exit): at a 0.8 match rate
@@ -324,7 +376,7 @@ size_t sv_greedy_workspace_bytes(int B, int k, int V, sv_dtype dt) {
 
 size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt) {
     if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
-    return align_up(sizeof(Partial) * static_cast<size_t>(B) * N * tiles_per_row(V, dt));
+    return tree_layout(B, N, V, dt).total;
 }
 
 size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt) {
@@ -405,9 +457,21 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
         return st;
     const int nT = static_cast<int>(tiles_per_row(V, dt));
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits);
-    auto* part = static_cast<Partial*>(workspace);
-    if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) != SV_OK)
+    const TreeLayout L = tree_layout(B, N, V, dt);
+    char* ws = static_cast<char*>(workspace);
+    auto* part = reinterpret_cast<Partial*>(ws + L.part);
+    const int64_t bytes = static_cast<int64_t>(B) * N * V * elem_bytes(dt);
+    if (N > 1 && bytes >= kTreeTwoPhaseMinBytes &&
+        static_cast<int64_t>(B) * (N - 1) * blocks_for_waves(nT) <= kMaxGrid) {
+        auto* list = reinterpret_cast<int32_t*>(ws + L.list);
+        auto* count = reinterpret_cast<int32_t*>(ws + L.count);
+        if ((st = tree_two_phase(dt, vec, target_logits, node_tokens, parent, parent_stride, B, N, V, nT, part, list,
+                                 count, stream)) != SV_OK)
+            return st;
+    } else if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) !=
+               SV_OK) {
         return st;
+    }
     // one thread per node, and at least 256 so that each node's argmax partials are spread over several lanes
     const int threads = std::max(256, (N + sv::kWave - 1) / sv::kWave * sv::kWave);
     return launch("tree_finalize", sv::tree_finalize_kernel, dim3(B), dim3(threads), stream, node_tokens, parent,

@@ -139,6 +139,107 @@ __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* _
 
 // ---------------------------------------------------------------- tree ---
 
+// A node's row is needed only if the node is accepted, and a node can be
+// accepted only if its depth-1 ancestor is, i.e. carries the root row's
+// argmax.  Large trees are therefore streamed in two phases: the root rows
+// first (tree_root_rows), then, after tree_plan has listed the nodes below an
+// accepted depth-1 node, only their rows (tree_rows_rest).  tree_finalize
+// is the same for both schedules: the partials of rows never streamed hold
+// stale values, and they only yield g_p for nodes p that are not accepted,
+// whose children fail their edge test whatever g_p is.
+
+// Argmax partials of every sequence's root row (node 0 of N).
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void tree_root_rows_kernel(const void* __restrict__ logits, int N, int V,
+                                                                int nT, int groups, Partial* __restrict__ part) {
+    greedy_rows<DT, VEC, U, false, 1>(logits, nullptr, N - 1, V, nT, groups, 1, 0, part);
+}
+
+// One workgroup per sequence, one thread per node: the root's argmax from its
+// partials (wave 0, one round trip), every node's depth-1 ancestor by
+// pointer jumping, then the list, in index order, of the nodes whose depth-1
+// ancestor carries that argmax (the ancestor included), and its length.  A
+// malformed parent link ends a node's walk there (tree_finalize reports such
+// trees); the rows it then lists are streamed needlessly, never skipped.
+__global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int32_t* __restrict__ node_tokens,
+                                                                      const int32_t* __restrict__ parent,
+                                                                      int parent_stride, int N, int nT,
+                                                                      const Partial* __restrict__ part,
+                                                                      int32_t* __restrict__ list,
+                                                                      int32_t* __restrict__ count) {
+    __shared__ int s_up[SV_MAX_TREE_NODES];
+    __shared__ int s_tok[SV_MAX_TREE_NODES];
+    __shared__ int s_wave[SV_MAX_TREE_NODES / kWave];
+    __shared__ int s_groot;
+    const int64_t b = blockIdx.x;
+    const int n = threadIdx.x;
+    const int lane = lane_id();
+    if (n < kWave) {
+        const Partial* p = part + b * N * static_cast<int64_t>(nT);
+        Partial q[kBatch];
+        group_load(p, nT, kWave, true, q);
+        int r;
+        double sum;
+        ArgMax am;
+        group_reduce<false>(p, nT, kWave, true, q, r, sum, am);
+        if (n == 0) s_groot = am.idx;
+    }
+    int up = n;
+    if (n < N) {
+        s_tok[n] = node_tokens[b * N + n];
+        const int p = n == 0 ? 0 : parent[b * static_cast<int64_t>(parent_stride) + n];
+        up = (p <= 0 || p >= n) ? n : p;  // the root, depth-1 nodes and malformed links are fixed points
+        s_up[n] = up;
+    }
+    __syncthreads();
+    for (int step = 1; step < N; step <<= 1) {
+        const int u2 = n < N ? s_up[up] : 0;
+        __syncthreads();
+        if (n < N) {
+            up = u2;
+            s_up[n] = up;
+        }
+        __syncthreads();
+    }
+    const bool need = n > 0 && n < N && s_tok[up] == s_groot;
+    const uint64_t m = __ballot(need);
+    const int w = n / kWave;
+    if (lane == 0) s_wave[w] = __popcll(m);
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += s_wave[i];
+    if (need) list[b * N + base + __popcll(m & ((uint64_t(1) << lane) - 1))] = n;
+    if (n == 0) {
+        int total = 0;
+        for (int i = 0; i < static_cast<int>(blockDim.x) / kWave; ++i) total += s_wave[i];
+        count[b] = total;
+    }
+}
+
+// Argmax partials of the listed rows: one workgroup per (sequence, list
+// entry i, group of kWavesPerBlock tiles), the group fastest (consecutive
+// workgroups go to different XCDs); entries past a sequence's count exit at
+// once.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void tree_rows_rest_kernel(const void* __restrict__ logits, int N, int V,
+                                                                int nT, int groups,
+                                                                const int32_t* __restrict__ list,
+                                                                const int32_t* __restrict__ count,
+                                                                Partial* __restrict__ part) {
+    const int64_t rest = blockIdx.x / groups;
+    const int group = static_cast<int>(blockIdx.x - rest * groups);
+    const int64_t b = rest / (N - 1);
+    const int i = static_cast<int>(rest - b * (N - 1));
+    const int cnt = count[b];
+    const int node = list[b * N + i];
+    if (i >= cnt) return;
+    const int64_t tile = static_cast<int64_t>(group) * kWavesPerBlock + threadIdx.x / kWave;
+    if (tile >= nT) return;
+    const int64_t row = b * N + node;
+    const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, row * static_cast<int64_t>(V), V, tile);
+    if (lane_id() == 0) part[row * nT + tile] = Partial{a.val, a.idx};
+}
+
 // One workgroup per sequence, one thread per node (N <= blockDim.x <= 1024).
 // The argmax of each node's row is combined by a group of G lanes (G as large
 // as the block allows; the first partials of every row, the tokens and the

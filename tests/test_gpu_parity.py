@@ -281,6 +281,74 @@ def test_tree_per_sequence_parents_and_invalid_trees(svl, orc):
     assert got["accepted_len"][4] == -1
 
 
+# Trees whose rows reach 96 MiB are streamed in two phases: the root rows,
+# then only the rows below a depth-1 node that carries the root's argmax.
+def _tree_two_phase_case(case):
+    V = 128256
+    if case == "per-sequence parents":
+        B, N = 12, 40
+        inp = W.tree_inputs(B, N, V, W.BF16, 21, max_depth=6)
+        parents = np.stack([W.random_tree(N, 200 + b) for b in range(B)]).astype(np.int32)
+        # tokens that follow each sequence's own tree (the argmax of the parent's row, or another token)
+        top = np.argmax(W.values(inp["target_logits"], W.BF16), axis=-1)
+        rng = np.random.default_rng(21)
+        tokens = inp["node_tokens"].copy()
+        for b in range(B):
+            for i in range(1, N):
+                g = int(top[b, parents[b, i]])
+                tokens[b, i] = g if rng.random() < 0.6 else (g + 1 + int(rng.integers(0, V - 1))) % V
+        parents[4, 7] = 9          # parent index not below the node: invalid
+        parents[9, 30] = -3        # negative parent: invalid
+        return dict(inp, parent=parents, node_tokens=tokens)
+    if case == "chain":
+        return W.tree_inputs(48, 11, V, W.BF16, 22, parent=np.arange(-1, 10, dtype=np.int32), match_p=0.8)
+    if case == "star":
+        return W.tree_inputs(16, 31, V, W.BF16, 23, parent=np.array([-1] + [0] * 30, np.int32), match_p=0.3)
+    if case == "f32 element loads":
+        return W.tree_inputs(8, 40, 100001, W.F32, 24)
+    if case == "two nodes":
+        return W.tree_inputs(400, 2, V, W.BF16, 25, parent=np.array([-1, 0], np.int32), match_p=0.5)
+    if case == "all match":
+        return W.tree_inputs(16, 64, V, W.BF16, 26, match_p=1.0)
+    if case == "none match":
+        return W.tree_inputs(16, 64, V, W.BF16, 27, match_p=0.0)
+    raise ValueError(case)
+
+
+TREE_TWO_PHASE = ["per-sequence parents", "chain", "star", "f32 element loads", "two nodes", "all match",
+                  "none match"]
+
+
+@pytest.fixture(scope="module")
+def tree_two_phase_ws(svl):
+    """One workspace for every two-phase tree case, 0xFF bytes at first and
+    then whatever the earlier cases left in it."""
+    import torch
+
+    return torch.full((svl.tree_workspace_bytes(400, 64, 128256, W.BF16),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("case", TREE_TWO_PHASE + TREE_TWO_PHASE[:1],
+                         ids=TREE_TWO_PHASE + ["per-sequence parents again"])
+def test_tree_two_phase(svl, orc, tree_two_phase_ws, case):
+    """Parity on trees that take the two phases, on one shared workspace: the
+    partials of rows a call skips are stale and must never reach its results
+    (nor may a malformed tree's rows)."""
+    import torch
+
+    inp = _tree_two_phase_case(case)
+    B, N, V, dt = inp["B"], inp["N"], inp["V"], inp["dtype"]
+    assert B * N * V * (2 if dt == W.BF16 else 4) >= 96 << 20
+    assert svl.tree_workspace_bytes(B, N, V, dt) <= tree_two_phase_ws.numel()
+    out = svl.verify_tree(dev(inp["node_tokens"].astype(np.int32)), dev(inp["parent"].astype(np.int32)),
+                          int(inp["max_depth"]), dev_logits(inp["target_logits"], dt), workspace=tree_two_phase_ws)
+    torch.cuda.synchronize()
+    ref = orc.verify_tree(inp)
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], err_msg=key)
+    _record("tree", f"two-phase {case}", dict(n=B, mean_accepted=float(ref["accepted_len"].mean())))
+
+
 def test_tree_linear_and_star_shapes(svl, orc):
     V = 5000
     for parent in (np.arange(-1, 11, dtype=np.int32), np.array([-1] + [0] * 30, np.int32)):
