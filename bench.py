@@ -254,8 +254,11 @@ def main():
             svl.verify_tree(t["node_tokens"], t["parent"], md, t["target_logits"], workspace=ws, out=out)
         units = B * (N - 1)                 # verified draft nodes per step
         # from 96 MiB of rows the library streams the root rows, then only the
-        # rows below a depth-1 node carrying the root's argmax (counted below)
+        # rows below an accepted depth-1 node (from 192 MiB and 48 nodes: depths
+        # 1-2 below an accepted depth-1 node, then depths 3+ below an accepted
+        # depth-3 node); those rows are counted below, from the outcome
         tree_two_phase = N > 1 and B * N * V * es >= 96 << 20
+        tree_ranges = ([(1, 2), (3, N)] if B * N * V * es >= 192 << 20 and N >= 48 else [(1, N)])
         dominant = "tree_rows_rest" if tree_two_phase else "argmax_rows"
         dominant_bytes = B * N * V * es
 
@@ -285,17 +288,28 @@ def main():
             elif a[b] == k:
                 final_bytes += V * es
     elif kind == "tree" and tree_two_phase:
-        # the second phase's rows: nodes whose depth-1 ancestor carries the root
-        # row's argmax, which is emitted[b][0] whatever the outcome
-        par = inp["parent"]
-        anc = np.arange(N)
+        # each later phase lists the nodes of its depth range whose ancestor at
+        # the range's first depth is accepted (node acceptance from the rows'
+        # argmax, host-side bookkeeping for the byte count only)
+        par, tok = inp["parent"], inp["node_tokens"]
+        top = np.argmax(W.values(inp["target_logits"], inp["dtype"]), axis=-1)
+        depth = np.zeros(N, np.int64)
         for n in range(1, N):
-            anc[n] = n if par[n] == 0 else anc[par[n]]
-        g0 = out["emitted"][:, 0].cpu().numpy()
-        tok = inp["node_tokens"]
-        rest_rows = int(sum(np.count_nonzero(tok[b, anc[1:]] == g0[b]) for b in range(B)))
-        dominant_bytes = rest_rows * V * es
-        final_bytes = B * V * es          # the root rows
+            depth[n] = depth[par[n]] + 1
+        rest_rows = 0
+        for b in range(B):
+            acc = np.zeros(N, bool)
+            acc[0] = True
+            for n in range(1, N):
+                acc[n] = acc[par[n]] and tok[b, n] == top[b, par[n]]
+            for lo, hi in tree_ranges:
+                for n in range(1, N):
+                    a = n
+                    while depth[a] > lo:
+                        a = par[a]
+                    rest_rows += int(lo <= depth[n] <= hi and acc[a])
+        dominant_bytes = rest_rows * V * es / len(tree_ranges)   # per tree_rows_rest launch
+        final_bytes = B * V * es + rest_rows * V * es - dominant_bytes  # root rows and the other launches
     elif kind == "greedy" and s_first <= inp["k"]:
         a = out["accepted_len"].cpu().numpy()
         final_bytes = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es

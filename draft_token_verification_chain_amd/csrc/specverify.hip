@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <tuple>
 #include <cstring>
@@ -293,36 +294,53 @@ sv_status greedy_rows(sv_dtype dt, bool vec, bool check, const void* logits, con
 // about 8 us: on random trees of 64 nodes at a 0.6 match rate the two phases
 // lose 2.8 us at 66 MB of rows and gain 6.2 us at 131 MB.
 constexpr int64_t kTreeTwoPhaseMinBytes = int64_t(96) << 20;
+// ... and in three (root rows, depths 1-2, depths 3 and more) from this size
+// and this many nodes on: the third phase pays where many nodes lie at depth
+// 3 and more, which the node count stands in for (the tree is on the device).
+// Measured on random trees at a 0.6 match rate: 64 nodes gain 2 us at 263 MB
+// and 13 us at 525 MB; 16 and 26 nodes lose 1-2.4 us at 253-263 MB.
+constexpr int64_t kTreeThreePhaseMinBytes = int64_t(192) << 20;
+constexpr int kTreeThreePhaseMinNodes = 48;
 
 template <int DT, bool VEC>
 sv_status run_tree_two_phase(const void* logits, const int32_t* tokens, const int32_t* parent, int parent_stride,
-                             int B, int N, int V, int nT, Partial* part, int32_t* list, int32_t* count,
+                             int B, int N, int V, int nT, bool three, Partial* part, int32_t* list, int32_t* count,
                              hipStream_t stream) {
     const int groups = static_cast<int>(blocks_for_waves(nT));
     sv_status st = launch("tree_root_rows", sv::tree_root_rows_kernel<DT, VEC, kU>,
                           dim3(static_cast<unsigned>(static_cast<int64_t>(B) * groups)), dim3(sv::kBlock), stream,
                           logits, N, V, nT, groups, part);
     if (st != SV_OK) return st;
-    st = launch("tree_plan", sv::tree_plan_kernel, dim3(B), dim3((N + sv::kWave - 1) / sv::kWave * sv::kWave), stream,
-                tokens, parent, parent_stride, N, nT, static_cast<const Partial*>(part), list, count);
-    if (st != SV_OK) return st;
-    return launch("tree_rows_rest", sv::tree_rows_rest_kernel<DT, VEC, kU>,
-                  dim3(static_cast<unsigned>(static_cast<int64_t>(B) * (N - 1) * groups)), dim3(sv::kBlock), stream,
-                  logits, N, V, nT, groups, static_cast<const int32_t*>(list), static_cast<const int32_t*>(count), part);
+    // depth ranges of the later phases: [1, inf), or [1, 2] then [3, inf)
+    const int ranges[2][2] = {{1, three ? 2 : INT_MAX}, {3, INT_MAX}};
+    const int nodes_threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
+    for (int ph = 0; ph < (three ? 2 : 1); ++ph) {
+        // the root's children alone need one wave per node; later ranges combine every row over at least 256 threads
+        const int threads = ph == 0 ? nodes_threads : std::max(256, nodes_threads);
+        st = launch("tree_plan", sv::tree_plan_kernel, dim3(B), dim3(threads), stream, tokens, parent, parent_stride, N,
+                    nT, static_cast<const Partial*>(part), ranges[ph][0], ranges[ph][1], list, count);
+        if (st != SV_OK) return st;
+        st = launch("tree_rows_rest", sv::tree_rows_rest_kernel<DT, VEC, kU>,
+                    dim3(static_cast<unsigned>(static_cast<int64_t>(B) * (N - 1) * groups)), dim3(sv::kBlock), stream,
+                    logits, N, V, nT, groups, static_cast<const int32_t*>(list), static_cast<const int32_t*>(count),
+                    part);
+        if (st != SV_OK) return st;
+    }
+    return SV_OK;
 }
 
 sv_status tree_two_phase(sv_dtype dt, bool vec, const void* logits, const int32_t* tokens, const int32_t* parent,
-                         int parent_stride, int B, int N, int V, int nT, Partial* part, int32_t* list, int32_t* count,
-                         hipStream_t stream) {
+                         int parent_stride, int B, int N, int V, int nT, bool three, Partial* part, int32_t* list,
+                         int32_t* count, hipStream_t stream) {
     if (dt == SV_BF16)
-        return vec ? run_tree_two_phase<SV_BF16, true>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
-                                                       count, stream)
-                   : run_tree_two_phase<SV_BF16, false>(logits, tokens, parent, parent_stride, B, N, V, nT, part,
-                                                        list, count, stream);
-    return vec ? run_tree_two_phase<SV_F32, true>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
-                                                  count, stream)
-               : run_tree_two_phase<SV_F32, false>(logits, tokens, parent, parent_stride, B, N, V, nT, part, list,
-                                                   count, stream);
+        return vec ? run_tree_two_phase<SV_BF16, true>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
+                                                       list, count, stream)
+                   : run_tree_two_phase<SV_BF16, false>(logits, tokens, parent, parent_stride, B, N, V, nT, three,
+                                                        part, list, count, stream);
+    return vec ? run_tree_two_phase<SV_F32, true>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
+                                                  list, count, stream)
+               : run_tree_two_phase<SV_F32, false>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
+                                                   list, count, stream);
 }
 
 // Greedy verification streams its rows in two phases only from this size on.
@@ -465,7 +483,8 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
         static_cast<int64_t>(B) * (N - 1) * blocks_for_waves(nT) <= kMaxGrid) {
         auto* list = reinterpret_cast<int32_t*>(ws + L.list);
         auto* count = reinterpret_cast<int32_t*>(ws + L.count);
-        if ((st = tree_two_phase(dt, vec, target_logits, node_tokens, parent, parent_stride, B, N, V, nT, part, list,
+        if ((st = tree_two_phase(dt, vec, target_logits, node_tokens, parent, parent_stride, B, N, V, nT,
+                                 bytes >= kTreeThreePhaseMinBytes && N >= kTreeThreePhaseMinNodes, part, list,
                                  count, stream)) != SV_OK)
             return st;
     } else if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) !=

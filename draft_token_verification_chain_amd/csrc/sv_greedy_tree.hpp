@@ -140,13 +140,14 @@ __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* _
 // ---------------------------------------------------------------- tree ---
 
 // A node's row is needed only if the node is accepted, and a node can be
-// accepted only if its depth-1 ancestor is, i.e. carries the root row's
-// argmax.  Large trees are therefore streamed in two phases: the root rows
-// first (tree_root_rows), then, after tree_plan has listed the nodes below an
-// accepted depth-1 node, only their rows (tree_rows_rest).  tree_finalize
-// is the same for both schedules: the partials of rows never streamed hold
-// stale values, and they only yield g_p for nodes p that are not accepted,
-// whose children fail their edge test whatever g_p is.
+// accepted only if all its ancestors are.  Large trees are therefore
+// streamed in phases by depth: the root rows first (tree_root_rows), then,
+// each time after tree_plan has listed the nodes of the next depth range
+// whose ancestor at the range's first depth is accepted, only their rows
+// (tree_rows_rest).  tree_finalize is the same for every schedule: the
+// partials of rows never streamed hold stale values, and they only yield g_p
+// for nodes p that are not accepted, whose children fail their edge test
+// whatever g_p is.
 
 // Argmax partials of every sequence's root row (node 0 of N).
 template <int DT, bool VEC, int U>
@@ -155,53 +156,104 @@ __global__ __launch_bounds__(kBlock) void tree_root_rows_kernel(const void* __re
     greedy_rows<DT, VEC, U, false, 1>(logits, nullptr, N - 1, V, nT, groups, 1, 0, part);
 }
 
-// One workgroup per sequence, one thread per node: the root's argmax from its
-// partials (wave 0, one round trip), every node's depth-1 ancestor by
-// pointer jumping, then the list, in index order, of the nodes whose depth-1
-// ancestor carries that argmax (the ancestor included), and its length.  A
-// malformed parent link ends a node's walk there (tree_finalize reports such
-// trees); the rows it then lists are streamed needlessly, never skipped.
+// The rows of one later phase, one workgroup per sequence and one thread per
+// node: the nodes n with d_lo <= depth(n) <= d_hi whose ancestor at depth
+// d_lo is accepted, listed in index order, and their number.  Earlier phases
+// have streamed the rows of every node at depth < d_lo that may be accepted,
+// so that ancestor's acceptance follows from their partials: the argmax of
+// every row (G lanes per row; the root's alone when d_lo = 1), then depth and
+// path acceptance by pointer jumping, then the ancestor at depth d_lo by
+// pointer jumping.  A malformed tree lists nothing (tree_finalize reports it).
 __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int32_t* __restrict__ node_tokens,
                                                                       const int32_t* __restrict__ parent,
                                                                       int parent_stride, int N, int nT,
-                                                                      const Partial* __restrict__ part,
-                                                                      int32_t* __restrict__ list,
+                                                                      const Partial* __restrict__ part, int d_lo,
+                                                                      int d_hi, int32_t* __restrict__ list,
                                                                       int32_t* __restrict__ count) {
-    __shared__ int s_up[SV_MAX_TREE_NODES];
+    __shared__ int s_g[SV_MAX_TREE_NODES];
     __shared__ int s_tok[SV_MAX_TREE_NODES];
+    __shared__ int s_anc[SV_MAX_TREE_NODES];
+    __shared__ int s_len[SV_MAX_TREE_NODES];
+    __shared__ int s_ok[SV_MAX_TREE_NODES];
     __shared__ int s_wave[SV_MAX_TREE_NODES / kWave];
-    __shared__ int s_groot;
+    __shared__ int s_bad;
     const int64_t b = blockIdx.x;
     const int n = threadIdx.x;
     const int lane = lane_id();
-    if (n < kWave) {
-        const Partial* p = part + b * N * static_cast<int64_t>(nT);
-        Partial q[kBatch];
-        group_load(p, nT, kWave, true, q);
+    const int nthreads = blockDim.x;
+    if (n == 0) s_bad = 0;
+    __syncthreads();
+    const int rows = d_lo == 1 ? 1 : N;
+    int G = kWave;
+    while (G > 1 && G * rows > nthreads) G >>= 1;
+    const int per_pass = nthreads / G;
+    const Partial* rows_base = part + b * N * static_cast<int64_t>(nT);
+    Partial q[kBatch];
+    group_load(rows_base + (n / G < rows ? n / G : 0) * static_cast<int64_t>(nT), nT, G, n / G < rows, q);
+    int p = 0;
+    if (n < N) {
+        s_tok[n] = node_tokens[b * N + n];
+        p = n == 0 ? 0 : parent[b * static_cast<int64_t>(parent_stride) + n];
+        if (n > 0 && (p < 0 || p >= n)) s_bad = 1;
+    }
+    for (int m0 = 0; m0 < rows; m0 += per_pass) {
+        const int m = m0 + n / G;
+        const bool valid = m < rows;
+        const Partial* pr = rows_base + (valid ? m : 0) * static_cast<int64_t>(nT);
+        if (m0 > 0) group_load(pr, nT, G, valid, q);
         int r;
         double sum;
         ArgMax am;
-        group_reduce<false>(p, nT, kWave, true, q, r, sum, am);
-        if (n == 0) s_groot = am.idx;
+        group_reduce<false>(pr, nT, G, valid, q, r, sum, am);
+        if (valid && (n & (G - 1)) == 0) s_g[m] = am.idx;
     }
-    int up = n;
+    __syncthreads();
+    if (s_bad) {
+        if (n == 0) count[b] = 0;
+        return;
+    }
+    // depth and path acceptance; with d_lo = 1 only the root's children are tested
+    int anc = p, len = n == 0 ? 0 : 1;
+    int ok = 1;
+    if (n > 0 && n < N) ok = (d_lo == 1 && p != 0) ? 1 : (s_tok[n] == s_g[p]);
     if (n < N) {
-        s_tok[n] = node_tokens[b * N + n];
-        const int p = n == 0 ? 0 : parent[b * static_cast<int64_t>(parent_stride) + n];
-        up = (p <= 0 || p >= n) ? n : p;  // the root, depth-1 nodes and malformed links are fixed points
-        s_up[n] = up;
+        s_anc[n] = anc;
+        s_len[n] = len;
+        s_ok[n] = ok;
     }
     __syncthreads();
     for (int step = 1; step < N; step <<= 1) {
-        const int u2 = n < N ? s_up[up] : 0;
+        int a2 = 0, l2 = 0, o2 = 1;
+        if (n < N) {
+            a2 = s_anc[anc];
+            l2 = s_len[anc];
+            o2 = s_ok[anc];
+        }
         __syncthreads();
         if (n < N) {
-            up = u2;
-            s_up[n] = up;
+            len += l2;
+            ok &= o2;
+            anc = a2;
+            s_anc[n] = anc;
+            s_len[n] = len;
+            s_ok[n] = ok;
         }
         __syncthreads();
     }
-    const bool need = n > 0 && n < N && s_tok[up] == s_groot;
+    // the ancestor at depth d_lo: nodes no deeper are fixed points (s_anc is reused)
+    int up = (n < N && len > d_lo) ? p : n;
+    if (n < N) s_anc[n] = up;
+    __syncthreads();
+    for (int step = 1; step < N; step <<= 1) {
+        const int u2 = n < N ? s_anc[up] : 0;
+        __syncthreads();
+        if (n < N) {
+            up = u2;
+            s_anc[n] = up;
+        }
+        __syncthreads();
+    }
+    const bool need = n > 0 && n < N && len >= d_lo && len <= d_hi && s_ok[up];
     const uint64_t m = __ballot(need);
     const int w = n / kWave;
     if (lane == 0) s_wave[w] = __popcll(m);
@@ -211,7 +263,7 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int3
     if (need) list[b * N + base + __popcll(m & ((uint64_t(1) << lane) - 1))] = n;
     if (n == 0) {
         int total = 0;
-        for (int i = 0; i < static_cast<int>(blockDim.x) / kWave; ++i) total += s_wave[i];
+        for (int i = 0; i < nthreads / kWave; ++i) total += s_wave[i];
         count[b] = total;
     }
 }

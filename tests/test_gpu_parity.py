@@ -283,10 +283,14 @@ def test_tree_per_sequence_parents_and_invalid_trees(svl, orc):
 
 # Trees whose rows reach 96 MiB are streamed in two phases: the root rows,
 # then only the rows below a depth-1 node that carries the root's argmax.
+# From 192 MiB and 48 nodes, in three: the root rows, depths 1-2 below an
+# accepted depth-1 node, then depths 3 and more below an accepted depth-3 node.
 def _tree_two_phase_case(case):
     V = 128256
-    if case == "per-sequence parents":
-        B, N = 12, 40
+    if case.startswith("per-sequence parents"):
+        B, N = (8, 64) if case.endswith("three phases") else (12, 40)
+        if case.endswith("three phases"):
+            V = 200003
         inp = W.tree_inputs(B, N, V, W.BF16, 21, max_depth=6)
         parents = np.stack([W.random_tree(N, 200 + b) for b in range(B)]).astype(np.int32)
         # tokens that follow each sequence's own tree (the argmax of the parent's row, or another token)
@@ -298,7 +302,7 @@ def _tree_two_phase_case(case):
                 g = int(top[b, parents[b, i]])
                 tokens[b, i] = g if rng.random() < 0.6 else (g + 1 + int(rng.integers(0, V - 1))) % V
         parents[4, 7] = 9          # parent index not below the node: invalid
-        parents[9, 30] = -3        # negative parent: invalid
+        parents[B - 3, 30] = -3    # negative parent: invalid
         return dict(inp, parent=parents, node_tokens=tokens)
     if case == "chain":
         return W.tree_inputs(48, 11, V, W.BF16, 22, parent=np.arange(-1, 10, dtype=np.int32), match_p=0.8)
@@ -316,7 +320,7 @@ def _tree_two_phase_case(case):
 
 
 TREE_TWO_PHASE = ["per-sequence parents", "chain", "star", "f32 element loads", "two nodes", "all match",
-                  "none match"]
+                  "none match", "per-sequence parents, three phases"]
 
 
 @pytest.fixture(scope="module")
