@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--accept-prob", action="store_true",
+                    help="chain workloads: also return accept_prob (tau of every draft, also past the first "
+                         "rejection), which makes the library read every row")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the timed region, run one plain device copy of MIB MiB (a reference "
                          "kernel of known traffic for hardware counters)")
@@ -193,7 +196,8 @@ def main():
         k = inp["k"]
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
                    emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"),
-                   accept_prob=torch.empty((B, k), dtype=torch.float32, device="cuda"))
+                   accept_prob=(torch.empty((B, k), dtype=torch.float32, device="cuda") if args.accept_prob
+                                else None))
         ws = torch.empty(svl.chain_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
 
         def step(i):
@@ -206,8 +210,12 @@ def main():
         nseg = -(-(-(-V // (16 // es))) // 64)  # ceil(ceil(V / (16 / es)) / 64)
         dominant = ("chain_rowstats" if k > 0 else
                     "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part")
-        # every draft row and target rows 0..k-1 once (k == 0: the sampled row)
-        dominant_bytes = 2 * B * k * V * es if k > 0 else B * V * es
+        # every draft row and target rows 0..k-1 once (k == 0: the sampled row);
+        # without accept_prob, from 6 drafts and 128 MiB of rows the library
+        # streams positions 0..s-1 first and the rest only for sequences that
+        # accept all of them (counted below, from the outcome)
+        chain_s = (max(1, k // 4) if not args.accept_prob and k >= 6 and 2 * B * k * V * es >= 128 << 20 else k)
+        dominant_bytes = 2 * B * chain_s * V * es if k > 0 else B * V * es
     elif kind == "greedy":
         k = inp["k"]
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
@@ -287,6 +295,8 @@ def main():
                 final_bytes += (2 if a[b] < k else 1) * V * es
             elif a[b] == k:
                 final_bytes += V * es
+        if chain_s < k:   # the second phase's rows
+            final_bytes += int((a >= chain_s).sum()) * 2 * (k - chain_s) * V * es
     elif kind == "tree" and tree_two_phase:
         # each later phase lists the nodes of its depth range whose ancestor at
         # the range's first depth is accepted (node acceptance from the rows'
@@ -365,7 +375,8 @@ def main():
         "data": "synthetic (seeded generator, shapes of the named workload)",
         "config": {"workload": cfg["name"], "B": B, "k": inp.get("k"), "N": inp.get("N"), "V": V,
                    "logits": W.DTYPE_NAMES[inp["dtype"]], "temperature": cfg.get("temperature"),
-                   "seed": args.seed, "input_copies_rotated": copies, "parallelism": "single GPU"},
+                   "seed": args.seed, "input_copies_rotated": copies, "parallelism": "single GPU",
+                   "accept_prob": bool(args.accept_prob) if kind == "chain" else None},
         "hbm_gbs": step_bytes / s_per_step / 1e9,
         "hbm_frac_of_peak": step_bytes / s_per_step / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": step_bytes,

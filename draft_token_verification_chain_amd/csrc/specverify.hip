@@ -73,6 +73,15 @@ int64_t final_chunks(int V, sv_dtype dt) {
 // sequence's acceptance; beyond it one wave per sequence computes it once.
 constexpr int64_t kInlineAcceptMaxBlocks = 2048;
 
+// Chains without accept_prob stream their rows in two phases (positions
+// 0 .. max(1, k/4)-1, then the rest for sequences accepting all of those)
+// from this many drafts and this many bytes of rows on.  The second phase
+// costs about 5 us beyond its rows: at k = 8 (265 MB, 28% of sequences past
+// position 1) the step gains 21%, at k = 4 (131 MB, 56% past position 0) it
+// loses 5%.
+constexpr int kChainTwoPhaseMinK = 6;
+constexpr int64_t kChainTwoPhaseMinBytes = int64_t(128) << 20;
+
 // The final draw runs one workgroup per sequence (chain_row_draw_kernel) from
 // this many sequences on, for rows of at most kRowDrawMaxSegs segments: one
 // row per CU fills the chip.  Below it a row alone on a CU streams too slowly
@@ -205,10 +214,29 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
     const int acc = k == 0 ? sv::kAcceptNone
                            : (fin_blocks <= kInlineAcceptMaxBlocks ? sv::kAcceptInline : sv::kAcceptRead);
     if (k > 0) {
-        const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * k * nT);
+        // Without accept_prob a sequence's rows after its first rejection are
+        // never needed: large chains stream positions 0 .. s-1 first, then the
+        // rest only for sequences that accept all of them.
+        const int64_t rows_bytes = static_cast<int64_t>(2) * B * k * V * sv::Elem<DT>::bytes;
+        const int groups = static_cast<int>(blocks_for_waves(nT));
+        const int s = accept_prob == nullptr && k >= kChainTwoPhaseMinK && rows_bytes >= kChainTwoPhaseMinBytes &&
+                              static_cast<int64_t>(B) * 2 * k * groups <= kMaxGrid
+                          ? std::max(1, k / 4)
+                          : k;
+        const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * s * nT);
         st = launch("chain_rowstats", sv::chain_rowstats_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
-                    dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, V, nT, part, gathered);
+                    dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, 0, s, V, nT, part, gathered);
         if (st != SV_OK) return st;
+        if (s < k) {
+            // about two workgroups per row
+            const int tpw = std::max(1, (nT + 2 * sv::kWavesPerBlock - 1) / (2 * sv::kWavesPerBlock));
+            const int rest_groups = (nT + sv::kWavesPerBlock * tpw - 1) / (sv::kWavesPerBlock * tpw);
+            st = launch("chain_rowstats_rest", sv::chain_rowstats_rest_kernel<DT, VEC, kU>,
+                        dim3(static_cast<unsigned>(static_cast<int64_t>(B) * 2 * (k - s) * rest_groups)),
+                        dim3(sv::kBlock), stream, target, draft, temperature, uniforms, tokens, B, k, s, V, nT,
+                        rest_groups, tpw, part, gathered);
+            if (st != SV_OK) return st;
+        }
     }
     if (B >= kRowDrawMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kRowDrawMaxSegs) {
         auto row_draw = k == 0 ? sv::chain_row_draw_kernel<DT, VEC, sv::kAcceptNone>

@@ -23,28 +23,16 @@ __device__ __forceinline__ Partial rowstats_tile(const void* base, int64_t row_e
     return Partial{a.val, a.idx};
 }
 
-// Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
-// rows (b, i).  The wave streaming tile 0 of a row also reads the row's logit
-// at its draft token into gathered[r], so that the acceptance needs no
-// dependent gather.  Draft rows of temperature-0 sequences are streamed too,
-// and their partials go unused: deciding to skip them would put the
-// temperature's load in front of every wave's tile loads.
+// Tile `tile` of target row (b, position rr - b*k) or of draft row rr of a
+// chain (partial rows rr and nbk + rr).  The wave of tile 0 also reads the
+// row's logit at its draft token into gathered.
 template <int DT, bool VEC, int U>
-__global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __restrict__ target,
-                                                                const void* __restrict__ draft,
-                                                                const float* __restrict__ temperature,
-                                                                const int32_t* __restrict__ tokens,
-                                                                int B, int k, int V, int nT,
-                                                                Partial* __restrict__ part,
-                                                                float* __restrict__ gathered) {
-    const int64_t gw = global_wave();
-    const int64_t nbk = static_cast<int64_t>(B) * k;
-    if (gw >= 2 * nbk * nT) return;
-    const int64_t r = gw / nT;
-    const int64_t tile = gw - r * nT;
-    const bool is_target = r < nbk;
-    const int64_t rr = is_target ? r : r - nbk;
-    const int64_t b = rr / k;
+__device__ __forceinline__ void rowstats_row_tile(const void* __restrict__ target, const void* __restrict__ draft,
+                                                  const float* __restrict__ temperature,
+                                                  const int32_t* __restrict__ tokens, int64_t nbk, int k,
+                                                  bool is_target, int64_t b, int64_t rr, int64_t tile, int V, int nT,
+                                                  Partial* __restrict__ part, float* __restrict__ gathered) {
+    const int64_t r = is_target ? rr : nbk + rr;
     const void* base = is_target ? target : draft;
     const int64_t row_elem = (is_target ? (b * (k + 1) + (rr - b * k)) : rr) * static_cast<int64_t>(V);
     if (tile == 0) {
@@ -59,6 +47,36 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
     if (lane_id() == 0) part[r * nT + tile] = p;
 }
 
+// Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
+// rows (b, i).  This pass streams the rows of positions j0 .. j0+np-1 of every
+// sequence (all of them when j0 = 0 and np = k).  The wave streaming tile 0 of
+// a row also reads the row's logit at its draft token into gathered[r], so
+// that the acceptance needs no dependent gather.  Draft rows of
+// temperature-0 sequences are streamed too, and their partials go unused:
+// deciding to skip them would put the temperature's load in front of every
+// wave's tile loads.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __restrict__ target,
+                                                                const void* __restrict__ draft,
+                                                                const float* __restrict__ temperature,
+                                                                const int32_t* __restrict__ tokens,
+                                                                int B, int k, int j0, int np, int V, int nT,
+                                                                Partial* __restrict__ part,
+                                                                float* __restrict__ gathered) {
+    const int64_t gw = global_wave();
+    const int64_t nbk = static_cast<int64_t>(B) * k;
+    const int64_t nbp = static_cast<int64_t>(B) * np;
+    if (gw >= 2 * nbp * nT) return;
+    const int64_t rp = gw / nT;
+    const int64_t tile = gw - rp * nT;
+    const bool is_target = rp < nbp;
+    const int64_t rq = is_target ? rp : rp - nbp;
+    const int64_t b = rq / np;
+    const int64_t rr = b * k + j0 + (rq - b * np);
+    rowstats_row_tile<DT, VEC, U>(target, draft, temperature, tokens, nbk, k, is_target, b, rr, tile, V, nT, part,
+                                  gathered);
+}
+
 // ---------------------------------------------------------------- chain: acceptance ---
 
 // Acceptance of sequence b, computed by one wave (the first of its block):
@@ -67,14 +85,18 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
 // the first rejection by ballot.  Writes the final draw's descriptor into
 // *out and, when `publish`, accepted_len, the accepted prefix of emitted
 // (the rest -1; the final token is written later) and accept_prob.
+// With npos < k only positions 0 .. npos-1 are tested (no outputs then): the
+// return value is the first rejection among them, or npos.  Each tested
+// position gets exactly the arithmetic of the full call (the same lanes per
+// row and the same order of combination), so the two agree on it.
 template <int DT>
-__device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ tokens,
-                                                const float* __restrict__ temperature,
-                                                const float* __restrict__ uniforms, int B, int k, int V, int nT,
-                                                const Partial* __restrict__ part, const float* __restrict__ gathered,
-                                                int64_t b, bool publish, int32_t* __restrict__ accepted_len,
-                                                int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
-                                                int* s_r, double* s_s, SeqInfo* out) {
+__device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ tokens,
+                                               const float* __restrict__ temperature,
+                                               const float* __restrict__ uniforms, int B, int k, int V, int nT,
+                                               const Partial* __restrict__ part, const float* __restrict__ gathered,
+                                               int64_t b, int npos, bool publish, int32_t* __restrict__ accepted_len,
+                                               int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+                                               int* s_r, double* s_s, SeqInfo* out) {
     const int lane = lane_id();
     const int64_t nbk = static_cast<int64_t>(B) * k;
     // every load first: none of them depends on another
@@ -83,14 +105,16 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
     while (G > 1 && G * rows > kWave) G >>= 1;
     const int per_pass = kWave / G;
     auto row_of = [&](int rho) -> int64_t { return rho < k ? b * k + rho : nbk + b * k + (rho - k); };
+    // rows of the positions tested (all of them in the full call)
+    auto tested = [&](int rho) { return rho < rows && (rho < k ? rho : rho - k) < npos; };
     Partial q[kBatch];
     const int rho_first = lane / G;
-    group_load(part + (rho_first < rows ? row_of(rho_first) : 0) * nT, nT, G, rho_first < rows, q);
+    group_load(part + (tested(rho_first) ? row_of(rho_first) : 0) * nT, nT, G, tested(rho_first), q);
     const float T = temperature[b];
     const float uk = uniforms[b * (k + 1) + k];
     int x = 0;
     float ui = 0.f, lt = 0.f, ld = 0.f;
-    if (lane < k) {
+    if (lane < npos) {
         x = tokens[b * k + lane];
         ui = uniforms[b * (k + 1) + lane];
         lt = gathered[b * k + lane];
@@ -101,7 +125,7 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
     // row statistics (at temperature 0 only the target rows' argmax matters)
     for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
         const int rho = rho0 + lane / G;
-        const bool valid = rho < rows;
+        const bool valid = tested(rho);
         const Partial* p = part + (valid ? row_of(rho) : 0) * nT;
         if (rho0 > 0) group_load(p, nT, G, valid, q);
         int r;
@@ -126,7 +150,7 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
     int g = -1;
     int rt = 0, rd = 0;
     double st = 1.0, sd = 1.0;
-    if (lane < k) {
+    if (lane < npos) {
         if (!sampled) g = s_r[lane];
         if (!xok) {
             acc = false;
@@ -148,8 +172,9 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
             tau = acc ? 1.0 : 0.0;
         }
     }
-    int a = first_lane(lane < k && !acc);
-    if (a < 0) a = k;
+    int a = first_lane(lane < npos && !acc);
+    if (a < 0) a = npos;
+    if (npos < k) return a;
     int32_t* em = emitted + b * (k + 1);
     if (publish) {
         if (accept_prob != nullptr && lane < k) accept_prob[b * k + lane] = static_cast<float>(tau);
@@ -179,6 +204,47 @@ __device__ __forceinline__ void accept_sequence(const int32_t* __restrict__ toke
         *out = si;
     }
     if (publish && lane == 0) accepted_len[b] = a;
+    return a;
+}
+
+// The second phase of a chain's rowstats: the rows of positions s .. k-1 of
+// the sequences whose drafts 0 .. s-1 are all accepted.  Wave 0 of every
+// workgroup finds that with accept_sequence over those positions, which is
+// the final acceptance's own arithmetic, so the two agree on them.  One
+// workgroup per (sequence, row, group of kWavesPerBlock * tpw tiles), the
+// group fastest; the rows are the target rows of positions s .. k-1, then the
+// draft rows.  Each wave takes tpw tiles in turn: the check costs about as
+// much as streaming a few tiles, so a workgroup checks once for many.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void chain_rowstats_rest_kernel(
+    const void* __restrict__ target, const void* __restrict__ draft, const float* __restrict__ temperature,
+    const float* __restrict__ uniforms, const int32_t* __restrict__ tokens, int B, int k, int s, int V, int nT,
+    int groups, int tpw, Partial* __restrict__ part, float* __restrict__ gathered) {
+    __shared__ int s_r[2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[2 * SV_MAX_DRAFTS];
+    __shared__ int s_go;
+    const int rest = k - s;
+    const int64_t per_seq = static_cast<int64_t>(groups) * 2 * rest;
+    const int64_t b = blockIdx.x / per_seq;
+    const int rem = static_cast<int>(blockIdx.x - b * per_seq);
+    const int z = rem / groups;
+    const int group = rem - z * groups;
+    if (threadIdx.x < kWave) {
+        const int a = accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, s, false,
+                                          nullptr, nullptr, nullptr, s_r, s_s, nullptr);
+        if (lane_id() == 0) s_go = a == s;
+    }
+    __syncthreads();
+    if (!s_go) return;
+    const bool is_target = z < rest;
+    const int64_t rr = b * k + s + (is_target ? z : z - rest);
+#pragma unroll 1
+    for (int i = 0; i < tpw; ++i) {
+        const int64_t tile = (static_cast<int64_t>(group) * tpw + i) * kWavesPerBlock + threadIdx.x / kWave;
+        if (tile >= nT) break;
+        rowstats_row_tile<DT, VEC, U>(target, draft, temperature, tokens, static_cast<int64_t>(B) * k, k, is_target, b,
+                                      rr, tile, V, nT, part, gathered);
+    }
 }
 
 // One wave per sequence, kAccWaves sequences per workgroup: the acceptance
@@ -196,7 +262,7 @@ __global__ __launch_bounds__(kAccWaves * kWave) void chain_accept_kernel(
     const int w = threadIdx.x / kWave;
     const int64_t b = static_cast<int64_t>(blockIdx.x) * kAccWaves + w;
     if (b >= B) return;  // whole waves only; the kernel has no workgroup barrier
-    accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, true, accepted_len, emitted,
+    accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, k, true, accepted_len, emitted,
                         accept_prob, s_r[w], s_s[w], info + b);
 }
 
@@ -361,7 +427,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
         __shared__ double s_s[2 * SV_MAX_DRAFTS];
         __shared__ SeqInfo s_info;
         if (threadIdx.x < kWave)
-            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, c == 0, accepted_len,
+            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, k, c == 0, accepted_len,
                                 emitted, accept_prob, s_r, s_s, &s_info);
         __syncthreads();
         si = s_info;
@@ -594,7 +660,7 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
         __shared__ double s_s[2 * SV_MAX_DRAFTS];
         __shared__ SeqInfo s_info;
         if (threadIdx.x < kWave)
-            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, true, accepted_len,
+            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, k, true, accepted_len,
                                 emitted, accept_prob, s_r, s_s, &s_info);
         __syncthreads();
         si = s_info;

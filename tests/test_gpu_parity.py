@@ -437,6 +437,55 @@ def test_row_draw_matches_split_batches(svl, orc, k, V, dt):
             np.testing.assert_array_equal(whole[key], np.concatenate([p[key] for p in parts]), err_msg=key)
 
 
+# Without accept_prob, chains of at least 6 drafts and 128 MiB of rows stream
+# positions 0 .. max(1, k/4)-1 first and the remaining positions only for
+# sequences that accept all of those.  Outputs must equal the one-pass
+# results (with accept_prob) exactly, whichever schedule runs.
+def _no_prob_case(case):
+    if case in ("llama_chain", "deepseek_chain", "mtp_chain"):
+        return W.make_inputs(case, 3)
+    if case == "row draw":
+        return W.chain_inputs(300, 2, 60000, W.F32, 31, target_sigma=3.0, draft_sigma=(0.2, 1.5))
+    if case == "acceptance kernel":
+        return W.chain_inputs(200, 3, 128256, W.BF16, 32, target_sigma=3.0, draft_sigma=(0.2, 1.5))
+    if case == "temperature 0 mix, two phases":
+        temps = np.where(np.arange(40) % 3 == 0, 0.0, 0.8).astype(np.float32)
+        inp = W.chain_inputs(40, 8, 128256, W.BF16, 33, target_sigma=3.0, draft_sigma=(0.05, 1.0), temperature=temps)
+        top = np.argmax(W.values(inp["target_logits"], W.BF16), axis=-1)
+        inp["draft_tokens"][::3] = top[::3, :8]      # greedy sequences that accept
+        inp["draft_tokens"][3, 1] = top[3, 0]        # ... and one that stops at position 1
+        return inp
+    if case == "64 drafts, two phases":
+        return W.chain_inputs(8, 64, 65536, W.BF16, 34, target_sigma=1.0, draft_sigma=(0.01, 0.3))
+    if case == "16 drafts element loads, two phases":
+        return W.chain_inputs(12, 16, 100001, W.F32, 35, target_sigma=2.0, draft_sigma=(0.05, 0.5))
+    if case == "row draw, two phases":
+        return W.chain_inputs(256, 6, 30000, W.F32, 36, target_sigma=3.0, draft_sigma=(0.1, 1.0))
+    if case == "acceptance kernel, two phases":
+        return W.chain_inputs(130, 6, 128256, W.BF16, 37, target_sigma=3.0, draft_sigma=(0.1, 1.0))
+    raise ValueError(case)
+
+
+NO_PROB = ["llama_chain", "deepseek_chain", "mtp_chain", "row draw", "acceptance kernel",
+           "temperature 0 mix, two phases", "64 drafts, two phases", "16 drafts element loads, two phases",
+           "row draw, two phases", "acceptance kernel, two phases"]
+
+
+@pytest.mark.parametrize("case", NO_PROB)
+def test_chain_without_accept_prob(svl, orc, case):
+    inp = _no_prob_case(case)
+    if case.endswith("two phases") or case == "deepseek_chain":
+        assert inp["k"] >= 6 and 2 * inp["B"] * inp["k"] * inp["V"] * (2 if inp["dtype"] == W.BF16 else 4) >= 128 << 20
+    full = run_chain(svl, inp)
+    ref = orc.verify_chain(inp)
+    lean = run_chain(svl, inp, accept_prob=False)
+    assert lean["accept_prob"] is None
+    for key in ("accepted_len", "emitted"):
+        np.testing.assert_array_equal(lean[key], full[key], err_msg=key)
+    stats = compare_chain(inp, lean, ref, f"no accept_prob {case}")
+    _record("chain", f"no accept_prob {case}", dict(stats, mean_accepted=float(lean["accepted_len"].mean())))
+
+
 # ------------------------------------------------------------ NEXT rows ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
