@@ -124,6 +124,10 @@ size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt);
  * ascending token ids with u[b][k]: from max(0, P_target,a - P_draft,a)
  * renormalised when a_b < k (from P_target,a if that residual is empty), from
  * P_target,k when a_b == k: y = min{ m : sum_{v<=m} w_v > u * sum_v w_v }.
+ *
+ * Without accept_prob, from k >= 6 and 128 MiB of draft and target rows
+ * 0..k-1, the rows of positions max(1, k/4) and later are read only for the
+ * sequences that accept all drafts before them.  The outputs are the same.
  */
 sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
                           const int32_t *draft_tokens, const void *draft_logits,
@@ -173,6 +177,11 @@ sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt,
  * Node i >= 1 is accepted when its parent is accepted and its token equals
  * the lowest-index argmax of its parent's row; the chosen node is the deepest
  * accepted node, the lowest index among equally deep ones.
+ *
+ * From 96 MiB of rows the root rows are read first, then only the rows of
+ * nodes whose depth-1 ancestor is accepted (from 192 MiB and N >= 48: nodes
+ * of depth 1-2 below an accepted depth-1 node, then deeper nodes below an
+ * accepted depth-3 node).  The outputs are the same.
  */
 sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
                          const int32_t *node_tokens, const int32_t *parent, int parent_stride,
