@@ -96,6 +96,37 @@ def test_graph_capture_and_replay(svl, orc, B, k):
         compare_chain(other, _np(eager), orc.verify_chain(other), f"eager between replays {rep}")
 
 
+def test_graph_replay_chain_two_phases(svl, orc):
+    """sv_verify_chain without accept_prob at a size that streams positions
+    0..1 first and the rest only for sequences accepting both (k = 8, 164 MB
+    of rows), captured once and replayed on inputs with other acceptance
+    patterns, with eager calls in between."""
+    import torch
+
+    B, k, V = 40, 8, 128256
+    sets = [W.chain_inputs(B, k, V, W.BF16, s, target_sigma=3.0, draft_sigma=sig)
+            for s, sig in ((81, (0.05, 0.6)), (82, (0.5, 2.5)))]
+    assert 2 * B * k * V * 2 >= 128 << 20
+    static = chain_tensors(sets[0])
+    ws = torch.zeros(svl.chain_workspace_bytes(B, k, V, W.BF16), dtype=torch.uint8, device="cuda")
+    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+               emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"), accept_prob=None)
+    g = _capture(lambda: svl.verify_chain(static["draft_tokens"], static["draft_logits"], static["target_logits"],
+                                          static["temperature"], static["uniforms"], workspace=ws, out=out))
+
+    def check(inp, rep):
+        compare_chain(inp, _np(out), orc.verify_chain(inp), f"two-phase graph replay {rep}")
+
+    def eager(inp, rep):
+        t = chain_tensors(inp)
+        e = svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                             t["uniforms"], accept_prob=False)
+        torch.cuda.synchronize()
+        compare_chain(inp, _np(e), orc.verify_chain(inp), f"two-phase eager {rep}")
+
+    _replay_each(g, static, sets + sets[:1], chain_tensors, check, eager)
+
+
 def test_two_streams_concurrently(svl, orc):
     """Two batches on two streams, each with its own workspace, in flight
     together for several rounds."""
