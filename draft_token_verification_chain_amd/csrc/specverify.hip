@@ -74,13 +74,15 @@ int64_t final_chunks(int V, sv_dtype dt) {
 constexpr int64_t kInlineAcceptMaxBlocks = 2048;
 
 // Chains without accept_prob stream their rows in two phases (positions
-// 0 .. max(1, k/4)-1, then the rest for sequences accepting all of those)
-// from this many drafts and this many bytes of rows on.  The second phase
-// costs about 5 us beyond its rows: at k = 8 (265 MB, 28% of sequences past
-// position 1) the step gains 21%, at k = 4 (131 MB, 56% past position 0) it
-// loses 5%.
+// 0 .. max(1, k/4)-1, then, after chain_prefix has flagged the sequences
+// that accept all of those, the rest for those sequences only) from this many
+// drafts and this many bytes of rows on.  The flag kernel and the second
+// launch cost about 6 us: at k = 8 (265 MB, 28% of sequences past position
+// 1) the step gains 24%, at k = 4 (131 MB, 56% past position 0) it loses 2%.
 constexpr int kChainTwoPhaseMinK = 6;
 constexpr int64_t kChainTwoPhaseMinBytes = int64_t(128) << 20;
+constexpr int kChainFirstPhaseDiv = 4;
+constexpr int kChainRestTilesPerWave = 1;
 
 // The final draw runs one workgroup per sequence (chain_row_draw_kernel) from
 // this many sequences on, for rows of at most kRowDrawMaxSegs segments: one
@@ -92,7 +94,7 @@ constexpr int kRowDrawMinRows = 256;
 // every sequence, their logits at the draft tokens, the final draw's
 // descriptors, segment masses and chunk argmaxes.
 struct ChainLayout {
-    size_t part, gathered, info, segs, chunkarg, total;
+    size_t part, gathered, info, segs, chunkarg, go, total;
 };
 
 ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
@@ -102,7 +104,8 @@ ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
     L.info = align_up(L.gathered + sizeof(float) * static_cast<size_t>(2) * B * k);
     L.segs = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
     L.chunkarg = align_up(L.segs + sizeof(Partial) * static_cast<size_t>(B) * segments_per_row(V, dt));
-    L.total = align_up(L.chunkarg + sizeof(Partial) * static_cast<size_t>(B) * final_chunks(V, dt));
+    L.go = align_up(L.chunkarg + sizeof(Partial) * static_cast<size_t>(B) * final_chunks(V, dt));
+    L.total = align_up(L.go + sizeof(int32_t) * static_cast<size_t>(B));
     return L;
 }
 
@@ -221,20 +224,25 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
         const int groups = static_cast<int>(blocks_for_waves(nT));
         const int s = accept_prob == nullptr && k >= kChainTwoPhaseMinK && rows_bytes >= kChainTwoPhaseMinBytes &&
                               static_cast<int64_t>(B) * 2 * k * groups <= kMaxGrid
-                          ? std::max(1, k / 4)
+                          ? std::max(1, k / kChainFirstPhaseDiv)
                           : k;
         const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * s * nT);
         st = launch("chain_rowstats", sv::chain_rowstats_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
                     dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, 0, s, V, nT, part, gathered);
         if (st != SV_OK) return st;
         if (s < k) {
-            // about two workgroups per row
-            const int tpw = std::max(1, (nT + 2 * sv::kWavesPerBlock - 1) / (2 * sv::kWavesPerBlock));
+            auto* go = reinterpret_cast<int32_t*>(ws + L.go);
+            st = launch("chain_prefix", sv::chain_prefix_kernel<DT>,
+                        dim3(static_cast<unsigned>((B + sv::kAccWaves - 1) / sv::kAccWaves)),
+                        dim3(sv::kAccWaves * sv::kWave), stream, tokens, temperature, uniforms, B, k, s, V, nT,
+                        static_cast<const Partial*>(part), static_cast<const float*>(gathered), go);
+            if (st != SV_OK) return st;
+            const int tpw = kChainRestTilesPerWave;
             const int rest_groups = (nT + sv::kWavesPerBlock * tpw - 1) / (sv::kWavesPerBlock * tpw);
             st = launch("chain_rowstats_rest", sv::chain_rowstats_rest_kernel<DT, VEC, kU>,
                         dim3(static_cast<unsigned>(static_cast<int64_t>(B) * 2 * (k - s) * rest_groups)),
-                        dim3(sv::kBlock), stream, target, draft, temperature, uniforms, tokens, B, k, s, V, nT,
-                        rest_groups, tpw, part, gathered);
+                        dim3(sv::kBlock), stream, target, draft, temperature, tokens, static_cast<const int32_t*>(go),
+                        B, k, s, V, nT, rest_groups, tpw, part, gathered);
             if (st != SV_OK) return st;
         }
     }

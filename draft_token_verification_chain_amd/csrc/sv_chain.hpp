@@ -207,35 +207,44 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     return a;
 }
 
+// Between the two phases of a chain's rowstats: whether each sequence
+// accepts all of its drafts 0 .. s-1 (one wave per sequence, kAccWaves per
+// workgroup), by accept_sequence over those positions, which is the final
+// acceptance's own arithmetic, so the two agree on them.
+constexpr int kAccWaves = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kAccWaves * kWave) void chain_prefix_kernel(
+    const int32_t* __restrict__ tokens, const float* __restrict__ temperature, const float* __restrict__ uniforms,
+    int B, int k, int s, int V, int nT, const Partial* __restrict__ part, const float* __restrict__ gathered,
+    int32_t* __restrict__ go) {
+    __shared__ int s_r[kAccWaves][2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[kAccWaves][2 * SV_MAX_DRAFTS];
+    const int w = threadIdx.x / kWave;
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kAccWaves + w;
+    if (b >= B) return;  // whole waves only; the kernel has no workgroup barrier
+    const int a = accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, s, false,
+                                      nullptr, nullptr, nullptr, s_r[w], s_s[w], nullptr);
+    if (lane_id() == 0) go[b] = a == s;
+}
+
 // The second phase of a chain's rowstats: the rows of positions s .. k-1 of
-// the sequences whose drafts 0 .. s-1 are all accepted.  Wave 0 of every
-// workgroup finds that with accept_sequence over those positions, which is
-// the final acceptance's own arithmetic, so the two agree on them.  One
+// the sequences that chain_prefix found to accept all drafts 0 .. s-1.  One
 // workgroup per (sequence, row, group of kWavesPerBlock * tpw tiles), the
 // group fastest; the rows are the target rows of positions s .. k-1, then the
-// draft rows.  Each wave takes tpw tiles in turn: the check costs about as
-// much as streaming a few tiles, so a workgroup checks once for many.
+// draft rows.
 template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kBlock) void chain_rowstats_rest_kernel(
     const void* __restrict__ target, const void* __restrict__ draft, const float* __restrict__ temperature,
-    const float* __restrict__ uniforms, const int32_t* __restrict__ tokens, int B, int k, int s, int V, int nT,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ go, int B, int k, int s, int V, int nT,
     int groups, int tpw, Partial* __restrict__ part, float* __restrict__ gathered) {
-    __shared__ int s_r[2 * SV_MAX_DRAFTS];
-    __shared__ double s_s[2 * SV_MAX_DRAFTS];
-    __shared__ int s_go;
     const int rest = k - s;
     const int64_t per_seq = static_cast<int64_t>(groups) * 2 * rest;
     const int64_t b = blockIdx.x / per_seq;
+    if (!go[b]) return;
     const int rem = static_cast<int>(blockIdx.x - b * per_seq);
     const int z = rem / groups;
     const int group = rem - z * groups;
-    if (threadIdx.x < kWave) {
-        const int a = accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, s, false,
-                                          nullptr, nullptr, nullptr, s_r, s_s, nullptr);
-        if (lane_id() == 0) s_go = a == s;
-    }
-    __syncthreads();
-    if (!s_go) return;
     const bool is_target = z < rest;
     const int64_t rr = b * k + s + (is_target ? z : z - rest);
 #pragma unroll 1
@@ -249,7 +258,6 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_rest_kernel(
 
 // One wave per sequence, kAccWaves sequences per workgroup: the acceptance
 // of every sequence, its outputs and the descriptor of its final draw.
-constexpr int kAccWaves = 4;
 
 template <int DT>
 __global__ __launch_bounds__(kAccWaves * kWave) void chain_accept_kernel(
