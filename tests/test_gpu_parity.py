@@ -486,6 +486,20 @@ def test_chain_without_accept_prob(svl, orc, case):
     _record("chain", f"no accept_prob {case}", dict(stats, mean_accepted=float(lean["accepted_len"].mean())))
 
 
+@pytest.mark.parametrize("fill", [0xFF, 0x7F], ids=["ff", "7f"])
+def test_chain_two_phases_on_a_garbage_workspace(svl, orc, fill):
+    """The second phase leaves the partials of skipped positions as the
+    workspace held them: NaNs (0xFF) or huge values (0x7F) there must never
+    reach the outputs."""
+    import torch
+
+    inp = _no_prob_case("temperature 0 mix, two phases")
+    ws = torch.full((svl.chain_workspace_bytes(inp["B"], inp["k"], inp["V"], inp["dtype"]),), fill,
+                    dtype=torch.uint8, device="cuda")
+    got = run_chain(svl, inp, accept_prob=False, workspace=ws)
+    compare_chain(inp, got, orc.verify_chain(inp), f"two phases, workspace {fill:#x}")
+
+
 # ------------------------------------------------------------ NEXT rows ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
