@@ -208,14 +208,11 @@ def main():
         # k == 0: one workgroup per row from 256 rows of at most 256 segments
         # (64 vectors of 16 bytes each)
         nseg = -(-(-(-V // (16 // es))) // 64)  # ceil(ceil(V / (16 / es)) / 64)
-        dominant = ("chain_rowstats" if k > 0 else
-                    "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part")
-        # every draft row and target rows 0..k-1 once (k == 0: the sampled row);
-        # without accept_prob, from 6 drafts and 128 MiB of rows the library
-        # streams positions 0..s-1 first and the rest only for sequences that
-        # accept all of them (counted below, from the outcome)
+        draw_kernel = "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part"
+        # every draft row and target rows 0..k-1 once; without accept_prob,
+        # from 6 drafts and 128 MiB of rows the library streams positions
+        # 0..s-1 first and the rest only for sequences that accept all of them
         chain_s = (max(1, k // 4) if not args.accept_prob and k >= 6 and 2 * B * k * V * es >= 128 << 20 else k)
-        dominant_bytes = 2 * B * chain_s * V * es if k > 0 else B * V * es
     elif kind == "greedy":
         k = inp["k"]
         out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
@@ -229,8 +226,6 @@ def main():
         # rows 0..s-1 of every sequence; at 256 MiB of rows and more the library
         # reads rows s..k only for sequences accepting their first s drafts
         s_first = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1
-        dominant = "greedy_rows"
-        dominant_bytes = B * s_first * V * es
     elif kind == "tree_sampled":
         N = inp["N"]
         md = inp["max_depth"]
@@ -244,11 +239,7 @@ def main():
             svl.verify_tree_sampled(t["node_tokens"], t["parent"], md, t["draft_logits"], t["target_logits"],
                                     t["temperature"], t["uniforms"], workspace=ws, out=out)
         units = B * (N - 1)                 # verified draft nodes per step
-        dominant = "tree_rowstats"
-        # every node's target row and the draft rows of inner nodes (the walk's
-        # passes over the rows of the nodes it visits come on top)
         inner = int(np.count_nonzero(np.bincount(inp["parent"][1:], minlength=N)))
-        dominant_bytes = B * (N + inner) * V * es
     else:
         N = inp["N"]
         md = inp["max_depth"]
@@ -267,8 +258,6 @@ def main():
         # depth-3 node); those rows are counted below, from the outcome
         tree_two_phase = N > 1 and B * N * V * es >= 96 << 20
         tree_ranges = ([(1, 2), (3, N)] if B * N * V * es >= 192 << 20 and N >= 48 else [(1, N)])
-        dominant = "tree_rows_rest" if tree_two_phase else "argmax_rows"
-        dominant_bytes = B * N * V * es
 
     unit = "sampled tokens/s" if kind == "chain" and inp["k"] == 0 else "verified draft tokens/s"
     for i in range(args.warmup):
@@ -281,23 +270,37 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # bytes read beyond the dominant kernel's, from this batch's outcome
-    # (identical in every copy): the chain's final draw, the greedy chain's
-    # second phase, the greedy tree's root rows (its second phase is then the
-    # dominant kernel, whose bytes also depend on the outcome)
-    final_bytes = 0
+    # algorithmic bytes per launch of every streaming kernel of the step, and
+    # its launches per step; where they depend on the outcome (the rows a
+    # draw or a later phase reads), from this batch's (identical in every copy)
+    kernel_bytes, kernel_launches = {}, {}
     if kind == "chain":
         a = out["accepted_len"].cpu().numpy()
         T = inp["temperature"]
         k = inp["k"]
+        if k > 0:
+            kernel_bytes["chain_rowstats"] = 2 * B * chain_s * V * es
+            if chain_s < k:
+                kernel_bytes["chain_rowstats_rest"] = int((a >= chain_s).sum()) * 2 * (k - chain_s) * V * es
+        # the final draw: both rows at a rejection, the bonus row after full
+        # acceptance, the row's argmax at temperature 0 (with no drafts: row 0)
+        draw = 0
         for b in range(B):
             if T[b] > 0:
-                final_bytes += (2 if a[b] < k else 1) * V * es
+                draw += (2 if a[b] < k else 1) * V * es
             elif a[b] == k:
-                final_bytes += V * es
-        if chain_s < k:   # the second phase's rows
-            final_bytes += int((a >= chain_s).sum()) * 2 * (k - chain_s) * V * es
-    elif kind == "tree" and tree_two_phase:
+                draw += V * es
+        kernel_bytes[draw_kernel] = draw
+    elif kind == "greedy":
+        kernel_bytes["greedy_rows"] = B * s_first * V * es
+        if s_first <= inp["k"]:
+            a = out["accepted_len"].cpu().numpy()
+            kernel_bytes["greedy_rows_rest"] = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es
+    elif kind == "tree_sampled":
+        # every node's target row and the draft rows of inner nodes (the walk's
+        # passes over the rows of the nodes it visits come on top, uncounted)
+        kernel_bytes["tree_rowstats"] = B * (N + inner) * V * es
+    elif tree_two_phase:
         # each later phase lists the nodes of its depth range whose ancestor at
         # the range's first depth is accepted (node acceptance from the rows'
         # argmax, host-side bookkeeping for the byte count only)
@@ -318,13 +321,12 @@ def main():
                     while depth[a] > lo:
                         a = par[a]
                     rest_rows += int(lo <= depth[n] <= hi and acc[a])
-        dominant_bytes = rest_rows * V * es / len(tree_ranges)   # per tree_rows_rest launch
-        final_bytes = B * V * es + rest_rows * V * es - dominant_bytes  # root rows and the other launches
-    elif kind == "greedy" and s_first <= inp["k"]:
-        a = out["accepted_len"].cpu().numpy()
-        final_bytes = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es
-    # with no drafts the final draw is the dominant pass itself (its row counted once)
-    step_bytes = final_bytes if kind == "chain" and inp["k"] == 0 else dominant_bytes + final_bytes
+        kernel_bytes["tree_root_rows"] = B * V * es
+        kernel_bytes["tree_rows_rest"] = rest_rows * V * es / len(tree_ranges)
+        kernel_launches["tree_rows_rest"] = len(tree_ranges)
+    else:
+        kernel_bytes["argmax_rows"] = B * N * V * es
+    step_bytes = sum(v * kernel_launches.get(name, 1) for name, v in kernel_bytes.items())
 
     def timed(profiled: bool) -> float:
         """K steps back to back behind a ~20 ms spin kernel (so that host launch
@@ -354,6 +356,12 @@ def main():
     s_per_step = ms_per_step * 1e-3
 
     kernels = {name: dict(launches=n, avg_us=1e3 * tot / max(n, 1)) for name, (n, tot) in prof.items()}
+    missing = [name for name in kernel_bytes if name not in kernels]
+    if missing:
+        raise RuntimeError(f"bench.py expects kernels the library did not launch: {missing}")
+    # the dominant kernel: the streaming kernel with the most time per step
+    dominant = max(kernel_bytes, key=lambda name: kernels[name]["avg_us"] * kernel_launches.get(name, 1))
+    dominant_bytes = kernel_bytes[dominant]
     dom_us = kernels[dominant]["avg_us"]
     achieved = dominant_bytes / (dom_us * 1e-6) / 1e9
     traffic = load_traffic(dominant, args.workload)
@@ -384,6 +392,7 @@ def main():
         # every sequence emits its accepted tokens plus one final token
         "emitted_tokens_per_s": float(out["accepted_len"].sum().item() + B) / s_per_step,
         "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
+        "kernels_bytes_per_launch": {n: int(v) for n, v in kernel_bytes.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "bytes_per_launch": dominant_bytes, "avg_launch_us": dom_us,
