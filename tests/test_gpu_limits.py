@@ -105,6 +105,36 @@ def test_tree_with_max_nodes(svl, orc):
         np.testing.assert_array_equal(got[key], ref[key])
 
 
+def test_tree_three_phases_with_max_nodes(svl, orc):
+    """1024 nodes and 256 MiB of rows: root rows, depths 1-2 below an accepted
+    depth-1 node, then deeper nodes below an accepted depth-3 node."""
+    parent = W.random_tree(1024, 28, max_branch=8, max_depth=12)
+    inp = W.tree_inputs(4, 1024, 32768, W.BF16, 28, parent=parent, max_depth=12, match_p=0.9)
+    assert 4 * 1024 * 32768 * 2 >= 192 << 20
+    got, ref = run_tree(svl, inp), orc.verify_tree(inp)
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(got[key], ref[key])
+    assert ref["accepted_len"].max() >= 4
+
+
+def test_greedy_two_phases_at_max_vocabulary(svl, orc):
+    inp = W.greedy_inputs(24, 5, VMAX, W.BF16, 29)
+    assert 24 * 6 * VMAX * 2 >= 256 << 20
+    got, ref = run_greedy(svl, inp), orc.verify_greedy(inp)
+    np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+    np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+
+
+def test_chain_two_phases_at_max_vocabulary(svl, orc):
+    """Without accept_prob: positions 0-1, then 2-7 for sequences accepting both."""
+    inp = W.chain_inputs(4, 8, VMAX, W.F32, 30, target_sigma=3.0, zipf_s=1.1, draft_sigma=[0.02, 3.0, 0.02, 3.0])
+    assert 2 * 4 * 8 * VMAX * 4 >= 128 << 20
+    print("[case] chain two phases at V = 2^20", flush=True)
+    got = run_chain(svl, inp, accept_prob=False)
+    ref = orc.verify_chain(inp)
+    _record("chain", "two phases at V = 2^20", compare_chain(inp, got, ref, "two phases at V = 2^20"))
+
+
 def test_sampled_tree_at_max_vocabulary(svl, orc):
     inp = W.sampled_tree_inputs(2, 16, VMAX, W.F32, 28, draft_sigma=(0.5, 2.0))
     print("[case] sampled tree Vmax", flush=True)
