@@ -238,14 +238,19 @@ def random_tree(N: int, seed: int, max_branch: int = 4, max_depth: int = 6) -> n
 
 def tree_inputs(B: int, N: int, V: int, dtype: int, seed: int, *,
                 target_sigma: float = 2.0, max_branch: int = 4, max_depth: int = 6,
-                match_p: float = 0.6, parent: np.ndarray | None = None) -> dict:
+                match_p: float = 0.6, parent: np.ndarray | None = None,
+                distinct_siblings: bool = False) -> dict:
     """Inputs for greedy static-tree verification.
 
     One parent array shared by all B sequences; target logits per node
     t[b, n, :] = target_sigma * N(0,1) rounded to dtype (row n is the target's
     prediction for the children of node n).  Node 0 is the root (its token is
     never matched); node i >= 1 carries the first argmax of its parent's row with
-    probability match_p, otherwise a uniform other token.
+    probability match_p, otherwise a uniform other token.  With
+    distinct_siblings, as the draft's top candidates are in a draft tree, the
+    children of a node carry distinct tokens: a child takes the argmax with
+    probability match_p only if no earlier sibling has it, and otherwise a
+    uniform token that differs from the argmax and from its earlier siblings'.
     """
     if parent is None:
         parent = random_tree(N, seed, max_branch, max_depth)
@@ -257,9 +262,21 @@ def tree_inputs(B: int, N: int, V: int, dtype: int, seed: int, *,
         target[b] = to_dtype(target_sigma * rt.standard_normal((N, V), dtype=np.float32), dtype)
         top = np.argmax(values(target[b], dtype), axis=-1)
         tokens[b, 0] = int(rx.integers(0, V))
+        taken: dict[int, set] = {}
         for i in range(1, N):
             g = int(top[parent[i]])
-            tokens[b, i] = g if rx.random() < match_p else _other_token(rx, g, V)
+            if not distinct_siblings:
+                tokens[b, i] = g if rx.random() < match_p else _other_token(rx, g, V)
+                continue
+            used = taken.setdefault(int(parent[i]), set())
+            if g not in used and rx.random() < match_p:
+                y = g
+            else:
+                y = _other_token(rx, g, V)
+                while y in used and len(used) < V - 1:
+                    y = _other_token(rx, g, V)
+            used.add(y)
+            tokens[b, i] = y
     depth = np.zeros(N, dtype=np.int64)
     for i in range(1, N):
         depth[i] = depth[parent[i]] + 1
@@ -364,7 +381,7 @@ WORKLOADS = {
     "deepseek_chain": dict(name="DeepSeek-scale chain verify", kind="chain", B=32, k=8, V=129280, dtype=F32,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=(0.3, 1.3)),
     "eagle_tree": dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
-            target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6),
+            target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6, distinct_siblings=True),
     # one draft token per sequence, as in the single-token multi-token-prediction
     # schedule (the target scores 2 tokens per sequence of the decode batch)
     "mtp_chain": dict(name="MTP single-token verify", kind="chain", B=256, k=1, V=129280, dtype=BF16,
