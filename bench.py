@@ -297,9 +297,10 @@ def main():
             a = out["accepted_len"].cpu().numpy()
             kernel_bytes["greedy_rows_rest"] = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es
     elif kind == "tree_sampled":
-        # every node's target row and the draft rows of inner nodes (the walk's
-        # passes over the rows of the nodes it visits come on top, uncounted)
-        kernel_bytes["tree_rowstats"] = B * (N + inner) * V * es
+        # the target and draft rows of every inner node (a leaf's rows are read
+        # only when a walk ends there; those and the walk's passes over the rows
+        # of the nodes it visits come on top, uncounted)
+        kernel_bytes["tree_rowstats"] = B * 2 * inner * V * es
     elif tree_two_phase:
         # each later phase lists the nodes of its depth range whose ancestor at
         # the range's first depth is accepted (node acceptance from the rows'

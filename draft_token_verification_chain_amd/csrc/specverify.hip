@@ -111,11 +111,12 @@ ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
 
 // The sampled-tree workspace: partials of every node's two rows, the
 // children's gathered logits, the walk's double-buffered state and pass
-// partial sums (P slices per sequence), the final draw's segment masses and
-// every node's combined normalisers.
+// partial sums (P slices per sequence), the final draw's segment masses,
+// every node's combined normalisers and the per-segment statistics of the
+// leaf a walk ends at.
 struct TreeSampledLayout {
     int P;
-    size_t part, tg, dg, state, z, tsegs, norm, total;
+    size_t part, tg, dg, state, z, tsegs, norm, leaf, total;
 };
 
 TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
@@ -132,7 +133,8 @@ TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
     L.z = align_up(L.state + sizeof(sv::WalkState) * 2 * static_cast<size_t>(B));
     L.tsegs = align_up(L.z + sizeof(double) * 2 * static_cast<size_t>(B) * L.P);
     L.norm = align_up(L.tsegs + sizeof(float) * static_cast<size_t>(B) * nseg);
-    L.total = align_up(L.norm + sizeof(sv::NodeNorm) * bn);
+    L.leaf = align_up(L.norm + sizeof(sv::NodeNorm) * bn);
+    L.total = align_up(L.leaf + sizeof(Partial) * static_cast<size_t>(B) * nseg);
     return L;
 }
 
@@ -562,6 +564,7 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
     auto* z = reinterpret_cast<double*>(ws + L.z);
     auto* tsegs = reinterpret_cast<float*>(ws + L.tsegs);
     auto* norm = reinterpret_cast<sv::NodeNorm*>(ws + L.norm);
+    auto* leafpart = reinterpret_cast<Partial*>(ws + L.leaf);
     const unsigned blocks = static_cast<unsigned>(blocks_for_waves(static_cast<int64_t>(2) * B * N * nT));
     auto rowstats = dt == SV_BF16 ? (vec ? sv::tree_rowstats_kernel<SV_BF16, true, kU>
                                          : sv::tree_rowstats_kernel<SV_BF16, false, kU>)
@@ -579,7 +582,8 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                     static_cast<const float*>(tg), static_cast<const float*>(dg),
                     static_cast<const sv::WalkState*>(state + (r & 1) * B), state + ((r + 1) & 1) * B,
                     static_cast<const double*>(z + static_cast<size_t>(r & 1) * B * L.P),
-                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, norm, L.P, r == 0 ? 1 : 0, accepted_len,
+                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, norm, leafpart, L.P, r == 0 ? 1 : 0,
+                    accepted_len,
                     emitted, accepted_nodes);
         if (st != SV_OK) return st;
     }

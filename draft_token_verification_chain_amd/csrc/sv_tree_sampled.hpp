@@ -18,7 +18,9 @@ namespace sv {
 // pass over the node's two rows.
 
 // Rows 0 .. B*N-1 are target rows (b, n), rows B*N .. 2*B*N-1 draft rows.
-// The draft row of a leaf is never needed and is skipped.
+// A leaf's rows are skipped: its draft row is never needed, and its target
+// row only if a walk ends at the leaf, which then computes that row's
+// statistics itself.
 // The wave streaming tile 0 of inner node n's draft row also gathers, for
 // every child i of n, the target and draft logits of row n at i's token into
 // tg[b][i] and dg[b][i] (0 for a token outside [0, V)), so that the walk's
@@ -40,13 +42,13 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
     const int64_t rr = is_target ? r : r - nbn;
     const int64_t b = rr / N;
     const int n = static_cast<int>(rr - b * N);
-    if (!is_target) {
+    {
         const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
         bool kid = false;
         for (int i = n + 1 + lane_id(); i < N; i += kWave) {
             const bool child = par[i] == n;
             kid |= child;
-            if (child && tile == 0) {
+            if (!is_target && child && tile == 0) {
                 const int y = node_tokens[b * N + i];
                 const bool yok = static_cast<unsigned>(y) < static_cast<unsigned>(V);
                 tg[b * N + i] = yok ? load_elem<DT>(target, rr * static_cast<int64_t>(V) + y) : 0.f;
@@ -62,6 +64,21 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
                           ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
                           : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
     if (lane_id() == 0) part[r * nT + tile] = p;
+}
+
+// The statistics of a leaf's target row, which tree_rowstats skips, for a
+// walk that ends at the leaf: one partial per segment (a segment is one
+// vector per lane), segments seg0, seg0 + stride, ... into out[segment].
+template <int DT, bool VEC>
+__device__ __forceinline__ void leaf_row_partials(const void* target, int64_t b, int N, int n, int V, int64_t nseg,
+                                                  float T, int64_t seg0, int64_t stride, Partial* out) {
+    const int64_t row_elem = (b * N + n) * static_cast<int64_t>(V);
+    for (int64_t g = seg0; g < nseg; g += stride) {
+        const Partial p = tile_is_full<VEC, 1>(g, V, Elem<DT>::per_vec)
+                              ? rowstats_tile<DT, VEC, 1, VEC>(target, row_elem, V, g, T)
+                              : rowstats_tile<DT, VEC, 1, false>(target, row_elem, V, g, T);
+        if (lane_id() == 0) out[g] = p;
+    }
 }
 
 // One workgroup per sequence walks its tree; each thread holds kWalkSlots
@@ -272,7 +289,8 @@ enum WalkPhase : int {
     kWalkPass = 2,   // a rejection advanced c; the partial sums of Z(c) are in z
     kWalkPick = 3,   // the final distribution's segment masses are written; the pick remains
     kWalkDone = 4,
-    kWalkStuck = 5   // a case the rounds leave to the one-workgroup walk (an empty final residual)
+    kWalkStuck = 5,  // a case the rounds leave to the one-workgroup walk (an empty final residual)
+    kWalkLeaf = 6    // at leaf `node`, whose target-row statistics the last round computed
 };
 
 // Normalisers of a node's target and draft rows, as the walk combines them
@@ -363,6 +381,7 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     __shared__ double s_norm[2];  // S_t, S_d of the current node
     __shared__ int s_ref[2];      // R_t, R_d (at temperature 0: the two argmaxes)
     __shared__ int s_bad, s_accept;
+    __shared__ Partial s_lp[kWalkMaxSegs];  // a leaf's target-row statistics, per segment
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     const int lane = lane_id();
@@ -420,18 +439,26 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
                 s_cld[rank] = yok ? load_elem<DT>(draft, row + y) : 0.f;
             }
         }
+        // a leaf's target row was skipped by tree_rowstats: its statistics here
+        const bool leaf = nkids == 0;
+        if (leaf) {
+            leaf_row_partials<DT, VEC>(target, b, N, n, V, nseg, T, wave, kWalkWaves, s_lp);
+            __syncthreads();
+        }
         if (wave == 0) {
             const bool is_draft = lane >= 32;
-            const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+            const bool valid = !(leaf && is_draft);  // a leaf's draft row is never needed
+            const Partial* pr = leaf ? s_lp : part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+            const int cnt = leaf ? static_cast<int>(nseg) : nT;
             Partial q[kBatch];
-            group_load(pr, nT, 32, true, q);
+            group_load(pr, cnt, 32, valid, q);
             int r;
             double sum;
             ArgMax am;
             if (sampled) {
-                group_reduce<true>(pr, nT, 32, true, q, r, sum, am);
+                group_reduce<true>(pr, cnt, 32, valid, q, r, sum, am);
             } else {
-                group_reduce<false>(pr, nT, 32, true, q, r, sum, am);
+                group_reduce<false>(pr, cnt, 32, valid, q, r, sum, am);
                 r = am.idx;
             }
             if ((lane & 31) == 0) {
@@ -549,7 +576,8 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ tg, const float* __restrict__ dg,
     const WalkState* __restrict__ st_in, WalkState* __restrict__ st_out, const double* __restrict__ z_in,
-    double* __restrict__ z_out, float* __restrict__ tsegs, NodeNorm* __restrict__ norm, int P, int first,
+    double* __restrict__ z_out, float* __restrict__ tsegs, NodeNorm* __restrict__ norm,
+    Partial* __restrict__ leafpart, int P, int first,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
     constexpr int VE = Elem<DT>::per_vec;
     __shared__ int s_par[SV_MAX_TREE_NODES];
@@ -703,9 +731,27 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     }
     const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
     const int nmask = (N + kWave - 1) / kWave;
+    bool leaf_now = false;
     for (;;) {
-        if (phase == kWalkEnter) {
-            if (cached && !first) {
+#pragma unroll
+        for (int q = 0; q < kRoundSlots; ++q) {
+            const int i = t + q * kRoundBlock;
+            const uint64_t km = __ballot(i < N && s_par[i] == n);
+            if (lane == 0 && wave + q * kRoundWaves < nmask) s_kids[wave + q * kRoundWaves] = km;
+        }
+        __syncthreads();
+        int nkids = 0;
+        for (int m = 0; m < nmask; ++m) nkids += __popcll(s_kids[m]);
+        if (phase == kWalkEnter && nkids == 0) {
+            // a leaf: tree_rowstats skipped its target row, whose statistics are
+            // computed below, the combination follows next round
+            phase = kWalkLeaf;
+            leaf_now = true;
+            break;
+        }
+        if (phase == kWalkEnter || phase == kWalkLeaf) {
+            const bool leaf = phase == kWalkLeaf;
+            if (cached && !first && !leaf) {
                 // combined in round 0; the thread holding node n shares them
 #pragma unroll
                 for (int q = 0; q < kRoundSlots; ++q) {
@@ -718,16 +764,18 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
                 }
             } else if (wave == 0) {
                 const bool is_draft = lane >= 32;
-                const Partial* pr = part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+                const bool valid = !(leaf && is_draft);  // a leaf's draft row is never needed
+                const Partial* pr = leaf ? leafpart + b * nseg : part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+                const int cnt = leaf ? static_cast<int>(nseg) : nT;
                 Partial qv[kBatch];
-                group_load(pr, nT, 32, true, qv);
+                group_load(pr, cnt, 32, valid, qv);
                 int r;
                 double sum;
                 ArgMax am;
                 if (sampled) {
-                    group_reduce<true>(pr, nT, 32, true, qv, r, sum, am);
+                    group_reduce<true>(pr, cnt, 32, valid, qv, r, sum, am);
                 } else {
-                    group_reduce<false>(pr, nT, 32, true, qv, r, sum, am);
+                    group_reduce<false>(pr, cnt, 32, valid, qv, r, sum, am);
                     r = am.idx;
                 }
                 if ((lane & 31) == 0) {
@@ -746,13 +794,6 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
             phase = kWalkTest;
             __syncthreads();  // s_ref and s_norm are reused at the next node
         }
-#pragma unroll
-        for (int q = 0; q < kRoundSlots; ++q) {
-            const int i = t + q * kRoundBlock;
-            const uint64_t km = __ballot(i < N && s_par[i] == n);
-            if (lane == 0 && wave + q * kRoundWaves < nmask) s_kids[wave + q * kRoundWaves] = km;
-        }
-        __syncthreads();
         const double lsum = t == 0 && sampled ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
         int next = -1, rank = 0;
         bool pass = false;
@@ -822,6 +863,12 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
             phase = kWalkPick;  // the masses are written below, the pick comes next round
         }
         break;
+    }
+    if (leaf_now) {
+        // the sequence's workgroups compute the leaf's target-row statistics,
+        // this one its share of the segments
+        leaf_row_partials<DT, VEC>(target, b, N, n, V, nseg, T, static_cast<int64_t>(j) * kRoundWaves + wave,
+                                   static_cast<int64_t>(P) * kRoundWaves, leafpart + b * nseg);
     }
     if (phase == kWalkPass || phase == kWalkPick) {
         // this workgroup's slice of the segments of node n's rows
