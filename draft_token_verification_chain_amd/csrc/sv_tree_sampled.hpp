@@ -25,7 +25,9 @@ namespace sv {
 // every child i of n, the target and draft logits of row n at i's token into
 // tg[b][i] and dg[b][i] (0 for a token outside [0, V)), so that the walk's
 // sibling tests need no dependent loads.
-template <int DT, bool VEC, int U>
+// A wave streams TPW consecutive tiles of one row, so that its parent scan,
+// a dependent load ahead of the tiles, is paid once per TPW tiles.
+template <int DT, bool VEC, int U, int TPW>
 __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __restrict__ target,
                                                                const void* __restrict__ draft,
                                                                const int32_t* __restrict__ parent, int parent_stride,
@@ -35,9 +37,10 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
                                                                float* __restrict__ tg, float* __restrict__ dg) {
     const int64_t gw = global_wave();
     const int64_t nbn = static_cast<int64_t>(B) * N;
-    if (gw >= 2 * nbn * nT) return;
-    const int64_t r = gw / nT;
-    const int64_t tile = gw - r * nT;
+    const int64_t wpr = (nT + TPW - 1) / TPW;  // waves per row
+    if (gw >= 2 * nbn * wpr) return;
+    const int64_t r = gw / wpr;
+    const int64_t tw = gw - r * wpr;
     const bool is_target = r < nbn;
     const int64_t rr = is_target ? r : r - nbn;
     const int64_t b = rr / N;
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
         for (int i = n + 1 + lane_id(); i < N; i += kWave) {
             const bool child = par[i] == n;
             kid |= child;
-            if (!is_target && child && tile == 0) {
+            if (!is_target && child && tw == 0) {
                 const int y = node_tokens[b * N + i];
                 const bool yok = static_cast<unsigned>(y) < static_cast<unsigned>(V);
                 tg[b * N + i] = yok ? load_elem<DT>(target, rr * static_cast<int64_t>(V) + y) : 0.f;
@@ -60,10 +63,15 @@ __global__ __launch_bounds__(kBlock) void tree_rowstats_kernel(const void* __res
     const void* base = is_target ? target : draft;
     const int64_t row_elem = rr * static_cast<int64_t>(V);
     const float T = temperature[b];
-    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
-                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
-                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
-    if (lane_id() == 0) part[r * nT + tile] = p;
+#pragma unroll 1
+    for (int i = 0; i < TPW; ++i) {
+        const int64_t tile = tw * TPW + i;
+        if (tile >= nT) break;
+        const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
+                              ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                              : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
+        if (lane_id() == 0) part[r * nT + tile] = p;
+    }
 }
 
 // The statistics of a leaf's target row, which tree_rowstats skips, for a
