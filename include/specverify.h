@@ -201,7 +201,8 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
  *                 target distribution)
  *   draft_logits  dt    [B][N][V]  row n: the draft distribution the children of n
  *                                  were drawn from (rows of leaves are not read)
- *   target_logits dt    [B][N][V]  row n: the target's prediction after node n
+ *   target_logits dt    [B][N][V]  row n: the target's prediction after node n (a
+ *                                  leaf's row is read only if the walk ends there)
  *   temperature   f32   [B]        >= 0; 0 means one-hot rows at the lowest-index argmax
  *   uniforms      f32   [B][N]     in [0,1): u[b][i] tests node i >= 1, u[b][0] drives
  *                                  the final draw
@@ -216,8 +217,12 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
  * renormalised (by P_target,n itself if that is empty).  When no child is kept
  * (or n is a leaf) the final token is drawn from r by the inverse CDF over
  * ascending token ids with u[b][0].  Token ids outside [0,V) are rejected.
- * One workgroup per sequence walks the tree after a streaming pass over all
- * target rows and the draft rows of inner nodes.
+ * A streaming pass reads the target and draft rows of inner nodes; a leaf's
+ * target row is read only when a walk ends at that leaf.  The walk then runs
+ * in a fixed number of launches, several workgroups per sequence, each launch
+ * testing siblings up to the next rejection and summing that rejection's
+ * residual mass; a last one-workgroup-per-sequence pass draws the final token
+ * or finishes any walk the launches did not complete.
  */
 sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt,
                                  const int32_t *node_tokens, const int32_t *parent, int parent_stride,

@@ -54,6 +54,7 @@ SHAPES = [
     (6, 64, 5000, W.BF16, 0.7),
     (5, 33, 4097, W.BF16, None),
     (3, 100, 1000, W.F32, 1.2),
+    (4, 24, 10000, W.BF16, 0.8),     # three tiles per row: an odd count, the last wave's second tile absent
     (4, 1, 2000, W.BF16, 0.9),       # the root alone: a plain draw from its target row
     (3, 64, 128257, W.BF16, 0.6),    # odd V: element loads, many segments
     (2, 40, 65536, W.F32, 0.5),
