@@ -1,0 +1,73 @@
+"""rocprof_summary.py and bench.py's use of its files (CPU only), on small
+synthetic rocprofv3 CSV files."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import rocprof_summary as rs  # noqa: E402
+
+KERNEL = "void sv::chain_rowstats_kernel<0, true, 8>(void const*, void const*, int)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+@pytest.mark.parametrize("full, short", [
+    (KERNEL, "chain_rowstats"),
+    ("void sv::(anonymous namespace)::tree_round_kernel<1, false>(int)", "tree_round"),
+    (COPY, COPY),
+])
+def test_short_name(full, short):
+    assert rs.short_name(full) == short
+
+
+def test_summary_scales_counters_by_the_plain_copy(tmp_path):
+    trace, fetch, write, out = (str(tmp_path / d) for d in ("trace", "fetch", "write", "out"))
+    _write_csv(os.path.join(trace, "bench_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [[KERNEL, 10, 214000, 21400, 60.0, 20000, 23000]])
+    mib = 256
+    # FETCH_SIZE counts half of a 256 MiB copy (scale 2); WRITE_SIZE all of it (scale 1); KiB per dispatch
+    _write_csv(os.path.join(fetch, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Value"],
+               [[COPY, mib * 1024 / 2], [KERNEL, 1000.0], [KERNEL, 3000.0]])
+    _write_csv(os.path.join(write, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Value"],
+               [[COPY, mib * 1024], [KERNEL, 10.0], [KERNEL, 30.0]])
+    subprocess.check_call([sys.executable, os.path.join(ROOT, "rocprof_summary.py"), "--trace", trace,
+                           "--fetch", fetch, "--write", write, "--workload", "w", "--prefix", "w",
+                           "--command", "python3 bench.py", "--out", out], stdout=subprocess.DEVNULL)
+    md = open(os.path.join(out, "w_kernel_trace.md")).read()
+    assert "| chain_rowstats | 10 | 21.40 | 20.00 | 23.00 | 60.0% |" in md
+    assert bench.kernel_source_digest() in md
+    rec = json.load(open(os.path.join(out, "chain_rowstats_w_traffic.json")))
+    assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["fetch_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == pytest.approx(20.0 * 1024)
+    assert rec["traffic_bytes_per_launch"] == pytest.approx(2000.0 * 2048 + 20.0 * 1024)
+    assert rec["kernel_source_digest"] == bench.kernel_source_digest()
+
+
+def test_bench_ignores_counters_taken_on_other_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"kernel_source_digest": bench.kernel_source_digest(), "traffic_bytes_per_launch": 123.0}
+    (prof / "k_w_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: rec["kernel_source_digest"])
+    assert bench.load_traffic("k", "w") == 123.0
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
+    assert bench.load_traffic("k", "w") is None
+    assert bench.load_traffic("missing", "w") is None
