@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
         _lib.svo_verify_tree.argtypes = (
             [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 4)
         _lib.svo_verify_tree_sampled.argtypes = (
-            [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 8 +
+            [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p] * 9 +
             [ctypes.c_double])
         _lib.svo_row_logz.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
         _lib.svo_row_argmax.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 2
@@ -150,11 +150,13 @@ def verify_tree_sampled(inp: dict, band_eps: float = BAND_EPS) -> dict:
     em = np.empty((B, md + 1), np.int32)
     nodes = np.empty((B, md + 1), np.int32)
     band = np.empty(B, np.int32)
+    mass = np.empty(B, np.float64)
     rc = lib().svo_verify_tree_sampled(B, N, V, dt, _ptr(tok), _ptr(par), stride, md, _ptr(d), _ptr(t), _ptr(T),
-                                       _ptr(u), _ptr(acc), _ptr(em), _ptr(nodes), _ptr(band), float(band_eps))
+                                       _ptr(u), _ptr(acc), _ptr(em), _ptr(nodes), _ptr(band), _ptr(mass),
+                                       float(band_eps))
     if rc != 0:
         raise ValueError(f"svo_verify_tree_sampled returned {rc}")
-    return dict(accepted_len=acc, emitted=em, accepted_nodes=nodes, band=band.astype(bool))
+    return dict(accepted_len=acc, emitted=em, accepted_nodes=nodes, band=band.astype(bool), final_mass=mass)
 
 
 def row_logz(logits: np.ndarray, dtype: int, temperature) -> np.ndarray:

@@ -420,26 +420,24 @@ int svo_verify_tree(int B, int N, int V, int dtype, const int32_t *node_tokens,
  * ascending index order against a running distribution r, which starts as
  * p_n: child i with token y is kept when u[b][i] < min(1, r(y) / q_n(y))
  * (the q = 0 rule as for chains), and the walk moves to it.  A rejection
- * replaces r by the normalised residual max(0, r - q_n).  When no child is
- * kept (or n is a leaf), the final token is drawn from r by the inverse CDF
- * with u[b][0].
- * The residual after j rejections is max(0, p - c_j q) / Z(c_j) with
- * Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0 and c_{j+1} = c_j + Z(c_j),
- * because max(0, max(0, a) / Z - q) = max(0, a - Z q) / Z for Z > 0.  Only
- * the scalar c is carried from one sibling to the next.  If a residual has no
- * mass (rounding), r falls back to p_n (c = 0), as for chains.
+ * replaces r by the normalised residual max(0, r - q_n) / Z, Z its total
+ * mass; if Z is 0 (rounding), r falls back to p_n, as for chains.  When no
+ * child is kept (or n is a leaf), the final token is drawn from r by the
+ * inverse CDF with u[b][0].
  * Outputs as for svo_verify_tree: accepted_len = depth of the last kept node,
  * emitted = the kept tokens then the final token then -1, accepted_nodes the
  * kept node ids then -1; an invalid tree gives -1 everywhere.  band[b] (T > 0
  * only) flags a tested uniform within band_eps of its threshold or u[b][0]
- * within band_eps of a CDF boundary of the final token.
+ * within band_eps of a CDF boundary of the final token.  final_mass[b]
+ * (optional) is the mass Z of the last residual formed at the node where the
+ * walk stopped (1 when no child of that node was rejected: r = p).
  */
 int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_tokens,
                             const int32_t *parent, int parent_stride, int max_depth,
                             const void *draft_logits, const void *target_logits,
                             const float *temperature, const float *uniforms,
                             int32_t *accepted_len, int32_t *emitted, int32_t *accepted_nodes,
-                            int32_t *band, double band_eps) {
+                            int32_t *band, double *final_mass, double band_eps) {
     if (B < 0 || N <= 0 || V <= 0 || max_depth < 0 || (dtype != SVO_F32 && dtype != SVO_BF16)) return 1;
     if (parent_stride != 0 && parent_stride < N) return 1;
     if (B == 0) return 0;
@@ -463,10 +461,10 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
         int *depth = (int *)malloc(sizeof(int) * (size_t)N);
         double *P = (double *)malloc(sizeof(double) * (size_t)V);
         double *Q = (double *)malloc(sizeof(double) * (size_t)V);
-        double *w = (double *)malloc(sizeof(double) * (size_t)V);
-        if (!depth || !P || !Q || !w) {
+        double *r = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!depth || !P || !Q || !r) {
             bad = 1;
-            free(depth); free(P); free(Q); free(w);
+            free(depth); free(P); free(Q); free(r);
             continue;
         }
         /* The same validity rule as the greedy tree. */
@@ -479,11 +477,11 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
             if (depth[i] > max_depth) valid = 0;
         }
         int flag = 0;
+        double mass = 1.0;
         if (!valid) {
             accepted_len[b] = -1;
         } else {
             int n = 0, d = 0;
-            double c = 0.0, Z = 1.0;
             for (;;) {
                 size_t trow = ((size_t)b * N + n) * (size_t)V;
                 row_distribution(target_logits, dtype, trow, V, T, P);
@@ -491,31 +489,36 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
                 for (int i = n + 1; i < N; ++i)
                     if (par[i] == n) has_children = 1;
                 if (has_children) row_distribution(draft_logits, dtype, trow, V, T, Q);
-                c = 0.0;
-                Z = 1.0;
+                /* the running distribution starts as the target row */
+                for (int v = 0; v < V; ++v) r[v] = P[v];
+                int rejected = 0;
+                mass = 1.0;
                 int next = -1;
                 for (int i = n + 1; i < N && next < 0; ++i) {
                     if (par[i] != n) continue;
                     int y = tok[i];
                     if (y < 0 || y >= V) { bad = 1; y = 0; }
-                    double cc = (g_mutation == MUT_TREE_STALE_RESIDUAL) ? 0.0 : c;
-                    double zz = (g_mutation == MUT_TREE_STALE_RESIDUAL) ? 1.0 : Z;
-                    double r = P[y] - cc * Q[y];
-                    r = (r > 0.0 ? r : 0.0) / zz;
-                    double tau = threshold(r, Q[y]);
+                    double ry = (g_mutation == MUT_TREE_STALE_RESIDUAL) ? P[y] : r[y];
+                    double tau = threshold(ry, Q[y]);
                     if (T > 0.0 && fabs((double)u[i] - tau) < band_eps) flag = 1;
                     if ((double)u[i] < tau) {
                         next = i;
                         break;
                     }
-                    /* rejected: the residual max(0, r - q) is max(0, p - (c + Z) q) / Z' */
-                    c += Z;
-                    Z = 0.0;
+                    /* rejected: r becomes the normalised residual max(0, r - q) */
+                    rejected = 1;
+                    double Z = 0.0;
                     for (int v = 0; v < V; ++v) {
-                        double e = P[v] - c * Q[v];
-                        Z += e > 0.0 ? e : 0.0;
+                        double e = r[v] - Q[v];
+                        r[v] = e > 0.0 ? e : 0.0;
+                        Z += r[v];
                     }
-                    if (Z == 0.0) { c = 0.0; Z = 1.0; }
+                    mass = Z;
+                    if (Z == 0.0) {
+                        for (int v = 0; v < V; ++v) r[v] = P[v];
+                    } else {
+                        for (int v = 0; v < V; ++v) r[v] /= Z;
+                    }
                 }
                 if (next >= 0) {
                     out[d] = tok[next];
@@ -524,20 +527,13 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
                     n = next;
                     continue;
                 }
-                /* No child kept: draw from max(0, p - c q) (p itself when c == 0). */
+                /* No child kept: draw from r (p itself when nothing was rejected). */
+                if (rejected && g_mutation == MUT_SAMPLE_TARGET_AT_MISMATCH)
+                    for (int v = 0; v < V; ++v) r[v] = P[v];
                 double W = 0.0;
-                for (int v = 0; v < V; ++v) {
-                    double e;
-                    if (c == 0.0 || g_mutation == MUT_SAMPLE_TARGET_AT_MISMATCH) e = P[v];
-                    else e = P[v] - c * Q[v];
-                    w[v] = e > 0.0 ? e : 0.0;
-                    W += w[v];
-                }
-                if (W == 0.0) {
-                    for (int v = 0; v < V; ++v) { w[v] = P[v]; W += w[v]; }
-                }
+                for (int v = 0; v < V; ++v) W += r[v];
                 double c_lo = 0.0, c_hi = 0.0;
-                int y = inverse_cdf(w, V, W, (double)u[0], &c_lo, &c_hi);
+                int y = inverse_cdf(r, V, W, (double)u[0], &c_lo, &c_hi);
                 if (T > 0.0 && (fabs((double)u[0] - c_lo / W) < band_eps ||
                                 fabs((double)u[0] - c_hi / W) < band_eps))
                     flag = 1;
@@ -547,7 +543,8 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
             }
         }
         if (band) band[b] = flag;
-        free(depth); free(P); free(Q); free(w);
+        if (final_mass) final_mass[b] = valid ? mass : 0.0;
+        free(depth); free(P); free(Q); free(r);
     }
     return bad;
 }
