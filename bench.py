@@ -15,9 +15,12 @@ kernel dispatch on its launch stream, which gives every kernel's duration
 (the roofline of the dominant kernel uses these).
 
 Prints one JSON line (see the metric, roofline and cpu_baseline fields).
-Other workloads (--workload greedy_chain, deepseek_chain, eagle_tree, mtp_chain,
-sampling, sampled_tree) print the same line for their own step; the default
-line is the Llama-scale chain.
+The line's `workloads` object holds every workload's step time, rate,
+dominant kernel (the one with the most time per step) and its fraction of
+peak, and the in-run parity against the oracle: the tiny chain, the greedy
+chain, the DeepSeek-scale chain, the EAGLE-style trees, MTP single-token
+verify, temperature sampling and the sampled tree.  --workload NAME puts
+another workload in the headline place; --no-workloads measures it alone.
 """
 
 import argparse
@@ -147,18 +150,266 @@ def cpu_baseline(inp, seconds: float, threads: int = 0):
     return reps, el, used
 
 
+# The headline workload first, then every other workload of the line's
+# `workloads` object: the five named configurations (tiny chain, Llama-scale
+# chain, greedy chain, DeepSeek-scale chain, EAGLE-style tree) and the further
+# shapes (MTP single-token verify, temperature sampling, the sampled tree, the
+# EAGLE-style tree with distinct sibling tokens).
+WORKLOAD_ORDER = ["llama_chain", "tiny_chain", "greedy_chain", "deepseek_chain", "eagle_tree", "eagle_tree_distinct",
+                  "mtp_chain", "sampling", "sampled_tree"]
+
+
+class Workload:
+    """One workload's inputs resident in HBM, its outputs and workspace, and
+    its step (one library call over one batch)."""
+
+    def __init__(self, name, seed, copies, accept_prob, torch, svl, W):
+        import numpy as np
+
+        self.name = name
+        self.cfg = W.WORKLOADS[name]
+        self.inp = inp = W.make_inputs(name, seed)
+        self.kind = kind = inp["kind"]
+        self.es = es = 2 if inp["dtype"] == W.BF16 else 4
+        in_bytes = sum(v.nbytes for v in inp.values() if isinstance(v, np.ndarray))
+        # enough copies to exceed twice the Infinity Cache (at most 32: a batch
+        # of a few MB is latency-bound whether or not it stays in a cache)
+        self.copies = copies or max(1, min(32, math.ceil(2 * MALL_BYTES / in_bytes)))
+        self.dev = dev = [to_device(inp, torch, W) for _ in range(self.copies)]
+        B, V = inp["B"], inp["V"]
+        self.accept_prob = accept_prob and kind == "chain"
+        i32 = dict(dtype=torch.int32, device="cuda")
+        if kind in ("chain", "greedy"):
+            k = inp["k"]
+            self.out = dict(accepted_len=torch.empty(B, **i32), emitted=torch.empty((B, k + 1), **i32))
+        else:
+            md = inp["max_depth"]
+            self.out = dict(accepted_len=torch.empty(B, **i32), emitted=torch.empty((B, md + 1), **i32),
+                            accepted_nodes=torch.empty((B, md + 1), **i32))
+        out = self.out
+        if kind == "chain":
+            k = inp["k"]
+            out["accept_prob"] = (torch.empty((B, k), dtype=torch.float32, device="cuda") if self.accept_prob
+                                  else None)
+            ws = torch.empty(svl.chain_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+            def step(i):
+                t = dev[i % self.copies]
+                svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                                 t["uniforms"], workspace=ws, out=out)
+            self.units = B * k if k > 0 else B
+        elif kind == "greedy":
+            k = inp["k"]
+            ws = torch.empty(svl.greedy_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+            def step(i):
+                t = dev[i % self.copies]
+                svl.verify_greedy(t["draft_tokens"], t["target_logits"], workspace=ws, out=out)
+            self.units = B * k
+        elif kind == "tree_sampled":
+            N, md = inp["N"], inp["max_depth"]
+            ws = torch.empty(svl.tree_sampled_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8,
+                             device="cuda")
+
+            def step(i):
+                t = dev[i % self.copies]
+                svl.verify_tree_sampled(t["node_tokens"], t["parent"], md, t["draft_logits"], t["target_logits"],
+                                        t["temperature"], t["uniforms"], workspace=ws, out=out)
+            self.units = B * (inp["N"] - 1)
+        else:
+            N, md = inp["N"], inp["max_depth"]
+            ws = torch.empty(svl.tree_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
+
+            def step(i):
+                t = dev[i % self.copies]
+                svl.verify_tree(t["node_tokens"], t["parent"], md, t["target_logits"], workspace=ws, out=out)
+            self.units = B * (inp["N"] - 1)
+        self.ws = ws
+        self.step = step
+        self.unit = ("sampled tokens/s" if kind == "chain" and inp["k"] == 0 else
+                     "verified draft nodes/s" if kind in ("tree", "tree_sampled") else "verified draft tokens/s")
+
+    def outputs(self):
+        return {key: (v.cpu().numpy() if v is not None else None) for key, v in self.out.items()}
+
+    def kernel_bytes(self, got, W):
+        """Algorithmic bytes per launch of every streaming kernel of the step,
+        and launches per step; where they depend on the outcome (the rows a draw
+        or a later phase reads), from this batch's outputs (identical in every
+        copy)."""
+        import numpy as np
+
+        inp, es, kind = self.inp, self.es, self.kind
+        B, V = inp["B"], inp["V"]
+        kb, launches = {}, {}
+        if kind == "chain":
+            k = inp["k"]
+            a = got["accepted_len"]
+            T = inp["temperature"]
+            # every draft row and target rows 0..k-1 once; without accept_prob,
+            # from 6 drafts and 128 MiB of rows the library streams positions
+            # 0..s-1 first and the rest only for sequences that accept all of them
+            s = (max(1, k // 4) if not self.accept_prob and k >= 6 and 2 * B * k * V * es >= 128 << 20 else k)
+            if k > 0:
+                kb["chain_rowstats"] = 2 * B * s * V * es
+                if s < k:
+                    kb["chain_rowstats_rest"] = int((a >= s).sum()) * 2 * (k - s) * V * es
+            # the final draw: both rows at a rejection, the bonus row after full
+            # acceptance, the row's argmax at temperature 0 (with no drafts: row 0);
+            # one workgroup per row from 256 rows of at most 256 segments
+            nseg = -(-(-(-V // (16 // es))) // 64)
+            draw_kernel = "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part"
+            draw = 0
+            for b in range(B):
+                if T[b] > 0:
+                    draw += (2 if a[b] < k else 1) * V * es
+                elif a[b] == k:
+                    draw += V * es
+            kb[draw_kernel] = draw
+        elif kind == "greedy":
+            k = inp["k"]
+            s = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1
+            kb["greedy_rows"] = B * s * V * es
+            if s <= k:
+                kb["greedy_rows_rest"] = int((got["accepted_len"] >= s).sum()) * (k + 1 - s) * V * es
+        elif kind == "tree_sampled":
+            N, par = inp["N"], inp["parent"]
+            # the target and draft rows of every inner node
+            inner = int(np.count_nonzero(np.bincount(par[1:], minlength=N)))
+            kb["tree_rowstats"] = B * 2 * inner * V * es
+            # the walk's passes (from the outputs and the tree): every rejected
+            # child costs one pass over its parent's two rows; the final draw's
+            # masses one more pass (two rows after a rejection at that node, the
+            # target row otherwise), and a walk ending at a leaf first forms the
+            # leaf's target-row statistics (one row)
+            kids = [[i for i in range(1, N) if par[i] == n] for n in range(N)]
+            T = inp["temperature"]
+            walk = 0
+            for b in range(B):
+                if got["accepted_len"][b] < 0 or not T[b] > 0:
+                    continue
+                path = [0] + [int(x) for x in got["accepted_nodes"][b] if x >= 0]
+                rejected_last = 0
+                for depth, n in enumerate(path):
+                    nxt = path[depth + 1] if depth + 1 < len(path) else None
+                    rej = sum(1 for c in kids[n] if nxt is None or c < nxt)
+                    walk += rej * 2 * V * es
+                    rejected_last = rej
+                last = path[-1]
+                walk += (2 if rejected_last else 1) * V * es + (V * es if not kids[last] else 0)
+            launches["tree_round"] = 7
+            kb["tree_round"] = walk / 7
+        else:
+            N = inp["N"]
+            tree_two_phase = N > 1 and B * N * V * es >= 96 << 20
+            if tree_two_phase:
+                # each later phase lists the nodes of its depth range whose ancestor
+                # at the range's first depth is accepted (node acceptance from the
+                # outputs: the accepted path; every node of the range below an
+                # accepted depth-lo ancestor is listed)
+                ranges = ([(1, 2), (3, N)] if B * N * V * es >= 192 << 20 and N >= 48 else [(1, N)])
+                par, tok = inp["parent"], inp["node_tokens"]
+                top = np.argmax(W.values(inp["target_logits"], inp["dtype"]), axis=-1)
+                depth = np.zeros(N, np.int64)
+                for n in range(1, N):
+                    depth[n] = depth[par[n]] + 1
+                rest_rows = 0
+                for b in range(B):
+                    acc = np.zeros(N, bool)
+                    acc[0] = True
+                    for n in range(1, N):
+                        acc[n] = acc[par[n]] and tok[b, n] == top[b, par[n]]
+                    for lo, hi in ranges:
+                        for n in range(1, N):
+                            an = n
+                            while depth[an] > lo:
+                                an = par[an]
+                            rest_rows += int(lo <= depth[n] <= hi and acc[an])
+                kb["tree_root_rows"] = B * V * es
+                kb["tree_rows_rest"] = rest_rows * V * es / len(ranges)
+                launches["tree_rows_rest"] = len(ranges)
+            else:
+                kb["argmax_rows"] = B * N * V * es
+        return kb, launches
+
+    def timed(self, svl, torch, steps, profiled):
+        """K steps back to back behind a ~20 ms spin kernel (so that host launch
+        overhead stays outside the measurement); returns ms per step."""
+        if profiled:
+            svl.profile_begin(16 * steps)
+        torch.cuda._sleep(int(50e6))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            self.step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+
+def measure(wl, svl, torch, W, steps, warmup):
+    """Times one workload: the median of three timed regions of `steps`
+    steps without per-kernel events (the throughput), then one region with an
+    event pair attached to each kernel dispatch (per-kernel durations); the
+    dominant kernel is the one with the most time per step."""
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    got = wl.outputs()
+    kb, launches = wl.kernel_bytes(got, W)
+    reps = [wl.timed(svl, torch, steps, False) for _ in range(3)]
+    ms = sorted(reps)[1]
+    ms_prof = wl.timed(svl, torch, steps, True)
+    prof = svl.profile_end()
+    kernels = {name: dict(launches=n, avg_us=1e3 * tot / max(n, 1)) for name, (n, tot) in prof.items()}
+    per_step = {name: v["launches"] / steps for name, v in kernels.items()}
+    missing = [name for name in kb if name not in kernels]
+    if missing:
+        raise RuntimeError(f"{wl.name}: bench.py expects kernels the library did not launch: {missing}")
+    step_bytes = sum(v * launches.get(name, 1) for name, v in kb.items())
+    # the dominant kernel: the kernel with the most time per step
+    dominant = max(kernels, key=lambda name: kernels[name]["avg_us"] * per_step[name])
+    dom_us = kernels[dominant]["avg_us"]
+    dom_bytes = kb.get(dominant)
+    return dict(ms=ms, reps=reps, ms_prof=ms_prof, got=got, kb=kb, launches=launches, kernels=kernels,
+                per_step=per_step, step_bytes=step_bytes, dominant=dominant, dom_us=dom_us, dom_bytes=dom_bytes)
+
+
+def workload_record(wl, m, parity):
+    """The `workloads` entry of one workload."""
+    s = m["ms"] * 1e-3
+    frac = (m["dom_bytes"] / (m["dom_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS) if m["dom_bytes"] else None
+    rec = {"name": wl.cfg["name"], "B": wl.inp["B"], "k": wl.inp.get("k"), "N": wl.inp.get("N"), "V": wl.inp["V"],
+           "logits": DTYPE_NAMES[wl.inp["dtype"]], "step_us": round(m["ms"] * 1e3, 2),
+           "value": wl.units / s, "unit": wl.unit,
+           "hbm_gbs": m["step_bytes"] / s / 1e9, "hbm_frac_of_peak": m["step_bytes"] / s / 1e9 / PEAK_HBM_GBS,
+           "algorithmic_bytes_per_step": m["step_bytes"],
+           "dominant_kernel": m["dominant"], "dominant_us": round(m["dom_us"], 3),
+           "dominant_bytes_per_launch": m["dom_bytes"], "dominant_frac_of_peak": frac,
+           "kernels_us": {n: round(v["avg_us"], 3) for n, v in m["kernels"].items()},
+           "kernel_launches_per_step": {n: round(v, 3) for n, v in m["per_step"].items()}}
+    if parity is not None:
+        rec["parity"] = parity
+    return rec
+
+
+DTYPE_NAMES = {0: "f32", 1: "bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="llama_chain",
-                    choices=["llama_chain", "greedy_chain", "deepseek_chain", "eagle_tree", "mtp_chain",
-                             "sampling", "sampled_tree"])
+    ap.add_argument("--workload", default="llama_chain", choices=WORKLOAD_ORDER)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = enough to exceed 2x the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="no oracle leg (no cpu_baseline, no parity)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure the chosen workload only (no `workloads` object)")
+    ap.add_argument("--workload-steps", type=int, default=200, help="timed steps of each further workload")
     ap.add_argument("--accept-prob", action="store_true",
                     help="chain workloads: also return accept_prob (tau of every draft, also past the first "
                          "rejection), which makes the library read every row")
@@ -173,7 +424,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import draft_token_verification_chain_amd as svl
@@ -183,200 +433,32 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     svl.load()
-    cfg = W.WORKLOADS[args.workload]
-    inp = W.make_inputs(args.workload, args.seed)
-    kind = inp["kind"]
-    es = 2 if inp["dtype"] == W.BF16 else 4
-    in_bytes = sum(v.nbytes for k, v in inp.items() if isinstance(v, np.ndarray))
-    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / in_bytes))
-    dev = [to_device(inp, torch, W) for _ in range(copies)]
-    B, V = inp["B"], inp["V"]
-
-    if kind == "chain":
-        k = inp["k"]
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
-                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"),
-                   accept_prob=(torch.empty((B, k), dtype=torch.float32, device="cuda") if args.accept_prob
-                                else None))
-        ws = torch.empty(svl.chain_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
-
-        def step(i):
-            t = dev[i % copies]
-            svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
-                             t["uniforms"], workspace=ws, out=out)
-        units = B * k if k > 0 else B       # verified draft tokens (sampled tokens when k == 0) per step
-        # k == 0: one workgroup per row from 256 rows of at most 256 segments
-        # (64 vectors of 16 bytes each)
-        nseg = -(-(-(-V // (16 // es))) // 64)  # ceil(ceil(V / (16 / es)) / 64)
-        draw_kernel = "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part"
-        # every draft row and target rows 0..k-1 once; without accept_prob,
-        # from 6 drafts and 128 MiB of rows the library streams positions
-        # 0..s-1 first and the rest only for sequences that accept all of them
-        chain_s = (max(1, k // 4) if not args.accept_prob and k >= 6 and 2 * B * k * V * es >= 128 << 20 else k)
-    elif kind == "greedy":
-        k = inp["k"]
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
-                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device="cuda"))
-        ws = torch.empty(svl.greedy_workspace_bytes(B, k, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
-
-        def step(i):
-            t = dev[i % copies]
-            svl.verify_greedy(t["draft_tokens"], t["target_logits"], workspace=ws, out=out)
-        units = B * k
-        # rows 0..s-1 of every sequence; at 256 MiB of rows and more the library
-        # reads rows s..k only for sequences accepting their first s drafts
-        s_first = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1
-    elif kind == "tree_sampled":
-        N = inp["N"]
-        md = inp["max_depth"]
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
-                   emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
-                   accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
-        ws = torch.empty(svl.tree_sampled_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
-
-        def step(i):
-            t = dev[i % copies]
-            svl.verify_tree_sampled(t["node_tokens"], t["parent"], md, t["draft_logits"], t["target_logits"],
-                                    t["temperature"], t["uniforms"], workspace=ws, out=out)
-        units = B * (N - 1)                 # verified draft nodes per step
-        inner = int(np.count_nonzero(np.bincount(inp["parent"][1:], minlength=N)))
-    else:
-        N = inp["N"]
-        md = inp["max_depth"]
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device="cuda"),
-                   emitted=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"),
-                   accepted_nodes=torch.empty((B, md + 1), dtype=torch.int32, device="cuda"))
-        ws = torch.empty(svl.tree_workspace_bytes(B, N, V, inp["dtype"]), dtype=torch.uint8, device="cuda")
-
-        def step(i):
-            t = dev[i % copies]
-            svl.verify_tree(t["node_tokens"], t["parent"], md, t["target_logits"], workspace=ws, out=out)
-        units = B * (N - 1)                 # verified draft nodes per step
-        # from 96 MiB of rows the library streams the root rows, then only the
-        # rows below an accepted depth-1 node (from 192 MiB and 48 nodes: depths
-        # 1-2 below an accepted depth-1 node, then depths 3+ below an accepted
-        # depth-3 node); those rows are counted below, from the outcome
-        tree_two_phase = N > 1 and B * N * V * es >= 96 << 20
-        tree_ranges = ([(1, 2), (3, N)] if B * N * V * es >= 192 << 20 and N >= 48 else [(1, N)])
-
-    unit = "sampled tokens/s" if kind == "chain" and inp["k"] == 0 else "verified draft tokens/s"
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    wl = Workload(args.workload, args.seed, args.copies, args.accept_prob, torch, svl, W)
     if args.calibrate_copy:
         src = torch.ones(args.calibrate_copy * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    # algorithmic bytes per launch of every streaming kernel of the step, and
-    # its launches per step; where they depend on the outcome (the rows a
-    # draw or a later phase reads), from this batch's (identical in every copy)
-    kernel_bytes, kernel_launches = {}, {}
-    if kind == "chain":
-        a = out["accepted_len"].cpu().numpy()
-        T = inp["temperature"]
-        k = inp["k"]
-        if k > 0:
-            kernel_bytes["chain_rowstats"] = 2 * B * chain_s * V * es
-            if chain_s < k:
-                kernel_bytes["chain_rowstats_rest"] = int((a >= chain_s).sum()) * 2 * (k - chain_s) * V * es
-        # the final draw: both rows at a rejection, the bonus row after full
-        # acceptance, the row's argmax at temperature 0 (with no drafts: row 0)
-        draw = 0
-        for b in range(B):
-            if T[b] > 0:
-                draw += (2 if a[b] < k else 1) * V * es
-            elif a[b] == k:
-                draw += V * es
-        kernel_bytes[draw_kernel] = draw
-    elif kind == "greedy":
-        kernel_bytes["greedy_rows"] = B * s_first * V * es
-        if s_first <= inp["k"]:
-            a = out["accepted_len"].cpu().numpy()
-            kernel_bytes["greedy_rows_rest"] = int((a >= s_first).sum()) * (inp["k"] + 1 - s_first) * V * es
-    elif kind == "tree_sampled":
-        # the target and draft rows of every inner node (a leaf's rows are read
-        # only when a walk ends there; those and the walk's passes over the rows
-        # of the nodes it visits come on top, uncounted)
-        kernel_bytes["tree_rowstats"] = B * 2 * inner * V * es
-    elif tree_two_phase:
-        # each later phase lists the nodes of its depth range whose ancestor at
-        # the range's first depth is accepted (node acceptance from the rows'
-        # argmax, host-side bookkeeping for the byte count only)
-        par, tok = inp["parent"], inp["node_tokens"]
-        top = np.argmax(W.values(inp["target_logits"], inp["dtype"]), axis=-1)
-        depth = np.zeros(N, np.int64)
-        for n in range(1, N):
-            depth[n] = depth[par[n]] + 1
-        rest_rows = 0
-        for b in range(B):
-            acc = np.zeros(N, bool)
-            acc[0] = True
-            for n in range(1, N):
-                acc[n] = acc[par[n]] and tok[b, n] == top[b, par[n]]
-            for lo, hi in tree_ranges:
-                for n in range(1, N):
-                    a = n
-                    while depth[a] > lo:
-                        a = par[a]
-                    rest_rows += int(lo <= depth[n] <= hi and acc[a])
-        kernel_bytes["tree_root_rows"] = B * V * es
-        kernel_bytes["tree_rows_rest"] = rest_rows * V * es / len(tree_ranges)
-        kernel_launches["tree_rows_rest"] = len(tree_ranges)
-    else:
-        kernel_bytes["argmax_rows"] = B * N * V * es
-    step_bytes = sum(v * kernel_launches.get(name, 1) for name, v in kernel_bytes.items())
-
-    def timed(profiled: bool) -> float:
-        """K steps back to back behind a ~20 ms spin kernel (so that host launch
-        overhead stays outside the measurement); returns ms per step."""
-        if profiled:
-            svl.profile_begin(8 * args.steps)
-        torch.cuda._sleep(int(50e6))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(args.steps):
-            step(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    # timed region 1: the throughput (no per-kernel events), K steps timed three
-    # times; the median is reported (the spread between back-to-back runs on one
-    # machine is about 1 us per step, mostly in the gaps between kernels)
-    ms_repeats = [timed(False) for _ in range(3)]
-    ms_per_step = sorted(ms_repeats)[1]
-    # timed region 2: the same steps, each kernel's own dispatch timed by HIP events
-    # (per-kernel durations for the roofline; the events themselves add gaps between
-    # kernels, so this region's step time is reported separately)
-    ms_profiled = timed(True)
-    prof = svl.profile_end()
-    s_per_step = ms_per_step * 1e-3
-
-    kernels = {name: dict(launches=n, avg_us=1e3 * tot / max(n, 1)) for name, (n, tot) in prof.items()}
-    missing = [name for name in kernel_bytes if name not in kernels]
-    if missing:
-        raise RuntimeError(f"bench.py expects kernels the library did not launch: {missing}")
-    # the dominant kernel: the streaming kernel with the most time per step
-    dominant = max(kernel_bytes, key=lambda name: kernels[name]["avg_us"] * kernel_launches.get(name, 1))
-    dominant_bytes = kernel_bytes[dominant]
-    dom_us = kernels[dominant]["avg_us"]
-    achieved = dominant_bytes / (dom_us * 1e-6) / 1e9
+    m = measure(wl, svl, torch, W, args.steps, args.warmup)
+    s_per_step = m["ms"] * 1e-3
+    dominant, dom_us = m["dominant"], m["dom_us"]
+    dom_bytes = m["dom_bytes"]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
     traffic = load_traffic(dominant, args.workload)
-
+    inp, cfg = wl.inp, wl.cfg
+    B, V, kind = inp["B"], inp["V"], wl.kind
     result = {
-        "metric": METRIC if args.workload == "llama_chain" else f"{unit[:-2]}/sec ({cfg['name']})",
-        "value": units / s_per_step,
-        "unit": unit,
+        "metric": METRIC if args.workload == "llama_chain" else f"{wl.unit[:-2]}/sec ({cfg['name']})",
+        "value": wl.units / s_per_step,
+        "unit": wl.unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "ms_per_step_repeats": ms_repeats,
-        "ms_per_step_with_kernel_events": ms_profiled,
+        "ms_per_step": m["ms"],
+        "ms_per_step_repeats": m["reps"],
+        "ms_per_step_with_kernel_events": m["ms_prof"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -384,33 +466,51 @@ def main():
         "data": "synthetic (seeded generator, shapes of the named workload)",
         "config": {"workload": cfg["name"], "B": B, "k": inp.get("k"), "N": inp.get("N"), "V": V,
                    "logits": W.DTYPE_NAMES[inp["dtype"]], "temperature": cfg.get("temperature"),
-                   "seed": args.seed, "input_copies_rotated": copies, "parallelism": "single GPU",
+                   "seed": args.seed, "input_copies_rotated": wl.copies, "parallelism": "single GPU",
                    "accept_prob": bool(args.accept_prob) if kind == "chain" else None},
-        "hbm_gbs": step_bytes / s_per_step / 1e9,
-        "hbm_frac_of_peak": step_bytes / s_per_step / 1e9 / PEAK_HBM_GBS,
-        "algorithmic_bytes_per_step": step_bytes,
-        "bytes_per_verified_token": step_bytes / units,
+        "hbm_gbs": m["step_bytes"] / s_per_step / 1e9,
+        "hbm_frac_of_peak": m["step_bytes"] / s_per_step / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": m["step_bytes"],
+        "bytes_per_verified_token": m["step_bytes"] / wl.units,
         # every sequence emits its accepted tokens plus one final token
-        "emitted_tokens_per_s": float(out["accepted_len"].sum().item() + B) / s_per_step,
-        "kernels_us": {n: round(v["avg_us"], 3) for n, v in kernels.items()},
-        "kernels_bytes_per_launch": {n: int(v) for n, v in kernel_bytes.items()},
+        "emitted_tokens_per_s": float((m["got"]["accepted_len"].clip(min=0) + 1).sum()) / s_per_step,
+        "kernels_us": {n: round(v["avg_us"], 3) for n, v in m["kernels"].items()},
+        "kernels_bytes_per_launch": {n: int(v) for n, v in m["kb"].items()},
+        # achieved: algorithmic bytes per launch over the kernel's average duration,
+        # measured with HIP events attached to its dispatches on its launch stream
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "bytes_per_launch": dominant_bytes, "avg_launch_us": dom_us,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": traffic,
+                     "bytes_per_launch": dom_bytes, "avg_launch_us": dom_us, "duration_source": "hip_events",
                      "traffic_gbs": traffic / (dom_us * 1e-6) / 1e9 if traffic else None},
     }
 
     if not args.no_cpu:
         reps, el, threads = cpu_baseline(inp, args.cpu_seconds)
         reps1, el1, _ = cpu_baseline(inp, args.cpu_seconds / 2, threads=1)
-        result["cpu_baseline"] = {"value": units * reps / el, "unit": unit, "cores": threads,
+        result["cpu_baseline"] = {"value": wl.units * reps / el, "unit": wl.unit, "cores": threads,
                                   "kind": "oracle",
                                   "sample": f"the full {cfg['name']} batch (B={B}) x {reps} repetitions, {el:.1f} s",
-                                  "value_1thread": units * reps1 / el1,
+                                  "value_1thread": wl.units * reps1 / el1,
                                   "sample_1thread": f"the same batch x {reps1} repetitions on one thread, {el1:.1f} s",
                                   "cpu_model": cpu_model()}
-        result["parity"] = check_against_oracle(inp, {key: (v.cpu().numpy() if v is not None else None)
-                                                      for key, v in out.items()})
+        result["parity"] = check_against_oracle(inp, m["got"])
+
+    if not args.no_workloads:
+        first = wl
+        records = {}
+        for name in WORKLOAD_ORDER:
+            if name == args.workload:
+                records[name] = workload_record(first, m, result.get("parity"))
+                continue
+            del wl
+            torch.cuda.empty_cache()
+            print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+            wl = Workload(name, args.seed, 0, args.accept_prob, torch, svl, W)
+            mw = measure(wl, svl, torch, W, args.workload_steps, min(args.warmup, 20))
+            parity = None if args.no_cpu else check_against_oracle(wl.inp, mw["got"])
+            records[name] = workload_record(wl, mw, parity)
+            print(f"[bench] {name}: {records[name]['step_us']} us per step", file=sys.stderr, flush=True)
+        result["workloads"] = records
     print(json.dumps(result), flush=True)
 
 

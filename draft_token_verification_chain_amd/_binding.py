@@ -3,12 +3,16 @@
 Every step of the computation runs in the HIP kernels behind the C ABI of
 ``include/specverify.h``; this module converts torch tensors to device
 pointers, allocates outputs and workspace with torch's caching allocator, and
-passes torch's current HIP stream.  There is no CPU fallback: when the shared
-library is missing or fails to load, every call raises.
+passes torch's current HIP stream (or the ``stream=`` given).  Outputs and
+workspace it allocates are allocated on the stream the call runs on, so the
+caching allocator reuses their memory only in that stream's order.  There is
+no CPU fallback: when the shared library is missing or fails to load, every
+call raises.
 """
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -104,6 +108,11 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context of a call: the given stream, else the current one."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def chain_workspace_bytes(B: int, k: int, V: int, dtype: int) -> int:
     return int(load().sv_chain_workspace_bytes(B, k, V, dtype))
 
@@ -145,15 +154,15 @@ def verify_chain(draft_tokens, draft_logits, target_logits, temperature, uniform
     _check_dev("draft_tokens", draft_tokens, torch.int32, (B, k))
     _check_dev("temperature", temperature, torch.float32, (B,))
     _check_dev("uniforms", uniforms, torch.float32, (B, k + 1))
-    if out is None:
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device=dev),
-                   accept_prob=torch.empty((B, k), dtype=torch.float32, device=dev) if accept_prob else None)
-    need = lib.sv_chain_workspace_bytes(B, k, V, dt)
-    ws = _workspace(need, dev, workspace)
+    with _on(stream):
+        if out is None:
+            out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                       emitted=torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                       accept_prob=torch.empty((B, k), dtype=torch.float32, device=dev) if accept_prob else None)
+        ws = _workspace(lib.sv_chain_workspace_bytes(B, k, V, dt), dev, workspace)
     st = lib.sv_verify_chain(B, k, V, dt, _ptr(draft_tokens), _ptr(draft_logits), _ptr(target_logits),
                              _ptr(temperature), _ptr(uniforms), _ptr(out["accepted_len"]), _ptr(out["emitted"]),
-                             _ptr(out["accept_prob"]), _ptr(ws), ws.numel(), _stream(stream))
+                             _ptr(out.get("accept_prob")), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError("sv_verify_chain", st)
     return out
@@ -168,10 +177,11 @@ def verify_greedy(draft_tokens, target_logits, *, workspace=None, stream=None, o
     dev = target_logits.device
     _check_dev("target_logits", target_logits)
     _check_dev("draft_tokens", draft_tokens, torch.int32, (B, k))
-    if out is None:
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-                   emitted=torch.empty((B, k + 1), dtype=torch.int32, device=dev))
-    ws = _workspace(lib.sv_greedy_workspace_bytes(B, k, V, dt), dev, workspace)
+    with _on(stream):
+        if out is None:
+            out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                       emitted=torch.empty((B, k + 1), dtype=torch.int32, device=dev))
+        ws = _workspace(lib.sv_greedy_workspace_bytes(B, k, V, dt), dev, workspace)
     st = lib.sv_verify_greedy(B, k, V, dt, _ptr(draft_tokens), _ptr(target_logits), _ptr(out["accepted_len"]),
                               _ptr(out["emitted"]), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
@@ -203,11 +213,12 @@ def verify_tree(node_tokens, parent, max_depth: int, target_logits, *, accepted_
             raise ValueError("parent must be [N] or [B, >=N]")
         stride = parent.shape[1]
     w = max_depth + 1
-    if out is None:
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-                   emitted=torch.empty((B, w), dtype=torch.int32, device=dev),
-                   accepted_nodes=torch.empty((B, w), dtype=torch.int32, device=dev) if accepted_nodes else None)
-    ws = _workspace(lib.sv_tree_workspace_bytes(B, N, V, dt), dev, workspace)
+    with _on(stream):
+        if out is None:
+            out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                       emitted=torch.empty((B, w), dtype=torch.int32, device=dev),
+                       accepted_nodes=torch.empty((B, w), dtype=torch.int32, device=dev) if accepted_nodes else None)
+        ws = _workspace(lib.sv_tree_workspace_bytes(B, N, V, dt), dev, workspace)
     st = lib.sv_verify_tree(B, N, V, dt, _ptr(node_tokens), _ptr(parent), stride, max_depth, _ptr(target_logits),
                             _ptr(out["accepted_len"]), _ptr(out["emitted"]), _ptr(out["accepted_nodes"]),
                             _ptr(ws), ws.numel(), _stream(stream))
@@ -245,11 +256,12 @@ def verify_tree_sampled(node_tokens, parent, max_depth: int, draft_logits, targe
             raise ValueError("parent must be [N] or [B, >=N]")
         stride = parent.shape[1]
     w = max_depth + 1
-    if out is None:
-        out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
-                   emitted=torch.empty((B, w), dtype=torch.int32, device=dev),
-                   accepted_nodes=torch.empty((B, w), dtype=torch.int32, device=dev) if accepted_nodes else None)
-    ws = _workspace(lib.sv_tree_sampled_workspace_bytes(B, N, V, dt), dev, workspace)
+    with _on(stream):
+        if out is None:
+            out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                       emitted=torch.empty((B, w), dtype=torch.int32, device=dev),
+                       accepted_nodes=torch.empty((B, w), dtype=torch.int32, device=dev) if accepted_nodes else None)
+        ws = _workspace(lib.sv_tree_sampled_workspace_bytes(B, N, V, dt), dev, workspace)
     st = lib.sv_verify_tree_sampled(B, N, V, dt, _ptr(node_tokens), _ptr(parent), stride, max_depth,
                                     _ptr(draft_logits), _ptr(target_logits), _ptr(temperature), _ptr(uniforms),
                                     _ptr(out["accepted_len"]), _ptr(out["emitted"]), _ptr(out["accepted_nodes"]),
@@ -278,9 +290,10 @@ def commit_tokens(accepted_len, emitted, seq_len, history=None, *, packed: bool 
             raise ValueError("history must be [B, capacity]")
         stride = history.shape[1]
     if out is None:
-        out = dict(packed_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev) if packed else None,
-                   packed=torch.empty(max(B * width, 1), dtype=torch.int32, device=dev) if packed else None,
-                   status=torch.empty(B, dtype=torch.int32, device=dev) if status else None)
+        with _on(stream):
+            out = dict(packed_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev) if packed else None,
+                       packed=torch.empty(max(B * width, 1), dtype=torch.int32, device=dev) if packed else None,
+                       status=torch.empty(B, dtype=torch.int32, device=dev) if status else None)
     st = lib.sv_commit_tokens(B, width, _ptr(accepted_len), _ptr(emitted), _ptr(seq_len), _ptr(history), stride,
                               _ptr(out["packed_offsets"]), _ptr(out["packed"]), _ptr(out["status"]), _stream(stream))
     if st != SV_OK:

@@ -103,7 +103,7 @@ ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
     L.gathered = align_up(L.part + sizeof(Partial) * static_cast<size_t>(2) * B * k * tiles_per_row(V, dt));
     L.info = align_up(L.gathered + sizeof(float) * static_cast<size_t>(2) * B * k);
     L.segs = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
-    L.chunkarg = align_up(L.segs + sizeof(Partial) * static_cast<size_t>(B) * segments_per_row(V, dt));
+    L.chunkarg = align_up(L.segs + sizeof(sv::SegMass) * static_cast<size_t>(B) * segments_per_row(V, dt));
     L.go = align_up(L.chunkarg + sizeof(Partial) * static_cast<size_t>(B) * final_chunks(V, dt));
     L.total = align_up(L.go + sizeof(int32_t) * static_cast<size_t>(B));
     return L;
@@ -131,7 +131,7 @@ TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
     L.dg = align_up(L.tg + sizeof(float) * bn);
     L.state = align_up(L.dg + sizeof(float) * bn);
     L.z = align_up(L.state + sizeof(sv::WalkState) * 2 * static_cast<size_t>(B));
-    L.tsegs = align_up(L.z + sizeof(double) * 2 * static_cast<size_t>(B) * L.P);
+    L.tsegs = align_up(L.z + sizeof(double) * 4 * 2 * static_cast<size_t>(B) * L.P);
     L.norm = align_up(L.tsegs + sizeof(float) * static_cast<size_t>(B) * nseg);
     L.leaf = align_up(L.norm + sizeof(sv::NodeNorm) * bn);
     L.total = align_up(L.leaf + sizeof(Partial) * static_cast<size_t>(B) * nseg);
@@ -212,7 +212,7 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
     auto* part = reinterpret_cast<Partial*>(ws + L.part);
     auto* gathered = reinterpret_cast<float*>(ws + L.gathered);
     auto* info = reinterpret_cast<SeqInfo*>(ws + L.info);
-    auto* segs = reinterpret_cast<Partial*>(ws + L.segs);
+    auto* segs = reinterpret_cast<sv::SegMass*>(ws + L.segs);
     auto* chunkarg = reinterpret_cast<Partial*>(ws + L.chunkarg);
     sv_status st;
     const int64_t fin_blocks = static_cast<int64_t>(B) * nchunk;
@@ -270,8 +270,8 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                 static_cast<const float*>(gathered), nchunk, accepted_len, emitted, accept_prob, info, segs,
                 chunkarg);
     if (st != SV_OK) return st;
-    return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kWave), stream, draft,
-                  target, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const Partial*>(segs),
+    return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kPickBlock), stream, draft,
+                  target, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const sv::SegMass*>(segs),
                   static_cast<const Partial*>(chunkarg), emitted);
 }
 
@@ -588,8 +588,8 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
                     target_logits, temperature, uniforms, B, V, nT, static_cast<const Partial*>(part),
                     static_cast<const float*>(tg), static_cast<const float*>(dg),
                     static_cast<const sv::WalkState*>(state + (r & 1) * B), state + ((r + 1) & 1) * B,
-                    static_cast<const double*>(z + static_cast<size_t>(r & 1) * B * L.P),
-                    z + static_cast<size_t>((r + 1) & 1) * B * L.P, tsegs, norm, leafpart, L.P, r == 0 ? 1 : 0,
+                    static_cast<const double*>(z + static_cast<size_t>(r & 1) * 4 * B * L.P),
+                    z + static_cast<size_t>((r + 1) & 1) * 4 * B * L.P, tsegs, norm, leafpart, L.P, r == 0 ? 1 : 0,
                     accepted_len,
                     emitted, accepted_nodes);
         if (st != SV_OK) return st;

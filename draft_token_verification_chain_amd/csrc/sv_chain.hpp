@@ -183,7 +183,7 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     if (lane == (a < k ? a : 0)) {
         SeqInfo si{};
         si.a = a;
-        temperature_scale(sampled ? T : 1.f, si.c_hi, si.c_lo);
+        temperature_scale(sampled ? T : 1.f, si);
         si.u = uk;
         if (!sampled) {
             if (a < k) {
@@ -196,8 +196,9 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
             si.mode = kFinalResidual;
             si.rt = static_cast<float>(rt);
             si.inv_st = static_cast<float>(1.0 / st);
-            si.rd = static_cast<float>(rd);
-            si.inv_sd = static_cast<float>(1.0 / sd);
+            si.st = static_cast<float>(st);
+            // log2(S_t / S_d) in the target row's reference; the draw corrects it
+            set_kappa(si, static_cast<double>(rt - rd) + (log2(st) - log2(sd)));
         } else {
             si.mode = kFinalBonus;
         }
@@ -276,19 +277,9 @@ __global__ __launch_bounds__(kAccWaves * kWave) void chain_accept_kernel(
 
 // ---------------------------------------------------------------- chain: final draw ---
 
-// Weight of the final draw for the U*VE elements a lane holds.
-//   residual: w = max(0, p - q), p = exp2(l_t c - rt) / S_t, q likewise;
+// Weights of the final draw for the elements a lane holds.
+//   residual: w = max(0, x), x the residual term (p - c q) S_t, see residual_term;
 //   bonus:    w = exp2(l c - ref), unnormalised (the draw is scale-free).
-template <int NE, bool FULL>
-__device__ __forceinline__ void residual_weights(const float* vt, const float* vd, const SeqInfo& s, float* w) {
-#pragma unroll
-    for (int j = 0; j < NE; ++j) {
-        const float p = exp_term<FULL>(vt[j], s.c_hi, s.c_lo, s.rt) * s.inv_st;
-        const float q = exp_term<FULL>(vd[j], s.c_hi, s.c_lo, s.rd) * s.inv_sd;
-        w[j] = fmaxf(p - q, 0.f);
-    }
-}
-
 template <int NE, bool FULL>
 __device__ __forceinline__ void bonus_weights(const float* v, const SeqInfo& s, float ref, float* w) {
 #pragma unroll
@@ -307,7 +298,7 @@ __device__ __forceinline__ void segment_weights_t(const void* draft, const void*
     if (residual) {
         float vd[VE];
         load_tile<DT, VEC, 1, FULL>(draft, drow, V, seg, lane_id(), vd);
-        residual_weights<VE, FULL>(vt, vd, s, w);
+        residual_weights<DT, VE, FULL>(vt, vd, s, w);
     } else {
         bonus_weights<VE, FULL>(vt, s, ref, w);
     }
@@ -385,7 +376,7 @@ constexpr int kSegPerChunk = kFinWaves * kFinU;  // segments per workgroup and t
 template <int DT, bool VEC, bool FULL>
 __device__ __forceinline__ void final_tile(const void* draft, const void* target, int64_t trow, int64_t drow,
                                            int V, int64_t tile, int64_t nseg, const SeqInfo& si, int mode,
-                                           Partial* __restrict__ seg_out, ArgMax& best) {
+                                           SegMass* __restrict__ seg_out, ArgMax& best) {
     constexpr int VE = Elem<DT>::per_vec;
     constexpr int NE = kFinU * VE;
     const int lane = lane_id();
@@ -395,27 +386,40 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
         best = better(best, argmax_of_tile<DT, kFinU>(w, tile));
         return;
     }
-    float ref = 0.f;
+    static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
+    float a[kFinU];
+    int i_own;
     if (mode == kFinalResidual) {
         float vd[NE];
         load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
-        residual_weights<NE, FULL>(w, vd, si, w);
-    } else {
-        float mx = w[0];
+        float e[kFinU], x[kFinU], sw[kFinU];
 #pragma unroll
-        for (int j = 1; j < NE; ++j) mx = fmaxf(mx, w[j]);
-        // a reference over the whole tile (which always holds an element of the row)
-        ref = ceilf(wave_max(mx) * si.c_hi);
-        bonus_weights<NE, FULL>(w, si, ref, w);
+        for (int i = 0; i < kFinU; ++i) {
+            const ResidualSums r = residual_sums<DT, VE, FULL>(w + i * VE, vd + i * VE, si);
+            a[i] = r.m;
+            e[i] = r.ea;
+            x[i] = r.x;
+            sw[i] = r.sw;
+        }
+        const float m = wave_sum4(a, i_own);
+        const float ea = wave_sum4(e, i_own);
+        const float xs = wave_sum4(x, i_own);
+        const float ss = wave_sum4(sw, i_own);
+        const int64_t g = tile * kFinU + i_own;
+        if (lane < kFinU && g < nseg) seg_out[g] = residual_seg(m, ea, xs, ss);
+        return;
     }
-    static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
-    float a[kFinU];
+    float mx = w[0];
+#pragma unroll
+    for (int j = 1; j < NE; ++j) mx = fmaxf(mx, w[j]);
+    // a reference over the whole tile (which always holds an element of the row)
+    const float ref = ceilf(wave_max(mx) * si.c_hi);
+    bonus_weights<NE, FULL>(w, si, ref, w);
 #pragma unroll
     for (int i = 0; i < kFinU; ++i) a[i] = pairwise_sum<VE>(w + i * VE);
-    int i_own;
     const float m = wave_sum4(a, i_own);
     const int64_t g = tile * kFinU + i_own;
-    if (lane < kFinU && g < nseg) seg_out[g] = Partial{m, static_cast<int>(ref)};
+    if (lane < kFinU && g < nseg) seg_out[g] = bonus_seg(m, static_cast<int>(ref));
 }
 
 template <int DT, bool VEC, int ACC>
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
-    SeqInfo* __restrict__ info, Partial* __restrict__ segs, Partial* __restrict__ chunkarg) {
+    SeqInfo* __restrict__ info, SegMass* __restrict__ segs, Partial* __restrict__ chunkarg) {
     constexpr int VE = Elem<DT>::per_vec;
     __shared__ ArgMax s_arg[kFinWaves];
     const int64_t b = blockIdx.x / nchunk;
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
         const float T = temperature[b];
         si = SeqInfo{};
         si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
-        temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+        temperature_scale(T > 0.f ? T : 1.f, si);
         si.u = uniforms[b];
         if (c == 0 && threadIdx.x == 0) {
             info[b] = si;
@@ -461,7 +465,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
     const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
     const int wave = threadIdx.x / kWave;
     const int64_t tile = static_cast<int64_t>(c) * kFinWaves + wave;  // the workgroup's waves read adjacent tiles
-    Partial* seg_out = segs + b * nseg;
+    SegMass* seg_out = segs + b * nseg;
     ArgMax best{-__builtin_inff(), kNoIndex};
     if (tile * kFinU < nseg) {
         if (tile_is_full<VEC, kFinU>(tile, V, VE))
@@ -514,12 +518,24 @@ __device__ int pick_from_target_row(const void* target, int64_t trow, int V, int
 // segments; a wave prefix over the run totals gives every segment's starting
 // mass, the segment holding u * W is found with a ballot, and only that
 // segment is read again to find the token.  `first` holds the lane's first
-// kSegRun segments, loaded by the caller (ahead of the descriptor).
+// kSegRun segments, loaded by the caller (ahead of the descriptor).  A
+// residual draw first corrects kappa from the row's total X (kappa_zeta) and
+// every segment's mass to first order; the segment read again is weighed with
+// the corrected kappa, which is also returned.  When that first order cannot
+// be trusted (correction_trusted) the token is kRedo: the caller forms the
+// masses again with the corrected kappa (exact_residual_masses) and draws
+// from them.
 constexpr int kSegRun = 8;
+constexpr int kRedo = -2;
+
+struct Draw {
+    int y;
+    double kappa;
+};
 
 template <int DT, bool VEC>
-__device__ int draw_from_segments(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
-                                  int64_t nseg, const SeqInfo& s, const Partial* sg, const Partial* first) {
+__device__ Draw draw_from_segments(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
+                                   int64_t nseg, SeqInfo s, const SegMass* sg, const SegMass* first) {
     constexpr int VE = Elem<DT>::per_vec;
     const int lane = lane_id();
     const int64_t per = (nseg + kWave - 1) / kWave;
@@ -527,26 +543,45 @@ __device__ int draw_from_segments(const void* draft, const void* target, int64_t
     const bool residual = s.mode == kFinalResidual;
     const int64_t nwin = (per + kSegRun - 1) / kSegRun;
     // segment g of this lane's window w
-    auto seg_at = [&](int64_t w, int j) -> Partial {
+    const SegMass zero = residual ? residual_seg(0.f, 0.f, 0.f, 0.f) : bonus_seg(0.f, kNoRef);
+    auto seg_at = [&](int64_t w, int j) -> SegMass {
         const int64_t g = g0 + w * kSegRun + j;
-        return w == 0 ? first[j] : (g < g1 ? sg[g] : Partial{0.f, kNoRef});
+        return w == 0 ? first[j] : (g < g1 ? sg[g] : zero);
     };
-    // global reference exponent (residual masses are absolute: reference 0)
+    auto in_run = [&](int64_t w, int j) { return g0 + w * kSegRun + j < g1; };
+    // residual: the correction zeta of kappa from the row's total X; bonus:
+    // the global reference exponent
     int R = 0;
-    if (!residual) {
+    double zeta = 0.0, sw = 0.0;
+    if (residual) {
+        // fp32 sums suffice: zeta needs X to about 1e-6 of sum |x|, and SW is a bound
+        float xs = 0.f, ss = 0.f;
+        for (int64_t w = 0; w < nwin; ++w)
+#pragma unroll
+            for (int j = 0; j < kSegRun; ++j)
+                if (in_run(w, j)) {
+                    xs += seg_at(w, j).x;
+                    ss += seg_at(w, j).sw;
+                }
+        zeta = kappa_zeta(static_cast<double>(wave_sum(xs)), static_cast<double>(s.st));
+        sw = static_cast<double>(wave_sum(ss));
+        set_kappa(s, s.kappa + zeta / kLn2);
+    } else {
         R = kNoRef;
         for (int64_t w = 0; w < nwin; ++w)
 #pragma unroll
-            for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).i);
+            for (int j = 0; j < kSegRun; ++j) R = max(R, seg_at(w, j).ref);
         R = wave_max(R);
     }
     // masses of this lane's window w in the global scale
     auto window = [&](int64_t w, double* mg) {
 #pragma unroll
         for (int j = 0; j < kSegRun; ++j) {
-            const Partial q = seg_at(w, j);
-            const bool in = g0 + w * kSegRun + j < g1;
-            mg[j] = !in ? 0.0 : residual ? static_cast<double>(q.f) : ldexp(static_cast<double>(q.f), q.i - R);
+            const SegMass q = seg_at(w, j);
+            const double m = static_cast<double>(q.m);
+            mg[j] = !in_run(w, j) ? 0.0
+                    : residual    ? fmax(0.0, m - zeta * (static_cast<double>(q.ea) - m))
+                                  : ldexp(m, q.ref - R);
         }
     };
     double tot = 0.0;
@@ -560,7 +595,8 @@ __device__ int draw_from_segments(const void* draft, const void* target, int64_t
     const double W = __shfl(incl, kWave - 1, kWave);
     const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
     double P = lane == 0 ? 0.0 : excl;
-    if (!(W > 0.0)) return residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0;
+    if (residual && !correction_trusted(zeta, sw, W)) return Draw{kRedo, s.kappa};
+    if (!(W > 0.0)) return Draw{residual ? pick_from_target_row<DT, VEC>(target, trow, V, nseg, s) : 0, s.kappa};
     const double target_mass = static_cast<double>(s.u) * W;
     int64_t found = -1, last_pos = -1;
     double Pfound = 0.0;
@@ -594,46 +630,146 @@ __device__ int draw_from_segments(const void* draft, const void* target, int64_t
         Ps = 0.0;
         fallback = true;
     }
-    const int tref = residual ? 0 : sg[seg].i;
+    const int tref = residual ? 0 : sg[seg].ref;
     const double scale = ldexp(1.0, tref - R);
     float w[VE];
     segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, static_cast<float>(tref), w);
     int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, scale, target_mass);
     if (y < 0) y = last_positive_in_segment<DT>(w, seg);
+    return Draw{y, s.kappa};
+}
+
+// Residual masses of every segment of rows trow / drow formed with kappa as
+// given in s (every wave of a workgroup of `waves` waves; mass of segment g
+// into m[g]).  The caller synchronises the workgroup before reading m.
+template <int DT, bool VEC>
+__device__ void exact_residual_masses(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
+                                      int64_t nseg, const SeqInfo& s, int waves, float* m) {
+    constexpr int VE = Elem<DT>::per_vec;
+    for (int64_t g = threadIdx.x / kWave; g < nseg; g += waves) {
+        float w[VE];
+        segment_weights<DT, VEC>(draft, target, trow, drow, V, g, s, true, 0.f, w);
+        const float t = wave_sum(pairwise_sum<VE>(w));
+        if (lane_id() == 0) m[g] = t;
+    }
+}
+
+// Inverse CDF of a distribution whose segment masses m are given (one wave;
+// returns the token in every lane, or -1 when the masses sum to zero).  The
+// segment holding u * W is read again with segment_weights (residual: the
+// residual terms with kappa as in s; else exp2(l c - rt)).
+template <int DT, bool VEC>
+__device__ int pick_from_masses_f(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
+                                  int64_t nseg, const SeqInfo& s, bool residual, const float* m, double u) {
+    const int lane = lane_id();
+    const int64_t per = (nseg + kWave - 1) / kWave;
+    const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+    double run = 0.0;
+    for (int64_t g = a; g < e; ++g) run += static_cast<double>(m[g]);
+    const double incl = wave_inclusive_scan(run);
+    const double W = __shfl(incl, kWave - 1, kWave);
+    const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
+    if (!(W > 0.0)) return -1;
+    double P = lane == 0 ? 0.0 : excl;
+    const double target_mass = u * W;
+    int64_t found = -1, last_pos = -1;
+    double Pfound = 0.0;
+    for (int64_t g = a; g < e; ++g) {
+        const double mg = static_cast<double>(m[g]);
+        if (found < 0 && P + mg > target_mass) {
+            found = g;
+            Pfound = P;
+        }
+        if (mg > 0.0) last_pos = g;
+        P += mg;
+    }
+    int fl = first_lane(found >= 0);
+    int64_t seg;
+    double Ps = 0.0;
+    bool fallback = false;
+    if (fl >= 0) {
+        seg = __shfl(found, fl, kWave);
+        Ps = __shfl(Pfound, fl, kWave);
+    } else {
+        const uint64_t mk = __ballot(last_pos >= 0);
+        fl = mk ? 63 - __builtin_clzll(mk) : 0;
+        seg = mk ? __shfl(last_pos, fl, kWave) : 0;
+        fallback = true;
+    }
+    float w[Elem<DT>::per_vec];
+    segment_weights<DT, VEC>(draft, target, trow, drow, V, seg, s, residual, s.rt, w);
+    int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, 1.0, target_mass);
+    if (y < 0) y = last_positive_in_segment<DT>(w, seg);
     return y;
 }
 
 // The lane's first kSegRun segments of draw_from_segments.
-__device__ __forceinline__ void first_segments(const Partial* sg, int64_t nseg, Partial* first) {
+__device__ __forceinline__ void first_segments(const SegMass* sg, int64_t nseg, SegMass* first) {
     const int64_t per = (nseg + kWave - 1) / kWave;
     const int64_t g0 = min<int64_t>(nseg, lane_id() * per), g1 = min<int64_t>(nseg, g0 + per);
 #pragma unroll
-    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : Partial{0.f, kNoRef};
+    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : bonus_seg(0.f, kNoRef);
 }
 
-// Select pass of the final draw: one wave per sequence.  The descriptor and
-// the lane's first segments are loaded together.
+// A residual draw whose first-order kappa correction is not trusted (see
+// draw_from_segments): the workgroup's `waves` waves form the row's masses
+// again with the corrected kappa into m, and wave 0 draws from them (the
+// target row itself when they sum to zero).  Returns the token in wave 0.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kWave) void chain_final_pick_kernel(
+__device__ int redo_residual_draw(const void* draft, const void* target, int64_t trow, int64_t drow, int V,
+                                  int64_t nseg, SeqInfo s, double kappa, int waves, float* m) {
+    set_kappa(s, kappa);
+    exact_residual_masses<DT, VEC>(draft, target, trow, drow, V, nseg, s, waves, m);
+    __syncthreads();
+    int y = 0;
+    if (threadIdx.x < kWave) {
+        y = pick_from_masses_f<DT, VEC>(draft, target, trow, drow, V, nseg, s, true, m, static_cast<double>(s.u));
+        if (y < 0) y = pick_from_target_row<DT, VEC>(target, trow, V, nseg, s);
+    }
+    return y;
+}
+
+// Select pass of the final draw: one workgroup per sequence, whose wave 0
+// draws the token (the descriptor and the lane's first segments are loaded
+// together); the other waves only help when the masses must be formed again
+// (redo_residual_draw).
+constexpr int kPickBlock = 256;
+constexpr int kMaxSegs = SV_MAX_VOCAB / (4 * 64);  // f32 rows have the most segments
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kPickBlock) void chain_final_pick_kernel(
     const void* __restrict__ draft, const void* __restrict__ target, int k, int V, int nchunk,
-    const SeqInfo* __restrict__ info, const Partial* __restrict__ segs, const Partial* __restrict__ chunkarg,
+    const SeqInfo* __restrict__ info, const SegMass* __restrict__ segs, const Partial* __restrict__ chunkarg,
     int32_t* __restrict__ emitted) {
     constexpr int VE = Elem<DT>::per_vec;
+    __shared__ float s_m[kMaxSegs];
+    __shared__ double s_kappa;
+    __shared__ int s_redo;
     const int64_t b = blockIdx.x;
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
-    const Partial* sg = segs + b * nseg;
-    Partial first[kSegRun];
-    first_segments(sg, nseg, first);
+    const SegMass* sg = segs + b * nseg;
     const SeqInfo s = info[b];
     if (s.mode == kFinalDone) return;
-    int y;
-    if (s.mode == kFinalArgmax) {
-        y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;
-    } else {
-        const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
-        const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
-        y = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, s, sg, first);
+    const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
+    if (threadIdx.x < kWave) {
+        SegMass first[kSegRun];
+        first_segments(sg, nseg, first);
+        Draw d{0, s.kappa};
+        if (s.mode == kFinalArgmax)
+            d.y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;
+        else
+            d = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, s, sg, first);
+        if (threadIdx.x == 0) {
+            s_redo = d.y == kRedo;
+            s_kappa = d.kappa;
+            if (d.y != kRedo) emitted[b * (k + 1) + s.a] = d.y;
+        }
     }
+    __syncthreads();
+    if (!s_redo) return;
+    const int y =
+        redo_residual_draw<DT, VEC>(draft, target, trow, drow, V, nseg, s, s_kappa, kPickBlock / kWave, s_m);
     if (threadIdx.x == 0) emitted[b * (k + 1) + s.a] = y;
 }
 
@@ -659,7 +795,7 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
     int32_t* __restrict__ emitted, float* __restrict__ accept_prob) {
     static_assert(ACC == kAcceptNone || ACC == kAcceptInline, "descriptor from the temperature or inline");
     constexpr int VE = Elem<DT>::per_vec;
-    __shared__ Partial s_seg[kRowDrawMaxSegs];
+    __shared__ SegMass s_seg[kRowDrawMaxSegs];
     __shared__ ArgMax s_arg[kRowDrawWaves];
     const int64_t b = blockIdx.x;
     SeqInfo si;
@@ -678,7 +814,7 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
         const float T = temperature[b];
         si = SeqInfo{};
         si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
-        temperature_scale(T > 0.f ? T : 1.f, si.c_hi, si.c_lo);
+        temperature_scale(T > 0.f ? T : 1.f, si);
         si.u = uniforms[b];
     }
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
@@ -695,21 +831,33 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
     }
     if (lane_id() == 0) s_arg[wave] = best;
     __syncthreads();
-    if (wave != 0) return;
-    int y;
-    if (si.mode == kFinalArgmax) {
-        ArgMax r = s_arg[0];
-        for (int w = 1; w < kRowDrawWaves; ++w) r = better(r, s_arg[w]);
-        y = r.idx;
-    } else {
-        Partial first[kSegRun];
-        first_segments(s_seg, nseg, first);
-        y = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_seg, first);
+    __shared__ int s_redo;
+    __shared__ double s_kappa;
+    if (wave == 0) {
+        Draw d{0, si.kappa};
+        if (si.mode == kFinalArgmax) {
+            ArgMax r = s_arg[0];
+            for (int w = 1; w < kRowDrawWaves; ++w) r = better(r, s_arg[w]);
+            d.y = r.idx;
+        } else {
+            SegMass first[kSegRun];
+            first_segments(s_seg, nseg, first);
+            d = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_seg, first);
+        }
+        if (threadIdx.x == 0) {
+            s_redo = d.y == kRedo;
+            s_kappa = d.kappa;
+            if (d.y != kRedo) emitted[b * (k + 1) + si.a] = d.y;
+            if constexpr (ACC == kAcceptNone) accepted_len[b] = 0;
+        }
     }
-    if (threadIdx.x == 0) {
-        emitted[b * (k + 1) + si.a] = y;
-        if constexpr (ACC == kAcceptNone) accepted_len[b] = 0;
-    }
+    __syncthreads();
+    if (!s_redo) return;
+    // wave 0 has read the segment records (before the barrier above), so
+    // their space holds the masses formed again
+    float* m = reinterpret_cast<float*>(s_seg);
+    const int y = redo_residual_draw<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_kappa, kRowDrawWaves, m);
+    if (threadIdx.x == 0) emitted[b * (k + 1) + si.a] = y;
 }
 
 }  // namespace sv

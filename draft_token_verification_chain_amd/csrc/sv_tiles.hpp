@@ -21,13 +21,190 @@ struct SeqInfo {
     int a;         // accepted drafts; the final token goes to emitted[b][a]
     float rt;      // target row a: integer reference of its normaliser
     float inv_st;  //               1 / sum exp2(l c - rt)
-    float rd;      // draft row a: the same
-    float inv_sd;
     float c_hi;    // log2(e) / T as a double-float pair
     float c_lo;
     float u;       // u[b][k]
-    int pad[3];
+    float st;      // sum exp2(l c - rt) of target row a (the residual's normaliser)
+    double kappa;  // residual: log2(c S_t / S_d) with both rows' normalisers in the reference rt
+    double cT;     // log2(e) / T
+    float k_hi;    // kappa as a double-float pair
+    float k_lo;
+    int pad[2];
 };
+static_assert(sizeof(SeqInfo) == 64, "descriptor layout");
+
+// The final draw's statistics of one segment: bonus draws store the mass
+// sum exp2(l c - ref) and its integer reference; residual draws store, in
+// units of the target row's reference, M = sum max(0, x), X = sum x,
+// E = sum of e = exp2(l_t c - r_t) over the elements with x > 0 and SW =
+// sum of e over the elements with |delta| < kSwitch, where x is the
+// element's residual term (see residual_term).
+struct alignas(16) SegMass {
+    float m;
+    union {
+        int ref;   // bonus: reference exponent
+        float ea;  // residual: E
+    };
+    float x;   // residual: X
+    float sw;  // residual: SW
+};
+static_assert(sizeof(SegMass) == 16, "segment record layout");
+
+__device__ __forceinline__ SegMass bonus_seg(float m, int ref) {
+    SegMass s;
+    s.m = m;
+    s.ref = ref;
+    s.x = 0.f;
+    s.sw = 0.f;
+    return s;
+}
+
+__device__ __forceinline__ SegMass residual_seg(float m, float ea, float x, float sw) {
+    SegMass s;
+    s.m = m;
+    s.ea = ea;
+    s.x = x;
+    s.sw = sw;
+    return s;
+}
+
+// ---------------------------------------------------------------- residual terms ---
+//
+// After a rejection the final draw samples w_v = max(0, p_v - c q_v): c = 1 in
+// a chain, and the running residual of a sampled tree after j rejections at a
+// node has this form with c = c_j.  When the draft nearly copies the target,
+// p_v and c q_v nearly cancel.  Formed separately in fp32 they leave an
+// absolute error of about 1e-7 p_v per term, which moves the draw's CDF
+// boundaries C / W by about 1e-7 / W for a residual of total mass W.  So each
+// term is formed with an error relative to itself instead.  In units of the
+// target row's reference r_t,
+//   x_v = e_t - e_q,  e_t = exp2(l_t c - r_t),  e_q = exp2(l_d c - r_t + kappa)
+//       = e_t (1 - 2^delta_v),  delta_v = (l_d - l_t) c + kappa,
+// kappa = log2(c S_t / S_d) with both normalisers in the reference r_t
+// (c = log2(e) / T).  delta_v is evaluated without cancellation error (an
+// exact logit difference, then a double-float or fp64 product and sum).
+// Where |delta| >= 1/8, 1 - 2^delta is at least 0.083 away from 0 and the
+// difference e_t - e_q is already within about 1e-6 of x; below, x is
+// e_t (-expm1(delta ln 2)) by a short series.  Every term then carries an
+// error of about 1e-6 of itself or less, whatever W.  kappa itself comes from
+// the normalisers, which fp32 sums know only to about 1e-7 relative; the draw
+// corrects it from the row's own total X = sum_v x_v = S_t - 2^kappa S_d
+// (see kappa_zeta).
+
+// |delta| below which a term is formed by the series.
+constexpr float kSeries = 0.125f;
+
+// expm1(delta ln 2) for |delta| < kSeries: Taylor series through degree 4
+// (truncation below 5e-7 relative).
+__device__ __forceinline__ float expm1_2(float d) {
+    float s = __builtin_fmaf(d, 9.61812910762847716e-3f, 5.55041086648215800e-2f);
+    s = __builtin_fmaf(d, s, 2.40226506959100712e-1f);
+    s = __builtin_fmaf(d, s, 6.93147180559945309e-1f);
+    return d * s;
+}
+
+// delta = (l_d - l_t) log2(e) / T + kappa.  bfloat16 logits differ exactly in
+// fp32 (unless their exponents lie more than 15 apart), and the products with
+// the double-float scale and offset then carry the cancellation exactly inside
+// the fma; float32 logits take the difference and the product in fp64.
+template <int DT>
+__device__ __forceinline__ float residual_delta(float lt, float ld, const SeqInfo& s);
+
+template <>
+__device__ __forceinline__ float residual_delta<SV_BF16>(float lt, float ld, const SeqInfo& s) {
+    const float d = ld - lt;
+    return __builtin_fmaf(d, s.c_hi, s.k_hi) + __builtin_fmaf(d, s.c_lo, s.k_lo);
+}
+
+template <>
+__device__ __forceinline__ float residual_delta<SV_F32>(float lt, float ld, const SeqInfo& s) {
+    return static_cast<float>(__builtin_fma(static_cast<double>(ld) - static_cast<double>(lt), s.cT, s.kappa));
+}
+
+// One element's residual term x (see above) and its e_t and delta.  l_t must
+// be finite (masked elements are handled by the callers).
+template <int DT>
+__device__ __forceinline__ float residual_term(float lt, float ld, const SeqInfo& s, float& et, float& delta) {
+    delta = residual_delta<DT>(lt, ld, s);
+    const float a = __builtin_fmaf(lt, s.c_lo, __builtin_fmaf(lt, s.c_hi, -s.rt));
+    et = __builtin_amdgcn_exp2f(a);
+    const float eq = __builtin_amdgcn_exp2f(a + delta);
+    const float small = -(et * expm1_2(delta));
+    return __builtin_fabsf(delta) < kSeries ? small : et - eq;
+}
+
+// Residual weights max(0, x) of NE loaded elements (masked elements weigh 0).
+template <int DT, int NE, bool FULL>
+__device__ __forceinline__ void residual_weights(const float* vt, const float* vd, const SeqInfo& s, float* w) {
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        float et, delta;
+        const float x = residual_term<DT>(vt[j], vd[j], s, et, delta);
+        w[j] = (FULL || vt[j] != -__builtin_inff()) ? __builtin_fmaxf(x, 0.f) : 0.f;
+    }
+}
+
+// |delta| below which an element's term may change sign when kappa is
+// corrected (see kappa_zeta): a bound on the correction, which fp32
+// normalisers and the terms' own errors keep below about 1e-6.
+constexpr float kSwitch = 1.9073486328125e-6f;  // 2^-19
+
+// The residual sums of one segment's VE elements held by this lane: M = sum
+// max(0, x), E = sum of e_t over the elements with x > 0, X = sum x and SW =
+// sum of e_t over the elements with |delta| < kSwitch (masked elements
+// contribute nothing).
+struct ResidualSums {
+    float m, ea, x, sw;
+};
+
+template <int DT, int VE, bool FULL>
+__device__ __forceinline__ ResidualSums residual_sums(const float* vt, const float* vd, const SeqInfo& s) {
+    float mm[VE], ee[VE], xx[VE], ss[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+        float et, delta;
+        float t = residual_term<DT>(vt[j], vd[j], s, et, delta);
+        if (!FULL && vt[j] == -__builtin_inff()) t = et = 0.f;
+        xx[j] = t;
+        mm[j] = __builtin_fmaxf(t, 0.f);
+        ee[j] = delta < 0.f ? et : 0.f;
+        ss[j] = __builtin_fabsf(delta) < kSwitch ? et : 0.f;
+    }
+    return ResidualSums{pairwise_sum<VE>(mm), pairwise_sum<VE>(ee), pairwise_sum<VE>(xx), pairwise_sum<VE>(ss)};
+}
+
+// The correction of kappa from a residual pass at c = 1: X = sum_v x_v =
+// S_t (1 - 2^(kappa_used - kappa_true)), so kappa_true = kappa_used + zeta /
+// ln 2 with zeta = -ln(1 - X / S_t), accurate to a few 1e-6 of the residual's
+// mass W whatever W (each x_v carries an error of about 1e-6 of itself, and
+// sum |x_v| = 2 W S_t).  To first order in zeta every term with x > 0 moves
+// by -zeta (e_t - x), so a segment's mass becomes M - zeta (E - M); zeta is
+// of the order of 1e-7, so second-order terms (1e-14) do not matter.  What
+// the first order misses are terms that change sign, those with |delta| <
+// |zeta| / ln 2, each by at most 2 |zeta| e_t.  The correction is therefore
+// trusted only when |zeta| / ln 2 <= kSwitch and 2 |zeta| SW <= kRedoTol
+// times the corrected mass; otherwise the masses are formed again with the
+// corrected kappa.
+__device__ __forceinline__ double kappa_zeta(double X, double St) {
+    const double y = X / St;  // |y| of the order of 1e-7: -ln(1 - y) to within 1e-21
+    return y + 0.5 * y * y;
+}
+
+constexpr double kRedoTol = 1e-7;
+
+__device__ __forceinline__ bool correction_trusted(double zeta, double sw, double mass) {
+    return fabs(zeta) <= static_cast<double>(kSwitch) * 0.69314718055994530942 &&
+           2.0 * fabs(zeta) * sw <= kRedoTol * mass;
+}
+
+// Sets kappa and its double-float forms.
+__device__ __forceinline__ void set_kappa(SeqInfo& s, double kappa) {
+    s.kappa = kappa;
+    s.k_hi = static_cast<float>(kappa);
+    s.k_lo = static_cast<float>(kappa - static_cast<double>(s.k_hi));
+}
+
+constexpr double kLn2 = 0.69314718055994530942;
 
 // log2 of a positive double with an exact exponent and an fp32 log2 of the
 // mantissa in [0.5, 1): absolute error about 1.5e-7, far below the 1e-5 band
@@ -42,6 +219,12 @@ __device__ __forceinline__ void temperature_scale(float T, float& c_hi, float& c
     const double c = kLog2e / static_cast<double>(T);
     c_hi = static_cast<float>(c);
     c_lo = static_cast<float>(c - static_cast<double>(c_hi));
+}
+
+// The descriptor's temperature fields: the double-float pair and the double.
+__device__ __forceinline__ void temperature_scale(float T, SeqInfo& s) {
+    temperature_scale(T, s.c_hi, s.c_lo);
+    s.cT = kLog2e / static_cast<double>(T);
 }
 
 // ---------------------------------------------------------------- wave tiles ---

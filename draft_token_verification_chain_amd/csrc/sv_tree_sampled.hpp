@@ -13,9 +13,14 @@ namespace sv {
 // tested in index order against a running distribution r that starts as the
 // target row p_n; a rejection replaces r by the normalised residual
 // max(0, r - q_n).  That residual after j rejections is max(0, p - c_j q) /
-// Z(c_j), Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0, c_{j+1} = c_j + Z(c_j),
-// so a sibling's test needs only the scalars (c, Z) and each rejection one
-// pass over the node's two rows.
+// Z(c_j), Z(c) = sum_v max(0, p_v - c q_v), c_0 = 0, c_{j+1} = c_j + Z(c_j)
+// (an exact identity: max(0, max(0, a) / Z - q) = max(0, a - Z q) / Z for
+// Z > 0), so a sibling's test needs only the scalars (c, Z) and each
+// rejection one pass over the node's two rows.  The passes form each term
+// relative to itself (residual_term, with kappa = log2(c S_t / S_d)), in
+// units of the target row's reference, so Z(c) = M / S_t for the pass's sum M
+// of the terms' positive parts.  The first rejection at a node has c = 1
+// exactly; its pass also corrects the node's log2(S_t / S_d) (kappa_zeta).
 
 // Rows 0 .. B*N-1 are target rows (b, n), rows B*N .. 2*B*N-1 draft rows.
 // A leaf's rows are skipped: its draft row is never needed, and its target
@@ -95,54 +100,78 @@ constexpr int kWalkBlock = 512;
 constexpr int kWalkWaves = kWalkBlock / kWave;
 constexpr int kWalkSlots = SV_MAX_TREE_NODES / kWalkBlock;
 constexpr int kWalkMaxSegs = SV_MAX_VOCAB / (4 * 64);  // f32 rows have the most segments
-constexpr int kWalkUnroll = 8;                          // segments in flight per wave
+constexpr int kWalkUnroll = 4;                          // segments in flight per wave
 
-// Normalised weights of segment g of the running distribution: p when the
-// residual scale c is 0, else max(0, p - c q) (s.inv_sd carries c / S_d).
+// Weights of segment g of the running distribution in units of the target
+// row's reference (S_t times the distribution): p when the residual scale c
+// is 0, else max(0, p - c q) by residual_term (s.kappa = log2(c S_t / S_d)).
 template <int DT, bool VEC>
 __device__ __forceinline__ void walk_weights(const void* draft, const void* target, int64_t row, int V, int64_t g,
                                              const SeqInfo& s, bool residual, float* w) {
-    constexpr int VE = Elem<DT>::per_vec;
     segment_weights<DT, VEC>(draft, target, row, row, V, g, s, residual, s.rt, w);
-    if (!residual) {
-#pragma unroll
-        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
-    }
 }
 
-// Weights of one full segment from its raw 16-byte vectors (the same
-// arithmetic as walk_weights on an unmasked segment).
+// One full segment's mass from its raw 16-byte vectors (the same arithmetic
+// as walk_weights on an unmasked segment), and for a residual its sums E and
+// X (residual_sums).
 template <int DT, bool RESIDUAL>
-__device__ __forceinline__ void walk_weights_raw(const uint4& rt, const uint4& rd, const SeqInfo& s, float* w) {
+__device__ __forceinline__ ResidualSums walk_sums_raw(const uint4& rt, const uint4& rd, const SeqInfo& s) {
     constexpr int VE = Elem<DT>::per_vec;
     float vt[VE];
     unpack<DT>(rt, vt);
     if constexpr (RESIDUAL) {
         float vd[VE];
         unpack<DT>(rd, vd);
-        residual_weights<VE, true>(vt, vd, s, w);
+        return residual_sums<DT, VE, true>(vt, vd, s);
     } else {
+        float w[VE];
         bonus_weights<VE, true>(vt, s, s.rt, w);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) w[e] *= s.inv_st;
+        return ResidualSums{pairwise_sum<VE>(w), 0.f, 0.f, 0.f};
     }
 }
 
-// Every thread of the workgroup: the mass of every segment of the running
-// distribution into s_mass, and their total (ascending order, fp64) as the
-// return value (identical in every thread).  Segments that lie wholly inside
-// the row are read kWalkUnroll per wave at a time with straight-line 16-byte
-// loads (indices clamped rather than branched on, so that all loads are in
-// flight together); the row's tail takes the masked path.
+// The same for a segment that may reach past the row's end (masked path).
 template <int DT, bool VEC, bool RESIDUAL>
-__device__ double walk_masses(const void* draft, const void* target, int64_t row, int V, int64_t nseg,
-                              const SeqInfo& s, float* s_mass, double* s_sum) {
+__device__ __forceinline__ ResidualSums walk_sums(const void* draft, const void* target, int64_t row, int V,
+                                                  int64_t g, const SeqInfo& s) {
+    constexpr int VE = Elem<DT>::per_vec;
+    float vt[VE];
+    load_tile<DT, VEC, 1, false>(target, row, V, g, lane_id(), vt);
+    if constexpr (RESIDUAL) {
+        float vd[VE];
+        load_tile<DT, VEC, 1, false>(draft, row, V, g, lane_id(), vd);
+        return residual_sums<DT, VE, false>(vt, vd, s);
+    } else {
+        float w[VE];
+        bonus_weights<VE, false>(vt, s, s.rt, w);
+        return ResidualSums{pairwise_sum<VE>(w), 0.f, 0.f, 0.f};
+    }
+}
+
+// Totals of one walk pass in units of the target row's reference: M, the
+// running distribution's mass (S_t Z(c) for a residual), and for a residual
+// E, X and SW (see kappa_zeta).
+struct PassSums {
+    double m, ea, x, sw;
+};
+
+// Every thread of the workgroup: the mass of every segment of the running
+// distribution into s_mass (and, for a residual, each segment's E into
+// s_ea), and the totals (fp64, in a fixed order; X summed per wave, then over
+// the waves) as the return value (identical in every thread).  Segments that lie wholly inside the row are
+// read kWalkUnroll per wave at a time with straight-line 16-byte loads
+// (indices clamped rather than branched on, so that all loads are in flight
+// together); the row's tail takes the masked path.
+template <int DT, bool VEC, bool RESIDUAL>
+__device__ PassSums walk_masses(const void* draft, const void* target, int64_t row, int V, int64_t nseg,
+                                const SeqInfo s, float* s_mass, float* s_ea, double* s_wx, PassSums* s_sum) {
     constexpr int VE = Elem<DT>::per_vec;
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
     const int64_t nfull = VEC ? ((V + VE - 1) / VE) / 64 : 0;
     const char* tr = static_cast<const char*>(target) + row * Elem<DT>::bytes;
     const char* dr = static_cast<const char*>(draft) + row * Elem<DT>::bytes;
+    double wx = 0.0, wsw = 0.0;  // this wave's shares of X and SW (the same in every lane)
     for (int64_t g0 = wave; g0 < nfull; g0 += kWalkWaves * kWalkUnroll) {
         uint4 rt[kWalkUnroll], rd[kWalkUnroll];
 #pragma unroll
@@ -154,74 +183,62 @@ __device__ double walk_masses(const void* draft, const void* target, int64_t row
 #pragma unroll
         for (int j = 0; j < kWalkUnroll; ++j) {
             const int64_t g = g0 + j * kWalkWaves;
-            float w[VE];
-            walk_weights_raw<DT, RESIDUAL>(rt[j], rd[j], s, w);
-            const float m = wave_sum(pairwise_sum<VE>(w));
-            if (lane == 0 && g < nfull) s_mass[g] = m;
+            ResidualSums r = walk_sums_raw<DT, RESIDUAL>(rt[j], rd[j], s);
+            r.m = wave_sum(r.m);
+            if constexpr (RESIDUAL) {
+                r.ea = wave_sum(r.ea);
+                r.x = wave_sum(r.x);
+                r.sw = wave_sum(r.sw);
+            }
+            if (g < nfull) {
+                wx += static_cast<double>(r.x);
+                wsw += static_cast<double>(r.sw);
+                if (lane == 0) {
+                    s_mass[g] = r.m;
+                    s_ea[g] = r.ea;
+                }
+            }
         }
     }
     for (int64_t g = nfull + wave; g < nseg; g += kWalkWaves) {
-        float w[VE];
-        walk_weights<DT, VEC>(draft, target, row, V, g, s, RESIDUAL, w);
-        const float m = wave_sum(pairwise_sum<VE>(w));
-        if (lane == 0) s_mass[g] = m;
+        ResidualSums r = walk_sums<DT, VEC, RESIDUAL>(draft, target, row, V, g, s);
+        r.m = wave_sum(r.m);
+        if constexpr (RESIDUAL) {
+            r.ea = wave_sum(r.ea);
+            r.x = wave_sum(r.x);
+            r.sw = wave_sum(r.sw);
+        }
+        wx += static_cast<double>(r.x);
+        wsw += static_cast<double>(r.sw);
+        if (lane == 0) {
+            s_mass[g] = r.m;
+            s_ea[g] = r.ea;
+        }
+    }
+    if (lane == 0) {
+        s_wx[wave] = wx;
+        s_wx[kWalkWaves + wave] = wsw;
     }
     __syncthreads();
     if (wave == 0) {
         const int64_t per = (nseg + kWave - 1) / kWave;
         const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
-        double run = 0.0;
-        for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
-        const double tot = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+        double rm = 0.0, re = 0.0;
+        for (int64_t g = a; g < e; ++g) {
+            rm += static_cast<double>(s_mass[g]);
+            re += static_cast<double>(s_ea[g]);
+        }
+        double rx = 0.0, rs = 0.0;
+        for (int w = 0; w < kWalkWaves; ++w) {
+            rx += s_wx[w];
+            rs += s_wx[kWalkWaves + w];
+        }
+        const PassSums tot{__shfl(wave_inclusive_scan(rm), kWave - 1, kWave),
+                           __shfl(wave_inclusive_scan(re), kWave - 1, kWave), rx, rs};
         if (lane == 0) *s_sum = tot;
     }
     __syncthreads();
     return *s_sum;
-}
-
-// Inverse CDF of the running distribution whose segment masses are in
-// s_mass (wave 0; returns the token in every lane).
-template <int DT, bool VEC>
-__device__ int walk_pick(const void* draft, const void* target, int64_t row, int V, int64_t nseg, const SeqInfo& s,
-                         bool residual, const float* s_mass, double W, double u) {
-    const int lane = lane_id();
-    const int64_t per = (nseg + kWave - 1) / kWave;
-    const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
-    double run = 0.0;
-    for (int64_t g = a; g < e; ++g) run += static_cast<double>(s_mass[g]);
-    const double incl = wave_inclusive_scan(run);
-    const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
-    double P = lane == 0 ? 0.0 : excl;
-    const double target_mass = u * W;
-    int64_t found = -1, last_pos = -1;
-    double Pfound = 0.0;
-    for (int64_t g = a; g < e; ++g) {
-        const double m = static_cast<double>(s_mass[g]);
-        if (found < 0 && P + m > target_mass) {
-            found = g;
-            Pfound = P;
-        }
-        if (m > 0.0) last_pos = g;
-        P += m;
-    }
-    int fl = first_lane(found >= 0);
-    int64_t seg;
-    double Ps = 0.0;
-    bool fallback = false;
-    if (fl >= 0) {
-        seg = __shfl(found, fl, kWave);
-        Ps = __shfl(Pfound, fl, kWave);
-    } else {
-        const uint64_t m = __ballot(last_pos >= 0);
-        fl = m ? 63 - __builtin_clzll(m) : 0;
-        seg = m ? __shfl(last_pos, fl, kWave) : 0;
-        fallback = true;
-    }
-    float w[Elem<DT>::per_vec];
-    walk_weights<DT, VEC>(draft, target, row, V, seg, s, residual, w);
-    int y = fallback ? -1 : pick_in_segment<DT>(w, seg, Ps, 1.0, target_mass);
-    if (y < 0) y = last_positive_in_segment<DT>(w, seg);
-    return y;
 }
 
 // Validity of a tree and the depth of every node (pointer jumping over the
@@ -312,9 +329,31 @@ struct alignas(8) NodeNorm {
 
 struct alignas(16) WalkState {
     int phase, node, depth, kidx;  // kidx: children of `node` already rejected
-    int Rt, Rd, pad0, pad1;        // node statistics (at temperature 0: the two argmaxes)
-    double St, Sd, c, Z;
+    int Rt, Rd;                    // node statistics (at temperature 0: the two argmaxes)
+    int redone;                    // the pending pass at c = 1 was formed with the corrected K
+    int pad;
+    double St;                     // target row's normaliser in the reference Rt
+    double K;                      // log2(S_t / S_d) in the reference Rt (corrected by the first pass)
+    double c, Z;
 };
+
+// log2(S_t / S_d) of a node's two rows with both normalisers in the
+// reference of the target row.
+__device__ __forceinline__ double node_log_ratio(int Rt, int Rd, double St, double Sd) {
+    return static_cast<double>(Rt - Rd) + (log2(St) - log2(Sd));
+}
+
+// The descriptor of a walk's weights at a node: the target row's reference
+// and, for a residual (c > 0), kappa = log2(c S_t / S_d).
+__device__ __forceinline__ SeqInfo walk_info(float T, int Rt, double St, double K, double c) {
+    SeqInfo s{};
+    temperature_scale(T > 0.f ? T : 1.f, s);
+    s.rt = static_cast<float>(Rt);
+    s.inv_st = static_cast<float>(1.0 / St);
+    s.st = static_cast<float>(St);
+    if (c > 0.0) set_kappa(s, K + log2(c));
+    return s;
+}
 
 // The final draw of a walk that stopped at st.node, from the segment masses m
 // of its final distribution (written by the last round): one wave.  Returns
@@ -325,12 +364,7 @@ __device__ bool pick_from_masses(const void* draft, const void* target, int64_t 
     constexpr int VE = Elem<DT>::per_vec;
     const int lane = lane_id();
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
-    SeqInfo s{};
-    temperature_scale(T > 0.f ? T : 1.f, s.c_hi, s.c_lo);
-    s.rt = static_cast<float>(st.Rt);
-    s.inv_st = static_cast<float>(1.0 / st.St);
-    s.rd = static_cast<float>(st.Rd);
-    s.inv_sd = static_cast<float>(st.c / st.Sd);
+    const SeqInfo s = walk_info(T, st.Rt, st.St, st.K, st.c);
     const int64_t per = (nseg + kWave - 1) / kWave;
     const int64_t a0 = min<int64_t>(nseg, lane * per), a1 = min<int64_t>(nseg, a0 + per);
     double run = 0.0;
@@ -338,7 +372,7 @@ __device__ bool pick_from_masses(const void* draft, const void* target, int64_t 
     const double W = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
     if (!(W > 0.0)) return false;
     const int64_t row = (b * N + st.node) * static_cast<int64_t>(V);
-    y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, st.c > 0.0, m, W, static_cast<double>(u));
+    y = pick_from_masses_f<DT, VEC>(draft, target, row, row, V, nseg, s, st.c > 0.0, m, static_cast<double>(u));
     return true;
 }
 
@@ -379,13 +413,15 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     __shared__ int s_len[SV_MAX_TREE_NODES];
     __shared__ uint64_t s_kids[SV_MAX_TREE_NODES / kWave];
     __shared__ float s_mass[kWalkMaxSegs];
+    __shared__ float s_ea[kWalkMaxSegs];
+    __shared__ double s_wx[2 * kWalkWaves];
     // the current node's children in index order: node id, uniform, and the
     // target and draft logits at the child's token
     __shared__ int s_cid[SV_MAX_TREE_NODES];
     __shared__ float s_cu[SV_MAX_TREE_NODES];
     __shared__ float s_clt[SV_MAX_TREE_NODES];
     __shared__ float s_cld[SV_MAX_TREE_NODES];
-    __shared__ double s_sum;
+    __shared__ PassSums s_sum;
     __shared__ double s_norm[2];  // S_t, S_d of the current node
     __shared__ int s_ref[2];      // R_t, R_d (at temperature 0: the two argmaxes)
     __shared__ int s_bad, s_accept;
@@ -412,8 +448,6 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
         return;
     }
 
-    SeqInfo s{};
-    temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
     const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const int nmask = (N + kWave - 1) / kWave;
@@ -477,22 +511,19 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
         __syncthreads();
         const int Rt = s_ref[0], Rd = s_ref[1];
         const double St = s_norm[0], Sd = s_norm[1];
-        s.rt = static_cast<float>(Rt);
-        s.inv_st = static_cast<float>(1.0 / St);
-        s.rd = static_cast<float>(Rd);
         double c = 0.0, Z = 1.0;
         int next = -1;
-        // log2 of the two normalisers' mantissas, once per node (thread 0 tests)
-        const double lsum = t == 0 && sampled && nkids > 0 ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
+        // log2(S_t / S_d), corrected by the first rejection's pass
+        double K = sampled && nkids > 0 ? node_log_ratio(Rt, Rd, St, Sd) : 0.0;
         for (int k = 0; k < nkids && next < 0; ++k) {
             if (t == 0) {
                 const int id = s_cid[k];
                 double tau = 0.0;
                 if (id >= 0) {
                     if (sampled) {
-                        // p/q = exp2((l_t - l_d) c - (R_t + log2 S_t) + (R_d + log2 S_d))
+                        // p/q = exp2((l_t - l_d) c - log2(S_t / S_d))
                         const double lt = s_clt[k], ld = s_cld[k];
-                        const double l2ratio = (lt * cT - ld * cT) - lsum;
+                        const double l2ratio = (lt - ld) * cT - K;
                         tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
                     } else {
                         const int y = node_tokens[b * N + id];
@@ -510,8 +541,38 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
                 // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
                 c += Z;
                 if (sampled) {
-                    s.inv_sd = static_cast<float>(c / Sd);
-                    Z = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+                    PassSums ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
+                                                              s_mass, s_ea, s_wx, &s_sum);
+                    if (c == 1.0) {
+                        // the node's first rejection: correct log2(S_t / S_d), and the
+                        // segment masses (which a final draw at c = 1 uses) to first
+                        // order, or form them again with the corrected value
+                        const double zeta = kappa_zeta(ps.x, St);
+                        K += zeta / kLn2;
+                        const double Mc = ps.m - zeta * (ps.ea - ps.m);
+                        if (correction_trusted(zeta, ps.sw, Mc)) {
+                            for (int64_t g = t; g < nseg; g += kWalkBlock) {
+                                const double m = static_cast<double>(s_mass[g]);
+                                s_mass[g] =
+                                    static_cast<float>(fmax(0.0, m - zeta * (static_cast<double>(s_ea[g]) - m)));
+                            }
+                            __syncthreads();
+                            if (wave == 0) {
+                                const int64_t per = (nseg + kWave - 1) / kWave;
+                                const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+                                double rm = 0.0;
+                                for (int64_t g = a; g < e; ++g) rm += static_cast<double>(s_mass[g]);
+                                rm = __shfl(wave_inclusive_scan(rm), kWave - 1, kWave);
+                                if (lane == 0) s_sum.m = rm;
+                            }
+                            __syncthreads();
+                            ps.m = s_sum.m;
+                        } else {
+                            ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
+                                                            s_mass, s_ea, s_wx, &s_sum);
+                        }
+                    }
+                    Z = ps.m / St;
                 } else {
                     Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
                 }
@@ -536,13 +597,14 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
         if (!sampled) {
             y = Rt;  // one-hot p; with c > 0 the residual is p itself or empty (then p)
         } else {
+            // a residual's segment masses are the last pass's (corrected at c = 1)
             const bool residual = c > 0.0;
-            double W = Z;
-            if (!residual) W = walk_masses<DT, VEC, false>(draft, target, row, V, nseg, s, s_mass, &s_sum);
+            const SeqInfo s = walk_info(T, Rt, St, K, c);
+            if (!residual) walk_masses<DT, VEC, false>(draft, target, row, V, nseg, s, s_mass, s_ea, s_wx, &s_sum);
             y = 0;
             if (wave == 0)
-                y = walk_pick<DT, VEC>(draft, target, row, V, nseg, s, residual, s_mass, W,
-                                       static_cast<double>(uniforms[b * N]));
+                y = pick_from_masses_f<DT, VEC>(draft, target, row, row, V, nseg, s, residual, s_mass,
+                                                static_cast<double>(uniforms[b * N]));
         }
         if (t == 0) {
             out[d] = y;
@@ -599,8 +661,8 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     __shared__ uint64_t s_kids[SV_MAX_TREE_NODES / kWave];
     __shared__ double s_norm[2];
     __shared__ int s_ref[2];
-    __shared__ double s_wsum[kRoundWaves];
-    __shared__ double s_z;
+    __shared__ double s_wsum[kRoundWaves][4];
+    __shared__ double s_z[4];
     __shared__ int s_accept;
     const int64_t b = blockIdx.x / P;
     const int j = static_cast<int>(blockIdx.x - b * P);
@@ -632,9 +694,12 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
             if (cached && !first) r_nrm[q] = norm[b * N + i];
         }
     }
-    double zz = 0.0;
+    // the pending pass's slice sums M, E, X, SW (see walk_masses)
+    double zz[4] = {0.0, 0.0, 0.0, 0.0};
     if (!first && wave == 0)
-        for (int q = lane; q < P; q += kWave) zz += z_in[b * P + q];
+        for (int q = lane; q < P; q += kWave)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zz[e] += z_in[(b * P + q) * 4 + e];
     const float T = temperature[b];
     const bool sampled = T > 0.f;
     WalkState st{};
@@ -688,8 +753,6 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         return;
     }
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
-    SeqInfo s{};
-    temperature_scale(sampled ? T : 1.f, s.c_hi, s.c_lo);
 
     if (st.phase == kWalkPick) {
         // the final distribution's masses were written last round: wave 0 of chunk 0 draws the token
@@ -722,25 +785,42 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         }
     }
     if (st.phase == kWalkPass && wave == 0) {
-        zz = wave_sum(zz);
-        if (lane == 0) s_z = zz;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            zz[e] = wave_sum(zz[e]);
+            if (lane == 0) s_z[e] = zz[e];
+        }
     }
     __syncthreads();
-    int n = st.node, d = st.depth, kidx = st.kidx, Rt = st.Rt, Rd = st.Rd;
-    double St = st.St, Sd = st.Sd, c = st.c, Z = st.Z;
+    int n = st.node, d = st.depth, kidx = st.kidx, Rt = st.Rt, Rd = st.Rd, redone = st.redone;
+    double St = st.St, K = st.K, c = st.c, Z = st.Z;
     int phase = st.phase;
+    bool redo = false;  // form the pending pass again, with the corrected K, this round
     if (phase == kWalkPass) {
-        Z = s_z;
-        if (!(Z > 0.0)) {
-            c = 0.0;
-            Z = 1.0;
+        double M = s_z[0];
+        if (c == 1.0) {
+            // the node's first rejection: correct log2(S_t / S_d) and, to first
+            // order, the pass's mass; or, when that order is not trusted, form
+            // the pass again with the corrected value (once)
+            const double zeta = kappa_zeta(s_z[2], St);
+            K += zeta / kLn2;
+            M -= zeta * (s_z[1] - M);
+            redo = !redone && !correction_trusted(zeta, s_z[3], M);
+            redone = redo;
         }
-        phase = kWalkTest;
+        if (!redo) {
+            Z = M / St;
+            if (!(Z > 0.0)) {
+                c = 0.0;
+                Z = 1.0;
+            }
+            phase = kWalkTest;
+        }
     }
     const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
     const int nmask = (N + kWave - 1) / kWave;
     bool leaf_now = false;
-    for (;;) {
+    while (!redo) {
 #pragma unroll
         for (int q = 0; q < kRoundSlots; ++q) {
             const int i = t + q * kRoundBlock;
@@ -795,14 +875,15 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
             Rt = s_ref[0];
             Rd = s_ref[1];
             St = s_norm[0];
-            Sd = s_norm[1];
+            // log2(S_t / S_d) (a leaf's draft row is never read: Rd = 0, S_d = 1)
+            K = sampled ? node_log_ratio(Rt, Rd, St, s_norm[1]) : 0.0;
             c = 0.0;
             Z = 1.0;
             kidx = 0;
+            redone = 0;
             phase = kWalkTest;
             __syncthreads();  // s_ref and s_norm are reused at the next node
         }
-        const double lsum = t == 0 && sampled ? (Rt + log2(St)) - (Rd + log2(Sd)) : 0.0;
         int next = -1, rank = 0;
         bool pass = false;
         for (int m = 0; m < nmask && next < 0 && !pass; ++m) {
@@ -816,8 +897,9 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
                     double tau = 0.0;
                     if (static_cast<unsigned>(y) < static_cast<unsigned>(V)) {
                         if (sampled) {
-                            const double l2ratio = (static_cast<double>(s_tg[i]) * cT -
-                                                    static_cast<double>(s_dg[i]) * cT) - lsum;
+                            // p/q = exp2((l_t - l_d) c - log2(S_t / S_d))
+                            const double l2ratio =
+                                (static_cast<double>(s_tg[i]) - static_cast<double>(s_dg[i])) * cT - K;
                             tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
                         } else {
                             const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
@@ -881,31 +963,33 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     if (phase == kWalkPass || phase == kWalkPick) {
         // this workgroup's slice of the segments of node n's rows
         const int64_t row = (b * N + n) * static_cast<int64_t>(V);
-        s.rt = static_cast<float>(Rt);
-        s.inv_st = static_cast<float>(1.0 / St);
-        s.rd = static_cast<float>(Rd);
-        s.inv_sd = static_cast<float>(c / Sd);
+        const SeqInfo s = walk_info(T, Rt, St, K, c);
         const bool residual = c > 0.0;
         const int64_t spc = (nseg + P - 1) / P;
         const int64_t g0 = j * spc, g1 = min<int64_t>(nseg, g0 + spc);
-        double acc = 0.0;
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
         for (int64_t g = g0 + wave; g < g1; g += kRoundWaves) {
-            float w[VE];
-            walk_weights<DT, VEC>(draft, target, row, V, g, s, residual, w);
-            const float m = wave_sum(pairwise_sum<VE>(w));
+            const ResidualSums r = residual ? walk_sums<DT, VEC, true>(draft, target, row, V, g, s)
+                                            : walk_sums<DT, VEC, false>(draft, target, row, V, g, s);
+            const float m = wave_sum(r.m);
             if (phase == kWalkPick) {
                 if (lane == 0) tsegs[b * nseg + g] = m;
             } else {
-                acc += static_cast<double>(m);
+                acc[0] += static_cast<double>(m);
+                acc[1] += static_cast<double>(wave_sum(r.ea));
+                acc[2] += static_cast<double>(wave_sum(r.x));
+                acc[3] += static_cast<double>(wave_sum(r.sw));
             }
         }
         if (phase == kWalkPass) {
-            if (lane == 0) s_wsum[wave] = acc;
+            if (lane == 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s_wsum[wave][e] = acc[e];
             __syncthreads();
-            if (t == 0) {
+            if (t < 4) {
                 double z = 0.0;
-                for (int w = 0; w < kRoundWaves; ++w) z += s_wsum[w];
-                z_out[b * P + j] = z;
+                for (int w = 0; w < kRoundWaves; ++w) z += s_wsum[w][t];
+                z_out[(b * P + j) * 4 + t] = z;
             }
         }
     }
@@ -917,7 +1001,8 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         st.Rt = Rt;
         st.Rd = Rd;
         st.St = St;
-        st.Sd = Sd;
+        st.K = K;
+        st.redone = redone;
         st.c = c;
         st.Z = Z;
         st_out[b] = st;

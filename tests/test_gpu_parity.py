@@ -190,13 +190,14 @@ def test_greedy_two_phase(svl, orc, two_phase_ws, case):
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
-def test_full_tree_workload(svl, orc, seed):
-    inp = W.make_inputs("eagle_tree", seed)
+@pytest.mark.parametrize("name", ["eagle_tree", "eagle_tree_distinct"])
+def test_full_tree_workload(svl, orc, name, seed):
+    inp = W.make_inputs(name, seed)
     got = run_tree(svl, inp)
     ref = orc.verify_tree(inp)
     for key in ("accepted_len", "emitted", "accepted_nodes"):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
-    _record("tree", f"eagle_tree seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
+    _record("tree", f"{name} seed{seed}", dict(n=inp["B"], mean_accepted=float(got["accepted_len"].mean())))
 
 
 def test_determinism(svl):

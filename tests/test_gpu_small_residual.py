@@ -1,0 +1,128 @@
+"""Parity in the high-acceptance regime: draws from residuals of small mass.
+
+When the draft distribution nearly equals the target's, a rejection leaves a
+residual max(0, p - q) of small total mass W, and every CDF boundary C / W of
+the final draw is a ratio of two small sums.  The pages require the output to
+follow the target distribution after any rejection ("Accelerating Sonar
+through speculation", section "Target-Draft"), so these draws must match the
+fp64 oracle bit-exactly outside the 1e-5 band like any other.
+
+The inputs force one rejection per sequence on near-copy draft rows (see
+workloads.near_copy_chain_inputs and near_copy_tree_inputs): float32 rows with
+small Gaussian noise (with and without a per-sequence logit offset, which
+leaves the distribution unchanged but makes the logits of the two rows
+differ by up to 4), and bfloat16 rows that differ from the target's in a
+sparse set of one-unit bumps.  Each batch is verified with several sets of
+final-draw uniforms; every draw is compared with the oracle's.  The residual
+masses of the compared draws span about 1e-2 to 1e-5 (chains) and 5e-3 to
+3e-6 (trees, after one to three rejections at a node).
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_common import chain_tensors, compare_chain, compare_tree_sampled, tree_sampled_tensors
+
+pytestmark = pytest.mark.gpu
+
+V = 128256
+
+
+@pytest.fixture(scope="module")
+def svl():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import draft_token_verification_chain_amd as svl
+
+    svl.load()
+    return svl
+
+
+def _decades(mass):
+    """Counts of draws per decade of residual mass ("<1e-06" below 1e-6)."""
+    edges = [0.0, 1e-6, 1e-5, 1e-4, 1e-3, 1e-2, 1e-1, 1.0]
+    h, _ = np.histogram(mass, bins=edges)
+    return {("<1e-06" if lo == 0.0 else f"{lo:.0e}"): int(c) for lo, c in zip(edges[:-1], h)}
+
+
+# name, dtype, generator keywords, B, sets of final-draw uniforms.  B covers the
+# three final-draw forms: descriptors recomputed by every workgroup (B * chunks
+# <= 2048), written once by an acceptance kernel (larger), and one workgroup per
+# sequence (bf16 rows of at most 256 segments from B = 256).
+CHAIN_CASES = [
+    ("f32 sigma 2e-2 offset", W.F32, dict(draft_sigma=2e-2, offset=(-4.0, 4.0)), 64, 32),
+    ("f32 sigma 2e-3 offset", W.F32, dict(draft_sigma=2e-3, offset=(-4.0, 4.0)), 128, 16),
+    ("f32 sigma 2e-4 offset", W.F32, dict(draft_sigma=2e-4, offset=(-4.0, 4.0)), 64, 32),
+    ("f32 sigma 2e-4", W.F32, dict(draft_sigma=2e-4), 128, 16),
+    ("bf16 density 0.3", W.BF16, dict(density=0.3), 128, 16),
+    ("bf16 density 0.3 one workgroup per row", W.BF16, dict(density=0.3), 256, 8),
+    ("bf16 density 0.03", W.BF16, dict(density=0.03), 192, 11),
+]
+
+
+@pytest.mark.parametrize("case", CHAIN_CASES, ids=[c[0] for c in CHAIN_CASES])
+def test_chain_small_residual(svl, orc, case):
+    import torch
+
+    name, dt, kw, B, R = case
+    inp = W.near_copy_chain_inputs(B, 2, V, dt, seed=11, **kw)
+    t = chain_tensors(inp)
+    ru = np.random.Generator(np.random.Philox(key=[11, 77]))
+    masses, banded, banded_diff, forced = [], 0, 0, 0
+    for r in range(R):
+        inp["uniforms"][:, 2] = ru.random(B, dtype=np.float32)
+        t["uniforms"].copy_(torch.from_numpy(inp["uniforms"]))
+        out = svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                               t["uniforms"])
+        torch.cuda.synchronize()
+        got = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+        ref = orc.verify_chain(inp)
+        st = compare_chain(inp, got, ref, f"{name} set {r}")
+        banded += st["banded"]
+        banded_diff += st["banded_mismatch"]
+        forced += int((ref["accepted_len"] == inp["reject_at"]).sum())
+        masses.append(ref["final_mass"])
+    mass = np.concatenate(masses)
+    print(f"[small residual] chain {name}: {mass.size} draws, {forced} forced rejections, banded {banded} "
+          f"(differing {banded_diff}), mass decades {_decades(mass)}", flush=True)
+    assert forced == B * R
+    assert mass.max() < 0.05
+
+
+TREE_CASES = [
+    ("f32 sigma 2e-3 offset", W.F32, dict(draft_sigma=2e-3, offset=(-4.0, 4.0)), 48, 16),
+    ("f32 sigma 2e-4", W.F32, dict(draft_sigma=2e-4), 48, 16),
+    ("bf16 density 0.3", W.BF16, dict(density=0.3), 48, 16),
+]
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=[c[0] for c in TREE_CASES])
+def test_tree_small_residual(svl, orc, case):
+    import torch
+
+    name, dt, kw, B, R = case
+    inp = W.near_copy_tree_inputs(B, V, dt, seed=13, **kw)
+    t = tree_sampled_tensors(inp)
+    ru = np.random.Generator(np.random.Philox(key=[13, 77]))
+    want_nodes = np.array([[-1, -1, -1], [1, -1, -1], [2, -1, -1]])[np.arange(B) % 3]
+    masses, banded, banded_diff = [], 0, 0
+    for r in range(R):
+        inp["uniforms"][:, 0] = ru.random(B, dtype=np.float32)
+        t["uniforms"].copy_(torch.from_numpy(inp["uniforms"]))
+        out = svl.verify_tree_sampled(t["node_tokens"], t["parent"], int(inp["max_depth"]), t["draft_logits"],
+                                      t["target_logits"], t["temperature"], t["uniforms"])
+        torch.cuda.synchronize()
+        got = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
+        ref = orc.verify_tree_sampled(inp)
+        assert (ref["accepted_nodes"] == want_nodes).all()
+        st = compare_tree_sampled(got, ref, f"{name} set {r}")
+        banded += st["banded"]
+        banded_diff += st["banded_mismatch"]
+        masses.append(ref["final_mass"])
+    mass = np.concatenate(masses)
+    print(f"[small residual] tree {name}: {mass.size} draws, banded {banded} (differing {banded_diff}), "
+          f"mass decades {_decades(mass)}", flush=True)
+    assert mass.max() < 0.05

@@ -10,8 +10,8 @@ import workloads as W
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])
-def test_eagle_tree_siblings_carry_distinct_tokens(seed):
-    inp = W.make_inputs("eagle_tree", seed, B=4, V=3000)
+def test_eagle_tree_distinct_siblings_carry_distinct_tokens(seed):
+    inp = W.make_inputs("eagle_tree_distinct", seed, B=4, V=3000)
     par = inp["parent"]
     for b in range(inp["B"]):
         for n in range(inp["N"]):
@@ -31,9 +31,9 @@ def test_tree_parent_array_is_topological_and_within_depth():
 
 
 def test_tree_match_rate_follows_match_p():
-    # a child carries its parent row's first argmax with probability match_p
-    # (distinct siblings lower it a little: a later sibling cannot repeat it)
-    inp = W.make_inputs("eagle_tree", 7, B=64, V=400, distinct_siblings=False)
+    # a child of the EAGLE-style workload carries its parent row's first argmax
+    # with probability match_p, independently of its siblings
+    inp = W.make_inputs("eagle_tree", 7, B=64, V=400)
     vals = W.values(inp["target_logits"], inp["dtype"])
     top = np.argmax(vals, axis=-1)
     par = inp["parent"]

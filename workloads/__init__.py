@@ -190,6 +190,148 @@ def repeated_trials(target_vals: np.ndarray, draft_vals: np.ndarray, temperature
                 uniforms=ru.random((n, k + 1), dtype=np.float32))
 
 
+# ------------------------------------------------------------ near-copy drafts ---
+
+# The largest float32 below 1: a test uniform that rejects every draft whose
+# acceptance probability is below 1 - 2^-24.
+U_MAX = np.float32(1.0) - np.float32(2.0 ** -24)
+
+
+def bump_bf16(bits: np.ndarray, mask: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns moved by one unit in the last place where ``mask``:
+    away from zero where ``up``, towards zero elsewhere (finite, nonzero inputs)."""
+    out = np.array(bits, dtype=np.uint16, copy=True)
+    step = np.where(up, 1, -1).astype(np.int32)
+    out[mask] = (out[mask].astype(np.int32) + step[mask]).astype(np.uint16)
+    return out
+
+
+def near_copy_chain_inputs(B: int, k: int, V: int, dtype: int, seed: int, *, draft_sigma: float = 0.0,
+                           density: float = 0.0, offset=0.0, temperature=0.7, target_sigma: float = 3.0,
+                           zipf_s: float | None = 1.1) -> dict:
+    """Chain inputs whose draft rows nearly copy the target rows, with every
+    sequence forced to reject one draft (so that the final draw is a residual
+    of small mass).
+
+    target logits  t[b, j, :] = target_sigma * N(0,1) (+ Zipf bias), j = 0..k
+    draft logits   float32: d[b, i, :] = t[b, i, :] + offset_b + draft_sigma * N(0,1)
+                   bfloat16: d = t, with a random subset of density ``density`` of
+                   each row moved one bf16 unit up or down (equally likely)
+    ``offset``: a scalar or a (lo, hi) tuple (per-sequence uniform draw); a shift
+    of a whole row leaves its distribution unchanged.
+    Rejection position j_b uniform in 0..k-1.  Drafts before j_b are drawn from
+    the draft softmax and tested with u = 0 (always kept); the draft at j_b is
+    the token with the largest d - t (the largest draft/target ratio) and is
+    tested with u = U_MAX; u[b, k] drives the residual draw.  Drafts after j_b
+    are drawn from the draft softmax (never tested).
+    """
+    assert k >= 1
+    temps = _per_seq(temperature, B, seed, "temperature")
+    offs = _per_seq(offset, B, seed, "sigma")
+    bias = zipf_bias(V, zipf_s, seed) if zipf_s else None
+    rt, rd, rx = rng_for(seed, "target"), rng_for(seed, "draft"), rng_for(seed, "draft_tokens")
+    ru = rng_for(seed, "uniforms")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, k + 1, V), dtype=np_dt)
+    draft = np.empty((B, k, V), dtype=np_dt)
+    tokens = np.empty((B, k), dtype=np.int32)
+    uniforms = ru.random((B, k + 1), dtype=np.float32)
+    reject_at = rx.integers(0, k, size=B).astype(np.int32)
+    for b in range(B):
+        t = target_sigma * rt.standard_normal((k + 1, V), dtype=np.float32)
+        if bias is not None:
+            t = t + bias
+        target[b] = to_dtype(t, dtype)
+        if dtype == BF16:
+            mask = rd.random((k, V)) < density
+            up = rd.random((k, V)) < 0.5
+            draft[b] = bump_bf16(target[b, :k], mask, up)
+        else:
+            tv = values(target[b, :k], F32)
+            draft[b] = tv + np.float32(offs[b]) + np.float32(draft_sigma) * rd.standard_normal((k, V), dtype=np.float32)
+        dv = values(draft[b], dtype)
+        tokens[b] = gumbel_max_tokens(dv, float(temps[b]), rx)
+        j = int(reject_at[b])
+        diff = dv[j].astype(np.float64) - values(target[b, j], dtype).astype(np.float64)
+        tokens[b, j] = int(np.argmax(diff))
+        uniforms[b, :j] = 0.0
+        uniforms[b, j] = U_MAX
+    return dict(kind="chain", B=B, k=k, V=V, dtype=dtype, draft_tokens=tokens, draft_logits=draft,
+                target_logits=target, temperature=temps.astype(np.float32), uniforms=uniforms,
+                reject_at=reject_at)
+
+
+# Tree of the near-copy sampled-tree inputs: the root has children 1, 2, 3;
+# node 1 has children 4, 5, 6 and node 2 has child 7.
+NEAR_COPY_TREE = np.array([-1, 0, 0, 0, 1, 1, 1, 2], dtype=np.int32)
+
+
+def near_copy_tree_inputs(B: int, V: int, dtype: int, seed: int, *, draft_sigma: float = 0.0,
+                          density: float = 0.0, offset=0.0, temperature=0.7, target_sigma: float = 3.0,
+                          zipf_s: float | None = 1.1) -> dict:
+    """Sampled-tree inputs on NEAR_COPY_TREE whose draft rows nearly copy the
+    target rows (as for near_copy_chain_inputs), with the walk forced into one
+    of three paths (sequence b takes mode b % 3):
+
+      0: the three children of the root are rejected; the final token is drawn
+         at the root after three rejections;
+      1: node 1 is kept, its three children are rejected; the final draw is at
+         node 1 after three rejections;
+      2: node 1 is rejected, node 2 kept, its one child rejected; the final
+         draw is at node 2 after one rejection.
+
+    A child meant to be rejected carries, among the tokens not yet used by
+    its siblings, the one with the largest d - t of its parent's rows (so its
+    draft probability exceeds its target probability) and is tested with
+    u = U_MAX; a child meant to be kept carries the token with the smallest
+    d - t (u = 0).  u[b, 0] drives the final draw.
+    """
+    parent = NEAR_COPY_TREE
+    N = parent.shape[0]
+    temps = _per_seq(temperature, B, seed, "temperature")
+    offs = _per_seq(offset, B, seed, "sigma")
+    bias = zipf_bias(V, zipf_s, seed) if zipf_s else None
+    rt, rd = rng_for(seed, "target"), rng_for(seed, "draft")
+    np_dt = np.uint16 if dtype == BF16 else np.float32
+    target = np.empty((B, N, V), dtype=np_dt)
+    draft = np.empty((B, N, V), dtype=np_dt)
+    tokens = np.zeros((B, N), dtype=np.int32)
+    uniforms = rng_for(seed, "tree_uniforms").random((B, N), dtype=np.float32)
+    keep = {0: (), 1: (1,), 2: (2,)}
+    for b in range(B):
+        t = target_sigma * rt.standard_normal((N, V), dtype=np.float32)
+        if bias is not None:
+            t = t + bias
+        target[b] = to_dtype(t, dtype)
+        if dtype == BF16:
+            mask = rd.random((N, V)) < density
+            up = rd.random((N, V)) < 0.5
+            draft[b] = bump_bf16(target[b], mask, up)
+        else:
+            draft[b] = (values(target[b], F32) + np.float32(offs[b]) +
+                        np.float32(draft_sigma) * rd.standard_normal((N, V), dtype=np.float32))
+        mode = b % 3
+        for n in range(N):
+            kids = [i for i in range(1, N) if parent[i] == n]
+            if not kids:
+                continue
+            diff = values(draft[b, n], dtype).astype(np.float64) - values(target[b, n], dtype).astype(np.float64)
+            order = np.argsort(-diff, kind="stable")
+            hi, lo = 0, V - 1
+            for i in kids:
+                if i in keep[mode]:
+                    tokens[b, i] = int(order[lo])
+                    lo -= 1
+                    uniforms[b, i] = 0.0
+                else:
+                    tokens[b, i] = int(order[hi])
+                    hi += 1
+                    uniforms[b, i] = U_MAX
+    return dict(kind="tree_sampled", B=B, N=N, V=V, dtype=dtype, node_tokens=tokens, parent=parent.copy(),
+                max_depth=2, draft_logits=draft, target_logits=target, temperature=temps.astype(np.float32),
+                uniforms=uniforms)
+
+
 # ------------------------------------------------------------ greedy ---
 
 def greedy_inputs(B: int, k: int, V: int, dtype: int, seed: int, *,
@@ -380,8 +522,15 @@ WORKLOADS = {
             target_sigma=2.0, match_p=0.8),
     "deepseek_chain": dict(name="DeepSeek-scale chain verify", kind="chain", B=32, k=8, V=129280, dtype=F32,
             target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0), temperature=(0.3, 1.3)),
+    # each child's token equals its parent's target argmax with probability 0.6,
+    # independently of its siblings
     "eagle_tree": dict(name="EAGLE-style static tree verify", kind="tree", B=16, N=64, V=128256, dtype=BF16,
-            target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6, distinct_siblings=True),
+            target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6, distinct_siblings=False),
+    # the same trees with distinct sibling tokens, as a draft tree's top
+    # candidates are (at most one child of a node can match)
+    "eagle_tree_distinct": dict(name="EAGLE-style static tree verify, distinct siblings", kind="tree", B=16, N=64,
+            V=128256, dtype=BF16, target_sigma=2.0, max_branch=4, max_depth=6, match_p=0.6,
+            distinct_siblings=True),
     # one draft token per sequence, as in the single-token multi-token-prediction
     # schedule (the target scores 2 tokens per sequence of the decode batch)
     "mtp_chain": dict(name="MTP single-token verify", kind="chain", B=256, k=1, V=129280, dtype=BF16,
