@@ -429,8 +429,9 @@ int svo_verify_tree(int B, int N, int V, int dtype, const int32_t *node_tokens,
  * kept node ids then -1; an invalid tree gives -1 everywhere.  band[b] (T > 0
  * only) flags a tested uniform within band_eps of its threshold or u[b][0]
  * within band_eps of a CDF boundary of the final token.  final_mass[b]
- * (optional) is the mass Z of the last residual formed at the node where the
- * walk stopped (1 when no child of that node was rejected: r = p).
+ * (optional) is the mass, in units of the target row, of the distribution the
+ * final token is drawn from: the product of the masses Z of the residuals
+ * formed at the node where the walk stopped (1 when none was: r = p).
  */
 int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_tokens,
                             const int32_t *parent, int parent_stride, int max_depth,
@@ -513,8 +514,9 @@ int svo_verify_tree_sampled(int B, int N, int V, int dtype, const int32_t *node_
                         r[v] = e > 0.0 ? e : 0.0;
                         Z += r[v];
                     }
-                    mass = Z;
+                    mass *= Z;
                     if (Z == 0.0) {
+                        mass = 1.0;
                         for (int v = 0; v < V; ++v) r[v] = P[v];
                     } else {
                         for (int v = 0; v < V; ++v) r[v] /= Z;
