@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
         getattr(lib, fn).argtypes = [i, i, i, i]
     lib.sv_verify_chain.restype = i
     lib.sv_verify_chain.argtypes = [i, i, i, i] + [p] * 9 + [sz, p]
+    lib.sv_verify_chain_static.restype = i
+    lib.sv_verify_chain_static.argtypes = [i, i, i, i] + [p] * 9
     lib.sv_verify_greedy.restype = i
     lib.sv_verify_greedy.argtypes = [i, i, i, i] + [p] * 5 + [sz, p]
     lib.sv_verify_tree.restype = i
@@ -165,6 +167,35 @@ def verify_chain(draft_tokens, draft_logits, target_logits, temperature, uniform
                              _ptr(out.get("accept_prob")), _ptr(ws), ws.numel(), _stream(stream))
     if st != SV_OK:
         raise SpecVerifyError("sv_verify_chain", st)
+    return out
+
+
+def verify_chain_static(draft_tokens, draft_logits, target_logits, temperature, uniforms, *,
+                        accept_prob: bool = True, stream=None, out=None) -> dict:
+    """Chain verification on the library's own device workspace; see
+    ``sv_verify_chain_static``.  Same arguments and outputs as verify_chain
+    (without a workspace); the library allocates nothing, and calls that
+    overlap on one GPU race."""
+    lib = load()
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    _check_dev("target_logits", target_logits)
+    _check_dev("draft_logits", draft_logits, target_logits.dtype, (B, k, V))
+    _check_dev("draft_tokens", draft_tokens, torch.int32, (B, k))
+    _check_dev("temperature", temperature, torch.float32, (B,))
+    _check_dev("uniforms", uniforms, torch.float32, (B, k + 1))
+    if out is None:
+        with _on(stream):
+            out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+                       emitted=torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+                       accept_prob=torch.empty((B, k), dtype=torch.float32, device=dev) if accept_prob else None)
+    st = lib.sv_verify_chain_static(B, k, V, dt, _ptr(draft_tokens), _ptr(draft_logits), _ptr(target_logits),
+                                    _ptr(temperature), _ptr(uniforms), _ptr(out["accepted_len"]),
+                                    _ptr(out["emitted"]), _ptr(out.get("accept_prob")), _stream(stream))
+    if st != SV_OK:
+        raise SpecVerifyError("sv_verify_chain_static", st)
     return out
 
 

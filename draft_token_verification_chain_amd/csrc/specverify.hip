@@ -22,6 +22,12 @@
 #include "specverify.h"
 #include "sv_kernels.hpp"
 
+// The workspace of sv_verify_chain_static: one copy per GPU, held until the
+// process ends.  Host code uses the device address that hipGetSymbolAddress
+// returns for the current device (see static_workspace), never the array's
+// name.
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 using sv::Partial;
@@ -403,6 +409,33 @@ sv_status check_workspace(void* ws, size_t have, size_t need) {
     return SV_OK;
 }
 
+// ---------------------------------------------------------------- static workspace ---
+
+struct StaticWorkspace {
+    std::mutex mu;
+    std::vector<void*> ptr;  // per device id, looked up on the first call there
+} g_static_ws;
+
+sv_status static_workspace(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return SV_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lk(g_static_ws.mu);
+    if (static_cast<size_t>(dev) >= g_static_ws.ptr.size()) g_static_ws.ptr.resize(dev + 1, nullptr);
+    if (g_static_ws.ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return SV_ERR_HIP;
+        }
+        g_static_ws.ptr[dev] = p;
+    }
+    *out = g_static_ws.ptr[dev];
+    return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +501,24 @@ sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt, const int32_t* draft
                                          uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream)
                : run_chain<SV_F32, false>(B, k, V, draft_tokens, draft_logits, target_logits, temperature,
                                           uniforms, accepted_len, emitted, accept_prob, ws, L, nT, nchunk, stream);
+}
+
+sv_status sv_verify_chain_static(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens,
+                                 const void* draft_logits, const void* target_logits, const float* temperature,
+                                 const float* uniforms, int32_t* accepted_len, int32_t* emitted, float* accept_prob,
+                                 hipStream_t stream) {
+    if (B < 0 || k < 0) return SV_ERR_INVALID_ARGUMENT;
+    if (k > SV_MAX_DRAFTS) return SV_ERR_UNSUPPORTED;
+    sv_status st = check_rows(static_cast<int64_t>(2) * B * (k + 1), V, dt);
+    if (st != SV_OK) return st;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !temperature || !uniforms || !accepted_len || !emitted) return SV_ERR_INVALID_ARGUMENT;
+    if (k > 0 && (!draft_tokens || !draft_logits)) return SV_ERR_INVALID_ARGUMENT;
+    if (chain_layout(B, k, V, dt).total > SV_STATIC_WORKSPACE_BYTES) return SV_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if ((st = static_workspace(&ws)) != SV_OK) return st;
+    return sv_verify_chain(B, k, V, dt, draft_tokens, draft_logits, target_logits, temperature, uniforms,
+                           accepted_len, emitted, accept_prob, ws, SV_STATIC_WORKSPACE_BYTES, stream);
 }
 
 sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draft_tokens, const void* target_logits,

@@ -136,6 +136,32 @@ sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
                           float *accept_prob, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* Bytes of the workspace that sv_verify_chain_static holds on each GPU. */
+#define SV_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+
+/*
+ * sv_verify_chain without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  It computes exactly what sv_verify_chain
+ * computes, with the same arguments and outputs, and calls no allocating
+ * routine: its workspace is a device array of SV_STATIC_WORKSPACE_BYTES
+ * compiled into the library, one per GPU, held until the process ends.  The
+ * first call on a device looks up that device's copy (hipGetSymbolAddress,
+ * with the device current).
+ *
+ * Sizes whose workspace (sv_chain_workspace_bytes) exceeds
+ * SV_STATIC_WORKSPACE_BYTES return SV_ERR_WORKSPACE_TOO_SMALL before any
+ * launch; a failed symbol lookup returns SV_ERR_HIP.  The array needs no
+ * clearing between calls (every call writes each byte it reads), but all
+ * calls on one GPU share it: calls that overlap on one GPU, on different
+ * streams or from different host threads, race and give undefined results.
+ */
+sv_status sv_verify_chain_static(int B, int k, int V, sv_dtype dt,
+                                 const int32_t *draft_tokens, const void *draft_logits,
+                                 const void *target_logits, const float *temperature,
+                                 const float *uniforms, int32_t *accepted_len, int32_t *emitted,
+                                 float *accept_prob, hipStream_t stream);
+
 /*
  * Greedy chain verification (temperature 0; section "Speculative decoding").
  *

@@ -111,6 +111,33 @@ def test_chain_empty_batch_and_k0_pointer_rules(lib):
     assert _chain(lib, k=0, tokens=None, draft=None, temp=None) == INVALID
 
 
+def test_chain_static_rejects_bad_arguments_on_the_host(lib):
+    """sv_verify_chain_static: the same argument checks as sv_verify_chain, and
+    sizes whose workspace exceeds SV_STATIC_WORKSPACE_BYTES refused, all
+    before the device lookup (no HIP call)."""
+    def cs(B=2, k=3, V=50, dt=BF16, tokens=FAKE, draft=FAKE, target=FAKE, temp=FAKE, u=FAKE, acc=FAKE, em=FAKE):
+        return lib.sv_verify_chain_static(B, k, V, dt, tokens, draft, target, temp, u, acc, em, None, None)
+
+    assert cs(B=-1) == INVALID
+    assert cs(k=-1) == INVALID
+    assert cs(dt=5) == INVALID
+    assert cs(k=65) == UNSUPPORTED
+    for key in ("target", "temp", "u", "acc", "em", "tokens", "draft"):
+        assert cs(**{key: None}) == INVALID, key
+    assert cs(B=0, target=None, temp=None, u=None, acc=None, em=None) == OK
+    # the largest batch that fits, and the first one that does not
+    static = 16 << 20
+    B = 1
+    while lib.sv_chain_workspace_bytes(2 * B, 4, 128256, BF16) <= static:
+        B *= 2
+    lo, hi = B, 2 * B
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if lib.sv_chain_workspace_bytes(mid, 4, 128256, BF16) <= static else (lo, mid)
+    assert lib.sv_chain_workspace_bytes(hi, 4, 128256, BF16) > static
+    assert cs(B=hi, k=4, V=128256) == WS_SMALL
+
+
 def test_greedy_rejects_bad_arguments_on_the_host(lib):
     def g(B=2, k=3, V=50, dt=BF16, tokens=FAKE, target=FAKE, acc=FAKE, em=FAKE, ws=FAKE, ws_bytes=1 << 20):
         return lib.sv_verify_greedy(B, k, V, dt, tokens, target, acc, em, ws, ws_bytes, None)
