@@ -256,9 +256,9 @@ class Workload:
                     kb["chain_rowstats_rest"] = int((a >= s).sum()) * 2 * (k - s) * V * es
             # the final draw: both rows at a rejection, the bonus row after full
             # acceptance, the row's argmax at temperature 0 (with no drafts: row 0);
-            # one workgroup per row from 256 rows of at most 256 segments
+            # plain sampling: one workgroup per row from 256 rows of at most 256 segments
             nseg = -(-(-(-V // (16 // es))) // 64)
-            draw_kernel = "chain_row_draw" if B >= 256 and nseg <= 256 else "chain_final_part"
+            draw_kernel = "chain_row_draw" if k == 0 and B >= 256 and nseg <= 256 else "chain_final_part"
             draw = 0
             for b in range(B):
                 if T[b] > 0:

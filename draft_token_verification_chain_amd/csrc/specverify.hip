@@ -90,10 +90,13 @@ constexpr int64_t kChainTwoPhaseMinBytes = int64_t(128) << 20;
 constexpr int kChainFirstPhaseDiv = 4;
 constexpr int kChainRestTilesPerWave = 1;
 
-// The final draw runs one workgroup per sequence (chain_row_draw_kernel) from
-// this many sequences on, for rows of at most kRowDrawMaxSegs segments: one
-// row per CU fills the chip.  Below it a row alone on a CU streams too slowly
-// and the two-kernel draw (rows split over many workgroups) is faster.
+// Plain sampling (no drafts) runs one workgroup per sequence
+// (chain_row_draw_kernel) from this many sequences on, for rows of at most
+// kRowDrawMaxSegs segments: one row per CU fills the chip.  Below it a row
+// alone on a CU streams too slowly and the two-kernel draw (rows split over
+// many workgroups) is faster.  With drafts the draw stays split: a residual
+// costs about three times the arithmetic of a bonus draw per element, so one
+// sequence per CU leaves the CUs that hold residuals as the kernel's tail.
 constexpr int kRowDrawMinRows = 256;
 
 // The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
@@ -254,12 +257,9 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
             if (st != SV_OK) return st;
         }
     }
-    if (B >= kRowDrawMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kRowDrawMaxSegs) {
-        auto row_draw = k == 0 ? sv::chain_row_draw_kernel<DT, VEC, sv::kAcceptNone>
-                               : sv::chain_row_draw_kernel<DT, VEC, sv::kAcceptInline>;
-        return launch("chain_row_draw", row_draw, dim3(static_cast<unsigned>(B)), dim3(sv::kRowDrawBlock), stream,
-                      tokens, draft, target, temperature, uniforms, B, k, V, nT, static_cast<const Partial*>(part),
-                      static_cast<const float*>(gathered), accepted_len, emitted, accept_prob);
+    if (k == 0 && B >= kRowDrawMinRows && segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kRowDrawMaxSegs) {
+        return launch("chain_row_draw", sv::chain_row_draw_kernel<DT, VEC>, dim3(static_cast<unsigned>(B)),
+                      dim3(sv::kRowDrawBlock), stream, target, temperature, uniforms, V, accepted_len, emitted);
     }
     if (acc == sv::kAcceptRead) {
         const unsigned acc_blocks = static_cast<unsigned>((B + sv::kAccWaves - 1) / sv::kAccWaves);

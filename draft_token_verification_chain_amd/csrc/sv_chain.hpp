@@ -392,19 +392,29 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     if (mode == kFinalResidual) {
         float vd[NE];
         load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
-        float e[kFinU], x[kFinU], sw[kFinU];
+        float e[kFinU], x[kFinU];
+        bool near = false;
 #pragma unroll
         for (int i = 0; i < kFinU; ++i) {
-            const ResidualSums r = residual_sums<DT, VE, FULL>(w + i * VE, vd + i * VE, si);
+            const ResidualSums r = residual_sums_marked<DT, VE, FULL>(w + i * VE, vd + i * VE, si, near);
             a[i] = r.m;
             e[i] = r.ea;
             x[i] = r.x;
-            sw[i] = r.sw;
         }
         const float m = wave_sum4(a, i_own);
         const float ea = wave_sum4(e, i_own);
         const float xs = wave_sum4(x, i_own);
-        const float ss = wave_sum4(sw, i_own);
+        // SW only for the rare tiles that have an element near the switch,
+        // from the tile loaded again (the first loads are no longer live)
+        float ss = 0.f;
+        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+            float rt[NE], rd[NE], sw[kFinU];
+            load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, rt);
+            load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, rd);
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) sw[i] = residual_sw<DT, VE, FULL>(rt + i * VE, rd + i * VE, si);
+            ss = wave_sum4(sw, i_own);
+        }
         const int64_t g = tile * kFinU + i_own;
         if (lane < kFinU && g < nseg) seg_out[g] = residual_seg(m, ea, xs, ss);
         return;
@@ -775,89 +785,61 @@ __global__ __launch_bounds__(kPickBlock) void chain_final_pick_kernel(
 
 // ---------------------------------------------------------------- final draw, one workgroup per row ---
 
-// When one row per CU fills the chip, a sequence's whole final draw is one
-// workgroup's work (rows of at most kRowDrawMaxSegs segments).  Wave 0 first
-// forms the draw's descriptor: from the temperature alone with no drafts
-// (kAcceptNone), else by running accept_sequence (kAcceptInline).  The 16
-// waves then stream the draw's row or rows with final_tile, the segment
-// masses going to LDS instead of HBM, and wave 0 draws the token with
+// Plain sampling (no drafts): when one row per CU fills the chip, a
+// sequence's whole draw is one workgroup's work (rows of at most
+// kRowDrawMaxSegs segments).  The descriptor follows from the temperature
+// alone; the 16 waves stream the row with final_tile, the segment masses
+// going to LDS instead of HBM, and wave 0 draws the token with
 // draw_from_segments.  It computes exactly what chain_final_part and
-// chain_final_pick compute, in one launch.
+// chain_final_pick compute for k = 0, in one launch.
 constexpr int kRowDrawBlock = 1024;
 constexpr int kRowDrawWaves = kRowDrawBlock / kWave;
 constexpr int kRowDrawMaxSegs = 256;
 
-template <int DT, bool VEC, int ACC>
-__global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(
-    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
-    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
-    const Partial* __restrict__ part, const float* __restrict__ gathered, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ emitted, float* __restrict__ accept_prob) {
-    static_assert(ACC == kAcceptNone || ACC == kAcceptInline, "descriptor from the temperature or inline");
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(const void* __restrict__ target,
+                                                                       const float* __restrict__ temperature,
+                                                                       const float* __restrict__ uniforms, int V,
+                                                                       int32_t* __restrict__ accepted_len,
+                                                                       int32_t* __restrict__ emitted) {
     constexpr int VE = Elem<DT>::per_vec;
     __shared__ SegMass s_seg[kRowDrawMaxSegs];
     __shared__ ArgMax s_arg[kRowDrawWaves];
     const int64_t b = blockIdx.x;
-    SeqInfo si;
-    if constexpr (ACC == kAcceptInline) {
-        __shared__ int s_r[2 * SV_MAX_DRAFTS];
-        __shared__ double s_s[2 * SV_MAX_DRAFTS];
-        __shared__ SeqInfo s_info;
-        if (threadIdx.x < kWave)
-            accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, k, true, accepted_len,
-                                emitted, accept_prob, s_r, s_s, &s_info);
-        __syncthreads();
-        si = s_info;
-        if (si.mode == kFinalDone) return;
-    } else {
-        // k == 0: draw from target row 0 (its argmax at temperature 0)
-        const float T = temperature[b];
-        si = SeqInfo{};
-        si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
-        temperature_scale(T > 0.f ? T : 1.f, si);
-        si.u = uniforms[b];
-    }
+    // draw from the sequence's one target row (its argmax at temperature 0)
+    const float T = temperature[b];
+    SeqInfo si{};
+    si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+    temperature_scale(T > 0.f ? T : 1.f, si);
+    si.u = uniforms[b];
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const int64_t ntile = (nseg + kFinU - 1) / kFinU;
-    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
-    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
+    const int64_t trow = b * static_cast<int64_t>(V);
     const int wave = threadIdx.x / kWave;
     ArgMax best{-__builtin_inff(), kNoIndex};
     for (int64_t tile = wave; tile < ntile; tile += kRowDrawWaves) {
         if (tile_is_full<VEC, kFinU>(tile, V, VE))
-            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
+            final_tile<DT, VEC, VEC>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
         else
-            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
+            final_tile<DT, VEC, false>(nullptr, target, trow, 0, V, tile, nseg, si, si.mode, s_seg, best);
     }
     if (lane_id() == 0) s_arg[wave] = best;
     __syncthreads();
-    __shared__ int s_redo;
-    __shared__ double s_kappa;
-    if (wave == 0) {
-        Draw d{0, si.kappa};
-        if (si.mode == kFinalArgmax) {
-            ArgMax r = s_arg[0];
-            for (int w = 1; w < kRowDrawWaves; ++w) r = better(r, s_arg[w]);
-            d.y = r.idx;
-        } else {
-            SegMass first[kSegRun];
-            first_segments(s_seg, nseg, first);
-            d = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_seg, first);
-        }
-        if (threadIdx.x == 0) {
-            s_redo = d.y == kRedo;
-            s_kappa = d.kappa;
-            if (d.y != kRedo) emitted[b * (k + 1) + si.a] = d.y;
-            if constexpr (ACC == kAcceptNone) accepted_len[b] = 0;
-        }
+    if (wave != 0) return;
+    int y;
+    if (si.mode == kFinalArgmax) {
+        ArgMax r = s_arg[0];
+        for (int w = 1; w < kRowDrawWaves; ++w) r = better(r, s_arg[w]);
+        y = r.idx;
+    } else {
+        SegMass first[kSegRun];
+        first_segments(s_seg, nseg, first);
+        y = draw_from_segments<DT, VEC>(nullptr, target, trow, 0, V, nseg, si, s_seg, first).y;
     }
-    __syncthreads();
-    if (!s_redo) return;
-    // wave 0 has read the segment records (before the barrier above), so
-    // their space holds the masses formed again
-    float* m = reinterpret_cast<float*>(s_seg);
-    const int y = redo_residual_draw<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_kappa, kRowDrawWaves, m);
-    if (threadIdx.x == 0) emitted[b * (k + 1) + si.a] = y;
+    if (threadIdx.x == 0) {
+        emitted[b] = y;
+        accepted_len[b] = 0;
+    }
 }
 
 }  // namespace sv

@@ -173,6 +173,41 @@ __device__ __forceinline__ ResidualSums residual_sums(const float* vt, const flo
     return ResidualSums{pairwise_sum<VE>(mm), pairwise_sum<VE>(ee), pairwise_sum<VE>(xx), pairwise_sum<VE>(ss)};
 }
 
+// The same sums without SW: elements within kSwitch of the switch are rare,
+// so a streaming pass only marks them (one compare per element, or-ed into a
+// lane mask in `near`) and forms SW with residual_sw, in a branch, for the
+// tiles of waves that have one.  M, E and X are the same as residual_sums'.
+template <int DT, int VE, bool FULL>
+__device__ __forceinline__ ResidualSums residual_sums_marked(const float* vt, const float* vd, const SeqInfo& s,
+                                                             bool& near) {
+    float mm[VE], ee[VE], xx[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+        float et, delta;
+        float t = residual_term<DT>(vt[j], vd[j], s, et, delta);
+        if (!FULL && vt[j] == -__builtin_inff()) t = et = 0.f;
+        xx[j] = t;
+        mm[j] = __builtin_fmaxf(t, 0.f);
+        ee[j] = delta < 0.f ? et : 0.f;
+        near = near || __builtin_fabsf(delta) < kSwitch;
+    }
+    return ResidualSums{pairwise_sum<VE>(mm), pairwise_sum<VE>(ee), pairwise_sum<VE>(xx), 0.f};
+}
+
+// SW of VE elements (residual_sums' value).
+template <int DT, int VE, bool FULL>
+__device__ __forceinline__ float residual_sw(const float* vt, const float* vd, const SeqInfo& s) {
+    float ss[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+        const float delta = residual_delta<DT>(vt[j], vd[j], s);
+        const float a = __builtin_fmaf(vt[j], s.c_lo, __builtin_fmaf(vt[j], s.c_hi, -s.rt));
+        const float et = __builtin_amdgcn_exp2f(a);
+        ss[j] = (FULL || vt[j] != -__builtin_inff()) && __builtin_fabsf(delta) < kSwitch ? et : 0.f;
+    }
+    return pairwise_sum<VE>(ss);
+}
+
 // The correction of kappa from a residual pass at c = 1: X = sum_v x_v =
 // S_t (1 - 2^(kappa_used - kappa_true)), so kappa_true = kappa_used + zeta /
 // ln 2 with zeta = -ln(1 - X / S_t), accurate to a few 1e-6 of the residual's

@@ -38,8 +38,9 @@ def _np(out):
 @pytest.mark.parametrize("B,k", [(32, 4), (256, 1), (256, 0)])
 def test_graph_capture_and_replay(svl, orc, B, k):
     """verify_chain + commit_tokens captured once; every replay, on freshly
-    copied inputs and with eager work in between, matches the oracle.  From
-    256 sequences the final draw runs one workgroup per sequence."""
+    copied inputs and with eager work in between, matches the oracle.  At 256
+    sequences the draw after drafts takes its acceptance from its own kernel,
+    and plain sampling runs one workgroup per sequence."""
     import torch
 
     sets = [_inputs(s, B=B, k=k) for s in (31, 32, 33, 34)]

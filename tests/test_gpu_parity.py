@@ -421,13 +421,14 @@ ROW_DRAW = [(0, V, dt) for V, dt in [(128256, W.BF16), (131072, W.BF16), (131073
 
 @pytest.mark.parametrize("k,V,dt", ROW_DRAW)
 def test_row_draw_matches_split_batches(svl, orc, k, V, dt):
-    """From 256 sequences on, the final draw of a sequence whose rows have at
-    most 256 segments runs in one workgroup (with no drafts, or after the
-    sequence's acceptance computed inline); smaller batches take the
-    two-kernel draw.  Both compute the same tiles, weights, segment masses and
-    pick: one batch of 256 sequences and the same sequences as four batches
-    of 64 give bit-identical outputs, which match the oracle outside the
-    band.  Temperature 0 sequences take the argmax."""
+    """With no drafts, from 256 sequences on, the draw of a row of at most 256
+    segments runs in one workgroup; smaller batches take the two-kernel draw.
+    With drafts the two batch sizes take the two-kernel draw with the
+    acceptance computed in every workgroup (64 sequences) or once per
+    sequence by its own kernel (256).  Every form computes the same tiles,
+    weights, segment masses and pick: one batch of 256 sequences and the same
+    sequences as four batches of 64 give bit-identical outputs, which match
+    the oracle outside the band.  Temperature 0 sequences take the argmax."""
     B = 256
     temps = np.where(np.arange(B) % 7 == 3, 0.0, np.linspace(0.3, 1.6, B)).astype(np.float32)
     inp = W.chain_inputs(B, k, V, dt, 77 + k, target_sigma=3.0, draft_sigma=(0.2, 1.5), temperature=temps)
@@ -445,7 +446,7 @@ def test_row_draw_matches_split_batches(svl, orc, k, V, dt):
 def _no_prob_case(case):
     if case in ("llama_chain", "deepseek_chain", "mtp_chain"):
         return W.make_inputs(case, 3)
-    if case == "row draw":
+    if case == "300 sequences f32":
         return W.chain_inputs(300, 2, 60000, W.F32, 31, target_sigma=3.0, draft_sigma=(0.2, 1.5))
     if case == "acceptance kernel":
         return W.chain_inputs(200, 3, 128256, W.BF16, 32, target_sigma=3.0, draft_sigma=(0.2, 1.5))
@@ -460,16 +461,16 @@ def _no_prob_case(case):
         return W.chain_inputs(8, 64, 65536, W.BF16, 34, target_sigma=1.0, draft_sigma=(0.01, 0.3))
     if case == "16 drafts element loads, two phases":
         return W.chain_inputs(12, 16, 100001, W.F32, 35, target_sigma=2.0, draft_sigma=(0.05, 0.5))
-    if case == "row draw, two phases":
+    if case == "256 sequences f32, two phases":
         return W.chain_inputs(256, 6, 30000, W.F32, 36, target_sigma=3.0, draft_sigma=(0.1, 1.0))
     if case == "acceptance kernel, two phases":
         return W.chain_inputs(130, 6, 128256, W.BF16, 37, target_sigma=3.0, draft_sigma=(0.1, 1.0))
     raise ValueError(case)
 
 
-NO_PROB = ["llama_chain", "deepseek_chain", "mtp_chain", "row draw", "acceptance kernel",
+NO_PROB = ["llama_chain", "deepseek_chain", "mtp_chain", "300 sequences f32", "acceptance kernel",
            "temperature 0 mix, two phases", "64 drafts, two phases", "16 drafts element loads, two phases",
-           "row draw, two phases", "acceptance kernel, two phases"]
+           "256 sequences f32, two phases", "acceptance kernel, two phases"]
 
 
 @pytest.mark.parametrize("case", NO_PROB)

@@ -49,16 +49,16 @@ def _decades(mass):
 
 
 # name, dtype, generator keywords, B, sets of final-draw uniforms.  B covers the
-# three final-draw forms: descriptors recomputed by every workgroup (B * chunks
-# <= 2048), written once by an acceptance kernel (larger), and one workgroup per
-# sequence (bf16 rows of at most 256 segments from B = 256).
+# two ways the final draw's workgroups obtain the draw's descriptor: each
+# recomputes its sequence's acceptance (B * chunks <= 2048), or an acceptance
+# kernel writes it once per sequence (larger batches).
 CHAIN_CASES = [
     ("f32 sigma 2e-2 offset", W.F32, dict(draft_sigma=2e-2, offset=(-4.0, 4.0)), 64, 32),
     ("f32 sigma 2e-3 offset", W.F32, dict(draft_sigma=2e-3, offset=(-4.0, 4.0)), 128, 16),
     ("f32 sigma 2e-4 offset", W.F32, dict(draft_sigma=2e-4, offset=(-4.0, 4.0)), 64, 32),
     ("f32 sigma 2e-4", W.F32, dict(draft_sigma=2e-4), 128, 16),
     ("bf16 density 0.3", W.BF16, dict(density=0.3), 128, 16),
-    ("bf16 density 0.3 one workgroup per row", W.BF16, dict(density=0.3), 256, 8),
+    ("bf16 density 0.3 acceptance kernel", W.BF16, dict(density=0.3), 256, 8),
     ("bf16 density 0.03", W.BF16, dict(density=0.03), 192, 11),
 ]
 
