@@ -38,22 +38,85 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
 METRIC = "verified draft tokens/sec and HBM GB/s (% of peak) at B=64,k=4,V=128256 bf16"
-KERNEL_SOURCES = ["draft_token_verification_chain_amd/csrc/" + f for f in (
+CSRC = "draft_token_verification_chain_amd/csrc/"
+KERNEL_SOURCES = [CSRC + f for f in (
     "sv_common.hpp", "sv_tiles.hpp", "sv_chain.hpp", "sv_greedy_tree.hpp", "sv_tree_sampled.hpp", "sv_commit.hpp",
-    "sv_kernels.hpp", "specverify.hip")]
+    "sv_kernels.hpp", "specverify.hip")] + ["include/specverify.h"]
+# The sources each kernel family's code comes from (its header and the ones it
+# includes, the public header and the host dispatch that sets its launch).
+_BASE = ["include/specverify.h", CSRC + "sv_common.hpp", CSRC + "specverify.hip"]
+KERNEL_FAMILY_SOURCES = {
+    "chain": _BASE + [CSRC + "sv_tiles.hpp", CSRC + "sv_chain.hpp"],
+    "greedy": _BASE + [CSRC + "sv_tiles.hpp", CSRC + "sv_greedy_tree.hpp"],
+    "tree_sampled": _BASE + [CSRC + "sv_tiles.hpp", CSRC + "sv_chain.hpp", CSRC + "sv_tree_sampled.hpp"],
+    "commit": _BASE + [CSRC + "sv_commit.hpp"],
+}
+_FAMILY_OF = [("tree_rowstats", "tree_sampled"), ("tree_round", "tree_sampled"), ("tree_sample", "tree_sampled"),
+              ("chain_", "chain"), ("greedy_", "greedy"), ("argmax_rows", "greedy"), ("tree_", "greedy"),
+              ("commit_", "commit")]
 
 
-def kernel_source_digest() -> str:
-    """Digest of the kernel sources' code: comments and whitespace are
-    dropped, so that only a change of code marks stored counters stale."""
+def kernel_sources(kernel: str = None) -> list:
+    """The source files a library kernel is built from (all kernel sources
+    when no kernel, or an unknown one, is named)."""
+    if kernel:
+        for prefix, fam in _FAMILY_OF:
+            if kernel.startswith(prefix):
+                return KERNEL_FAMILY_SOURCES[fam]
+    return KERNEL_SOURCES
+
+
+def sources_digest(paths) -> str:
+    """Digest of the code of source files: comments and whitespace are
+    dropped, so that only a change of code changes it."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest(kernel: str = None) -> str:
+    """Digest of what a kernel is built from (kernel_sources): stored counters
+    of the kernel stay valid while it does not change."""
+    return sources_digest(kernel_sources(kernel))
+
+
+def trace_digest(kernels) -> str:
+    """Digest of the sources of every library kernel of a kernel trace."""
+    return sources_digest(sorted({p for k in kernels for p in kernel_sources(k)}))
+
+
+def load_trace_average(kernel: str, workload: str):
+    """The kernel's average duration (us) in the committed rocprofv3 kernel
+    trace of the workload, if that trace was taken on the current sources of
+    its kernels; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Kernel sources digest: `([0-9a-f]+)`", text)
+    rows, col = {}, None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if cells and cells[0] == "kernel" and "average (us)" in cells:
+            col = cells.index("average (us)")
+        elif col is not None and len(cells) > col and re.fullmatch(r"\d+", cells[1]):
+            rows[cells[0]] = float(cells[col])
+    lib = [k for k in rows if k in LIBRARY_KERNELS]
+    if not m or kernel not in rows or m.group(1) != trace_digest(lib):
+        return None
+    return rows[kernel]
+
+
+# The library's kernels (launch names; the profile summaries use the same names).
+LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "chain_accept", "chain_final_part",
+                   "chain_final_pick", "chain_row_draw", "argmax_rows", "greedy_rows", "greedy_rows_rest",
+                   "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
+                   "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
 
 
 def load_traffic(kernel: str, workload: str):
@@ -64,7 +127,7 @@ def load_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    if rec.get("kernel_source_digest") != kernel_source_digest(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -447,6 +510,7 @@ def main():
     dom_bytes = m["dom_bytes"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
     traffic = load_traffic(dominant, args.workload)
+    rocprof_us = load_trace_average(dominant, args.workload)
     inp, cfg = wl.inp, wl.cfg
     B, V, kind = inp["B"], inp["V"], wl.kind
     result = {
@@ -481,7 +545,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "avg_launch_us": dom_us, "duration_source": "hip_events",
-                     "traffic_gbs": traffic / (dom_us * 1e-6) / 1e9 if traffic else None},
+                     "traffic_gbs": traffic / (dom_us * 1e-6) / 1e9 if traffic else None,
+                     # the same kernel's average in the committed rocprofv3 trace (null once
+                     # its sources have changed) and the fraction it gives
+                     "rocprof_avg_us": rocprof_us,
+                     "frac_rocprof": (dom_bytes / (rocprof_us * 1e-6) / 1e9 / PEAK_HBM_GBS
+                                      if rocprof_us and dom_bytes else None)},
     }
 
     if not args.no_cpu:

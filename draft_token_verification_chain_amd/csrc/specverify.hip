@@ -646,7 +646,7 @@ sv_status sv_verify_tree_sampled(int B, int N, int V, sv_dtype dt, const int32_t
         if (st != SV_OK) return st;
     }
     // what the rounds leave: the final draw from masses the last round wrote, or the
-    // one-workgroup walk from the start
+    // rest of the walk on one workgroup per sequence, from the last round's state
     auto walk = dt == SV_BF16 ? (vec ? sv::tree_sample_kernel<SV_BF16, true> : sv::tree_sample_kernel<SV_BF16, false>)
                               : (vec ? sv::tree_sample_kernel<SV_F32, true> : sv::tree_sample_kernel<SV_F32, false>);
     return launch("tree_sample", walk, dim3(B), dim3(sv::kWalkBlock), stream, node_tokens, parent, parent_stride, N,

@@ -376,6 +376,14 @@ __device__ bool pick_from_masses(const void* draft, const void* target, int64_t 
     return true;
 }
 
+// The walk's last launch, one workgroup per sequence.  It returns at once
+// for a sequence the rounds finished, draws the final token of one whose
+// last round wrote its final masses, and otherwise goes on from the state the
+// last round left, on one CU: the pending rejection pass (formed here from
+// the rows), the remaining children's tests and passes, the nodes below, and
+// the final draw.  The paths the rounds wrote stay.  A final residual with no
+// mass falls back to the node's target row.  With no state (state ==
+// nullptr) it walks from the root and checks the tree itself.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent, int parent_stride, int N,
@@ -384,8 +392,10 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     const Partial* __restrict__ part, const WalkState* __restrict__ state, const float* __restrict__ tsegs,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, int32_t* __restrict__ accepted_nodes) {
     constexpr int VE = Elem<DT>::per_vec;
+    WalkState st{};
+    bool from_p = false;  // the final residual at st.node was empty: draw from its target row
     if (state != nullptr) {
-        const WalkState st = state[blockIdx.x];
+        st = state[blockIdx.x];
         if (st.phase == kWalkDone) return;  // finished by the rounds
         if (st.phase == kWalkPick) {
             // the rounds left only the final draw: its segment masses are written
@@ -405,8 +415,10 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
                 }
             }
             __syncthreads();
-            if (s_picked) return;  // else (an empty residual) the walk below starts over
+            if (s_picked) return;
+            from_p = true;
         }
+        if (st.phase == kWalkStuck) from_p = true;
     }
     __shared__ int s_par[SV_MAX_TREE_NODES];
     __shared__ int s_anc[SV_MAX_TREE_NODES];
@@ -436,23 +448,33 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
     int32_t* out = emitted + b * width;
     int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
 
-    // validity and depths (pointer jumping), as for the greedy tree
+    // validity and depths (pointer jumping), as for the greedy tree; after the
+    // rounds (which checked the tree) only the parent links are needed
     const bool bad = walk_validate<kWalkBlock>(parent + b * static_cast<int64_t>(parent_stride), N, max_depth, s_par,
                                                s_anc, s_len, &s_bad);
-    for (int j = t; j < width; j += kWalkBlock) {
-        out[j] = -1;
-        if (nodes) nodes[j] = -1;
-    }
-    if (bad) {
-        if (t == 0) accepted_len[b] = -1;
-        return;
+    if (state == nullptr) {
+        for (int j = t; j < width; j += kWalkBlock) {
+            out[j] = -1;
+            if (nodes) nodes[j] = -1;
+        }
+        if (bad) {
+            if (t == 0) accepted_len[b] = -1;
+            return;
+        }
     }
 
     const double cT = kLog2e / static_cast<double>(sampled ? T : 1.f);
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const int nmask = (N + kWave - 1) / kWave;
     const int64_t nbn = static_cast<int64_t>(B) * N;
-    int n = 0, d = 0;
+    // where the walk goes on: the state's node, with its statistics, c, Z and
+    // the children already rejected when a pass is pending (or the final
+    // residual was empty); entered afresh otherwise
+    int n = st.node, d = st.depth;
+    bool resumed = state != nullptr && (from_p || st.phase == kWalkPass);
+    bool pending = resumed && !from_p;
+    int Rt = st.Rt, Rd = st.Rd, k0 = st.kidx, redone = st.redone;
+    double St = st.St, K = st.K, c = st.c, Z = st.Z;
     for (;;) {
         const int64_t row = (b * N + n) * static_cast<int64_t>(V);
         // children of n, and the statistics of its target and draft rows
@@ -481,107 +503,130 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
                 s_cld[rank] = yok ? load_elem<DT>(draft, row + y) : 0.f;
             }
         }
-        // a leaf's target row was skipped by tree_rowstats: its statistics here
-        const bool leaf = nkids == 0;
-        if (leaf) {
-            leaf_row_partials<DT, VEC>(target, b, N, n, V, nseg, T, wave, kWalkWaves, s_lp);
-            __syncthreads();
-        }
-        if (wave == 0) {
-            const bool is_draft = lane >= 32;
-            const bool valid = !(leaf && is_draft);  // a leaf's draft row is never needed
-            const Partial* pr = leaf ? s_lp : part + ((is_draft ? nbn : 0) + b * N + n) * nT;
-            const int cnt = leaf ? static_cast<int>(nseg) : nT;
-            Partial q[kBatch];
-            group_load(pr, cnt, 32, valid, q);
-            int r;
-            double sum;
-            ArgMax am;
-            if (sampled) {
-                group_reduce<true>(pr, cnt, 32, valid, q, r, sum, am);
-            } else {
-                group_reduce<false>(pr, cnt, 32, valid, q, r, sum, am);
-                r = am.idx;
+        if (!resumed) {
+            // a leaf's target row was skipped by tree_rowstats: its statistics here
+            const bool leaf = nkids == 0;
+            if (leaf) {
+                leaf_row_partials<DT, VEC>(target, b, N, n, V, nseg, T, wave, kWalkWaves, s_lp);
+                __syncthreads();
             }
-            if ((lane & 31) == 0) {
-                s_ref[is_draft] = r;
-                s_norm[is_draft] = sum;
-            }
-        }
-        __syncthreads();
-        const int Rt = s_ref[0], Rd = s_ref[1];
-        const double St = s_norm[0], Sd = s_norm[1];
-        double c = 0.0, Z = 1.0;
-        int next = -1;
-        // log2(S_t / S_d), corrected by the first rejection's pass
-        double K = sampled && nkids > 0 ? node_log_ratio(Rt, Rd, St, Sd) : 0.0;
-        for (int k = 0; k < nkids && next < 0; ++k) {
-            if (t == 0) {
-                const int id = s_cid[k];
-                double tau = 0.0;
-                if (id >= 0) {
-                    if (sampled) {
-                        // p/q = exp2((l_t - l_d) c - log2(S_t / S_d))
-                        const double lt = s_clt[k], ld = s_cld[k];
-                        const double l2ratio = (lt - ld) * cT - K;
-                        tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
-                    } else {
-                        const int y = node_tokens[b * N + id];
-                        const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
-                        const double rv = fmax(0.0, pv - c * qv) / Z;
-                        tau = qv > 0.0 ? fmin(1.0, rv / qv) : (rv > 0.0 ? 1.0 : 0.0);
-                    }
-                }
-                s_accept = static_cast<double>(s_cu[k]) < tau;
-            }
-            __syncthreads();
-            if (s_accept) {
-                next = s_cid[k];
-            } else {
-                // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
-                c += Z;
+            if (wave == 0) {
+                const bool is_draft = lane >= 32;
+                const bool valid = !(leaf && is_draft);  // a leaf's draft row is never needed
+                const Partial* pr = leaf ? s_lp : part + ((is_draft ? nbn : 0) + b * N + n) * nT;
+                const int cnt = leaf ? static_cast<int>(nseg) : nT;
+                Partial q[kBatch];
+                group_load(pr, cnt, 32, valid, q);
+                int r;
+                double sum;
+                ArgMax am;
                 if (sampled) {
-                    PassSums ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
-                                                              s_mass, s_ea, s_wx, &s_sum);
-                    if (c == 1.0) {
-                        // the node's first rejection: correct log2(S_t / S_d), and the
-                        // segment masses (which a final draw at c = 1 uses) to first
-                        // order, or form them again with the corrected value
-                        const double zeta = kappa_zeta(ps.x, St);
-                        K += zeta / kLn2;
-                        const double Mc = ps.m - zeta * (ps.ea - ps.m);
-                        if (correction_trusted(zeta, ps.sw, Mc)) {
-                            for (int64_t g = t; g < nseg; g += kWalkBlock) {
-                                const double m = static_cast<double>(s_mass[g]);
-                                s_mass[g] =
-                                    static_cast<float>(fmax(0.0, m - zeta * (static_cast<double>(s_ea[g]) - m)));
-                            }
-                            __syncthreads();
-                            if (wave == 0) {
-                                const int64_t per = (nseg + kWave - 1) / kWave;
-                                const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
-                                double rm = 0.0;
-                                for (int64_t g = a; g < e; ++g) rm += static_cast<double>(s_mass[g]);
-                                rm = __shfl(wave_inclusive_scan(rm), kWave - 1, kWave);
-                                if (lane == 0) s_sum.m = rm;
-                            }
-                            __syncthreads();
-                            ps.m = s_sum.m;
+                    group_reduce<true>(pr, cnt, 32, valid, q, r, sum, am);
+                } else {
+                    group_reduce<false>(pr, cnt, 32, valid, q, r, sum, am);
+                    r = am.idx;
+                }
+                if ((lane & 31) == 0) {
+                    s_ref[is_draft] = r;
+                    s_norm[is_draft] = sum;
+                }
+            }
+            __syncthreads();
+            Rt = s_ref[0];
+            Rd = s_ref[1];
+            St = s_norm[0];
+            // log2(S_t / S_d), corrected by the first rejection's pass
+            K = sampled && nkids > 0 ? node_log_ratio(Rt, Rd, St, s_norm[1]) : 0.0;
+            c = 0.0;
+            Z = 1.0;
+            k0 = 0;
+            redone = 0;
+            __syncthreads();  // s_ref and s_norm are reused at the next node
+        }
+        resumed = false;
+        // a rejection's pass at the advanced c: Z(c) = M / S_t from the segment
+        // masses of max(0, p - c q) (left in s_mass for a final draw).  The
+        // node's first (c = 1) corrects log2(S_t / S_d) and the masses to first
+        // order, or forms them again with the corrected value, unless the
+        // rounds already formed this pass again
+        auto rejection_pass = [&]() {
+            if (sampled) {
+                PassSums ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
+                                                          s_mass, s_ea, s_wx, &s_sum);
+                if (c == 1.0) {
+                    const double zeta = kappa_zeta(ps.x, St);
+                    K += zeta / kLn2;
+                    const double Mc = ps.m - zeta * (ps.ea - ps.m);
+                    if (redone || correction_trusted(zeta, ps.sw, Mc)) {
+                        for (int64_t g = t; g < nseg; g += kWalkBlock) {
+                            const double m = static_cast<double>(s_mass[g]);
+                            s_mass[g] = static_cast<float>(fmax(0.0, m - zeta * (static_cast<double>(s_ea[g]) - m)));
+                        }
+                        __syncthreads();
+                        if (wave == 0) {
+                            const int64_t per = (nseg + kWave - 1) / kWave;
+                            const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
+                            double rm = 0.0;
+                            for (int64_t g = a; g < e; ++g) rm += static_cast<double>(s_mass[g]);
+                            rm = __shfl(wave_inclusive_scan(rm), kWave - 1, kWave);
+                            if (lane == 0) s_sum.m = rm;
+                        }
+                        __syncthreads();
+                        ps.m = s_sum.m;
+                    } else {
+                        ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
+                                                        s_mass, s_ea, s_wx, &s_sum);
+                    }
+                    redone = 0;
+                }
+                Z = ps.m / St;
+            } else {
+                Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
+            }
+            if (!(Z > 0.0)) {
+                c = 0.0;
+                Z = 1.0;
+            }
+        };
+        int next = -1;
+        if (from_p) {
+            from_p = false;
+            c = 0.0;
+            Z = 1.0;
+        } else {
+            if (pending) {
+                pending = false;
+                rejection_pass();
+            }
+            for (int k = k0; k < nkids && next < 0; ++k) {
+                if (t == 0) {
+                    const int id = s_cid[k];
+                    double tau = 0.0;
+                    if (id >= 0) {
+                        if (sampled) {
+                            // p/q = exp2((l_t - l_d) c - log2(S_t / S_d))
+                            const double lt = s_clt[k], ld = s_cld[k];
+                            const double l2ratio = (lt - ld) * cT - K;
+                            tau = fmin(1.0, fmax(0.0, exp2(l2ratio) - c) / Z);
                         } else {
-                            ps = walk_masses<DT, VEC, true>(draft, target, row, V, nseg, walk_info(T, Rt, St, K, c),
-                                                            s_mass, s_ea, s_wx, &s_sum);
+                            const int y = node_tokens[b * N + id];
+                            const double pv = y == Rt ? 1.0 : 0.0, qv = y == Rd ? 1.0 : 0.0;
+                            const double rv = fmax(0.0, pv - c * qv) / Z;
+                            tau = qv > 0.0 ? fmin(1.0, rv / qv) : (rv > 0.0 ? 1.0 : 0.0);
                         }
                     }
-                    Z = ps.m / St;
+                    s_accept = static_cast<double>(s_cu[k]) < tau;
+                }
+                __syncthreads();
+                if (s_accept) {
+                    next = s_cid[k];
                 } else {
-                    Z = Rt != Rd ? 1.0 : fmax(0.0, 1.0 - c);
+                    // rejected: the residual becomes max(0, p - (c + Z) q) / Z(c + Z)
+                    c += Z;
+                    rejection_pass();
                 }
-                if (!(Z > 0.0)) {
-                    c = 0.0;
-                    Z = 1.0;
-                }
+                __syncthreads();
             }
-            __syncthreads();
         }
         if (next >= 0) {
             if (t == 0) {
@@ -632,8 +677,15 @@ __global__ __launch_bounds__(kWalkBlock) void tree_sample_kernel(
 // from round 1 on a round reads all its inputs in one round trip and entering
 // a child needs no dependent load; otherwise every entry combines the node's
 // partials.  After the launched rounds, tree_sample draws the final token of
-// a sequence whose last round wrote its final masses, and walks any other
-// unfinished sequence again from the start.
+// a sequence whose last round wrote its final masses, and goes on with any
+// other unfinished walk from the state its last round left.
+//
+// A walk needs one round per rejection pass, one per leaf it enters and one
+// for its final draw's masses, then its pick: kWalkRounds rounds make up to
+// seven of these, and the pick of a walk that needs all seven comes in
+// tree_sample.  The number of passes depends on the outcome, which stays on
+// the device, so the launches cannot follow it; a longer walk finishes on one
+// CU in tree_sample.
 constexpr int kRoundBlock = 256;
 constexpr int kRoundWaves = kRoundBlock / kWave;
 constexpr int kRoundSlots = SV_MAX_TREE_NODES / kRoundBlock;

@@ -5,10 +5,12 @@ Inputs (rocprofv3 CSV output directories):
   --trace DIR   from  rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o bench -- python3 bench.py ...
   --fetch DIR   from  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
   --write DIR   from  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
+  --sq DIR      from  rocprofv3 --pmc <SQ_COUNTERS> --output-format csv -d DIR -o bench -- python3 bench.py ...
 
 Outputs:
   profiles/<prefix>_kernel_trace.md          per-kernel calls / average / min / max duration
   profiles/<kernel>_<workload>_traffic.json  HBM-side bytes per launch of each library kernel
+  profiles/<prefix>_sq_counters.md           per-kernel SQ counters and the VALU floor
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
 the calibration copy (one plain device-to-device copy of MIB MiB, which reads
@@ -20,6 +22,7 @@ import collections
 import csv
 import json
 import os
+import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +33,17 @@ def short_name(full: str) -> str:
     """'void sv::chain_rowstats_kernel<1, true, 8>(...)' -> 'chain_rowstats'."""
     n = full.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0].split("::")[-1]
     return n[:-len("_kernel")] if n.endswith("_kernel") else n
+
+
+def trace_medians(d: str) -> dict:
+    """Median duration (us) per kernel from the per-dispatch kernel trace, if present."""
+    path = os.path.join(d, "bench_kernel_trace.csv")
+    if not os.path.exists(path):
+        return {}
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: statistics.median(v) for k, v in per.items()}
 
 
 def read_counters(d: str) -> dict:
@@ -46,9 +60,46 @@ def calibration_scale(per: dict, mib: int) -> float:
     return mib * 2 ** 20 / counted
 
 
+CUS, SIMDS_PER_CU, CLOCK_HZ = 256, 4, 2.4e9
+SQ_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY "
+               "SQ_INSTS_VMEM_RD SQ_INSTS_SALU GRBM_GUI_ACTIVE")
+
+
+def sq_summary(d: str, prefix: str, command: str) -> str:
+    """Per-kernel SQ counters (averages per dispatch) and what follows from
+    them without assuming counter units: instructions per wave, the fraction
+    of wave-cycles spent waiting for an instruction's operands, and the VALU
+    floor, the time the SIMDs need just to issue the kernel's VALU
+    instructions (a wave64 instruction occupies a 16-lane SIMD for 4 cycles;
+    1024 SIMDs at 2.4 GHz)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(os.path.join(d, "bench_counter_collection.csv"))):
+        per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 SQ counters: {prefix}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", f"rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d <dir> -o bench -- {command}", "```", "",
+             "Averages per dispatch. VALU floor = SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x 2.4 GHz): the time the "
+             "chip needs only to issue the kernel's vector instructions (packed fp32 is not used). Wait fraction = "
+             "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.", "",
+             "| kernel | dispatches | waves | VALU / wave | SALU / wave | VMEM reads / wave | VALU floor (us) | "
+             "wait fraction |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for full, c in per.items():
+        if "sv::" not in full:
+            continue
+        a = {k: sum(v) / len(v) for k, v in c.items()}
+        waves = a.get("SQ_WAVES", 0.0)
+        if not waves:
+            continue
+        floor = a["SQ_INSTS_VALU"] * 4 / (CUS * SIMDS_PER_CU * CLOCK_HZ) * 1e6
+        lines.append(f"| {short_name(full)} | {len(c['SQ_WAVES'])} | {waves:.0f} | {a['SQ_INSTS_VALU'] / waves:.0f} | "
+                     f"{a['SQ_INSTS_SALU'] / waves:.0f} | {a['SQ_INSTS_VMEM_RD'] / waves:.1f} | {floor:.2f} | "
+                     f"{a['SQ_WAIT_INST_ANY'] / a['SQ_WAVE_CYCLES']:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--trace")
+    ap.add_argument("--sq", help="rocprofv3 --pmc output of the SQ counters (SQ_COUNTERS)")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calibrate-mib", type=int, default=256)
@@ -60,19 +111,29 @@ def main():
     args = ap.parse_args()
     pmc_cmd = args.pmc_command or args.command
     os.makedirs(args.out, exist_ok=True)
+    if args.sq:
+        text = sq_summary(args.sq, args.prefix, pmc_cmd)
+        with open(os.path.join(args.out, f"{args.prefix}_sq_counters.md"), "w") as f:
+            f.write(text)
+        print(text)
+    if not args.trace:
+        return
 
-    from bench import kernel_source_digest
+    from bench import LIBRARY_KERNELS, kernel_source_digest, kernel_sources, trace_digest
 
-    digest = kernel_source_digest()
     rows = list(csv.DictReader(open(os.path.join(args.trace, "bench_kernel_stats.csv"))))
+    digest = trace_digest([short_name(r["Name"]) for r in rows if short_name(r["Name"]) in LIBRARY_KERNELS])
     lines = [f"# rocprofv3 kernel trace: {args.prefix}", "",
              "Command (run from the repository root on one MI355X):", "",
              "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- {args.command}", "```",
              "", f"Kernel sources digest: `{digest}`", "",
-             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---:|---:|---:|---:|---:|"]
+             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    medians = trace_medians(args.trace)
     for r in rows:
+        med = medians.get(r["Name"])
         lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{'%.2f' % med if med is not None else '-'} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
     with open(os.path.join(args.out, f"{args.prefix}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -88,7 +149,8 @@ def main():
             wv = write.get(full, [0.0])
             wb = sum(wv) / len(wv) * 1024.0 * wsc
             rec = {
-                "kernel": name, "workload": args.workload, "kernel_source_digest": digest,
+                "kernel": name, "workload": args.workload, "kernel_source_digest": kernel_source_digest(name),
+                "kernel_sources": kernel_sources(name),
                 "traffic_bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                 "fetch_scale": fs, "write_scale": wsc, "launches_counted": len(vals),
                 "calibration": f"one plain device copy of {args.calibrate_mib} MiB",

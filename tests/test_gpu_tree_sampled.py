@@ -225,8 +225,8 @@ def test_walks_ending_around_the_last_round(svl, orc, kids):
     almost no mass: every child is rejected, so the walk needs `kids` passes
     over the root's rows and then the final draw.  With seven rounds the
     draw then falls in the last round (5), in the finisher from the masses
-    the last round wrote (6), or the finisher walks the sequence again from
-    the start (7, 12)."""
+    the last round wrote (6), or the finisher forms the pending pass from the
+    last round's state and goes on from there (7, 12)."""
     B, V = 8, 3000
     star = np.full(kids + 1, 0, dtype=np.int32)
     star[0] = -1
@@ -237,6 +237,60 @@ def test_walks_ending_around_the_last_round(svl, orc, kids):
         inp["draft_logits"][b, 0, toks] = 8.0
     got, ref = _check(svl, orc, inp, f"star{kids}")
     assert (ref["accepted_len"] == 0).all()  # the oracle rejected every child
+
+
+# Trees whose walks are fixed by their logits: at every inner node the first
+# R children carry tokens the node's target row gives almost no mass and its
+# draft row much (certain rejections, each one pass), and the next child a
+# token the target row favours and the draft row does not (certainly kept,
+# whatever the residual).  parent, rejections per level, whether the last kept
+# node has children (all rejected), and the state the seven rounds leave.
+RESUME_CASES = [
+    ([-1, 0, 0, 0, 0, 0, 0, 0], [6], "leaf: entered in the last round"),
+    ([-1, 0, 0, 0, 0, 0, 0, 0, 7, 7], [6, 2], "first pass (c = 1) at depth 1 pending"),
+    ([-1, 0, 0, 0, 0, 0, 5, 5, 5, 5], [4, 4], "third pass at depth 1 pending, one more child"),
+    ([-1, 0, 0, 0, 0, 4, 4, 4, 4, 8, 8, 8, 8], [3, 3, 3], "three levels, walk ends at a leaf"),
+    ([-1, 0, 0, 0, 3, 3, 3, 3, 3, 3, 3, 3, 3], [2, 8], "eight passes at depth 1, four in the finisher, a leaf"),
+]
+
+
+@pytest.mark.parametrize("case", RESUME_CASES, ids=[c[2] for c in RESUME_CASES])
+def test_walks_going_on_after_the_rounds(svl, orc, case):
+    """Walks longer than the rounds: the finisher goes on from the state the
+    last round left (a leaf to enter, a pending pass at c = 1 or later, a
+    node's remaining children) and keeps the path the rounds wrote."""
+    parent, rejections, label = np.array(case[0], np.int32), case[1], case[2]
+    N, V, B = len(parent), 3000, 8
+    depth = np.zeros(N, np.int64)
+    for i in range(1, N):
+        depth[i] = depth[parent[i]] + 1
+    for dt in (W.F32, W.BF16):
+        inp = W.sampled_tree_inputs(B, N, V, dt, 60 + N, parent=parent, max_depth=int(depth.max()),
+                                    draft_sigma=0.5)
+        tl, dl = W.values(inp["target_logits"], dt).copy(), W.values(inp["draft_logits"], dt).copy()
+        want = []
+        for b in range(B):
+            path, n, level = [], 0, 0
+            while True:
+                kids = [i for i in range(1, N) if parent[i] == n]
+                if not kids:
+                    break
+                R = rejections[level] if level < len(rejections) else len(kids)
+                toks = 11 + 37 * np.arange(len(kids)) + 5 * b
+                inp["node_tokens"][b, kids] = toks
+                tl[b, n, toks[:R]], dl[b, n, toks[:R]] = -30.0, 8.0       # certain rejections
+                if R < len(kids):
+                    tl[b, n, toks[R]], dl[b, n, toks[R]] = 12.0, -30.0    # certainly kept
+                    path.append(kids[R])
+                    n, level = kids[R], level + 1
+                else:
+                    break
+            want.append(path)
+        inp["target_logits"], inp["draft_logits"] = W.to_dtype(tl, dt), W.to_dtype(dl, dt)
+        got, ref = _check(svl, orc, inp, f"resume {label} dt{dt}")
+        for b in range(B):
+            assert ref["accepted_nodes"][b][:len(want[b])].tolist() == want[b]
+            assert ref["accepted_len"][b] == len(want[b])
 
 
 @pytest.mark.parametrize("V", [1, 2, 9, 64, 257, 512, 2049, 4096])

@@ -50,24 +50,66 @@ def test_summary_scales_counters_by_the_plain_copy(tmp_path):
                            "--fetch", fetch, "--write", write, "--workload", "w", "--prefix", "w",
                            "--command", "python3 bench.py", "--out", out], stdout=subprocess.DEVNULL)
     md = open(os.path.join(out, "w_kernel_trace.md")).read()
-    assert "| chain_rowstats | 10 | 21.40 | 20.00 | 23.00 | 60.0% |" in md
-    assert bench.kernel_source_digest() in md
+    assert "| chain_rowstats | 10 | 21.40 | - | 20.00 | 23.00 | 60.0% |" in md
+    assert f"Kernel sources digest: `{bench.trace_digest(['chain_rowstats'])}`" in md
     rec = json.load(open(os.path.join(out, "chain_rowstats_w_traffic.json")))
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
     assert rec["fetch_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2)
     assert rec["write_bytes_per_launch"] == pytest.approx(20.0 * 1024)
     assert rec["traffic_bytes_per_launch"] == pytest.approx(2000.0 * 2048 + 20.0 * 1024)
-    assert rec["kernel_source_digest"] == bench.kernel_source_digest()
+    assert rec["kernel_source_digest"] == bench.kernel_source_digest("chain_rowstats")
+    assert rec["kernel_sources"] == bench.kernel_sources("chain_rowstats")
+
+
+def test_kernel_digests_follow_each_family_sources():
+    """A kernel's counters stay valid while the sources it is built from do
+    not change: every family's files include the public header, the common
+    header and the host dispatch, and no family reads another's header."""
+    csrc = "draft_token_verification_chain_amd/csrc/"
+    for k in ("chain_rowstats", "chain_final_part", "chain_row_draw", "greedy_rows", "argmax_rows", "tree_plan",
+              "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"):
+        srcs = bench.kernel_sources(k)
+        assert {"include/specverify.h", csrc + "sv_common.hpp", csrc + "specverify.hip"} <= set(srcs), k
+        assert all(os.path.exists(os.path.join(ROOT, p)) for p in srcs)
+    assert csrc + "sv_tree_sampled.hpp" not in bench.kernel_sources("chain_final_part")
+    assert csrc + "sv_greedy_tree.hpp" not in bench.kernel_sources("tree_round")
+    assert csrc + "sv_chain.hpp" in bench.kernel_sources("tree_round")  # the walk's pick lives there
+    assert bench.kernel_source_digest("chain_rowstats") != bench.kernel_source_digest("greedy_rows")
+    assert set(bench.kernel_sources()) >= set(bench.kernel_sources("tree_round"))
 
 
 def test_bench_ignores_counters_taken_on_other_sources(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"kernel_source_digest": bench.kernel_source_digest(), "traffic_bytes_per_launch": 123.0}
+    rec = {"kernel_source_digest": bench.kernel_source_digest("k"), "traffic_bytes_per_launch": 123.0}
     (prof / "k_w_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: rec["kernel_source_digest"])
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda kernel=None: rec["kernel_source_digest"])
     assert bench.load_traffic("k", "w") == 123.0
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda kernel=None: "0" * 16)
     assert bench.load_traffic("k", "w") is None
     assert bench.load_traffic("missing", "w") is None
+
+
+def test_bench_reads_the_trace_average_of_current_sources(tmp_path, monkeypatch):
+    """roofline.rocprof_avg_us comes from the committed trace summary of the
+    workload, and only while that trace's digest matches the sources of the
+    library kernels it lists."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    table = ["| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|---:|",
+             "| spin | 4 | 20000.00 | 20000.00 | 19000.00 | 21000.00 | 70.0% |",
+             "| chain_rowstats | 820 | 21.75 | 21.70 | 20.10 | 27.00 | 16.0% |",
+             "| chain_final_pick | 820 | 4.60 | 4.50 | 3.80 | 6.30 | 3.0% |"]
+    good = bench.trace_digest(["chain_rowstats", "chain_final_pick"])
+    (prof / "w_kernel_trace.md").write_text("\n".join([f"Kernel sources digest: `{good}`", ""] + table) + "\n")
+    (prof / "v_kernel_trace.md").write_text("\n".join(["Kernel sources digest: `0000000000000000`", ""] + table))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "trace_digest", lambda kernels: good if sorted(kernels) == [
+        "chain_final_pick", "chain_rowstats"] else "x")
+    assert bench.load_trace_average("chain_rowstats", "w") == pytest.approx(21.75)
+    assert bench.load_trace_average("spin", "w") == pytest.approx(20000.0)
+    assert bench.load_trace_average("chain_final_part", "w") is None
+    assert bench.load_trace_average("chain_rowstats", "v") is None
+    assert bench.load_trace_average("chain_rowstats", "missing") is None
