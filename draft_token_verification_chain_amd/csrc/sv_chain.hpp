@@ -380,17 +380,13 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     constexpr int VE = Elem<DT>::per_vec;
     constexpr int NE = kFinU * VE;
     const int lane = lane_id();
-    float w[NE];  // the target's logits, then (in place) the weights
-    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
-    if (mode == kFinalArgmax) {
-        best = better(best, argmax_of_tile<DT, kFinU>(w, tile));
-        return;
-    }
     static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
     float a[kFinU];
     int i_own;
     if (mode == kFinalResidual) {
-        float vd[NE];
+        // both rows' loads go out together, ahead of any use
+        float w[NE], vd[NE];
+        load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
         load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
         float e[kFinU], x[kFinU];
         bool near = false;
@@ -417,6 +413,12 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
         }
         const int64_t g = tile * kFinU + i_own;
         if (lane < kFinU && g < nseg) seg_out[g] = residual_seg(m, ea, xs, ss);
+        return;
+    }
+    float w[NE];  // the target's logits, then (in place) the weights
+    load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
+    if (mode == kFinalArgmax) {
+        best = better(best, argmax_of_tile<DT, kFinU>(w, tile));
         return;
     }
     float mx = w[0];
@@ -555,8 +557,12 @@ __device__ Draw draw_from_segments(const void* draft, const void* target, int64_
     // segment g of this lane's window w
     const SegMass zero = residual ? residual_seg(0.f, 0.f, 0.f, 0.f) : bonus_seg(0.f, kNoRef);
     auto seg_at = [&](int64_t w, int j) -> SegMass {
+        if (w == 0) return first[j];
+        // an unconditional load (index clamped), so that a window's loads
+        // are in flight together
         const int64_t g = g0 + w * kSegRun + j;
-        return w == 0 ? first[j] : (g < g1 ? sg[g] : zero);
+        const SegMass q = sg[min<int64_t>(g, nseg - 1)];
+        return g < g1 ? q : zero;
     };
     auto in_run = [&](int64_t w, int j) { return g0 + w * kSegRun + j < g1; };
     // residual: the correction zeta of kappa from the row's total X; bonus:
@@ -568,11 +574,12 @@ __device__ Draw draw_from_segments(const void* draft, const void* target, int64_
         float xs = 0.f, ss = 0.f;
         for (int64_t w = 0; w < nwin; ++w)
 #pragma unroll
-            for (int j = 0; j < kSegRun; ++j)
-                if (in_run(w, j)) {
-                    xs += seg_at(w, j).x;
-                    ss += seg_at(w, j).sw;
-                }
+            for (int j = 0; j < kSegRun; ++j) {
+                const SegMass q = seg_at(w, j);
+                const bool in = in_run(w, j);
+                xs += in ? q.x : 0.f;
+                ss += in ? q.sw : 0.f;
+            }
         zeta = kappa_zeta(static_cast<double>(wave_sum(xs)), static_cast<double>(s.st));
         sw = static_cast<double>(wave_sum(ss));
         set_kappa(s, s.kappa + zeta / kLn2);
@@ -649,6 +656,26 @@ __device__ Draw draw_from_segments(const void* draft, const void* target, int64_
     return Draw{y, s.kappa};
 }
 
+// kSegRun segment masses m[c0 ..] (indices clamped into the row's nseg
+// segments): unconditional loads, all in flight together.
+__device__ __forceinline__ void load_masses(const float* m, int64_t c0, int64_t nseg, float* v) {
+#pragma unroll
+    for (int j = 0; j < kSegRun; ++j) v[j] = m[min<int64_t>(c0 + j, nseg - 1)];
+}
+
+// The sum of segment masses m[a .. e), in index order.
+__device__ __forceinline__ double run_sum(const float* m, int64_t a, int64_t e, int64_t nseg) {
+    double run = 0.0;
+    for (int64_t c0 = a; c0 < e; c0 += kSegRun) {
+        float v[kSegRun];
+        load_masses(m, c0, nseg, v);
+#pragma unroll
+        for (int j = 0; j < kSegRun; ++j)
+            if (c0 + j < e) run += static_cast<double>(v[j]);
+    }
+    return run;
+}
+
 // Residual masses of every segment of rows trow / drow formed with kappa as
 // given in s (every wave of a workgroup of `waves` waves; mass of segment g
 // into m[g]).  The caller synchronises the workgroup before reading m.
@@ -674,8 +701,7 @@ __device__ int pick_from_masses_f(const void* draft, const void* target, int64_t
     const int lane = lane_id();
     const int64_t per = (nseg + kWave - 1) / kWave;
     const int64_t a = min<int64_t>(nseg, lane * per), e = min<int64_t>(nseg, a + per);
-    double run = 0.0;
-    for (int64_t g = a; g < e; ++g) run += static_cast<double>(m[g]);
+    const double run = run_sum(m, a, e, nseg);
     const double incl = wave_inclusive_scan(run);
     const double W = __shfl(incl, kWave - 1, kWave);
     const double excl = __shfl_up(incl, 1, kWave);  // every lane shuffles
@@ -684,14 +710,21 @@ __device__ int pick_from_masses_f(const void* draft, const void* target, int64_t
     const double target_mass = u * W;
     int64_t found = -1, last_pos = -1;
     double Pfound = 0.0;
-    for (int64_t g = a; g < e; ++g) {
-        const double mg = static_cast<double>(m[g]);
-        if (found < 0 && P + mg > target_mass) {
-            found = g;
-            Pfound = P;
+    for (int64_t c0 = a; c0 < e; c0 += kSegRun) {
+        float v[kSegRun];
+        load_masses(m, c0, nseg, v);
+#pragma unroll
+        for (int j = 0; j < kSegRun; ++j) {
+            const int64_t g = c0 + j;
+            if (g >= e) break;
+            const double mg = static_cast<double>(v[j]);
+            if (found < 0 && P + mg > target_mass) {
+                found = g;
+                Pfound = P;
+            }
+            if (mg > 0.0) last_pos = g;
+            P += mg;
         }
-        if (mg > 0.0) last_pos = g;
-        P += mg;
     }
     int fl = first_lane(found >= 0);
     int64_t seg;
@@ -713,12 +746,15 @@ __device__ int pick_from_masses_f(const void* draft, const void* target, int64_t
     return y;
 }
 
-// The lane's first kSegRun segments of draw_from_segments.
+// The lane's first kSegRun segments of draw_from_segments (records past the
+// lane's run are never used).  Every load is unconditional, its index clamped
+// into the row's segments, so that all of them are in flight together rather
+// than each behind a branch and a wait of its own.
 __device__ __forceinline__ void first_segments(const SegMass* sg, int64_t nseg, SegMass* first) {
     const int64_t per = (nseg + kWave - 1) / kWave;
-    const int64_t g0 = min<int64_t>(nseg, lane_id() * per), g1 = min<int64_t>(nseg, g0 + per);
+    const int64_t g0 = min<int64_t>(nseg, lane_id() * per);
 #pragma unroll
-    for (int j = 0; j < kSegRun; ++j) first[j] = (g0 + j < g1) ? sg[g0 + j] : bonus_seg(0.f, kNoRef);
+    for (int j = 0; j < kSegRun; ++j) first[j] = sg[min<int64_t>(g0 + j, nseg - 1)];
 }
 
 // A residual draw whose first-order kappa correction is not trusted (see

@@ -367,9 +367,7 @@ __device__ bool pick_from_masses(const void* draft, const void* target, int64_t 
     const SeqInfo s = walk_info(T, st.Rt, st.St, st.K, st.c);
     const int64_t per = (nseg + kWave - 1) / kWave;
     const int64_t a0 = min<int64_t>(nseg, lane * per), a1 = min<int64_t>(nseg, a0 + per);
-    double run = 0.0;
-    for (int64_t g = a0; g < a1; ++g) run += static_cast<double>(m[g]);
-    const double W = __shfl(wave_inclusive_scan(run), kWave - 1, kWave);
+    const double W = __shfl(wave_inclusive_scan(run_sum(m, a0, a1, nseg)), kWave - 1, kWave);
     if (!(W > 0.0)) return false;
     const int64_t row = (b * N + st.node) * static_cast<int64_t>(V);
     y = pick_from_masses_f<DT, VEC>(draft, target, row, row, V, nseg, s, st.c > 0.0, m, static_cast<double>(u));
