@@ -725,9 +725,13 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
     int32_t* nodes = accepted_nodes ? accepted_nodes + b * width : nullptr;
     const int64_t nbn = static_cast<int64_t>(B) * N;
     const int32_t* par = parent + b * static_cast<int64_t>(parent_stride);
-    // every input of the round first (none depends on another): the tree, the
-    // tokens, uniforms and gathered logits of every node, the pending pass's
-    // partial sums and, after round 0, the node normalisers
+    // every input of the round first (none depends on another): the
+    // sequence's temperature and walk state, the tree, the tokens, uniforms
+    // and gathered logits of every node, the pending pass's partial sums and,
+    // after round 0, the node normalisers
+    const float T = temperature[b];
+    WalkState st{};
+    if (!first) st = st_in[b];
     int r_par[kRoundSlots], r_tok[kRoundSlots];
     float r_u[kRoundSlots], r_tg[kRoundSlots], r_dg[kRoundSlots];
     NodeNorm r_nrm[kRoundSlots];
@@ -750,9 +754,7 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         for (int q = lane; q < P; q += kWave)
 #pragma unroll
             for (int e = 0; e < 4; ++e) zz[e] += z_in[(b * P + q) * 4 + e];
-    const float T = temperature[b];
     const bool sampled = T > 0.f;
-    WalkState st{};
     if (first) {
         // with the cache: node j + (3 - wave) P of this workgroup, if any, is
         // combined by this wave (lanes 0-31 the target row, 32-63 the draft
@@ -795,8 +797,6 @@ __global__ __launch_bounds__(kRoundBlock) void tree_round_kernel(
         st.phase = bad ? kWalkDone : kWalkEnter;
         st.Z = 1.0;
         if (bad && lead && t == 0) accepted_len[b] = -1;
-    } else {
-        st = st_in[b];
     }
     if (st.phase == kWalkDone || st.phase == kWalkStuck) {
         if (lead && t == 0) st_out[b] = st;
