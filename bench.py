@@ -90,10 +90,12 @@ def trace_digest(kernels) -> str:
     return sources_digest(sorted({p for k in kernels for p in kernel_sources(k)}))
 
 
-def load_trace_average(kernel: str, workload: str):
+def load_trace_average(kernel: str, workload: str, column: str = "average (us)"):
     """The kernel's average duration (us) in the committed rocprofv3 kernel
-    trace of the workload, if that trace was taken on the current sources of
-    its kernels; otherwise None."""
+    trace of the workload (by default over all its dispatches; "event-timed
+    region average (us)": over the region whose durations bench.py reports),
+    if that trace was taken on the current sources of its kernels; otherwise
+    None."""
     path = os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md")
     if not os.path.exists(path):
         return None
@@ -102,10 +104,11 @@ def load_trace_average(kernel: str, workload: str):
     rows, col = {}, None
     for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if cells and cells[0] == "kernel" and "average (us)" in cells:
-            col = cells.index("average (us)")
+        if cells and cells[0] == "kernel" and column in cells:
+            col = cells.index(column)
         elif col is not None and len(cells) > col and re.fullmatch(r"\d+", cells[1]):
-            rows[cells[0]] = float(cells[col])
+            if re.fullmatch(r"[0-9.]+", cells[col]):
+                rows[cells[0]] = float(cells[col])
     lib = [k for k in rows if k in LIBRARY_KERNELS]
     if not m or kernel not in rows or m.group(1) != trace_digest(lib):
         return None
@@ -510,7 +513,8 @@ def main():
     dom_bytes = m["dom_bytes"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9 if dom_bytes else None
     traffic = load_traffic(dominant, args.workload)
-    rocprof_us = load_trace_average(dominant, args.workload)
+    rocprof_us = load_trace_average(dominant, args.workload, "event-timed region average (us)")
+    rocprof_b2b_us = load_trace_average(dominant, args.workload)
     inp, cfg = wl.inp, wl.cfg
     B, V, kind = inp["B"], inp["V"], wl.kind
     result = {
@@ -546,11 +550,14 @@ def main():
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS if achieved else None, "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "avg_launch_us": dom_us, "duration_source": "hip_events",
                      "traffic_gbs": traffic / (dom_us * 1e-6) / 1e9 if traffic else None,
-                     # the same kernel's average in the committed rocprofv3 trace (null once
-                     # its sources have changed) and the fraction it gives
+                     # the same kernel in the committed rocprofv3 trace of this command (null
+                     # once its sources have changed): its average over the event-timed
+                     # region, the fraction that gives, and its average over all dispatches,
+                     # most of them back to back (slower by the preceding kernel's tail)
                      "rocprof_avg_us": rocprof_us,
                      "frac_rocprof": (dom_bytes / (rocprof_us * 1e-6) / 1e9 / PEAK_HBM_GBS
-                                      if rocprof_us and dom_bytes else None)},
+                                      if rocprof_us and dom_bytes else None),
+                     "rocprof_avg_us_all_dispatches": rocprof_b2b_us},
     }
 
     if not args.no_cpu:

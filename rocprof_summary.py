@@ -6,11 +6,13 @@ Inputs (rocprofv3 CSV output directories):
   --fetch DIR   from  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
   --write DIR   from  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
   --sq DIR      from  rocprofv3 --pmc <SQ_COUNTERS> --output-format csv -d DIR -o bench -- python3 bench.py ...
+  --lat DIR     from  rocprofv3 --pmc <LAT_COUNTERS> --output-format csv -d DIR -o bench -- python3 bench.py ...
 
 Outputs:
   profiles/<prefix>_kernel_trace.md          per-kernel calls / average / min / max duration
   profiles/<kernel>_<workload>_traffic.json  HBM-side bytes per launch of each library kernel
   profiles/<prefix>_sq_counters.md           per-kernel SQ counters and the VALU floor
+  profiles/<prefix>_latency_counters.md      per-kernel L2 read latency and waiting
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
 the calibration copy (one plain device-to-device copy of MIB MiB, which reads
@@ -35,15 +37,27 @@ def short_name(full: str) -> str:
     return n[:-len("_kernel")] if n.endswith("_kernel") else n
 
 
-def trace_medians(d: str) -> dict:
-    """Median duration (us) per kernel from the per-dispatch kernel trace, if present."""
+def trace_durations(d: str) -> dict:
+    """Per-dispatch durations (us, in dispatch order) per kernel from the kernel trace, if present."""
     path = os.path.join(d, "bench_kernel_trace.csv")
     if not os.path.exists(path):
         return {}
     per = collections.defaultdict(list)
-    for r in csv.DictReader(open(path)):
+    for r in sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"])):
         per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    return {k: statistics.median(v) for k, v in per.items()}
+    return per
+
+
+def event_region_average(durs: list, steps: int, warmup: int):
+    """bench.py runs warmup steps, three timed regions of `steps` steps and
+    last the region with an event pair attached to each dispatch: the
+    average over that last region's dispatches (a kernel launched n times
+    per step has n * steps of them)."""
+    total = warmup + 4 * steps
+    if not durs or len(durs) % total:
+        return None
+    n = len(durs) // total * steps
+    return sum(durs[-n:]) / n
 
 
 def read_counters(d: str) -> dict:
@@ -96,13 +110,50 @@ def sq_summary(d: str, prefix: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+LAT_COUNTERS = ("SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INST_LEVEL_VMEM SQ_ACTIVE_INST_ANY SQ_LEVEL_WAVES "
+                "SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_TRANS_F32 TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum")
+
+
+def latency_summary(d: str, prefix: str, command: str) -> str:
+    """Per-kernel memory latency and waiting (averages per dispatch): the mean
+    latency of an L1-to-L2 read request in cycles (TCP_TCC_READ_REQ_LATENCY
+    over TCP_TCC_READ_REQ, the L2's misses to HBM included), the fraction of
+    wave-cycles spent waiting for anything (SQ_WAIT_ANY over SQ_WAVE_CYCLES:
+    memory counters, barriers, dependencies) and the transcendental
+    instructions per wave."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(os.path.join(d, "bench_counter_collection.csv"))):
+        per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 latency counters: {prefix}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", f"rocprofv3 --pmc {LAT_COUNTERS} --output-format csv -d <dir> -o bench -- {command}", "```", "",
+             "Averages per dispatch. L2 read latency = TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum (cycles "
+             "from an L1 request to its data, L2 misses included); wait fraction = SQ_WAIT_ANY / SQ_WAVE_CYCLES.", "",
+             "| kernel | waves | L2 read requests | L2 read latency (cycles) | wait fraction | transcendentals / wave |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for full, c in per.items():
+        if "sv::" not in full:
+            continue
+        a = {k: sum(v) / len(v) for k, v in c.items()}
+        waves = a.get("SQ_WAVES", 0.0)
+        if not waves:
+            continue
+        req = a["TCP_TCC_READ_REQ_sum"]
+        lat = a["TCP_TCC_READ_REQ_LATENCY_sum"] / req if req else float("nan")
+        lines.append(f"| {short_name(full)} | {waves:.0f} | {req:.0f} | {lat:.0f} | "
+                     f"{a['SQ_WAIT_ANY'] / a['SQ_WAVE_CYCLES']:.2f} | {a['SQ_INSTS_VALU_TRANS_F32'] / waves:.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace")
     ap.add_argument("--sq", help="rocprofv3 --pmc output of the SQ counters (SQ_COUNTERS)")
+    ap.add_argument("--lat", help="rocprofv3 --pmc output of the latency counters (LAT_COUNTERS)")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calibrate-mib", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=200, help="--steps of the traced bench.py command")
+    ap.add_argument("--warmup", type=int, default=20, help="--warmup of the traced bench.py command")
     ap.add_argument("--workload", default="llama_chain")
     ap.add_argument("--prefix", default="llama_chain")
     ap.add_argument("--command", required=True, help="the bench command of the kernel-trace run")
@@ -116,6 +167,11 @@ def main():
         with open(os.path.join(args.out, f"{args.prefix}_sq_counters.md"), "w") as f:
             f.write(text)
         print(text)
+    if args.lat:
+        text = latency_summary(args.lat, args.prefix, pmc_cmd)
+        with open(os.path.join(args.out, f"{args.prefix}_latency_counters.md"), "w") as f:
+            f.write(text)
+        print(text)
     if not args.trace:
         return
 
@@ -127,14 +183,21 @@ def main():
              "Command (run from the repository root on one MI355X):", "",
              "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- {args.command}", "```",
              "", f"Kernel sources digest: `{digest}`", "",
-             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---:|---:|---:|---:|---:|---:|"]
-    medians = trace_medians(args.trace)
+             "The event-timed region is bench.py's last timed region, in which an event pair is attached to "
+             "each dispatch (the durations bench.py reports); its kernels run apart, the other regions' back to "
+             "back.", "",
+             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time | "
+             "event-timed region average (us) |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    durs = trace_durations(args.trace)
     for r in rows:
-        med = medians.get(r["Name"])
+        d = durs.get(r["Name"], [])
+        med = statistics.median(d) if d else None
+        ev = event_region_average(d, args.steps, args.warmup)
         lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{'%.2f' % med if med is not None else '-'} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% | "
+                     f"{'%.2f' % ev if ev is not None else '-'} |")
     with open(os.path.join(args.out, f"{args.prefix}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 

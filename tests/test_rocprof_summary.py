@@ -35,6 +35,15 @@ def test_short_name(full, short):
     assert rs.short_name(full) == short
 
 
+def test_event_region_is_the_last_of_the_bench_regions():
+    """20 warmup steps, three timed regions of 200 and the event-timed region
+    last: a kernel launched twice per step has 400 dispatches there."""
+    durs = [1.0] * (2 * 20 + 3 * 2 * 200) + [3.0] * (2 * 200)
+    assert rs.event_region_average(durs, 200, 20) == pytest.approx(3.0)
+    assert rs.event_region_average(durs[1:], 200, 20) is None  # not a whole number of steps
+    assert rs.event_region_average([], 200, 20) is None
+
+
 def test_summary_scales_counters_by_the_plain_copy(tmp_path):
     trace, fetch, write, out = (str(tmp_path / d) for d in ("trace", "fetch", "write", "out"))
     _write_csv(os.path.join(trace, "bench_kernel_stats.csv"),
@@ -50,7 +59,7 @@ def test_summary_scales_counters_by_the_plain_copy(tmp_path):
                            "--fetch", fetch, "--write", write, "--workload", "w", "--prefix", "w",
                            "--command", "python3 bench.py", "--out", out], stdout=subprocess.DEVNULL)
     md = open(os.path.join(out, "w_kernel_trace.md")).read()
-    assert "| chain_rowstats | 10 | 21.40 | - | 20.00 | 23.00 | 60.0% |" in md
+    assert "| chain_rowstats | 10 | 21.40 | - | 20.00 | 23.00 | 60.0% | - |" in md
     assert f"Kernel sources digest: `{bench.trace_digest(['chain_rowstats'])}`" in md
     rec = json.load(open(os.path.join(out, "chain_rowstats_w_traffic.json")))
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
@@ -97,11 +106,12 @@ def test_bench_reads_the_trace_average_of_current_sources(tmp_path, monkeypatch)
     library kernels it lists."""
     prof = tmp_path / "profiles"
     prof.mkdir()
-    table = ["| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
-             "|---|---:|---:|---:|---:|---:|---:|",
-             "| spin | 4 | 20000.00 | 20000.00 | 19000.00 | 21000.00 | 70.0% |",
-             "| chain_rowstats | 820 | 21.75 | 21.70 | 20.10 | 27.00 | 16.0% |",
-             "| chain_final_pick | 820 | 4.60 | 4.50 | 3.80 | 6.30 | 3.0% |"]
+    table = ["| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time | "
+             "event-timed region average (us) |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|",
+             "| spin | 4 | 20000.00 | 20000.00 | 19000.00 | 21000.00 | 70.0% | - |",
+             "| chain_rowstats | 820 | 21.75 | 21.70 | 20.10 | 27.00 | 16.0% | 21.10 |",
+             "| chain_final_pick | 820 | 4.60 | 4.50 | 3.80 | 6.30 | 3.0% | 4.40 |"]
     good = bench.trace_digest(["chain_rowstats", "chain_final_pick"])
     (prof / "w_kernel_trace.md").write_text("\n".join([f"Kernel sources digest: `{good}`", ""] + table) + "\n")
     (prof / "v_kernel_trace.md").write_text("\n".join(["Kernel sources digest: `0000000000000000`", ""] + table))
@@ -109,7 +119,9 @@ def test_bench_reads_the_trace_average_of_current_sources(tmp_path, monkeypatch)
     monkeypatch.setattr(bench, "trace_digest", lambda kernels: good if sorted(kernels) == [
         "chain_final_pick", "chain_rowstats"] else "x")
     assert bench.load_trace_average("chain_rowstats", "w") == pytest.approx(21.75)
+    assert bench.load_trace_average("chain_rowstats", "w", "event-timed region average (us)") == pytest.approx(21.10)
     assert bench.load_trace_average("spin", "w") == pytest.approx(20000.0)
+    assert bench.load_trace_average("spin", "w", "event-timed region average (us)") is None
     assert bench.load_trace_average("chain_final_part", "w") is None
     assert bench.load_trace_average("chain_rowstats", "v") is None
     assert bench.load_trace_average("chain_rowstats", "missing") is None
