@@ -755,6 +755,9 @@ __device__ __forceinline__ void first_segments(const SegMass* sg, int64_t nseg, 
     const int64_t g0 = min<int64_t>(nseg, lane_id() * per);
 #pragma unroll
     for (int j = 0; j < kSegRun; ++j) first[j] = sg[min<int64_t>(g0 + j, nseg - 1)];
+    // keep the scheduler from moving the records' first uses in between the
+    // loads, which makes them wait for one another
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // A residual draw whose first-order kappa correction is not trusted (see
@@ -794,13 +797,17 @@ __global__ __launch_bounds__(kPickBlock) void chain_final_pick_kernel(
     const int64_t b = blockIdx.x;
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
     const SegMass* sg = segs + b * nseg;
+    // the descriptor and the lane's first segment records are in flight
+    // together (a sequence with nothing to draw leaves the records unused);
+    // wave 0, which draws, is told apart with a wave-uniform test
+    const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x) < kWave;
     const SeqInfo s = info[b];
+    SegMass first[kSegRun];
+    if (wave0) first_segments(sg, nseg, first);
     if (s.mode == kFinalDone) return;
     const int64_t trow = (b * (k + 1) + s.a) * static_cast<int64_t>(V);
     const int64_t drow = (b * k + s.a) * static_cast<int64_t>(V);
-    if (threadIdx.x < kWave) {
-        SegMass first[kSegRun];
-        first_segments(sg, nseg, first);
+    if (wave0) {
         Draw d{0, s.kappa};
         if (s.mode == kFinalArgmax)
             d.y = wave_combine_argmax(chunkarg + b * nchunk, nchunk).idx;

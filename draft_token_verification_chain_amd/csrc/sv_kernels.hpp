@@ -13,15 +13,19 @@
 //              large ones, not at all without drafts;
 //   final_part streams only the row(s) the final draw needs (target and draft
 //              row a at a rejection, target row k after full acceptance) and
-//              writes the residual mass of every 64-vector segment;
-//   final_pick one wave per sequence: prefix over the segment masses, picks
-//              the segment holding u * W and rescans only that segment to find
-//              the token.
+//              writes the statistics of every 64-vector segment: a residual's
+//              terms are formed relative to themselves, with the sums that
+//              correct log2(S_t / S_d) afterwards;
+//   final_pick one wave per sequence: corrects a residual's masses, prefix
+//              over the segment masses, picks the segment holding u * W and
+//              rescans only that segment to find the token (the workgroup
+//              forms the masses again when the correction cannot be trusted).
+// Plain sampling of many rows draws each row in one workgroup (row_draw).
 // sv_verify_greedy and sv_verify_tree use argmax_rows (the streaming argmax)
 // followed by a per-sequence finaliser.  sv_verify_tree_sampled streams the
 // tree's rows (tree_rowstats), then walks every tree in rounds of launches
-// (tree_round), with a one-workgroup walk (tree_sample) for what the rounds
-// leave.  sv_commit_tokens is one workgroup (commit_tokens).
+// (tree_round), with a one-workgroup walk (tree_sample) that finishes what
+// the rounds leave.  sv_commit_tokens is one workgroup (commit_tokens).
 //
 // Scheme: "Accelerating Sonar through speculation" (Perplexity, 2025),
 // sections "Speculative decoding", "Target-Draft" and "EAGLE"; acceptance
