@@ -385,17 +385,41 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     int i_own;
     if (mode == kFinalResidual) {
         // both rows' loads go out together, ahead of any use
-        float w[NE], vd[NE];
-        load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
-        load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
         float e[kFinU], x[kFinU];
         bool near = false;
+        if constexpr (FULL && VEC) {
+            // raw 16-byte vectors, unpacked one segment at a time: fewer live
+            // registers, so more waves per SIMD
+            const char* tr = static_cast<const char*>(target) + trow * Elem<DT>::bytes;
+            const char* dr = static_cast<const char*>(draft) + drow * Elem<DT>::bytes;
+            const int64_t v0 = tile * (64 * kFinU) + lane;
+            uint4 rt4[kFinU], rd4[kFinU];
 #pragma unroll
-        for (int i = 0; i < kFinU; ++i) {
-            const ResidualSums r = residual_sums_marked<DT, VE, FULL>(w + i * VE, vd + i * VE, si, near);
-            a[i] = r.m;
-            e[i] = r.ea;
-            x[i] = r.x;
+            for (int i = 0; i < kFinU; ++i) {
+                rt4[i] = *reinterpret_cast<const uint4*>(tr + (v0 + i * 64) * 16);
+                rd4[i] = *reinterpret_cast<const uint4*>(dr + (v0 + i * 64) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) {
+                float vt[VE], vd[VE];
+                unpack<DT>(rt4[i], vt);
+                unpack<DT>(rd4[i], vd);
+                const ResidualSums r = residual_sums_marked<DT, VE, true>(vt, vd, si, near);
+                a[i] = r.m;
+                e[i] = r.ea;
+                x[i] = r.x;
+            }
+        } else {
+            float w[NE], vd[NE];
+            load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
+            load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) {
+                const ResidualSums r = residual_sums_marked<DT, VE, FULL>(w + i * VE, vd + i * VE, si, near);
+                a[i] = r.m;
+                e[i] = r.ea;
+                x[i] = r.x;
+            }
         }
         const float m = wave_sum4(a, i_own);
         const float ea = wave_sum4(e, i_own);
@@ -404,11 +428,33 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
         // from the tile loaded again (the first loads are no longer live)
         float ss = 0.f;
         if (__builtin_amdgcn_ballot_w64(near) != 0) {
-            float rt[NE], rd[NE], sw[kFinU];
-            load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, rt);
-            load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, rd);
+            float sw[kFinU];
+            if constexpr (FULL && VEC) {
+                // raw vectors again, unpacked one segment at a time (the
+                // branch then does not raise the kernel's register count)
+                const char* tr = static_cast<const char*>(target) + trow * Elem<DT>::bytes;
+                const char* dr = static_cast<const char*>(draft) + drow * Elem<DT>::bytes;
+                const int64_t v0 = tile * (64 * kFinU) + lane;
+                uint4 rt4[kFinU], rd4[kFinU];
 #pragma unroll
-            for (int i = 0; i < kFinU; ++i) sw[i] = residual_sw<DT, VE, FULL>(rt + i * VE, rd + i * VE, si);
+                for (int i = 0; i < kFinU; ++i) {
+                    rt4[i] = *reinterpret_cast<const uint4*>(tr + (v0 + i * 64) * 16);
+                    rd4[i] = *reinterpret_cast<const uint4*>(dr + (v0 + i * 64) * 16);
+                }
+#pragma unroll
+                for (int i = 0; i < kFinU; ++i) {
+                    float vt[VE], vd[VE];
+                    unpack<DT>(rt4[i], vt);
+                    unpack<DT>(rd4[i], vd);
+                    sw[i] = residual_sw<DT, VE, true>(vt, vd, si);
+                }
+            } else {
+                float rt[NE], rd[NE];
+                load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, rt);
+                load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, rd);
+#pragma unroll
+                for (int i = 0; i < kFinU; ++i) sw[i] = residual_sw<DT, VE, FULL>(rt + i * VE, rd + i * VE, si);
+            }
             ss = wave_sum4(sw, i_own);
         }
         const int64_t g = tile * kFinU + i_own;
@@ -454,7 +500,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
             accept_sequence<DT>(tokens, temperature, uniforms, B, k, V, nT, part, gathered, b, k, c == 0, accepted_len,
                                 emitted, accept_prob, s_r, s_s, &s_info);
         __syncthreads();
-        si = s_info;
+        si = uniform_info(s_info);
         if (c == 0 && threadIdx.x == 0) info[b] = si;
         if (si.mode == kFinalDone) return;
     } else if constexpr (ACC == kAcceptNone) {
@@ -469,7 +515,7 @@ __global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
             accepted_len[b] = 0;
         }
     } else {
-        si = info[b];
+        si = uniform_info(info[b]);
         if (si.mode == kFinalDone) return;
     }
     const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;

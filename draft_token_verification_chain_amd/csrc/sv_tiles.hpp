@@ -33,6 +33,20 @@ struct SeqInfo {
 };
 static_assert(sizeof(SeqInfo) == 64, "descriptor layout");
 
+// A descriptor that every lane of the wave holds alike (read from LDS or
+// memory at a uniform address), moved to scalar registers: the compiler
+// cannot tell that an LDS value is uniform and would keep all sixteen words
+// in vector registers.
+__device__ __forceinline__ SeqInfo uniform_info(const SeqInfo& s) {
+    SeqInfo u;
+    const int* src = reinterpret_cast<const int*>(&s);
+    int* dst = reinterpret_cast<int*>(&u);
+#pragma unroll
+    for (int i = 0; i < static_cast<int>(sizeof(SeqInfo) / sizeof(int)); ++i)
+        dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+    return u;
+}
+
 // The final draw's statistics of one segment: bonus draws store the mass
 // sum exp2(l c - ref) and its integer reference; residual draws store, in
 // units of the target row's reference, M = sum max(0, x), X = sum x,
