@@ -125,3 +125,30 @@ def test_bench_reads_the_trace_average_of_current_sources(tmp_path, monkeypatch)
     assert bench.load_trace_average("chain_final_part", "w") is None
     assert bench.load_trace_average("chain_rowstats", "v") is None
     assert bench.load_trace_average("chain_rowstats", "missing") is None
+
+
+def test_sq_and_latency_summaries(tmp_path):
+    """Per-kernel figures from synthetic counter files: instructions per wave,
+    the VALU floor (instructions x 4 cycles over 1024 SIMDs at 2.4 GHz), the
+    wait fractions, the mean L2 read latency and transcendentals per wave."""
+    d = str(tmp_path / "sq")
+    rows = []
+    for name, val in [("SQ_WAVES", 1024), ("SQ_INSTS_VALU", 1024 * 600), ("SQ_INSTS_SALU", 1024 * 50),
+                      ("SQ_INSTS_VMEM_RD", 1024 * 8), ("SQ_WAIT_INST_ANY", 250), ("SQ_WAVE_CYCLES", 1000),
+                      ("SQ_BUSY_CYCLES", 1), ("SQ_ACTIVE_INST_VALU", 1), ("GRBM_GUI_ACTIVE", 1)]:
+        rows += [[KERNEL, name, val], [KERNEL, name, val]]
+    rows.append([COPY, "SQ_WAVES", 8])
+    _write_csv(os.path.join(d, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    md = rs.sq_summary(d, "w", "python3 bench.py")
+    floor = 1024 * 600 * 4 / (1024 * 2.4e9) * 1e6
+    assert f"| chain_rowstats | 2 | 1024 | 600 | 50 | 8.0 | {floor:.2f} | 0.25 |" in md
+    assert COPY not in md
+    d2 = str(tmp_path / "lat")
+    rows = []
+    for name, val in [("SQ_WAVES", 100), ("SQ_WAVE_CYCLES", 1000), ("SQ_WAIT_ANY", 400),
+                      ("SQ_INSTS_VALU_TRANS_F32", 6400), ("TCP_TCC_READ_REQ_LATENCY_sum", 120000),
+                      ("TCP_TCC_READ_REQ_sum", 100)]:
+        rows.append([KERNEL, name, val])
+    _write_csv(os.path.join(d2, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    md = rs.latency_summary(d2, "w", "python3 bench.py")
+    assert "| chain_rowstats | 100 | 100 | 1200 | 0.40 | 64 |" in md

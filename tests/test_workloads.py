@@ -55,3 +55,34 @@ def test_named_workloads_have_their_stated_shapes(name):
         N = c["N"]
         assert inp["target_logits"].shape == (2, N, 700)
         assert inp["node_tokens"].shape == (2, N)
+
+
+@pytest.mark.parametrize("dt,kw", [(W.F32, dict(draft_sigma=2e-3, offset=(-4.0, 4.0))), (W.BF16, dict(density=0.3))],
+                         ids=["f32", "bf16"])
+def test_near_copy_chain_forces_one_rejection_with_a_small_residual(orc, dt, kw):
+    """The near-copy chain generator: every sequence rejects exactly at its
+    reject_at (the oracle decides), its residual has small mass, and the bf16
+    draft rows differ from the target rows by one bf16 unit on about the
+    stated fraction of entries."""
+    inp = W.near_copy_chain_inputs(12, 3, 3000, dt, seed=5, **kw)
+    ref = orc.verify_chain(inp)
+    np.testing.assert_array_equal(ref["accepted_len"], inp["reject_at"])
+    assert ref["final_mass"].max() < 0.05
+    if dt == W.BF16:
+        t = inp["target_logits"][:, :3].astype(np.int32)
+        d = inp["draft_logits"].astype(np.int32)
+        moved = t != d
+        assert abs(moved.mean() - 0.3) < 0.02
+        assert np.abs(t - d)[moved].max() == 1  # one unit of the bf16 bit pattern
+
+
+def test_near_copy_tree_walks_take_their_three_paths(orc):
+    """The near-copy tree generator forces the oracle's walk into the path of
+    its mode b % 3: all three root children rejected; node 1 kept and its
+    children rejected; node 1 rejected, node 2 kept and its child rejected."""
+    inp = W.near_copy_tree_inputs(9, 3000, W.F32, seed=6, draft_sigma=2e-3)
+    ref = orc.verify_tree_sampled(inp)
+    want = {0: [-1, -1, -1], 1: [1, -1, -1], 2: [2, -1, -1]}
+    for b in range(inp["B"]):
+        assert ref["accepted_nodes"][b].tolist() == want[b % 3], b
+    assert ref["final_mass"].max() < 0.05
