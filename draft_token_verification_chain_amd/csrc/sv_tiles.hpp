@@ -301,20 +301,20 @@ template <int DT, int U>
 __device__ __forceinline__ ArgMax argmax_of_tile(const float* v, int64_t tile) {
     constexpr int VE = Elem<DT>::per_vec;
     const int lane = lane_id();
-    ArgMax a{-__builtin_inff(), kNoIndex};
-    const int64_t v0 = tile * (64 * U) + lane;
+    // the lane's best element by its position in v (a constant per
+    // comparison, so no index arithmetic per element), then its row index
+    float best = -__builtin_inff();
+    int pos = -1;
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            const float x = v[i * VE + e];
-            if (x > a.val) {
-                a.val = x;
-                a.idx = static_cast<int>((v0 + i * 64) * VE + e);
-            }
+    for (int j = 0; j < U * VE; ++j) {
+        if (v[j] > best) {
+            best = v[j];
+            pos = j;
         }
     }
-    return wave_argmax(a);
+    const int64_t v0 = tile * (64 * U) + lane;
+    const int idx = pos < 0 ? kNoIndex : static_cast<int>((v0 + (pos / VE) * 64) * VE + pos % VE);
+    return wave_argmax(ArgMax{best, idx});
 }
 
 // (max, lowest index) of one tile of raw logits.
