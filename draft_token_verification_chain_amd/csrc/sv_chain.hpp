@@ -150,6 +150,7 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     int g = -1;
     int rt = 0, rd = 0;
     double st = 1.0, sd = 1.0;
+    double lq = 0.0;  // log2 of the draft token's draft probability
     if (lane < npos) {
         if (!sampled) g = s_r[lane];
         if (!xok) {
@@ -162,8 +163,8 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
             sd = s_s[k + lane];
             const double c = kLog2e / static_cast<double>(T);
             // log2 p - log2 q with log2 p = l c - R - log2 S (the same for q)
-            const double l2ratio = (static_cast<double>(lt) * c - rt - log2_of_sum(st)) -
-                                   (static_cast<double>(ld) * c - rd - log2_of_sum(sd));
+            lq = static_cast<double>(ld) * c - rd - log2_of_sum(sd);
+            const double l2ratio = (static_cast<double>(lt) * c - rt - log2_of_sum(st)) - lq;
             // exp2 of a non-positive argument in fp32: relative error about 1e-7
             tau = static_cast<double>(exp2f(static_cast<float>(fmin(0.0, l2ratio))));
             acc = static_cast<double>(ui) < tau;
@@ -199,6 +200,8 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
             si.st = static_cast<float>(st);
             // log2(S_t / S_d) in the target row's reference; the draw corrects it
             set_kappa(si, static_cast<double>(rt - rd) + (log2(st) - log2(sd)));
+            // a lower bound of the residual's mass: q(x) - p(x) = q(x) (1 - tau)
+            si.fast = static_cast<double>(exp2f(static_cast<float>(lq))) * (1.0 - tau) >= kFastResidualMass;
         } else {
             si.mode = kFinalBonus;
         }
@@ -294,12 +297,14 @@ __device__ __forceinline__ void segment_weights_t(const void* draft, const void*
     constexpr int VE = Elem<DT>::per_vec;
     // a segment is tile seg/U's load seg%U, i.e. vectors 64*seg .. 64*seg+63
     float vt[VE];
-    load_tile<DT, VEC, 1, FULL>(target, trow, V, seg, lane_id(), vt);
     if (residual) {
+        // both rows' loads out together
         float vd[VE];
+        load_tile<DT, VEC, 1, FULL>(target, trow, V, seg, lane_id(), vt);
         load_tile<DT, VEC, 1, FULL>(draft, drow, V, seg, lane_id(), vd);
         residual_weights<DT, VE, FULL>(vt, vd, s, w);
     } else {
+        load_tile<DT, VEC, 1, FULL>(target, trow, V, seg, lane_id(), vt);
         bonus_weights<VE, FULL>(vt, s, ref, w);
     }
 }
@@ -383,6 +388,41 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     static_assert(kFinU == 4, "the four segment sums use one reduce-scatter");
     float a[kFinU];
     int i_own;
+    if (mode == kFinalResidual && si.fast) {
+        // a residual of large mass: the direct difference (kFastResidualMass);
+        // E, X and SW stay 0, so the pick applies no correction
+        const double kr = si.kappa - static_cast<double>(si.rt);
+        const float kr_hi = static_cast<float>(kr);
+        const float kr_lo = static_cast<float>(kr - static_cast<double>(kr_hi));
+        if constexpr (FULL && VEC) {
+            const char* tr = static_cast<const char*>(target) + trow * Elem<DT>::bytes;
+            const char* dr = static_cast<const char*>(draft) + drow * Elem<DT>::bytes;
+            const int64_t v0 = tile * (64 * kFinU) + lane;
+            uint4 rt4[kFinU], rd4[kFinU];
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) {
+                rt4[i] = *reinterpret_cast<const uint4*>(tr + (v0 + i * 64) * 16);
+                rd4[i] = *reinterpret_cast<const uint4*>(dr + (v0 + i * 64) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) {
+                float vt[VE], vd[VE];
+                unpack<DT>(rt4[i], vt);
+                unpack<DT>(rd4[i], vd);
+                a[i] = residual_mass_fast<VE, true>(vt, vd, si, kr_hi, kr_lo);
+            }
+        } else {
+            float w[NE], vd[NE];
+            load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
+            load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
+#pragma unroll
+            for (int i = 0; i < kFinU; ++i) a[i] = residual_mass_fast<VE, FULL>(w + i * VE, vd + i * VE, si, kr_hi, kr_lo);
+        }
+        const float m = wave_sum4(a, i_own);
+        const int64_t g = tile * kFinU + i_own;
+        if (lane < kFinU && g < nseg) seg_out[g] = residual_seg(m, 0.f, 0.f, 0.f);
+        return;
+    }
     if (mode == kFinalResidual) {
         // both rows' loads go out together, ahead of any use
         float e[kFinU], x[kFinU];

@@ -29,7 +29,8 @@ struct SeqInfo {
     double cT;     // log2(e) / T
     float k_hi;    // kappa as a double-float pair
     float k_lo;
-    int pad[2];
+    int fast;      // residual of large mass: the direct difference suffices (kFastResidualMass)
+    int pad;
 };
 static_assert(sizeof(SeqInfo) == 64, "descriptor layout");
 
@@ -145,6 +146,33 @@ __device__ __forceinline__ float residual_term(float lt, float ld, const SeqInfo
     const float eq = __builtin_amdgcn_exp2f(a + delta);
     const float small = -(et * expm1_2(delta));
     return __builtin_fabsf(delta) < kSeries ? small : et - eq;
+}
+
+// A residual whose mass W is known to be at least kFastResidualMass needs
+// neither the relative terms nor the correction of kappa: formed as the
+// direct difference e_t - e_q of the two exponentials, each term carries an
+// absolute error of about 1.2e-7 (e_t + e_q), and all of them together at
+// most about 2.4e-7 S_t, so the CDF boundaries C / W move by at most about
+// 1.2e-6 (fp32 normalisers move them by about 1e-7 / W more): eight times
+// inside the 1e-5 band.  The acceptance knows such a lower bound at the
+// rejected draft x: W = TV(p, q) >= q(x) - p(x).
+constexpr double kFastResidualMass = 0.2;
+
+// M = sum max(0, e_t - e_q) of VE elements by the direct difference, e_q =
+// exp2(l_d c - r_t + kappa) with c and kappa - r_t (kr_hi + kr_lo) as
+// double-float pairs (masked elements weigh 0).
+template <int VE, bool FULL>
+__device__ __forceinline__ float residual_mass_fast(const float* vt, const float* vd, const SeqInfo& s, float kr_hi,
+                                                    float kr_lo) {
+    float mm[VE];
+#pragma unroll
+    for (int j = 0; j < VE; ++j) {
+        const float at = __builtin_fmaf(vt[j], s.c_lo, __builtin_fmaf(vt[j], s.c_hi, -s.rt));
+        const float ad = __builtin_fmaf(vd[j], s.c_hi, kr_hi) + __builtin_fmaf(vd[j], s.c_lo, kr_lo);
+        const float x = __builtin_amdgcn_exp2f(at) - __builtin_amdgcn_exp2f(ad);
+        mm[j] = (FULL || vt[j] != -__builtin_inff()) ? __builtin_fmaxf(x, 0.f) : 0.f;
+    }
+    return pairwise_sum<VE>(mm);
 }
 
 // Residual weights max(0, x) of NE loaded elements (masked elements weigh 0).
