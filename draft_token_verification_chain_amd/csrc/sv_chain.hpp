@@ -521,7 +521,7 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
 }
 
 template <int DT, bool VEC, int ACC>
-__global__ __launch_bounds__(kFinBlock) void chain_final_part_kernel(
+__global__ __launch_bounds__(kFinBlock, ACC == kAcceptRead ? 5 : 1) void chain_final_part_kernel(
     const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
     const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
     const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
