@@ -123,6 +123,10 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     const bool sampled = T > 0.f;
     const bool xok = static_cast<unsigned>(x) < static_cast<unsigned>(V);  // out-of-range ids are rejected
     // row statistics (at temperature 0 only the target rows' argmax matters)
+    // the lane's row's normaliser, kept for tile_tv (one pass only)
+    int r_own = 0;
+    double s_own = 1.0;
+    bool v_own = false;
     for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
         const int rho = rho0 + lane / G;
         const bool valid = tested(rho);
@@ -137,6 +141,9 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
                 s_r[rho] = r;
                 s_s[rho] = sum;
             }
+            r_own = r;
+            s_own = sum;
+            v_own = valid;
         } else {
             group_reduce<false>(p, nT, G, valid, q, r, sum, am);
             if (valid && (lane & (G - 1)) == 0) s_r[rho] = am.idx;
@@ -176,6 +183,11 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     int a = first_lane(lane < npos && !acc);
     if (a < 0) a = npos;
     if (npos < k) return a;
+    // a lower bound of the rejected row's TV(p, q), from the partials still
+    // held when one pass covered every row
+    float tv_a = 0.f;
+    if (sampled && a < k && rows <= per_pass)
+        tv_a = __shfl(tile_tv(q, nT, G, v_own, r_own, s_own, k), a * G, kWave);
     int32_t* em = emitted + b * (k + 1);
     if (publish) {
         if (accept_prob != nullptr && lane < k) accept_prob[b * k + lane] = static_cast<float>(tau);
@@ -200,8 +212,11 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
             si.st = static_cast<float>(st);
             // log2(S_t / S_d) in the target row's reference; the draw corrects it
             set_kappa(si, static_cast<double>(rt - rd) + (log2(st) - log2(sd)));
-            // a lower bound of the residual's mass: q(x) - p(x) = q(x) (1 - tau)
-            si.fast = static_cast<double>(exp2f(static_cast<float>(lq))) * (1.0 - tau) >= kFastResidualMass;
+            // lower bounds of the residual's mass: q(x) - p(x) = q(x) (1 - tau),
+            // and the rows' tile masses apart
+            const double w_lo = fmax(static_cast<double>(exp2f(static_cast<float>(lq))) * (1.0 - tau),
+                                     static_cast<double>(tv_a));
+            si.fast = w_lo >= kFastResidualMass;
         } else {
             si.mode = kFinalBonus;
         }
@@ -389,11 +404,8 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     float a[kFinU];
     int i_own;
     if (mode == kFinalResidual && si.fast) {
-        // a residual of large mass: the direct difference (kFastResidualMass);
-        // E, X and SW stay 0, so the pick applies no correction
-        const double kr = si.kappa - static_cast<double>(si.rt);
-        const float kr_hi = static_cast<float>(kr);
-        const float kr_lo = static_cast<float>(kr - static_cast<double>(kr_hi));
+        // a residual of large mass (kFastResidualMass): E, X and SW stay 0,
+        // so the pick applies no correction
         if constexpr (FULL && VEC) {
             const char* tr = static_cast<const char*>(target) + trow * Elem<DT>::bytes;
             const char* dr = static_cast<const char*>(draft) + drow * Elem<DT>::bytes;
@@ -409,14 +421,14 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
                 float vt[VE], vd[VE];
                 unpack<DT>(rt4[i], vt);
                 unpack<DT>(rd4[i], vd);
-                a[i] = residual_mass_fast<VE, true>(vt, vd, si, kr_hi, kr_lo);
+                a[i] = residual_mass_fast<DT, VE, true>(vt, vd, si);
             }
         } else {
             float w[NE], vd[NE];
             load_tile<DT, VEC, kFinU, FULL>(target, trow, V, tile, lane, w);
             load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
 #pragma unroll
-            for (int i = 0; i < kFinU; ++i) a[i] = residual_mass_fast<VE, FULL>(w + i * VE, vd + i * VE, si, kr_hi, kr_lo);
+            for (int i = 0; i < kFinU; ++i) a[i] = residual_mass_fast<DT, VE, FULL>(w + i * VE, vd + i * VE, si);
         }
         const float m = wave_sum4(a, i_own);
         const int64_t g = tile * kFinU + i_own;

@@ -149,28 +149,32 @@ __device__ __forceinline__ float residual_term(float lt, float ld, const SeqInfo
 }
 
 // A residual whose mass W is known to be at least kFastResidualMass needs
-// neither the relative terms nor the correction of kappa: formed as the
-// direct difference e_t - e_q of the two exponentials, each term carries an
-// absolute error of about 1.2e-7 (e_t + e_q), and all of them together at
-// most about 2.4e-7 S_t, so the CDF boundaries C / W move by at most about
-// 1.2e-6 (fp32 normalisers move them by about 1e-7 / W more): eight times
-// inside the 1e-5 band.  The acceptance knows such a lower bound at the
-// rejected draft x: W = TV(p, q) >= q(x) - p(x).
+// neither the series nor the sums behind the correction of kappa.  Each term
+// is formed as x = e_t (1 - 2^min(delta, 0)), from the same accurate delta as
+// residual_term: e_t carries a relative error of about 6e-8 (2 + |a| ln 2)
+// (the exponential and its rounded exponent a), which stays relative to x;
+// 2^delta an absolute error of about 1.2e-7 and delta's own relative error
+// (1e-7) adds at most about 1e-7 more, both times e_t, so the terms of W
+// together are off by at most about 3e-7 S_t + 1e-6 W S_t, and the
+// normalisers' fp32 error (kappa to about 1e-7, uncorrected here) adds about
+// 1e-7 S_t.  The CDF boundaries C / W then move by at most twice that over W
+// S_t: about 6e-6 at W = 0.2, inside the 1e-5 band.  The acceptance has two
+// lower bounds of W = TV(p, q): q(x) - p(x) at the rejected draft x, and the
+// distance between the two rows' tile masses (tile_tv).
 constexpr double kFastResidualMass = 0.2;
 
-// M = sum max(0, e_t - e_q) of VE elements by the direct difference, e_q =
-// exp2(l_d c - r_t + kappa) with c and kappa - r_t (kr_hi + kr_lo) as
-// double-float pairs (masked elements weigh 0).
-template <int VE, bool FULL>
-__device__ __forceinline__ float residual_mass_fast(const float* vt, const float* vd, const SeqInfo& s, float kr_hi,
-                                                    float kr_lo) {
+// M = sum max(0, x) of VE elements, each x = e_t (1 - 2^min(delta, 0)) (see
+// above; masked elements weigh 0).
+template <int DT, int VE, bool FULL>
+__device__ __forceinline__ float residual_mass_fast(const float* vt, const float* vd, const SeqInfo& s) {
     float mm[VE];
 #pragma unroll
     for (int j = 0; j < VE; ++j) {
-        const float at = __builtin_fmaf(vt[j], s.c_lo, __builtin_fmaf(vt[j], s.c_hi, -s.rt));
-        const float ad = __builtin_fmaf(vd[j], s.c_hi, kr_hi) + __builtin_fmaf(vd[j], s.c_lo, kr_lo);
-        const float x = __builtin_amdgcn_exp2f(at) - __builtin_amdgcn_exp2f(ad);
-        mm[j] = (FULL || vt[j] != -__builtin_inff()) ? __builtin_fmaxf(x, 0.f) : 0.f;
+        const float delta = residual_delta<DT>(vt[j], vd[j], s);
+        const float a = __builtin_fmaf(vt[j], s.c_lo, __builtin_fmaf(vt[j], s.c_hi, -s.rt));
+        const float et = __builtin_amdgcn_exp2f(a);
+        const float x = __builtin_fmaf(-et, __builtin_amdgcn_exp2f(__builtin_fminf(delta, 0.f)), et);
+        mm[j] = (FULL || vt[j] != -__builtin_inff()) ? x : 0.f;
     }
     return pairwise_sum<VE>(mm);
 }
@@ -396,6 +400,29 @@ __device__ __forceinline__ void group_load(const Partial* p, int nT, int G, bool
         const int t = sl + j * G;
         q[j] = (valid && t < nT) ? p[t] : Partial{0.f, 0};
     }
+}
+
+// Half the L1 distance between the tile masses of target row i and draft
+// row i, over the tiles of the first kBatch partials of each lane of the
+// group (t = l % G + j G), summed over the group: a lower bound of the
+// total variation distance TV(p_i, q_i), since merging tokens into tiles can
+// only lower it, and so can leaving tiles out.  The target rows' groups are
+// the first k, each followed k groups later by its draft row's; the result
+// holds in the lanes of target row i's group.  (r, s) is the lane's row's
+// combined normaliser, `valid` whether the lane's row is a tested one.
+__device__ __forceinline__ float tile_tv(const Partial* q, int nT, int G, bool valid, int r, double s, int k) {
+    const int lane = lane_id();
+    const int sl = lane & (G - 1);
+    const float inv = valid ? __builtin_amdgcn_rcpf(static_cast<float>(s)) : 0.f;  // a bound: 1 ulp suffices
+    const int src = min(lane + k * G, kWave - 1);  // the draft row's lane (target lanes only)
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        const float m = sl + j * G < nT ? __builtin_ldexpf(q[j].f, q[j].i - r) * inv : 0.f;
+        acc += __builtin_fabsf(m - __shfl(m, src, kWave));
+    }
+    for (int m = G >> 1; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+    return 0.5f * acc;
 }
 
 template <bool SOFTMAX>
