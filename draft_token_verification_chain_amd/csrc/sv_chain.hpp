@@ -438,7 +438,7 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     if (mode == kFinalResidual) {
         // both rows' loads go out together, ahead of any use
         float e[kFinU], x[kFinU];
-        bool near = false;
+        float dmin = __builtin_inff();  // masked elements: |delta| = inf or NaN (fmin ignores NaN)
         if constexpr (FULL && VEC) {
             // raw 16-byte vectors, unpacked one segment at a time: fewer live
             // registers, so more waves per SIMD
@@ -456,7 +456,7 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
                 float vt[VE], vd[VE];
                 unpack<DT>(rt4[i], vt);
                 unpack<DT>(rd4[i], vd);
-                const ResidualSums r = residual_sums_marked<DT, VE, true>(vt, vd, si, near);
+                const ResidualSums r = residual_sums_marked<DT, VE, true>(vt, vd, si, dmin);
                 a[i] = r.m;
                 e[i] = r.ea;
                 x[i] = r.x;
@@ -467,7 +467,7 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
             load_tile<DT, VEC, kFinU, FULL>(draft, drow, V, tile, lane, vd);
 #pragma unroll
             for (int i = 0; i < kFinU; ++i) {
-                const ResidualSums r = residual_sums_marked<DT, VE, FULL>(w + i * VE, vd + i * VE, si, near);
+                const ResidualSums r = residual_sums_marked<DT, VE, FULL>(w + i * VE, vd + i * VE, si, dmin);
                 a[i] = r.m;
                 e[i] = r.ea;
                 x[i] = r.x;
@@ -479,7 +479,7 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
         // SW only for the rare tiles that have an element near the switch,
         // from the tile loaded again (the first loads are no longer live)
         float ss = 0.f;
-        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        if (__builtin_amdgcn_ballot_w64(dmin < kSwitch) != 0) {
             float sw[kFinU];
             if constexpr (FULL && VEC) {
                 // raw vectors again, unpacked one segment at a time (the

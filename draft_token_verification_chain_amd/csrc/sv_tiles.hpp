@@ -220,12 +220,12 @@ __device__ __forceinline__ ResidualSums residual_sums(const float* vt, const flo
 }
 
 // The same sums without SW: elements within kSwitch of the switch are rare,
-// so a streaming pass only marks them (one compare per element, or-ed into a
-// lane mask in `near`) and forms SW with residual_sw, in a branch, for the
-// tiles of waves that have one.  M, E and X are the same as residual_sums'.
+// so a streaming pass only tracks the smallest |delta| of the lane in
+// `dmin` and forms SW with residual_sw, in a branch, for the tiles of waves
+// that have one.  M, E and X are the same as residual_sums'.
 template <int DT, int VE, bool FULL>
 __device__ __forceinline__ ResidualSums residual_sums_marked(const float* vt, const float* vd, const SeqInfo& s,
-                                                             bool& near) {
+                                                             float& dmin) {
     float mm[VE], ee[VE], xx[VE];
 #pragma unroll
     for (int j = 0; j < VE; ++j) {
@@ -235,7 +235,7 @@ __device__ __forceinline__ ResidualSums residual_sums_marked(const float* vt, co
         xx[j] = t;
         mm[j] = __builtin_fmaxf(t, 0.f);
         ee[j] = delta < 0.f ? et : 0.f;
-        near = near || __builtin_fabsf(delta) < kSwitch;
+        dmin = __builtin_fminf(dmin, __builtin_fabsf(delta));
     }
     return ResidualSums{pairwise_sum<VE>(mm), pairwise_sum<VE>(ee), pairwise_sum<VE>(xx), 0.f};
 }
