@@ -16,6 +16,12 @@ sparse set of one-unit bumps.  Each batch is verified with several sets of
 final-draw uniforms; every draw is compared with the oracle's.  The residual
 masses of the compared draws span about 1e-2 to 1e-5 (chains) and 5e-3 to
 3e-6 (trees, after one to three rejections at a node).
+
+The chain draw forms a residual whose mass the acceptance can bound below by
+0.2 in a cheaper way (each term as e_t (1 - 2^delta), without the correction
+of the normalisers' ratio), and every other residual in full.  The last test
+draws from residuals on both sides of that threshold, many of them within a
+factor of two of it, through both ways of obtaining the descriptor.
 """
 
 import numpy as np
@@ -126,3 +132,49 @@ def test_tree_small_residual(svl, orc, case):
     print(f"[small residual] tree {name}: {mass.size} draws, banded {banded} (differing {banded_diff}), "
           f"mass decades {_decades(mass)}", flush=True)
     assert mass.max() < 0.05
+
+
+# name, generator, B, sets of final-draw uniforms.  The near-copy rows force a
+# rejection in every sequence; the ordinary chain rows reject where their
+# uniforms say.  B = 256 takes the acceptance kernel.
+THRESHOLD_CASES = [
+    ("f32 sigma 0.6 offset", lambda B: W.near_copy_chain_inputs(B, 2, V, W.F32, seed=17, draft_sigma=0.6,
+                                                                offset=(-4.0, 4.0)), 64, 16),
+    ("f32 sigma 0.6 offset acceptance kernel",
+     lambda B: W.near_copy_chain_inputs(B, 2, V, W.F32, seed=19, draft_sigma=0.6, offset=(-4.0, 4.0)), 256, 4),
+    ("bf16 sigma 0.4", lambda B: W.chain_inputs(B, 4, V, W.BF16, seed=17, target_sigma=3.0, zipf_s=1.1,
+                                                 draft_sigma=0.4, temperature=0.7), 128, 16),
+    ("bf16 sigma 0.4 acceptance kernel",
+     lambda B: W.chain_inputs(B, 4, V, W.BF16, seed=19, target_sigma=3.0, zipf_s=1.1, draft_sigma=0.4,
+                              temperature=0.7), 256, 8),
+]
+
+
+@pytest.mark.parametrize("case", THRESHOLD_CASES, ids=[c[0] for c in THRESHOLD_CASES])
+def test_chain_residual_mass_threshold(svl, orc, case):
+    import torch
+
+    name, make, B, R = case
+    inp = make(B)
+    k = inp["k"]
+    t = chain_tensors(inp)
+    ru = np.random.Generator(np.random.Philox(key=[17, 77]))
+    masses, banded, banded_diff = [], 0, 0
+    for r in range(R):
+        inp["uniforms"][:, k] = ru.random(B, dtype=np.float32)
+        t["uniforms"].copy_(torch.from_numpy(inp["uniforms"]))
+        out = svl.verify_chain(t["draft_tokens"], t["draft_logits"], t["target_logits"], t["temperature"],
+                               t["uniforms"])
+        torch.cuda.synchronize()
+        got = {kk: (v.cpu().numpy() if v is not None else None) for kk, v in out.items()}
+        ref = orc.verify_chain(inp)
+        st = compare_chain(inp, got, ref, f"{name} set {r}")
+        banded += st["banded"]
+        banded_diff += st["banded_mismatch"]
+        masses.append(ref["final_mass"][ref["accepted_len"] < k])
+    mass = np.concatenate(masses)
+    below, near, above = int((mass < 0.2).sum()), int(((mass >= 0.2) & (mass < 0.4)).sum()), int((mass >= 0.4).sum())
+    print(f"[residual threshold] chain {name}: {mass.size} residual draws, W < 0.2: {below}, "
+          f"0.2 <= W < 0.4: {near}, W >= 0.4: {above}, banded {banded} (differing {banded_diff})", flush=True)
+    # both forms of the draw are exercised, and near the threshold
+    assert below >= mass.size // 10 and near >= mass.size // 10
