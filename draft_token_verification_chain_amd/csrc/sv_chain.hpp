@@ -122,11 +122,11 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     }
     const bool sampled = T > 0.f;
     const bool xok = static_cast<unsigned>(x) < static_cast<unsigned>(V);  // out-of-range ids are rejected
-    // row statistics (at temperature 0 only the target rows' argmax matters)
     // the lane's row's normaliser, kept for tile_tv (one pass only)
     int r_own = 0;
     double s_own = 1.0;
     bool v_own = false;
+    // row statistics (at temperature 0 only the target rows' argmax matters)
     for (int rho0 = 0; rho0 < rows; rho0 += per_pass) {
         const int rho = rho0 + lane / G;
         const bool valid = tested(rho);

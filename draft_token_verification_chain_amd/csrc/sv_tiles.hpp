@@ -29,7 +29,7 @@ struct SeqInfo {
     double cT;     // log2(e) / T
     float k_hi;    // kappa as a double-float pair
     float k_lo;
-    int fast;      // residual of large mass: the direct difference suffices (kFastResidualMass)
+    int fast;      // residual of known large mass: the cheap form suffices (kFastResidualMass)
     int pad;
 };
 static_assert(sizeof(SeqInfo) == 64, "descriptor layout");
