@@ -7,12 +7,14 @@ Inputs (rocprofv3 CSV output directories):
   --write DIR   from  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o bench -- python3 bench.py ... --calibrate-copy MIB
   --sq DIR      from  rocprofv3 --pmc <SQ_COUNTERS> --output-format csv -d DIR -o bench -- python3 bench.py ...
   --lat DIR     from  rocprofv3 --pmc <LAT_COUNTERS> --output-format csv -d DIR -o bench -- python3 bench.py ...
+  --mem D1,D2,D3  from three runs, rocprofv3 --pmc <MEM_PASSES[i]> --output-format csv -d Di -o bench -- python3 bench.py ...
 
 Outputs:
   profiles/<prefix>_kernel_trace.md          per-kernel calls / average / min / max duration
   profiles/<kernel>_<workload>_traffic.json  HBM-side bytes per launch of each library kernel
   profiles/<prefix>_sq_counters.md           per-kernel SQ counters and the VALU floor
   profiles/<prefix>_latency_counters.md      per-kernel L2 read latency and waiting
+  profiles/<prefix>_memory_counters.md       per-kernel L2-to-memory latency, DRAM credit stalls, TLB misses
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
 the calibration copy (one plain device-to-device copy of MIB MiB, which reads
@@ -144,11 +146,56 @@ def latency_summary(d: str, prefix: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+# One counter pass each (the TCC block collects at most four counters per pass).
+MEM_PASSES = ("TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_HIT_sum TCC_MISS_sum",
+              "TCC_EA0_RDREQ_DRAM_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
+              "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TCP_PENDING_STALL_CYCLES_sum "
+              "TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum")
+
+
+def memory_summary(dirs: list, prefix: str, command: str) -> str:
+    """Per-kernel memory-side counters (averages per dispatch, three passes):
+    the L2's read requests to memory and its hit rate, the mean time a read
+    request to memory stays in flight (TCC_EA0_RDREQ_LEVEL over
+    TCC_EA0_RDREQ, in L2 cycles, by Little's law), the cycles the L2 waited
+    for DRAM credits per request to DRAM (the memory controllers' queues
+    full), and the address-translation miss rate of the vector L1."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "bench_counter_collection.csv"))):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 memory-side counters: {prefix}", "", "Commands (run from the repository root on one MI355X), "
+             "one counter pass each:", "", "```"]
+    lines += [f"rocprofv3 --pmc {p} --output-format csv -d <dir{i + 1}> -o bench -- {command}"
+              for i, p in enumerate(MEM_PASSES)]
+    lines += ["```", "", "Averages per dispatch. Memory latency = TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum (L2 "
+              "cycles a read request to memory is in flight); DRAM credit stalls = TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum "
+              "/ TCC_EA0_RDREQ_DRAM_sum (cycles the L2 waited for the memory controllers per request); TLB misses = "
+              "TCP_UTCL1_TRANSLATION_MISS / (MISS + HIT).", "",
+              "| kernel | L2 reads to memory | L2 hit rate | memory latency (L2 cycles) | DRAM credit stalls per request "
+              "| TLB miss rate |", "|---|---:|---:|---:|---:|---:|"]
+    for full, c in per.items():
+        if "sv::" not in full:
+            continue
+        a = {k: sum(v) / len(v) for k, v in c.items()}
+        rq = a.get("TCC_EA0_RDREQ_sum", 0.0)
+        dram = a.get("TCC_EA0_RDREQ_DRAM_sum", 0.0)
+        if not rq or not dram:
+            continue
+        hits = a["TCC_HIT_sum"] / (a["TCC_HIT_sum"] + a["TCC_MISS_sum"])
+        tlb = a["TCP_UTCL1_TRANSLATION_MISS_sum"] / (a["TCP_UTCL1_TRANSLATION_MISS_sum"] +
+                                                      a["TCP_UTCL1_TRANSLATION_HIT_sum"])
+        lines.append(f"| {short_name(full)} | {rq:.0f} | {hits:.3f} | {a['TCC_EA0_RDREQ_LEVEL_sum'] / rq:.0f} | "
+                     f"{a['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / dram:.2f} | {tlb:.4f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace")
     ap.add_argument("--sq", help="rocprofv3 --pmc output of the SQ counters (SQ_COUNTERS)")
     ap.add_argument("--lat", help="rocprofv3 --pmc output of the latency counters (LAT_COUNTERS)")
+    ap.add_argument("--mem", help="three comma-separated rocprofv3 --pmc outputs, one per MEM_PASSES entry")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calibrate-mib", type=int, default=256)
@@ -170,6 +217,11 @@ def main():
     if args.lat:
         text = latency_summary(args.lat, args.prefix, pmc_cmd)
         with open(os.path.join(args.out, f"{args.prefix}_latency_counters.md"), "w") as f:
+            f.write(text)
+        print(text)
+    if args.mem:
+        text = memory_summary(args.mem.split(","), args.prefix, pmc_cmd)
+        with open(os.path.join(args.out, f"{args.prefix}_memory_counters.md"), "w") as f:
             f.write(text)
         print(text)
     if not args.trace:

@@ -152,3 +152,26 @@ def test_sq_and_latency_summaries(tmp_path):
     _write_csv(os.path.join(d2, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
     md = rs.latency_summary(d2, "w", "python3 bench.py")
     assert "| chain_rowstats | 100 | 100 | 1200 | 0.40 | 64 |" in md
+
+
+def test_memory_summary(tmp_path):
+    """Memory-side figures from three synthetic counter passes: the L2's hit
+    rate, the mean time a read request to memory is in flight (Little's
+    law), DRAM credit stalls per request and the translation miss rate."""
+    passes = [[("TCC_EA0_RDREQ_sum", 1000), ("TCC_EA0_RDREQ_LEVEL_sum", 1600000), ("TCC_HIT_sum", 30),
+               ("TCC_MISS_sum", 970)],
+              [("TCC_EA0_RDREQ_DRAM_sum", 1000), ("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", 280)],
+              [("TCP_UTCL1_TRANSLATION_MISS_sum", 1), ("TCP_UTCL1_TRANSLATION_HIT_sum", 999),
+               ("TCP_PENDING_STALL_CYCLES_sum", 5), ("TA_BUSY_avr", 5), ("TA_ADDR_STALLED_BY_TC_CYCLES_sum", 5)]]
+    dirs = []
+    for i, counters in enumerate(passes):
+        d = str(tmp_path / f"p{i}")
+        rows = [[KERNEL, n, v] for n, v in counters] + [[COPY, counters[0][0], 7]]
+        _write_csv(os.path.join(d, "bench_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+                   rows)
+        dirs.append(d)
+    md = rs.memory_summary(dirs, "w", "python3 bench.py")
+    assert "| chain_rowstats | 1000 | 0.030 | 1600 | 0.28 | 0.0010 |" in md
+    assert COPY not in md
+    for p in rs.MEM_PASSES:
+        assert p in md
