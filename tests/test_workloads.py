@@ -86,3 +86,28 @@ def test_near_copy_tree_walks_take_their_three_paths(orc):
     for b in range(inp["B"]):
         assert ref["accepted_nodes"][b].tolist() == want[b % 3], b
     assert ref["final_mass"].max() < 0.05
+
+
+@pytest.mark.parametrize("dt", [W.F32, W.BF16], ids=["f32", "bf16"])
+def test_flat_tail_chain_has_its_stated_mass_profile(orc, dt):
+    """The flat-tail chain generator: every sequence rejects its one draft,
+    the residual's mass is about 0.22, the two vocabulary halves' masses
+    differ by more than 0.2 (a coarse lower bound of W), the tail holds over
+    90% of p, and under p the tokens lie on average about 8 binary orders
+    below the top one."""
+    V = 128256
+    inp = W.flat_tail_chain_inputs(4, V, dt, seed=5)
+    ref = orc.verify_chain(inp)
+    assert (ref["accepted_len"] == 0).all()
+    assert ((ref["final_mass"] > 0.205) & (ref["final_mass"] < 0.24)).all()
+    t = W.values(inp["target_logits"][:, 0], dt).astype(np.float64)
+    d = W.values(inp["draft_logits"][:, 0], dt).astype(np.float64)
+    p = np.exp(t - t.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    q = np.exp(d - d.max(1, keepdims=True))
+    q /= q.sum(1, keepdims=True)
+    halves = np.abs(p[:, :V // 2].sum(1) - q[:, :V // 2].sum(1))
+    assert ((halves > 0.2) & (halves <= ref["final_mass"] + 1e-12)).all()
+    assert (p[:, 0] < 0.1).all()
+    depth = (p * np.log2(p.max(1, keepdims=True) / p)).sum(1)
+    assert ((depth > 7) & (depth < 10)).all()

@@ -261,6 +261,41 @@ def near_copy_chain_inputs(B: int, k: int, V: int, dtype: int, seed: int, *, dra
                 reject_at=reject_at)
 
 
+
+def flat_tail_chain_inputs(B: int, V: int, dtype: int, seed: int, *, tail: int = 8192, gap: float = 6.2,
+                           shift: float = 0.5, noise: float = 0.3, draft_sigma: float = 0.05) -> dict:
+    """Chain inputs (k = 1, T = 1) whose rows put most of their mass in a flat
+    tail far below the top token, with a residual of moderate mass that the
+    rows' coarse masses already show, every sequence forced to reject.
+
+    target logits  t[b, j, v] = noise * N(0,1) + o_v, with o_0 = 0 (the top
+                   token), o_v = -gap on ``tail`` tokens spread evenly over the
+                   vocabulary, and o_v = -40 elsewhere (no mass)
+    draft logits   d[b, 0, v] = t[b, 0, v] + draft_sigma * N(0,1) + shift (v < V/2), - shift (v >= V/2)
+    (both rounded to ``dtype``).  With the defaults the tail carries about 92%
+    of the mass, the mean of log2(p_max / p_v) under p is about 8, the
+    residual's mass W is about 0.23 and the two halves' masses alone differ
+    by about 0.22; the residual lives on about tail/2 tokens, so its CDF
+    boundaries lie far more than 1e-5 apart.  The draft token is the one with
+    the largest d - t, tested with u = U_MAX; u[b, 1] drives the residual draw.
+    """
+    base = near_copy_chain_inputs(B, 1, V, F32, seed, draft_sigma=draft_sigma, target_sigma=noise, zipf_s=None,
+                                  temperature=1.0)
+    off = np.full(V, -40.0, dtype=np.float32)
+    off[np.linspace(1, V - 1, tail).astype(np.int64)] = -gap
+    off[0] = 0.0
+    half = np.where(np.arange(V) < V // 2, shift, -shift).astype(np.float32)
+    t = values(base["target_logits"], F32) + off
+    d = values(base["draft_logits"], F32) + off + half
+    target, draft = to_dtype(t, dtype), to_dtype(d, dtype)
+    diff = values(draft[:, 0], dtype).astype(np.float64) - values(target[:, 0], dtype).astype(np.float64)
+    tokens = np.argmax(diff, axis=-1).astype(np.int32).reshape(B, 1)
+    uniforms = base["uniforms"]
+    uniforms[:, 0] = U_MAX
+    return dict(kind="chain", B=B, k=1, V=V, dtype=dtype, draft_tokens=tokens, draft_logits=draft,
+                target_logits=target, temperature=base["temperature"], uniforms=uniforms,
+                reject_at=np.zeros(B, dtype=np.int32))
+
 # Tree of the near-copy sampled-tree inputs: the root has children 1, 2, 3;
 # node 1 has children 4, 5, 6 and node 2 has child 7.
 NEAR_COPY_TREE = np.array([-1, 0, 0, 0, 1, 1, 1, 2], dtype=np.int32)
