@@ -117,7 +117,7 @@ def load_trace_average(kernel: str, workload: str, column: str = "average (us)")
 
 # The library's kernels (launch names; the profile summaries use the same names).
 LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "chain_accept", "chain_final_part",
-                   "chain_final_pick", "chain_row_draw", "argmax_rows", "greedy_rows", "greedy_rows_rest",
+                   "chain_final_pick", "chain_row_draw", "chain_small", "argmax_rows", "greedy_rows", "greedy_rows_rest",
                    "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
                    "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
 
@@ -332,6 +332,10 @@ class Workload:
                 elif a[b] == k:
                     draw += V * es
             kb[draw_kernel] = draw
+            # small chains: the whole verification in one launch, one workgroup per sequence
+            nT = -(-V * es // 8192)
+            if B <= 256 and (k > 0 or B < 256) and nseg <= 64 and 2 * k * nT <= 160 and (2 * k + 1) * V * es <= 144 << 10:
+                kb = {"chain_small": kb.pop("chain_rowstats", 0) + kb.pop(draw_kernel)}
         elif kind == "greedy":
             k = inp["k"]
             s = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1

@@ -75,6 +75,14 @@ int64_t final_chunks(int V, sv_dtype dt) {
     return (segments_per_row(V, dt) + sv::kSegPerChunk - 1) / sv::kSegPerChunk;
 }
 
+// Small chains take one launch, one workgroup per sequence
+// (chain_small_kernel): up to kSmallMaxRows sequences whose rows have at
+// most kSmallMaxSegs segments and whose 2k + 1 rows hold at most
+// kSmallMaxBytes, which one CU streams in about the launches it saves
+// (without drafts, below the one-workgroup-per-row draw's batch size).
+constexpr int kSmallMaxRows = 256;
+constexpr int64_t kSmallMaxBytes = 144 * 1024;
+
 // Largest final-draw grid for which every workgroup recomputes its
 // sequence's acceptance; beyond it one wave per sequence computes it once.
 constexpr int64_t kInlineAcceptMaxBlocks = 2048;
@@ -224,6 +232,14 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
     auto* segs = reinterpret_cast<sv::SegMass*>(ws + L.segs);
     auto* chunkarg = reinterpret_cast<Partial*>(ws + L.chunkarg);
     sv_status st;
+    if (B <= kSmallMaxRows && (k > 0 || B < kRowDrawMinRows) &&
+        segments_per_row(V, static_cast<sv_dtype>(DT)) <= sv::kSmallMaxSegs &&
+        static_cast<int64_t>(2 * k) * nT <= sv::kSmallMaxParts &&
+        static_cast<int64_t>(2 * k + 1) * V * sv::Elem<DT>::bytes <= kSmallMaxBytes) {
+        return launch("chain_small", sv::chain_small_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(B)),
+                      dim3(sv::kSmallBlock), stream, tokens, draft, target, temperature, uniforms, k, V, nT,
+                      accepted_len, emitted, accept_prob);
+    }
     const int64_t fin_blocks = static_cast<int64_t>(B) * nchunk;
     const int acc = k == 0 ? sv::kAcceptNone
                            : (fin_blocks <= kInlineAcceptMaxBlocks ? sv::kAcceptInline : sv::kAcceptRead);

@@ -983,4 +983,116 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(const voi
     }
 }
 
+// ---------------------------------------------------------------- small chains, one workgroup per sequence ---
+
+// When a sequence's rows are short (at most kSmallMaxSegs segments) and the
+// batch is small, launches dominate the three-kernel path, and one workgroup
+// per sequence does the whole verification in one launch: its 16 waves
+// stream the 2k rows' tiles (rowstats_tile, partials and the draft tokens'
+// logits to LDS), wave 0 runs the acceptance from them (accept_sequence on
+// the sequence alone, the same code and order of combination as everywhere
+// else), the waves then stream the draw's row or rows with final_tile into
+// segment records in LDS, and wave 0 draws the token with
+// draw_from_segments; when the residual's first-order correction cannot be
+// trusted the workgroup forms the masses again (redo_residual_draw).  It
+// computes what chain_rowstats, chain_final_part and chain_final_pick
+// compute.
+constexpr int kSmallBlock = 1024;
+constexpr int kSmallWaves = kSmallBlock / kWave;
+constexpr int kSmallMaxSegs = 64;    // rows of at most 32768 bf16 or 16384 f32 logits
+constexpr int kSmallMaxParts = 160;  // 2k x tiles per row
+
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kSmallBlock) void chain_small_kernel(
+    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int k, int V, int nT,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob) {
+    constexpr int VE = Elem<DT>::per_vec;
+    __shared__ Partial s_part[kSmallMaxParts];
+    __shared__ float s_gath[2 * SV_MAX_DRAFTS];
+    __shared__ SegMass s_seg[kSmallMaxSegs];
+    __shared__ float s_m[kSmallMaxSegs];
+    __shared__ ArgMax s_arg[kSmallWaves];
+    __shared__ int s_r[2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[2 * SV_MAX_DRAFTS];
+    __shared__ SeqInfo s_info;
+    __shared__ double s_kappa;
+    __shared__ int s_redo;
+    const int64_t b = blockIdx.x;
+    const int wave = threadIdx.x / kWave;
+    SeqInfo si;
+    if (k == 0) {
+        // no drafts: a draw from target row 0 (its argmax at temperature 0)
+        const float T = temperature[b];
+        si = SeqInfo{};
+        si.mode = T > 0.f ? kFinalBonus : kFinalArgmax;
+        temperature_scale(T > 0.f ? T : 1.f, si);
+        si.u = uniforms[b];
+        if (threadIdx.x == 0) accepted_len[b] = 0;
+    } else {
+        // rows 0 .. k-1: target rows, k .. 2k-1: draft rows (the layout
+        // accept_sequence reads for a batch of one sequence)
+        const float T = temperature[b];
+        for (int w = wave; w < 2 * k * nT; w += kSmallWaves) {
+            const int rp = w / nT;
+            const int tile = w - rp * nT;
+            const bool is_target = rp < k;
+            const int j = is_target ? rp : rp - k;
+            const void* base = is_target ? target : draft;
+            const int64_t row_elem = (is_target ? b * (k + 1) + j : b * k + j) * static_cast<int64_t>(V);
+            if (tile == 0) {
+                const int x = tokens[b * k + j];
+                if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
+                    s_gath[rp] = load_elem<DT>(base, row_elem + x);
+            }
+            const Partial p = tile_is_full<VEC, U>(tile, V, VE) ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                                                                : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
+            if (lane_id() == 0) s_part[w] = p;
+        }
+        __syncthreads();  // the partials and gathered logits before the acceptance reads them
+        if (threadIdx.x < kWave)
+            accept_sequence<DT>(tokens + b * k, temperature + b, uniforms + b * (k + 1), 1, k, V, nT, s_part, s_gath,
+                                0, k, true, accepted_len + b, emitted + b * (k + 1),
+                                accept_prob ? accept_prob + b * k : nullptr, s_r, s_s, &s_info);
+        __syncthreads();
+        si = uniform_info(s_info);
+        if (si.mode == kFinalDone) return;
+    }
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int64_t ntile = (nseg + kFinU - 1) / kFinU;
+    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
+    ArgMax best{-__builtin_inff(), kNoIndex};
+    for (int64_t tile = wave; tile < ntile; tile += kSmallWaves) {
+        if (tile_is_full<VEC, kFinU>(tile, V, VE))
+            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
+        else
+            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, s_seg, best);
+    }
+    if (lane_id() == 0) s_arg[wave] = best;
+    __syncthreads();
+    int32_t* out = emitted + b * (k + 1) + si.a;
+    if (wave == 0) {
+        Draw d{0, si.kappa};
+        if (si.mode == kFinalArgmax) {
+            ArgMax r = s_arg[0];
+            for (int w = 1; w < kSmallWaves; ++w) r = better(r, s_arg[w]);
+            d.y = r.idx;
+        } else {
+            SegMass first[kSegRun];
+            first_segments(s_seg, nseg, first);
+            d = draw_from_segments<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_seg, first);
+        }
+        if (threadIdx.x == 0) {
+            s_redo = d.y == kRedo;
+            s_kappa = d.kappa;
+            if (d.y != kRedo) *out = d.y;
+        }
+    }
+    __syncthreads();
+    if (!s_redo) return;
+    const int y = redo_residual_draw<DT, VEC>(draft, target, trow, drow, V, nseg, si, s_kappa, kSmallWaves, s_m);
+    if (threadIdx.x == 0) *out = y;
+}
+
 }  // namespace sv

@@ -121,6 +121,35 @@ def test_empty_batch_is_a_no_op(svl):
     assert out["accepted_len"].numel() == 0
 
 
+
+# Small chains run in one launch (one workgroup per sequence) while the batch
+# is at most 256 sequences, every row has at most 64 segments and a
+# sequence's 2k + 1 rows hold at most 144 KiB (without drafts: below 256
+# sequences); each shape here sits on one side of one bound.
+SMALL_PATH = [
+    # B, k, V, dtype, expect the one-launch path
+    (16, 4, 8192, W.BF16, True),     # 144 KiB exactly
+    (16, 4, 8200, W.BF16, False),    # just above it
+    (256, 2, 4096, W.BF16, True),    # the largest batch
+    (257, 2, 4096, W.BF16, False),
+    (8, 0, 16384, W.F32, True),      # 64 segments of fp32
+    (8, 0, 16385, W.F32, False),     # 65 segments
+    (255, 0, 2048, W.F32, True),     # no drafts, below the row draw's batch size
+    (256, 0, 2048, W.F32, False),    # the row draw
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_PATH, ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_small_chain_path_and_its_bounds(svl, orc, shape):
+    B, k, V, dt, small = shape
+    inp = W.chain_inputs(B, k, V, dt, 9, target_sigma=3.0, zipf_s=1.1, draft_sigma=(0.2, 3.0),
+                         temperature=np.where(np.arange(B) % 5 == 0, 0.0, 0.8).astype(np.float32))
+    svl.profile_begin(64)
+    got, ref = _check_chain(svl, orc, inp, f"small path B{B}k{k}V{V}dt{dt}")
+    launched = set(svl.profile_end())
+    assert (launched == {"chain_small"}) == small, launched
+
+
 # ------------------------------------------------------------ full workloads ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
