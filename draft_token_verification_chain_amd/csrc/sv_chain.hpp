@@ -1018,9 +1018,19 @@ __global__ __launch_bounds__(kSmallBlock) void chain_small_kernel(
     __shared__ SeqInfo s_info;
     __shared__ double s_kappa;
     __shared__ int s_redo;
+    __shared__ int32_t s_tok[SV_MAX_DRAFTS];
+    __shared__ float s_unif[SV_MAX_DRAFTS + 1];
+    __shared__ float s_temp;
     const int64_t b = blockIdx.x;
     const int wave = threadIdx.x / kWave;
     SeqInfo si;
+    if (k > 0 && threadIdx.x <= SV_MAX_DRAFTS) {
+        // the acceptance's scalars, in flight with the row tiles (copied to LDS)
+        const int t = threadIdx.x;
+        if (t < k) s_tok[t] = tokens[b * k + t];
+        if (t <= k) s_unif[t] = uniforms[b * (k + 1) + t];
+        if (t == 0) s_temp = temperature[b];
+    }
     if (k == 0) {
         // no drafts: a draw from target row 0 (its argmax at temperature 0)
         const float T = temperature[b];
@@ -1051,9 +1061,9 @@ __global__ __launch_bounds__(kSmallBlock) void chain_small_kernel(
         }
         __syncthreads();  // the partials and gathered logits before the acceptance reads them
         if (threadIdx.x < kWave)
-            accept_sequence<DT>(tokens + b * k, temperature + b, uniforms + b * (k + 1), 1, k, V, nT, s_part, s_gath,
-                                0, k, true, accepted_len + b, emitted + b * (k + 1),
-                                accept_prob ? accept_prob + b * k : nullptr, s_r, s_s, &s_info);
+            accept_sequence<DT>(s_tok, &s_temp, s_unif, 1, k, V, nT, s_part, s_gath, 0, k, true, accepted_len + b,
+                                emitted + b * (k + 1), accept_prob ? accept_prob + b * k : nullptr, s_r, s_s,
+                                &s_info);
         __syncthreads();
         si = uniform_info(s_info);
         if (si.mode == kFinalDone) return;
