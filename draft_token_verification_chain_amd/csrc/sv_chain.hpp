@@ -158,6 +158,7 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     int rt = 0, rd = 0;
     double st = 1.0, sd = 1.0;
     double lq = 0.0;  // log2 of the draft token's draft probability
+    const double c = sampled ? kLog2e / static_cast<double>(T) : kLog2e;
     if (lane < npos) {
         if (!sampled) g = s_r[lane];
         if (!xok) {
@@ -168,7 +169,6 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
             st = s_s[lane];
             rd = s_r[k + lane];
             sd = s_s[k + lane];
-            const double c = kLog2e / static_cast<double>(T);
             // log2 p - log2 q with log2 p = l c - R - log2 S (the same for q)
             lq = static_cast<double>(ld) * c - rd - log2_of_sum(sd);
             const double l2ratio = (static_cast<double>(lt) * c - rt - log2_of_sum(st)) - lq;
@@ -196,7 +196,7 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     if (lane == (a < k ? a : 0)) {
         SeqInfo si{};
         si.a = a;
-        temperature_scale(sampled ? T : 1.f, si);
+        temperature_scale_from(c, si);
         si.u = uk;
         if (!sampled) {
             if (a < k) {
@@ -208,7 +208,6 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
         } else if (a < k) {
             si.mode = kFinalResidual;
             si.rt = static_cast<float>(rt);
-            si.inv_st = static_cast<float>(1.0 / st);
             si.st = static_cast<float>(st);
             // log2(S_t / S_d) in the target row's reference; the draw corrects it
             set_kappa(si, static_cast<double>(rt - rd) + (log2(st) - log2(sd)));

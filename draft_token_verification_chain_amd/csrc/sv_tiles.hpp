@@ -20,17 +20,16 @@ struct SeqInfo {
     int mode;
     int a;         // accepted drafts; the final token goes to emitted[b][a]
     float rt;      // target row a: integer reference of its normaliser
-    float inv_st;  //               1 / sum exp2(l c - rt)
     float c_hi;    // log2(e) / T as a double-float pair
     float c_lo;
     float u;       // u[b][k]
     float st;      // sum exp2(l c - rt) of target row a (the residual's normaliser)
+    int fast;      // residual of known large mass: the cheap form suffices (kFastResidualMass)
     double kappa;  // residual: log2(c S_t / S_d) with both rows' normalisers in the reference rt
     double cT;     // log2(e) / T
     float k_hi;    // kappa as a double-float pair
     float k_lo;
-    int fast;      // residual of known large mass: the cheap form suffices (kFastResidualMass)
-    int pad;
+    int pad[2];
 };
 static_assert(sizeof(SeqInfo) == 64, "descriptor layout");
 
@@ -302,10 +301,16 @@ __device__ __forceinline__ void temperature_scale(float T, float& c_hi, float& c
     c_lo = static_cast<float>(c - static_cast<double>(c_hi));
 }
 
-// The descriptor's temperature fields: the double-float pair and the double.
+// The descriptor's temperature fields from c = log2(e) / T: the double-float
+// pair and the double.
+__device__ __forceinline__ void temperature_scale_from(double c, SeqInfo& s) {
+    s.c_hi = static_cast<float>(c);
+    s.c_lo = static_cast<float>(c - static_cast<double>(s.c_hi));
+    s.cT = c;
+}
+
 __device__ __forceinline__ void temperature_scale(float T, SeqInfo& s) {
-    temperature_scale(T, s.c_hi, s.c_lo);
-    s.cT = kLog2e / static_cast<double>(T);
+    temperature_scale_from(kLog2e / static_cast<double>(T), s);
 }
 
 // ---------------------------------------------------------------- wave tiles ---

@@ -349,7 +349,6 @@ __device__ __forceinline__ SeqInfo walk_info(float T, int Rt, double St, double 
     SeqInfo s{};
     temperature_scale(T > 0.f ? T : 1.f, s);
     s.rt = static_cast<float>(Rt);
-    s.inv_st = static_cast<float>(1.0 / St);
     s.st = static_cast<float>(St);
     if (c > 0.0) set_kappa(s, K + log2(c));
     return s;
