@@ -118,6 +118,7 @@ def load_trace_average(kernel: str, workload: str, column: str = "average (us)")
 # The library's kernels (launch names; the profile summaries use the same names).
 LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "chain_accept", "chain_final_part",
                    "chain_final_pick", "chain_row_draw", "chain_small", "argmax_rows", "greedy_rows", "greedy_rows_rest",
+                   "greedy_small",
                    "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
                    "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
 
@@ -342,6 +343,9 @@ class Workload:
             kb["greedy_rows"] = B * s * V * es
             if s <= k:
                 kb["greedy_rows_rest"] = int((got["accepted_len"] >= s).sum()) * (k + 1 - s) * V * es
+            # small greedy chains: one launch, one workgroup per sequence
+            if B <= 256 and (k + 1) * -(-V * es // 8192) <= 16:
+                kb = {"greedy_small": B * (k + 1) * V * es}
         elif kind == "tree_sampled":
             N, par = inp["N"], inp["parent"]
             # the target and draft rows of every inner node

@@ -80,6 +80,9 @@ int64_t final_chunks(int V, sv_dtype dt) {
 // most kSmallMaxSegs segments and whose 2k + 1 rows hold at most
 // kSmallMaxBytes, which one CU streams in about the launches it saves
 // (without drafts, below the one-workgroup-per-row draw's batch size).
+// Small greedy chains likewise (greedy_small_kernel), when their k + 1 rows
+// fit in one tile per wave (at most 128 KiB): the argmax is cheap enough
+// that a second round of tiles costs more than the launch saved.
 constexpr int kSmallMaxRows = 256;
 constexpr int64_t kSmallMaxBytes = 144 * 1024;
 
@@ -552,6 +555,14 @@ sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draf
     if (static_cast<int64_t>(B) * (k + 1) * blocks_for_waves(nT) > kMaxGrid) return SV_ERR_UNSUPPORTED;
     const bool vec = (static_cast<int64_t>(V) * elem_bytes(dt)) % 16 == 0 && aligned16(target_logits);
     auto* part = static_cast<Partial*>(workspace);
+    if (B <= kSmallMaxRows && static_cast<int64_t>(k + 1) * nT <= sv::kSmallWaves) {
+        auto small = dt == SV_BF16 ? (vec ? sv::greedy_small_kernel<SV_BF16, true, kU>
+                                          : sv::greedy_small_kernel<SV_BF16, false, kU>)
+                                   : (vec ? sv::greedy_small_kernel<SV_F32, true, kU>
+                                          : sv::greedy_small_kernel<SV_F32, false, kU>);
+        return launch("greedy_small", small, dim3(static_cast<unsigned>(B)), dim3(sv::kSmallBlock), stream,
+                      target_logits, draft_tokens, k, V, nT, accepted_len, emitted);
+    }
     // Two phases when the rows they may skip outweigh a dependent launch: rows
     // 0 .. s-1 first, the rest only for sequences whose first s drafts match.
     const int64_t bytes = static_cast<int64_t>(B) * (k + 1) * V * elem_bytes(dt);

@@ -996,10 +996,7 @@ __global__ __launch_bounds__(kRowDrawBlock) void chain_row_draw_kernel(const voi
 // trusted the workgroup forms the masses again (redo_residual_draw).  It
 // computes what chain_rowstats, chain_final_part and chain_final_pick
 // compute.
-constexpr int kSmallBlock = 1024;
-constexpr int kSmallWaves = kSmallBlock / kWave;
-constexpr int kSmallMaxSegs = 64;    // rows of at most 32768 bf16 or 16384 f32 logits
-constexpr int kSmallMaxParts = 160;  // 2k x tiles per row
+constexpr int kSmallMaxSegs = 64;  // rows of at most 32768 bf16 or 16384 f32 logits
 
 template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kSmallBlock) void chain_small_kernel(

@@ -95,24 +95,19 @@ __global__ __launch_bounds__(kBlock) void greedy_rows_rest_kernel(const void* __
     greedy_rows<DT, VEC, U, true, TPW>(logits, tokens, k, V, nT, groups, nrows, j0, part);
 }
 
-// One wave per sequence.  The argmax g_j of each of the k + 1 rows is
-// combined by a group of G lanes (the first partials of every row and the
-// draft tokens in flight together); the first position with x_j != g_j is the
-// rejection, and g_a is the emitted target token.  The partials of rows a
-// second phase skipped hold stale values; they only yield g_j for j past a
-// mismatch in the first phase's rows, which are never used.
-__global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* __restrict__ tokens, int k,
-                                                                int nT, const Partial* __restrict__ part,
-                                                                int32_t* __restrict__ accepted_len,
-                                                                int32_t* __restrict__ emitted) {
-    __shared__ int s_g[SV_MAX_DRAFTS + 1];
-    const int64_t b = blockIdx.x;
-    const int lane = threadIdx.x;
+// One wave: the argmax g_j of each of the k + 1 rows of sequence b (partials
+// rows_base[j * nT + t]) is combined by a group of G lanes (the first
+// partials of every row and the draft tokens in flight together); the first
+// position with x_j != g_j is the rejection, and g_a is the emitted target
+// token.  s_g: k + 1 ints of LDS.
+__device__ __forceinline__ void greedy_finish(const int32_t* __restrict__ tokens, int k, int nT,
+                                              const Partial* rows_base, int64_t b, int* s_g,
+                                              int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted) {
+    const int lane = lane_id();
     const int rows = k + 1;
     int G = kWave;
     while (G > 1 && G * rows > kWave) G >>= 1;
     const int per_pass = kWave / G;
-    const Partial* rows_base = part + b * rows * static_cast<int64_t>(nT);
     Partial q[kBatch];
     group_load(rows_base + (lane / G < rows ? lane / G : 0) * static_cast<int64_t>(nT), nT, G, lane / G < rows, q);
     const int x = lane < k ? tokens[b * k + lane] : 0;
@@ -127,7 +122,9 @@ __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* _
         group_reduce<false>(p, nT, G, valid, q, r, sum, am);
         if (valid && (lane & (G - 1)) == 0) s_g[rho] = am.idx;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int g = lane < k ? s_g[lane] : -1;
     int a = first_lane(lane < k && x != g);
     if (a < 0) a = k;
@@ -135,6 +132,41 @@ __global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* _
     int32_t* out = emitted + b * (k + 1);
     for (int j = lane; j <= k; j += kWave) out[j] = j < a ? tokens[b * k + j] : (j == a ? y : -1);
     if (lane == 0) accepted_len[b] = a;
+}
+
+// One wave per sequence, from the streamed partials.  The partials of rows a
+// second phase skipped hold stale values; they only yield g_j for j past a
+// mismatch in the first phase's rows, which are never used.
+__global__ __launch_bounds__(kWave) void greedy_finalize_kernel(const int32_t* __restrict__ tokens, int k,
+                                                                int nT, const Partial* __restrict__ part,
+                                                                int32_t* __restrict__ accepted_len,
+                                                                int32_t* __restrict__ emitted) {
+    __shared__ int s_g[SV_MAX_DRAFTS + 1];
+    const int64_t b = blockIdx.x;
+    greedy_finish(tokens, k, nT, part + b * (k + 1) * static_cast<int64_t>(nT), b, s_g, accepted_len, emitted);
+}
+
+// Small greedy chains in one launch: one workgroup per sequence streams the
+// k + 1 rows' tiles (the tile argmax, partials to LDS) and its first wave
+// finishes as greedy_finalize does (at most kSmallMaxParts tiles; the host
+// sends at most one per wave).
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kSmallBlock) void greedy_small_kernel(const void* __restrict__ logits,
+                                                                   const int32_t* __restrict__ tokens, int k, int V,
+                                                                   int nT, int32_t* __restrict__ accepted_len,
+                                                                   int32_t* __restrict__ emitted) {
+    __shared__ Partial s_part[kSmallMaxParts];
+    __shared__ int s_g[SV_MAX_DRAFTS + 1];
+    const int64_t b = blockIdx.x;
+    const int wave = threadIdx.x / kWave;
+    for (int w = wave; w < (k + 1) * nT; w += kSmallWaves) {
+        const int row = w / nT;
+        const int tile = w - row * nT;
+        const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, (b * (k + 1) + row) * static_cast<int64_t>(V), V, tile);
+        if (lane_id() == 0) s_part[w] = Partial{a.val, a.idx};
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) greedy_finish(tokens, k, nT, s_part, b, s_g, accepted_len, emitted);
 }
 
 // ---------------------------------------------------------------- tree ---

@@ -374,6 +374,12 @@ __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_
 // together rather than one round trip each.
 constexpr int kBatch = 8;
 
+// Small calls run in one launch, one workgroup of kSmallBlock threads per
+// sequence, with at most kSmallMaxParts row tiles held in LDS.
+constexpr int kSmallBlock = 1024;
+constexpr int kSmallWaves = kSmallBlock / kWave;
+constexpr int kSmallMaxParts = 160;
+
 // The argmax of a row from its nT partials, the whole wave striding over them.
 __device__ inline ArgMax wave_combine_argmax(const Partial* p, int nT) {
     ArgMax a{-__builtin_inff(), kNoIndex};

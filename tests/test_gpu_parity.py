@@ -150,6 +150,33 @@ def test_small_chain_path_and_its_bounds(svl, orc, shape):
     assert (launched == {"chain_small"}) == small, launched
 
 
+
+# Small greedy chains run in one launch too: at most 256 sequences whose k + 1
+# rows fit in 16 tiles of 8 KiB (one per wave).
+GREEDY_SMALL_PATH = [
+    # B, k, V, dtype, expect the one-launch path
+    (16, 3, 16384, W.BF16, True),    # 4 rows of 4 tiles
+    (16, 3, 16385, W.BF16, False),   # 4 rows of 5
+    (256, 1, 1000, W.F32, True),
+    (257, 1, 1000, W.F32, False),
+    (2, 15, 512, W.F32, True),       # 16 tiles
+    (2, 16, 512, W.F32, False),      # 17
+]
+
+
+@pytest.mark.parametrize("shape", GREEDY_SMALL_PATH, ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_small_greedy_path_and_its_bounds(svl, orc, shape):
+    B, k, V, dt, small = shape
+    inp = W.greedy_inputs(B, k, V, dt, 12, match_p=0.85)
+    svl.profile_begin(64)
+    got = run_greedy(svl, inp)
+    launched = set(svl.profile_end())
+    ref = orc.verify_greedy(inp)
+    np.testing.assert_array_equal(got["accepted_len"], ref["accepted_len"])
+    np.testing.assert_array_equal(got["emitted"], ref["emitted"])
+    assert (launched == {"greedy_small"}) == small, launched
+
+
 # ------------------------------------------------------------ full workloads ---
 
 @pytest.mark.parametrize("seed", [1, 2, 3, 4, 5])
