@@ -117,10 +117,19 @@ def load_trace_average(kernel: str, workload: str, column: str = "average (us)")
 
 # The library's kernels (launch names; the profile summaries use the same names).
 LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "chain_accept", "chain_final_part",
-                   "chain_final_pick", "chain_row_draw", "chain_small", "argmax_rows", "greedy_rows", "greedy_rows_rest",
+                   "chain_final_pick", "chain_row_draw", "chain_small", "chain_clear", "chain_fused", "argmax_rows",
+                   "greedy_rows", "greedy_rows_rest",
                    "greedy_small",
                    "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
                    "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
+
+
+def fused_group(k: int) -> int:
+    """Lanes per row when one wave combines a chain's 2k rows."""
+    G = 64
+    while G > 1 and G * 2 * k > 64:
+        G //= 2
+    return G
 
 
 def load_traffic(kernel: str, workload: str):
@@ -337,6 +346,9 @@ class Workload:
             nT = -(-V * es // 8192)
             if B <= 256 and (k > 0 or B < 256) and nseg <= 64 and 2 * k * nT <= 160 and (2 * k + 1) * V * es <= 144 << 10:
                 kb = {"chain_small": kb.pop("chain_rowstats", 0) + kb.pop(draw_kernel)}
+            elif 0 < k == s and B * -(-nseg // 16) <= 2048 and 2 * k <= 64 and nT <= 8 * fused_group(k):
+                # rows and draw in one launch (after a launch that clears the partial slots)
+                kb = {"chain_fused": kb.pop("chain_rowstats") + kb.pop(draw_kernel)}
         elif kind == "greedy":
             k = inp["k"]
             s = (k + 1) // 2 if k >= 1 and B * (k + 1) * V * es >= 256 << 20 else k + 1

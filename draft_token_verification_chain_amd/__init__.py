@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     load,
     profile_begin,
     profile_end,
+    set_handoff_polls,
     status_string,
     tree_sampled_workspace_bytes,
     tree_workspace_bytes,

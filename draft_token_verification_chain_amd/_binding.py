@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.sv_verify_tree_sampled.argtypes = [i, i, i, i, p, p, i, i] + [p] * 8 + [sz, p]
     lib.sv_commit_tokens.restype = i
     lib.sv_commit_tokens.argtypes = [i, i, p, p, p, p, i, p, p, p, p]
+    lib.sv_set_handoff_polls.restype = i
+    lib.sv_set_handoff_polls.argtypes = [i]
     lib.sv_profile_begin.restype = i
     lib.sv_profile_begin.argtypes = [i]
     lib.sv_profile_end.restype = i
@@ -330,6 +332,11 @@ def commit_tokens(accepted_len, emitted, seq_len, history=None, *, packed: bool 
     if st != SV_OK:
         raise SpecVerifyError("sv_commit_tokens", st)
     return out
+
+
+def set_handoff_polls(polls: int) -> int:
+    """sv_set_handoff_polls: returns the previous value."""
+    return int(load().sv_set_handoff_polls(int(polls)))
 
 
 def profile_begin(max_launches: int) -> None:

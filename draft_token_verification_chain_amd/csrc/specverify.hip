@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <tuple>
@@ -110,6 +111,48 @@ constexpr int kChainRestTilesPerWave = 1;
 // sequence per CU leaves the CUs that hold residuals as the kernel's tail.
 constexpr int kRowDrawMinRows = 256;
 
+// Chains whose draw recomputes the acceptance in every workgroup stream
+// their rows and draw in one launch (chain_fused_kernel) when one wave's
+// group_load holds all 2k rows' partials: G lanes per row with G * 2k <= 64,
+// at most kBatch partials per lane.
+bool fused_fits(int k, int nT) {
+    if (2 * k > sv::kWave) return false;
+    int G = sv::kWave;
+    while (G > 1 && G * 2 * k > sv::kWave) G >>= 1;
+    return nT <= sv::kBatch * G;
+}
+
+// How many times a drawing workgroup of chain_fused_kernel reads its
+// sequence's published partials before computing any still missing itself
+// (sv_set_handoff_polls).  About 80 ms of waiting: far beyond any call's
+// streaming, so the bound only guarantees that every wait ends.
+constexpr int kDefaultHandoffPolls = 1 << 16;
+std::atomic<int> g_handoff_polls{kDefaultHandoffPolls};
+
+// The tag of a call's handed-over partials (sv::CallTag): a new 64-bit epoch
+// per call, mapped one-to-one onto the two words' halves.  Epoch 0 would map
+// to (0, 0), the cleared slots' tag; epoch 1 is the one tag of every call
+// made while its stream is captured into a graph (a graph replays its
+// arguments), whose slots are therefore cleared first.
+std::atomic<uint64_t> g_call_epoch{2};
+constexpr uint64_t kCaptureEpoch = 1;
+
+sv::CallTag call_tag(uint64_t e) {
+    const uint32_t lo = static_cast<uint32_t>(e);
+    return sv::CallTag{lo, static_cast<uint32_t>(e >> 32) ^ (lo * 0x9e3779b9u)};
+}
+
+// Whether work issued to `stream` is being captured (or the query fails:
+// then the caller takes the path that is right either way).
+bool stream_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 // The chain workspace: the per-(row, tile) partials of the 2k streamed rows of
 // every sequence, their logits at the draft tokens, the final draw's
 // descriptors, segment masses and chunk argmaxes.
@@ -120,7 +163,8 @@ struct ChainLayout {
 ChainLayout chain_layout(int B, int k, int V, sv_dtype dt) {
     ChainLayout L{};
     L.part = 0;
-    L.gathered = align_up(L.part + sizeof(Partial) * static_cast<size_t>(2) * B * k * tiles_per_row(V, dt));
+    // room for the tagged slots of the one-launch path (chain_fused_kernel)
+    L.gathered = align_up(L.part + sizeof(sv::TaggedPartial) * static_cast<size_t>(2) * B * k * tiles_per_row(V, dt));
     L.info = align_up(L.gathered + sizeof(float) * static_cast<size_t>(2) * B * k);
     L.segs = align_up(L.info + sizeof(SeqInfo) * static_cast<size_t>(B));
     L.chunkarg = align_up(L.segs + sizeof(sv::SegMass) * static_cast<size_t>(B) * segments_per_row(V, dt));
@@ -246,16 +290,41 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
     const int64_t fin_blocks = static_cast<int64_t>(B) * nchunk;
     const int acc = k == 0 ? sv::kAcceptNone
                            : (fin_blocks <= kInlineAcceptMaxBlocks ? sv::kAcceptInline : sv::kAcceptRead);
+    // Without accept_prob a sequence's rows after its first rejection are
+    // never needed: large chains stream positions 0 .. s-1 first, then the
+    // rest only for sequences that accept all of them.
+    const int64_t rows_bytes = static_cast<int64_t>(2) * B * k * V * sv::Elem<DT>::bytes;
+    const int groups = static_cast<int>(blocks_for_waves(nT));
+    const int s = k > 0 && accept_prob == nullptr && k >= kChainTwoPhaseMinK && rows_bytes >= kChainTwoPhaseMinBytes &&
+                          static_cast<int64_t>(B) * 2 * k * groups <= kMaxGrid
+                      ? std::max(1, k / kChainFirstPhaseDiv)
+                      : k;
+    auto* segs_c = static_cast<const sv::SegMass*>(segs);
+    if (k > 0 && s == k && acc == sv::kAcceptInline && fused_fits(k, nT)) {
+        // the rows and the draw in one launch, the partials handed over in
+        // slots tagged for this call
+        auto* slots = reinterpret_cast<sv::TaggedPartial*>(ws + L.part);
+        const int64_t nslots = static_cast<int64_t>(2) * B * k * nT;
+        uint64_t epoch = kCaptureEpoch;
+        if (stream_capturing(stream)) {
+            st = launch("chain_clear", sv::chain_clear_kernel,
+                        dim3(static_cast<unsigned>((nslots + sv::kBlock - 1) / sv::kBlock)), dim3(sv::kBlock), stream,
+                        slots, nslots);
+            if (st != SV_OK) return st;
+        } else {
+            epoch = g_call_epoch.fetch_add(1, std::memory_order_relaxed);
+        }
+        const int64_t row_blocks = blocks_for_waves(nslots);
+        st = launch("chain_fused", sv::chain_fused_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(row_blocks + fin_blocks)),
+                    dim3(sv::kFinBlock), stream, tokens, draft, target, temperature, uniforms, B, k, V, nT, row_blocks,
+                    nchunk, g_handoff_polls.load(std::memory_order_relaxed), slots, call_tag(epoch), accepted_len,
+                    emitted, accept_prob, info, segs, chunkarg);
+        if (st != SV_OK) return st;
+        return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kPickBlock), stream,
+                      draft, target, k, V, nchunk, static_cast<const SeqInfo*>(info), segs_c,
+                      static_cast<const Partial*>(chunkarg), emitted);
+    }
     if (k > 0) {
-        // Without accept_prob a sequence's rows after its first rejection are
-        // never needed: large chains stream positions 0 .. s-1 first, then the
-        // rest only for sequences that accept all of them.
-        const int64_t rows_bytes = static_cast<int64_t>(2) * B * k * V * sv::Elem<DT>::bytes;
-        const int groups = static_cast<int>(blocks_for_waves(nT));
-        const int s = accept_prob == nullptr && k >= kChainTwoPhaseMinK && rows_bytes >= kChainTwoPhaseMinBytes &&
-                              static_cast<int64_t>(B) * 2 * k * groups <= kMaxGrid
-                          ? std::max(1, k / kChainFirstPhaseDiv)
-                          : k;
         const int64_t blocks = blocks_for_waves(static_cast<int64_t>(2) * B * s * nT);
         st = launch("chain_rowstats", sv::chain_rowstats_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(blocks)),
                     dim3(sv::kBlock), stream, target, draft, temperature, tokens, B, k, 0, s, V, nT, part, gathered);
@@ -296,8 +365,8 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
                 chunkarg);
     if (st != SV_OK) return st;
     return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kPickBlock), stream, draft,
-                  target, k, V, nchunk, static_cast<const SeqInfo*>(info), static_cast<const sv::SegMass*>(segs),
-                  static_cast<const Partial*>(chunkarg), emitted);
+                  target, k, V, nchunk, static_cast<const SeqInfo*>(info), segs_c, static_cast<const Partial*>(chunkarg),
+                  emitted);
 }
 
 template <int DT, bool VEC>
@@ -460,6 +529,10 @@ sv_status static_workspace(void** out) {
 extern "C" {
 
 int sv_version(void) { return 100; }
+
+int sv_set_handoff_polls(int polls) {
+    return g_handoff_polls.exchange(polls < 0 ? kDefaultHandoffPolls : polls, std::memory_order_relaxed);
+}
 
 const char* sv_status_string(sv_status s) {
     switch (s) {

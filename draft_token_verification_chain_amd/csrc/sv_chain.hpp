@@ -23,28 +23,42 @@ __device__ __forceinline__ Partial rowstats_tile(const void* base, int64_t row_e
     return Partial{a.val, a.idx};
 }
 
+// Partial of tile `tile` of a row, either way the tile ends.
+template <int DT, bool VEC, int U>
+__device__ __forceinline__ Partial row_tile_partial(const void* base, int64_t row_elem, int V, int64_t tile, float T) {
+    return tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec) ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
+                                                            : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
+}
+
 // Tile `tile` of target row (b, position rr - b*k) or of draft row rr of a
 // chain (partial rows rr and nbk + rr).  The wave of tile 0 also reads the
-// row's logit at its draft token into gathered.
-template <int DT, bool VEC, int U>
+// row's logit at its draft token into gathered.  With SHARED the partial is
+// published to other workgroups of the launch (store_partial_tagged into
+// the slots `tagged`, with the call's tag) and gathered is not written: their
+// reader takes those logits from the rows.
+template <int DT, bool VEC, int U, bool SHARED = false>
 __device__ __forceinline__ void rowstats_row_tile(const void* __restrict__ target, const void* __restrict__ draft,
                                                   const float* __restrict__ temperature,
                                                   const int32_t* __restrict__ tokens, int64_t nbk, int k,
                                                   bool is_target, int64_t b, int64_t rr, int64_t tile, int V, int nT,
-                                                  Partial* __restrict__ part, float* __restrict__ gathered) {
+                                                  Partial* __restrict__ part, float* __restrict__ gathered,
+                                                  TaggedPartial* __restrict__ tagged = nullptr, CallTag tag = {}) {
     const int64_t r = is_target ? rr : nbk + rr;
     const void* base = is_target ? target : draft;
     const int64_t row_elem = (is_target ? (b * (k + 1) + (rr - b * k)) : rr) * static_cast<int64_t>(V);
-    if (tile == 0) {
+    if (!SHARED && tile == 0) {
         const int x = tokens[rr];  // draft token scored by this row (rr = b * k + position)
         if (lane_id() == 0 && static_cast<unsigned>(x) < static_cast<unsigned>(V))
             gathered[r] = load_elem<DT>(base, row_elem + x);
     }
     const float T = temperature[b];
-    const Partial p = tile_is_full<VEC, U>(tile, V, Elem<DT>::per_vec)
-                          ? rowstats_tile<DT, VEC, U, VEC>(base, row_elem, V, tile, T)
-                          : rowstats_tile<DT, VEC, U, false>(base, row_elem, V, tile, T);
-    if (lane_id() == 0) part[r * nT + tile] = p;
+    const Partial p = row_tile_partial<DT, VEC, U>(base, row_elem, V, tile, T);
+    if (lane_id() == 0) {
+        if constexpr (SHARED)
+            store_partial_tagged(tagged + r * nT + tile, p, tag);
+        else
+            part[r * nT + tile] = p;
+    }
 }
 
 // Rows 0 .. B*k-1 are target rows (b, j < k); rows B*k .. 2*B*k-1 are draft
@@ -79,24 +93,96 @@ __global__ __launch_bounds__(kBlock) void chain_rowstats_kernel(const void* __re
 
 // ---------------------------------------------------------------- chain: acceptance ---
 
+// Where an acceptance reads the partials that the streaming workgroups of its
+// own launch publish (chain_fused_kernel): the rows, for the logits at the
+// draft tokens and for any partial still missing after `polls` reads.
+struct SharedRows {
+    const void* target = nullptr;
+    const void* draft = nullptr;
+    const TaggedPartial* slots = nullptr;  // the published partials, laid out as `part`
+    CallTag tag{};
+    int polls = 0;
+};
+
+// Sleep between two reads of published partials (s_sleep units of 64 clocks).
+constexpr int kPollSleep = 8;
+
+// group_load's slots (lane l: row rho = l / G of sequence b, partial row prow,
+// tiles l % G + j G, every tile of the row in one load), filled from
+// partials that other workgroups of the launch publish: read with
+// load_partial_tagged until all carry the call's tag, at most sh.polls times
+// with a short sleep between reads.  A partial still missing after that is
+// computed here by the whole wave from the row itself with the streaming
+// wave's own arithmetic (row_tile_partial), so the values are the same
+// either way; the slots wait in LDS (s_q, kBatch * 64 partials) meanwhile,
+// which keeps that rare path's registers within the kernel's budget.  When
+// the launch's workgroups start in index order none is missing by then: the
+// streaming workgroups come first and wait on nothing.
+template <int DT, bool VEC, int U>
+__device__ __forceinline__ void await_partials(int64_t prow, bool valid, int nT, int G, int64_t b, int k, int V,
+                                               float T, const SharedRows& sh, Partial* q, Partial* s_q) {
+    const int lane = lane_id();
+    const int sl = lane & (G - 1);
+    unsigned have = 0;  // bit j: q[j] holds its partial (or the lane has no partial j)
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        q[j] = Partial{0.f, 0};
+        if (!valid || sl + j * G >= nT) have |= 1u << j;
+    }
+    constexpr unsigned kAll = (1u << kBatch) - 1;
+    bool any = true;
+    for (int it = 0; it < sh.polls && any; ++it) {
+        if (it > 0) __builtin_amdgcn_s_sleep(kPollSleep);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (!((have >> j) & 1u) && load_partial_tagged(sh.slots + prow * nT + sl + j * G, sh.tag, q[j]))
+                have |= 1u << j;
+        }
+        any = __builtin_amdgcn_ballot_w64(have != kAll) != 0;
+    }
+    if (!any) return;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) s_q[j * kWave + lane] = q[j];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int j = 0; j < kBatch; ++j) {
+        uint64_t m = __builtin_amdgcn_ballot_w64(!((have >> j) & 1u));
+        while (m != 0) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const int rho = l / G;
+            const bool is_target = rho < k;
+            const int64_t row = is_target ? b * (k + 1) + rho : b * k + (rho - k);
+            const Partial p = row_tile_partial<DT, VEC, U>(is_target ? sh.target : sh.draft,
+                                                           row * static_cast<int64_t>(V), V, (l & (G - 1)) + j * G, T);
+            if (lane == l) s_q[j * kWave + l] = p;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) q[j] = s_q[j * kWave + lane];
+}
+
 // Acceptance of sequence b, computed by one wave (the first of its block):
 // the row statistics from the streaming partials (G lanes per row, one
 // round trip), the 2k logits at the draft tokens, tau_i in the log domain,
 // the first rejection by ballot.  Writes the final draw's descriptor into
 // *out and, when `publish`, accepted_len, the accepted prefix of emitted
-// (the rest -1; the final token is written later) and accept_prob.
+// and -1 after position a (the final token at a is written by the draw's
+// pick, or here after a rejection at temperature 0) and accept_prob.
 // With npos < k only positions 0 .. npos-1 are tested (no outputs then): the
 // return value is the first rejection among them, or npos.  Each tested
 // position gets exactly the arithmetic of the full call (the same lanes per
 // row and the same order of combination), so the two agree on it.
-template <int DT>
+template <int DT, bool SHARED = false, bool VEC = false, int U = 1>
 __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ tokens,
                                                const float* __restrict__ temperature,
                                                const float* __restrict__ uniforms, int B, int k, int V, int nT,
                                                const Partial* __restrict__ part, const float* __restrict__ gathered,
                                                int64_t b, int npos, bool publish, int32_t* __restrict__ accepted_len,
                                                int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
-                                               int* s_r, double* s_s, SeqInfo* out) {
+                                               int* s_r, double* s_s, SeqInfo* out,
+                                               const SharedRows& sh = SharedRows{}, Partial* s_q = nullptr) {
     const int lane = lane_id();
     const int64_t nbk = static_cast<int64_t>(B) * k;
     // every load first: none of them depends on another
@@ -109,7 +195,8 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     auto tested = [&](int rho) { return rho < rows && (rho < k ? rho : rho - k) < npos; };
     Partial q[kBatch];
     const int rho_first = lane / G;
-    group_load(part + (tested(rho_first) ? row_of(rho_first) : 0) * nT, nT, G, tested(rho_first), q);
+    if constexpr (!SHARED)
+        group_load(part + (tested(rho_first) ? row_of(rho_first) : 0) * nT, nT, G, tested(rho_first), q);
     const float T = temperature[b];
     const float uk = uniforms[b * (k + 1) + k];
     int x = 0;
@@ -117,9 +204,20 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     if (lane < npos) {
         x = tokens[b * k + lane];
         ui = uniforms[b * (k + 1) + lane];
-        lt = gathered[b * k + lane];
-        ld = gathered[nbk + b * k + lane];
+        if constexpr (SHARED) {
+            // the logits at the draft token from the rows themselves
+            if (static_cast<unsigned>(x) < static_cast<unsigned>(V)) {
+                lt = load_elem<DT>(sh.target, (b * (k + 1) + lane) * static_cast<int64_t>(V) + x);
+                ld = load_elem<DT>(sh.draft, (b * k + lane) * static_cast<int64_t>(V) + x);
+            }
+        } else {
+            lt = gathered[b * k + lane];
+            ld = gathered[nbk + b * k + lane];
+        }
     }
+    if constexpr (SHARED)
+        await_partials<DT, VEC, U>(row_of(tested(rho_first) ? rho_first : 0), tested(rho_first), nT, G, b, k, V, T,
+                                   sh, q, s_q);
     const bool sampled = T > 0.f;
     const bool xok = static_cast<unsigned>(x) < static_cast<unsigned>(V);  // out-of-range ids are rejected
     // the lane's row's normaliser, kept for tile_tv (one pass only)
@@ -191,7 +289,11 @@ __device__ __forceinline__ int accept_sequence(const int32_t* __restrict__ token
     int32_t* em = emitted + b * (k + 1);
     if (publish) {
         if (accept_prob != nullptr && lane < k) accept_prob[b * k + lane] = static_cast<float>(tau);
-        for (int j = lane; j <= k; j += kWave) em[j] = j < a ? tokens[b * k + j] : -1;
+        // em[a] is left to the final token's one writer: below at temperature
+        // 0 after a rejection, else the pick, which may run concurrently in
+        // another workgroup of the same launch (fused_pick)
+        for (int j = lane; j <= k; j += kWave)
+            if (j != a) em[j] = j < a ? tokens[b * k + j] : -1;
     }
     if (lane == (a < k ? a : 0)) {
         SeqInfo si{};
@@ -531,6 +633,39 @@ __device__ __forceinline__ void final_tile(const void* draft, const void* target
     if (lane < kFinU && g < nseg) seg_out[g] = bonus_seg(m, static_cast<int>(ref));
 }
 
+// Chunk c of sequence b's final draw, its descriptor known: the workgroup's
+// waves stream adjacent tiles of the row(s) the draw needs and write each
+// segment's record, or, at temperature 0, the chunk's argmax.
+template <int DT, bool VEC>
+__device__ __forceinline__ void final_chunk(const void* __restrict__ draft, const void* __restrict__ target, int k,
+                                            int V, int64_t b, int c, int nchunk, const SeqInfo& si,
+                                            SegMass* __restrict__ segs, Partial* __restrict__ chunkarg,
+                                            ArgMax* s_arg) {
+    constexpr int VE = Elem<DT>::per_vec;
+    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
+    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
+    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
+    const int wave = threadIdx.x / kWave;
+    const int64_t tile = static_cast<int64_t>(c) * kFinWaves + wave;  // the workgroup's waves read adjacent tiles
+    SegMass* seg_out = segs + b * nseg;
+    ArgMax best{-__builtin_inff(), kNoIndex};
+    if (tile * kFinU < nseg) {
+        if (tile_is_full<VEC, kFinU>(tile, V, VE))
+            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+        else
+            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
+    }
+    if (si.mode == kFinalArgmax) {
+        if (lane_id() == 0) s_arg[wave] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            ArgMax r = s_arg[0];
+            for (int w = 1; w < kFinWaves; ++w) r = better(r, s_arg[w]);
+            chunkarg[b * nchunk + c] = Partial{r.val, r.idx};
+        }
+    }
+}
+
 template <int DT, bool VEC, int ACC>
 __global__ __launch_bounds__(kFinBlock, ACC == kAcceptRead ? 5 : 1) void chain_final_part_kernel(
     const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
@@ -538,7 +673,6 @@ __global__ __launch_bounds__(kFinBlock, ACC == kAcceptRead ? 5 : 1) void chain_f
     const Partial* __restrict__ part, const float* __restrict__ gathered, int nchunk,
     int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
     SeqInfo* __restrict__ info, SegMass* __restrict__ segs, Partial* __restrict__ chunkarg) {
-    constexpr int VE = Elem<DT>::per_vec;
     __shared__ ArgMax s_arg[kFinWaves];
     const int64_t b = blockIdx.x / nchunk;
     const int c = static_cast<int>(blockIdx.x - b * nchunk);
@@ -569,29 +703,9 @@ __global__ __launch_bounds__(kFinBlock, ACC == kAcceptRead ? 5 : 1) void chain_f
         si = uniform_info(info[b]);
         if (si.mode == kFinalDone) return;
     }
-    const int64_t nseg = ((V + VE - 1) / VE + 63) / 64;
-    const int64_t trow = (b * (k + 1) + si.a) * static_cast<int64_t>(V);
-    const int64_t drow = (b * k + si.a) * static_cast<int64_t>(V);
-    const int wave = threadIdx.x / kWave;
-    const int64_t tile = static_cast<int64_t>(c) * kFinWaves + wave;  // the workgroup's waves read adjacent tiles
-    SegMass* seg_out = segs + b * nseg;
-    ArgMax best{-__builtin_inff(), kNoIndex};
-    if (tile * kFinU < nseg) {
-        if (tile_is_full<VEC, kFinU>(tile, V, VE))
-            final_tile<DT, VEC, VEC>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
-        else
-            final_tile<DT, VEC, false>(draft, target, trow, drow, V, tile, nseg, si, si.mode, seg_out, best);
-    }
-    if (si.mode == kFinalArgmax) {
-        if (lane_id() == 0) s_arg[wave] = best;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            ArgMax r = s_arg[0];
-            for (int w = 1; w < kFinWaves; ++w) r = better(r, s_arg[w]);
-            chunkarg[b * nchunk + c] = Partial{r.val, r.idx};
-        }
-    }
+    final_chunk<DT, VEC>(draft, target, k, V, b, c, nchunk, si, segs, chunkarg, s_arg);
 }
+
 
 // Slow path of the draw, one wave: inverse CDF of the target row's own
 // distribution with two sequential sweeps over its segments.  Used only when
@@ -921,6 +1035,65 @@ __global__ __launch_bounds__(kPickBlock) void chain_final_pick_kernel(
     const int y =
         redo_residual_draw<DT, VEC>(draft, target, trow, drow, V, nseg, s, s_kappa, kPickBlock / kWave, s_m);
     if (threadIdx.x == 0) emitted[b * (k + 1) + s.a] = y;
+}
+
+// ---------------------------------------------------------------- chain: rows and draw in one launch ---
+
+// The first pass and the final draw in one launch, for chains whose draw
+// recomputes the acceptance in every workgroup and whose 2k rows' partials
+// fit one wave's group_load.  Workgroups 0 .. row_blocks-1 stream the rows
+// as chain_rowstats_kernel does (without gathered) and publish each tile's
+// partial into `slots` with the call's tag (store_partial_tagged); the
+// others draw, chunk c of sequence b each, as chain_final_part_kernel with
+// the acceptance inline does, reading the sequence's partials as they are
+// published (await_partials).  A sequence's draw thus starts as soon as its
+// rows are streamed, while the rows of later sequences still stream.
+// chain_final_pick_kernel follows.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kFinBlock, 5) void chain_fused_kernel(
+    const int32_t* __restrict__ tokens, const void* __restrict__ draft, const void* __restrict__ target,
+    const float* __restrict__ temperature, const float* __restrict__ uniforms, int B, int k, int V, int nT,
+    int64_t row_blocks, int nchunk, int polls, TaggedPartial* __restrict__ slots, CallTag tag,
+    int32_t* __restrict__ accepted_len, int32_t* __restrict__ emitted, float* __restrict__ accept_prob,
+    SeqInfo* __restrict__ info, SegMass* __restrict__ segs, Partial* __restrict__ chunkarg) {
+    static_assert(kFinBlock == kBlock, "both roles use one workgroup size");
+    if (blockIdx.x < row_blocks) {
+        const int64_t gw = global_wave();
+        const int64_t nbk = static_cast<int64_t>(B) * k;
+        if (gw >= 2 * nbk * nT) return;
+        const int64_t rp = gw / nT;
+        const int64_t tile = gw - rp * nT;
+        const bool is_target = rp < nbk;
+        const int64_t rr = is_target ? rp : rp - nbk;
+        rowstats_row_tile<DT, VEC, U, true>(target, draft, temperature, tokens, nbk, k, is_target, rr / k, rr, tile,
+                                            V, nT, nullptr, nullptr, slots, tag);
+        return;
+    }
+    __shared__ ArgMax s_arg[kFinWaves];
+    __shared__ int s_r[2 * SV_MAX_DRAFTS];
+    __shared__ double s_s[2 * SV_MAX_DRAFTS];
+    __shared__ SeqInfo s_info;
+    __shared__ Partial s_q[kBatch * kWave];
+    const int64_t db = blockIdx.x - row_blocks;
+    const int64_t b = db / nchunk;
+    const int c = static_cast<int>(db - b * nchunk);
+    if (threadIdx.x < kWave)
+        accept_sequence<DT, true, VEC, U>(tokens, temperature, uniforms, B, k, V, nT, nullptr, nullptr, b, k, c == 0,
+                                          accepted_len, emitted, accept_prob, s_r, s_s, &s_info,
+                                          SharedRows{target, draft, slots, tag, polls}, s_q);
+    __syncthreads();
+    const SeqInfo si = uniform_info(s_info);
+    if (c == 0 && threadIdx.x == 0) info[b] = si;
+    if (si.mode == kFinalDone) return;
+    final_chunk<DT, VEC>(draft, target, k, V, b, c, nchunk, si, segs, chunkarg, s_arg);
+}
+
+// Sets n tagged partial slots to zero words (tag (0, 0), which no call
+// uses), ahead of chain_fused_kernel in a stream being captured into a
+// graph, whose replays all carry one tag.
+__global__ __launch_bounds__(kBlock) void chain_clear_kernel(TaggedPartial* __restrict__ slots, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i < n) slots[i] = TaggedPartial{{0, 0}};
 }
 
 // ---------------------------------------------------------------- final draw, one workgroup per row ---

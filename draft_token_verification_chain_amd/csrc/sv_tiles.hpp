@@ -374,6 +374,42 @@ __device__ __forceinline__ ArgMax tile_argmax_any(const void* base, int64_t row_
 // together rather than one round trip each.
 constexpr int kBatch = 8;
 
+// Partials handed from one workgroup to another inside a launch.  Each slot
+// is two 8-byte words, (f, t0) and (i, t1), written with relaxed
+// device-scope atomic stores and read with relaxed device-scope atomic
+// loads; (t0, t1) is a tag unique to the call (CallTag).  A reader takes a
+// slot once both words carry the call's tag: each word is one atomic
+// access, so it then holds this call's value, and no fence is needed (on
+// this GPU a device-scope release or acquire writes back or invalidates a
+// whole L2).  Words left by an earlier call, by other use of the memory or
+// by nothing carry another tag; a tag is 64 bits, so unrelated bytes pass
+// for the call's own with probability 2^-64 per slot.
+struct TaggedPartial {
+    uint64_t w[2];
+};
+static_assert(sizeof(TaggedPartial) == 16, "a tagged partial is two atomic words");
+
+struct CallTag {
+    uint32_t t0, t1;
+};
+
+__device__ __forceinline__ void store_partial_tagged(TaggedPartial* p, Partial v, CallTag tag) {
+    const uint64_t w0 = (static_cast<uint64_t>(tag.t0) << 32) | __builtin_bit_cast(uint32_t, v.f);
+    const uint64_t w1 = (static_cast<uint64_t>(tag.t1) << 32) | static_cast<uint32_t>(v.i);
+    __hip_atomic_store(&p->w[0], w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p->w[1], w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whether slot p holds this call's partial; if so, it is in v.
+__device__ __forceinline__ bool load_partial_tagged(const TaggedPartial* p, CallTag tag, Partial& v) {
+    const uint64_t w0 = __hip_atomic_load(&p->w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w1 = __hip_atomic_load(&p->w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v.f = __builtin_bit_cast(float, static_cast<uint32_t>(w0));
+    v.i = static_cast<int>(static_cast<uint32_t>(w1));
+    return static_cast<uint32_t>(w0 >> 32) == tag.t0 && static_cast<uint32_t>(w1 >> 32) == tag.t1;
+}
+
+
 // Small calls run in one launch, one workgroup of kSmallBlock threads per
 // sequence, with at most kSmallMaxParts row tiles held in LDS.
 constexpr int kSmallBlock = 1024;

@@ -89,6 +89,16 @@ int sv_version(void);
 /* Static text for a status code (never NULL). */
 const char *sv_status_string(sv_status s);
 
+/* Testing aid for the one-launch chain path (see sv_verify_chain): how many
+ * times a drawing workgroup reads the row statistics that the streaming
+ * workgroups of the same launch publish, before it computes any still
+ * missing itself with the same arithmetic (the outputs do not change).
+ * Default 65536 (a bound far beyond any call's streaming); 0 makes the
+ * drawing workgroups compute every statistic themselves; a negative value
+ * restores the default.  Returns the previous value.  Applies to launches
+ * issued after it returns, from any thread. */
+int sv_set_handoff_polls(int polls);
+
 /* Workspace bytes for one call of the matching entry point with these sizes;
  * 0 when the sizes are invalid. */
 size_t sv_chain_workspace_bytes(int B, int k, int V, sv_dtype dt);
@@ -128,6 +138,15 @@ size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt);
  * Without accept_prob, from k >= 6 and 128 MiB of draft and target rows
  * 0..k-1, the rows of positions max(1, k/4) and later are read only for the
  * sequences that accept all drafts before them.  The outputs are the same.
+ * When the final draw takes at most 2048 workgroups and a sequence's 2k rows
+ * have at most 512 tiles of 8 KiB (k <= 32), the rows are streamed and the
+ * draw made in one launch: each sequence's draw starts once its own rows are
+ * streamed, waiting within a bound for their statistics
+ * (sv_set_handoff_polls).  The statistics pass through the workspace tagged
+ * with a 64-bit value unique to the call, so whatever the workspace held
+ * before is never taken for them (unrelated bytes match a tag with
+ * probability 2^-64); a call made while its stream is captured into a graph
+ * clears them first instead, with one more launch.  The outputs are the same.
  */
 sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
                           const int32_t *draft_tokens, const void *draft_logits,
@@ -152,9 +171,11 @@ sv_status sv_verify_chain(int B, int k, int V, sv_dtype dt,
  * Sizes whose workspace (sv_chain_workspace_bytes) exceeds
  * SV_STATIC_WORKSPACE_BYTES return SV_ERR_WORKSPACE_TOO_SMALL before any
  * launch; a failed symbol lookup returns SV_ERR_HIP.  The array needs no
- * clearing between calls (every call writes each byte it reads), but all
- * calls on one GPU share it: calls that overlap on one GPU, on different
- * streams or from different host threads, race and give undefined results.
+ * clearing between calls (every call writes each byte it uses, and the
+ * one-launch path tells its own statistics from earlier calls' by their
+ * tag), but all calls on one GPU share it: calls that overlap on one GPU, on
+ * different streams or from different host threads, race and give undefined
+ * results.
  */
 sv_status sv_verify_chain_static(int B, int k, int V, sv_dtype dt,
                                  const int32_t *draft_tokens, const void *draft_logits,
