@@ -117,19 +117,24 @@ def load_trace_average(kernel: str, workload: str, column: str = "average (us)")
 
 # The library's kernels (launch names; the profile summaries use the same names).
 LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "chain_accept", "chain_final_part",
-                   "chain_final_pick", "chain_row_draw", "chain_small", "chain_clear", "chain_fused", "argmax_rows",
-                   "greedy_rows", "greedy_rows_rest",
+                   "chain_final_pick", "chain_row_draw", "chain_small", "clear_slots", "chain_fused", "argmax_rows",
+                   "greedy_rows", "greedy_rows_rest", "greedy_fused",
                    "greedy_small",
                    "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
                    "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
 
 
-def fused_group(k: int) -> int:
-    """Lanes per row when one wave combines a chain's 2k rows."""
+def fused_group_rows(rows: int) -> int:
+    """Lanes per row when one wave combines `rows` rows' partials."""
     G = 64
-    while G > 1 and G * 2 * k > 64:
+    while G > 1 and G * rows > 64:
         G //= 2
     return G
+
+
+def fused_group(k: int) -> int:
+    """Lanes per row when one wave combines a chain's 2k rows."""
+    return fused_group_rows(2 * k)
 
 
 def load_traffic(kernel: str, workload: str):
@@ -355,6 +360,9 @@ class Workload:
             kb["greedy_rows"] = B * s * V * es
             if s <= k:
                 kb["greedy_rows_rest"] = int((got["accepted_len"] >= s).sum()) * (k + 1 - s) * V * es
+                # both phases in one launch when the first s rows' partials fit one wave
+                if -(-V * es // 8192) <= 8 * fused_group_rows(s):
+                    kb = {"greedy_fused": kb["greedy_rows"] + kb["greedy_rows_rest"]}
             # small greedy chains: one launch, one workgroup per sequence
             if B <= 256 and (k + 1) * -(-V * es // 8192) <= 16:
                 kb = {"greedy_small": B * (k + 1) * V * es}

@@ -268,6 +268,23 @@ sv_status launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 blo
 
 // ---------------------------------------------------------------- dispatch ---
 
+// The tag of a launch that hands partials between its workgroups in tagged
+// slots (sv::CallTag): a new epoch per call, or, while the stream is being
+// captured, the one capture epoch after a launch that clears the slots.
+sv_status handover_tag(hipStream_t stream, sv::TaggedPartial* slots, int64_t nslots, sv::CallTag& tag) {
+    uint64_t epoch = kCaptureEpoch;
+    if (stream_capturing(stream)) {
+        const sv_status st = launch("clear_slots", sv::clear_slots_kernel,
+                                    dim3(static_cast<unsigned>((nslots + sv::kBlock - 1) / sv::kBlock)),
+                                    dim3(sv::kBlock), stream, slots, nslots);
+        if (st != SV_OK) return st;
+    } else {
+        epoch = g_call_epoch.fetch_add(1, std::memory_order_relaxed);
+    }
+    tag = call_tag(epoch);
+    return SV_OK;
+}
+
 template <int DT, bool VEC>
 sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draft, const void* target,
                     const float* temperature, const float* uniforms, int32_t* accepted_len, int32_t* emitted,
@@ -305,19 +322,12 @@ sv_status run_chain(int B, int k, int V, const int32_t* tokens, const void* draf
         // slots tagged for this call
         auto* slots = reinterpret_cast<sv::TaggedPartial*>(ws + L.part);
         const int64_t nslots = static_cast<int64_t>(2) * B * k * nT;
-        uint64_t epoch = kCaptureEpoch;
-        if (stream_capturing(stream)) {
-            st = launch("chain_clear", sv::chain_clear_kernel,
-                        dim3(static_cast<unsigned>((nslots + sv::kBlock - 1) / sv::kBlock)), dim3(sv::kBlock), stream,
-                        slots, nslots);
-            if (st != SV_OK) return st;
-        } else {
-            epoch = g_call_epoch.fetch_add(1, std::memory_order_relaxed);
-        }
+        sv::CallTag tag;
+        if ((st = handover_tag(stream, slots, nslots, tag)) != SV_OK) return st;
         const int64_t row_blocks = blocks_for_waves(nslots);
         st = launch("chain_fused", sv::chain_fused_kernel<DT, VEC, kU>, dim3(static_cast<unsigned>(row_blocks + fin_blocks)),
                     dim3(sv::kFinBlock), stream, tokens, draft, target, temperature, uniforms, B, k, V, nT, row_blocks,
-                    nchunk, g_handoff_polls.load(std::memory_order_relaxed), slots, call_tag(epoch), accepted_len,
+                    nchunk, g_handoff_polls.load(std::memory_order_relaxed), slots, tag, accepted_len,
                     emitted, accept_prob, info, segs, chunkarg);
         if (st != SV_OK) return st;
         return launch("chain_final_pick", sv::chain_final_pick_kernel<DT, VEC>, dim3(B), dim3(sv::kPickBlock), stream,
@@ -405,6 +415,38 @@ sv_status run_greedy_rows(const void* logits, const int32_t* tokens, int B, int 
                       tokens, k, V, nT, groups, nrows, j0, part);
 }
 
+// Both phases of a two-phase greedy chain in one launch (greedy_fused_kernel).
+template <int DT, bool VEC>
+sv_status run_greedy_fused(const void* logits, const int32_t* tokens, int B, int k, int V, int nT, int s,
+                           sv::TaggedPartial* slots, sv::CallTag tag, Partial* part, hipStream_t stream) {
+    constexpr int tpw = kGreedyRestTilesPerWave;
+    const int groups1 = (nT + sv::kWavesPerBlock - 1) / sv::kWavesPerBlock;
+    const int groups2 = (nT + sv::kWavesPerBlock * tpw - 1) / (sv::kWavesPerBlock * tpw);
+    const int64_t p1_blocks = static_cast<int64_t>(B) * s * groups1;
+    const int64_t blocks = p1_blocks + static_cast<int64_t>(B) * (k + 1 - s) * groups2;
+    return launch("greedy_fused", sv::greedy_fused_kernel<DT, VEC, kU, tpw>, dim3(static_cast<unsigned>(blocks)),
+                  dim3(sv::kBlock), stream, logits, tokens, k, V, nT, s, groups1, groups2, p1_blocks, slots, tag,
+                  g_handoff_polls.load(std::memory_order_relaxed), part);
+}
+
+sv_status greedy_fused(sv_dtype dt, bool vec, const void* logits, const int32_t* tokens, int B, int k, int V, int nT,
+                       int s, sv::TaggedPartial* slots, sv::CallTag tag, Partial* part, hipStream_t stream) {
+    if (dt == SV_BF16)
+        return vec ? run_greedy_fused<SV_BF16, true>(logits, tokens, B, k, V, nT, s, slots, tag, part, stream)
+                   : run_greedy_fused<SV_BF16, false>(logits, tokens, B, k, V, nT, s, slots, tag, part, stream);
+    return vec ? run_greedy_fused<SV_F32, true>(logits, tokens, B, k, V, nT, s, slots, tag, part, stream)
+               : run_greedy_fused<SV_F32, false>(logits, tokens, B, k, V, nT, s, slots, tag, part, stream);
+}
+
+// Whether the first s rows' partials of a sequence fit one wave's group_load
+// (the second phase's check in greedy_fused_kernel reads them as published).
+bool greedy_fused_fits(int s, int nT) {
+    if (s > sv::kWave) return false;
+    int G = sv::kWave;
+    while (G > 1 && G * s > sv::kWave) G >>= 1;
+    return nT <= sv::kBatch * G;
+}
+
 sv_status greedy_rows(sv_dtype dt, bool vec, bool check, const void* logits, const int32_t* tokens, int B, int k, int V,
                       int nT, int j0, int nrows, Partial* part, hipStream_t stream) {
     if (dt == SV_BF16) {
@@ -473,6 +515,13 @@ sv_status tree_two_phase(sv_dtype dt, bool vec, const void* logits, const int32_
                                                   list, count, stream)
                : run_tree_two_phase<SV_F32, false>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
                                                    list, count, stream);
+}
+
+// The greedy workspace: the partials of every row, then the tagged slots of
+// the first phase's rows (at most (k + 1) / 2 per sequence) that
+// greedy_fused_kernel hands between its phases.
+size_t greedy_slots_offset(int B, int k, int V, sv_dtype dt) {
+    return align_up(sizeof(Partial) * static_cast<size_t>(B) * (k + 1) * tiles_per_row(V, dt));
 }
 
 // Greedy verification streams its rows in two phases only from this size on.
@@ -552,7 +601,8 @@ size_t sv_chain_workspace_bytes(int B, int k, int V, sv_dtype dt) {
 
 size_t sv_greedy_workspace_bytes(int B, int k, int V, sv_dtype dt) {
     if (B < 0 || k < 0 || k > SV_MAX_DRAFTS || V < 1 || V > SV_MAX_VOCAB || !valid_dtype(dt)) return 0;
-    return align_up(sizeof(Partial) * static_cast<size_t>(B) * (k + 1) * tiles_per_row(V, dt));
+    return greedy_slots_offset(B, k, V, dt) +
+           align_up(sizeof(sv::TaggedPartial) * static_cast<size_t>(B) * ((k + 1) / 2) * tiles_per_row(V, dt));
 }
 
 size_t sv_tree_workspace_bytes(int B, int N, int V, sv_dtype dt) {
@@ -640,11 +690,23 @@ sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt, const int32_t* draf
     // 0 .. s-1 first, the rest only for sequences whose first s drafts match.
     const int64_t bytes = static_cast<int64_t>(B) * (k + 1) * V * elem_bytes(dt);
     const int s = (k >= 1 && bytes >= kGreedyTwoPhaseMinBytes) ? (k + 1) / 2 : k + 1;
-    if ((st = greedy_rows(dt, vec, false, target_logits, draft_tokens, B, k, V, nT, 0, s, part, stream)) != SV_OK)
-        return st;
-    if (s < k + 1 &&
-        (st = greedy_rows(dt, vec, true, target_logits, draft_tokens, B, k, V, nT, s, k + 1 - s, part, stream)) != SV_OK)
-        return st;
+    if (s < k + 1 && greedy_fused_fits(s, nT)) {
+        // both phases in one launch, the first phase's partials handed over
+        // in slots tagged for this call
+        auto* slots = reinterpret_cast<sv::TaggedPartial*>(static_cast<char*>(workspace) +
+                                                           greedy_slots_offset(B, k, V, dt));
+        sv::CallTag tag;
+        if ((st = handover_tag(stream, slots, static_cast<int64_t>(B) * s * nT, tag)) != SV_OK) return st;
+        if ((st = greedy_fused(dt, vec, target_logits, draft_tokens, B, k, V, nT, s, slots, tag, part, stream)) !=
+            SV_OK)
+            return st;
+    } else {
+        if ((st = greedy_rows(dt, vec, false, target_logits, draft_tokens, B, k, V, nT, 0, s, part, stream)) != SV_OK)
+            return st;
+        if (s < k + 1 && (st = greedy_rows(dt, vec, true, target_logits, draft_tokens, B, k, V, nT, s, k + 1 - s, part,
+                                           stream)) != SV_OK)
+            return st;
+    }
     return launch("greedy_finalize", sv::greedy_finalize_kernel, dim3(B), dim3(sv::kWave), stream, draft_tokens, k,
                   nT, part, accepted_len, emitted);
 }

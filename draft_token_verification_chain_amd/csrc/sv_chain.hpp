@@ -104,63 +104,19 @@ struct SharedRows {
     int polls = 0;
 };
 
-// Sleep between two reads of published partials (s_sleep units of 64 clocks).
-constexpr int kPollSleep = 8;
-
-// group_load's slots (lane l: row rho = l / G of sequence b, partial row prow,
-// tiles l % G + j G, every tile of the row in one load), filled from
-// partials that other workgroups of the launch publish: read with
-// load_partial_tagged until all carry the call's tag, at most sh.polls times
-// with a short sleep between reads.  A partial still missing after that is
-// computed here by the whole wave from the row itself with the streaming
-// wave's own arithmetic (row_tile_partial), so the values are the same
-// either way; the slots wait in LDS (s_q, kBatch * 64 partials) meanwhile,
-// which keeps that rare path's registers within the kernel's budget.  When
-// the launch's workgroups start in index order none is missing by then: the
-// streaming workgroups come first and wait on nothing.
+// group_load's slots of sequence b's 2k rows (lane l: row rho = l / G,
+// partial row prow) from the partials that the streaming workgroups of the
+// launch publish (await_slots); a partial still missing is computed with the
+// streaming wave's own arithmetic (row_tile_partial).
 template <int DT, bool VEC, int U>
 __device__ __forceinline__ void await_partials(int64_t prow, bool valid, int nT, int G, int64_t b, int k, int V,
                                                float T, const SharedRows& sh, Partial* q, Partial* s_q) {
-    const int lane = lane_id();
-    const int sl = lane & (G - 1);
-    unsigned have = 0;  // bit j: q[j] holds its partial (or the lane has no partial j)
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-        q[j] = Partial{0.f, 0};
-        if (!valid || sl + j * G >= nT) have |= 1u << j;
-    }
-    constexpr unsigned kAll = (1u << kBatch) - 1;
-    bool any = true;
-    for (int it = 0; it < sh.polls && any; ++it) {
-        if (it > 0) __builtin_amdgcn_s_sleep(kPollSleep);
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (!((have >> j) & 1u) && load_partial_tagged(sh.slots + prow * nT + sl + j * G, sh.tag, q[j]))
-                have |= 1u << j;
-        }
-        any = __builtin_amdgcn_ballot_w64(have != kAll) != 0;
-    }
-    if (!any) return;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) s_q[j * kWave + lane] = q[j];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll 1
-    for (int j = 0; j < kBatch; ++j) {
-        uint64_t m = __builtin_amdgcn_ballot_w64(!((have >> j) & 1u));
-        while (m != 0) {
-            const int l = __builtin_ctzll(m);
-            m &= m - 1;
-            const int rho = l / G;
-            const bool is_target = rho < k;
-            const int64_t row = is_target ? b * (k + 1) + rho : b * k + (rho - k);
-            const Partial p = row_tile_partial<DT, VEC, U>(is_target ? sh.target : sh.draft,
-                                                           row * static_cast<int64_t>(V), V, (l & (G - 1)) + j * G, T);
-            if (lane == l) s_q[j * kWave + l] = p;
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) q[j] = s_q[j * kWave + lane];
+    await_slots(sh.slots + prow * nT, valid, nT, G, sh.tag, sh.polls, q, s_q, [&](int rho, int64_t tile) {
+        const bool is_target = rho < k;
+        const int64_t row = is_target ? b * (k + 1) + rho : b * k + (rho - k);
+        return row_tile_partial<DT, VEC, U>(is_target ? sh.target : sh.draft, row * static_cast<int64_t>(V), V, tile,
+                                            T);
+    });
 }
 
 // Acceptance of sequence b, computed by one wave (the first of its block):
@@ -1088,13 +1044,6 @@ __global__ __launch_bounds__(kFinBlock, 5) void chain_fused_kernel(
     final_chunk<DT, VEC>(draft, target, k, V, b, c, nchunk, si, segs, chunkarg, s_arg);
 }
 
-// Sets n tagged partial slots to zero words (tag (0, 0), which no call
-// uses), ahead of chain_fused_kernel in a stream being captured into a
-// graph, whose replays all carry one tag.
-__global__ __launch_bounds__(kBlock) void chain_clear_kernel(TaggedPartial* __restrict__ slots, int64_t n) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (i < n) slots[i] = TaggedPartial{{0, 0}};
-}
 
 // ---------------------------------------------------------------- final draw, one workgroup per row ---
 

@@ -29,17 +29,23 @@ __global__ __launch_bounds__(kBlock) void argmax_rows_kernel(const void* __restr
 // rows' argmax, which wave 0 of each workgroup finds from the first phase's
 // partials (G lanes per row, one round trip).  Each wave takes TPW tiles, a
 // workgroup kWavesPerBlock * TPW consecutive ones (`groups` workgroups per
-// row).  The one-dimensional grid runs over (sequence, row, group) with the
-// group fastest: the dispatcher deals consecutive workgroups out to the XCDs
-// in turn, so every sequence's work is spread over the XCDs and each gets an
-// even share of the second phase however its sequences fall.
-template <int DT, bool VEC, int U, bool CHECK, int TPW>
+// row).  The one-dimensional grid (workgroup blk) runs over (sequence, row,
+// group) with the group fastest: the dispatcher deals consecutive workgroups
+// out to the XCDs in turn, so every sequence's work is spread over the XCDs
+// and each gets an even share of the second phase however its sequences
+// fall.  With SHARED both phases run in one launch (greedy_fused_kernel): the
+// first also publishes its partials in tagged slots (slot row b * s + j), and
+// the second's check reads them from there as they are published
+// (await_slots, which needs all of a row's partials in one group_load).
+template <int DT, bool VEC, int U, bool CHECK, int TPW, bool SHARED = false>
 __device__ __forceinline__ void greedy_rows(const void* __restrict__ logits, const int32_t* __restrict__ tokens,
                                             int k, int V, int nT, int groups, int nrows, int j0,
-                                            Partial* __restrict__ part) {
+                                            Partial* __restrict__ part, int64_t blk,
+                                            TaggedPartial* __restrict__ slots = nullptr, int s_rows = 0,
+                                            CallTag tag = {}, int polls = 0, Partial* s_q = nullptr) {
     const int per_seq = groups * nrows;
-    const int64_t b = blockIdx.x / per_seq;
-    const int rem = static_cast<int>(blockIdx.x - b * per_seq);
+    const int64_t b = blk / per_seq;
+    const int rem = static_cast<int>(blk - b * per_seq);
     const int z = rem / groups;
     const int group = rem - z * groups;
     const int rows = k + 1;
@@ -54,7 +60,15 @@ __device__ __forceinline__ void greedy_rows(const void* __restrict__ logits, con
             const bool valid = rho < s;
             const Partial* p = part + (b * rows + (valid ? rho : 0)) * static_cast<int64_t>(nT);
             Partial q[kBatch];
-            group_load(p, nT, G, valid, q);
+            if constexpr (SHARED)
+                await_slots(slots + (b * s_rows + (valid ? rho : 0)) * static_cast<int64_t>(nT), valid, nT, G, tag,
+                            polls, q, s_q, [&](int r, int64_t tile) {
+                                const ArgMax a = tile_argmax_any<DT, VEC, U>(
+                                    logits, (b * rows + r) * static_cast<int64_t>(V), V, tile);
+                                return Partial{a.val, a.idx};
+                            });
+            else
+                group_load(p, nT, G, valid, q);
             const int x = valid ? tokens[b * k + rho] : 0;
             int r;
             double sum;
@@ -73,7 +87,12 @@ __device__ __forceinline__ void greedy_rows(const void* __restrict__ logits, con
         const int64_t tile = (static_cast<int64_t>(group) * TPW + i) * kWavesPerBlock + wave;
         if (tile >= nT) break;
         const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, row * static_cast<int64_t>(V), V, tile);
-        if (lane_id() == 0) part[row * nT + tile] = Partial{a.val, a.idx};
+        if (lane_id() == 0) {
+            part[row * nT + tile] = Partial{a.val, a.idx};
+            if constexpr (SHARED && !CHECK)
+                store_partial_tagged(slots + (b * s_rows + j0 + z) * static_cast<int64_t>(nT) + tile,
+                                     Partial{a.val, a.idx}, tag);
+        }
     }
 }
 
@@ -83,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void greedy_rows_kernel(const void* __restr
                                                              const int32_t* __restrict__ tokens, int k, int V,
                                                              int nT, int groups, int nrows, int j0,
                                                              Partial* __restrict__ part) {
-    greedy_rows<DT, VEC, U, false, 1>(logits, tokens, k, V, nT, groups, nrows, j0, part);
+    greedy_rows<DT, VEC, U, false, 1>(logits, tokens, k, V, nT, groups, nrows, j0, part, blockIdx.x);
 }
 
 // The second phase.
@@ -92,7 +111,29 @@ __global__ __launch_bounds__(kBlock) void greedy_rows_rest_kernel(const void* __
                                                                   const int32_t* __restrict__ tokens, int k, int V,
                                                                   int nT, int groups, int nrows, int j0,
                                                                   Partial* __restrict__ part) {
-    greedy_rows<DT, VEC, U, true, TPW>(logits, tokens, k, V, nT, groups, nrows, j0, part);
+    greedy_rows<DT, VEC, U, true, TPW>(logits, tokens, k, V, nT, groups, nrows, j0, part, blockIdx.x);
+}
+
+// Both phases in one launch: workgroups 0 .. p1_blocks - 1 stream rows
+// 0 .. s - 1 of every sequence (groups1 workgroups per row) and publish their
+// partials; the rest stream rows s .. k of the sequences whose first s
+// drafts match, each checking its sequence as the partials arrive.  Every
+// second-phase workgroup waits only on first-phase ones, which come first in
+// the grid and wait on nothing.
+template <int DT, bool VEC, int U, int TPW>
+__global__ __launch_bounds__(kBlock) void greedy_fused_kernel(const void* __restrict__ logits,
+                                                              const int32_t* __restrict__ tokens, int k, int V,
+                                                              int nT, int s, int groups1, int groups2,
+                                                              int64_t p1_blocks, TaggedPartial* __restrict__ slots,
+                                                              CallTag tag, int polls, Partial* __restrict__ part) {
+    if (blockIdx.x < p1_blocks) {
+        greedy_rows<DT, VEC, U, false, 1, true>(logits, tokens, k, V, nT, groups1, s, 0, part, blockIdx.x, slots, s,
+                                                tag);
+        return;
+    }
+    __shared__ Partial s_q[kBatch * kWave];
+    greedy_rows<DT, VEC, U, true, TPW, true>(logits, tokens, k, V, nT, groups2, k + 1 - s, s, part,
+                                             blockIdx.x - p1_blocks, slots, s, tag, polls, s_q);
 }
 
 // One wave: the argmax g_j of each of the k + 1 rows of sequence b (partials
@@ -185,7 +226,7 @@ __global__ __launch_bounds__(kSmallBlock) void greedy_small_kernel(const void* _
 template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kBlock) void tree_root_rows_kernel(const void* __restrict__ logits, int N, int V,
                                                                 int nT, int groups, Partial* __restrict__ part) {
-    greedy_rows<DT, VEC, U, false, 1>(logits, nullptr, N - 1, V, nT, groups, 1, 0, part);
+    greedy_rows<DT, VEC, U, false, 1>(logits, nullptr, N - 1, V, nT, groups, 1, 0, part, blockIdx.x);
 }
 
 // The rows of one later phase, one workgroup per sequence and one thread per

@@ -410,6 +410,68 @@ __device__ __forceinline__ bool load_partial_tagged(const TaggedPartial* p, Call
 }
 
 
+// Sets n tagged partial slots to zero words (tag (0, 0), which no call
+// uses), ahead of a launch that hands partials over in them when its stream
+// is being captured into a graph, whose replays all carry one tag.
+__global__ __launch_bounds__(kBlock) void clear_slots_kernel(TaggedPartial* __restrict__ slots, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (i < n) slots[i] = TaggedPartial{{0, 0}};
+}
+
+// Sleep between two reads of published partials (s_sleep units of 64 clocks).
+constexpr int kPollSleep = 8;
+
+// group_load's slots (lane l: row l / G, tiles l % G + j G, every tile of
+// the row in one load; the lane's row's nT slots at row_slots) filled from
+// partials that other workgroups of the launch publish with
+// store_partial_tagged: read until all carry the call's tag, at most `polls`
+// times with a short sleep between reads.  A partial still missing after
+// that is computed by the whole wave with late(rho, tile), which gives the
+// publishing wave's own value.  The slots wait in LDS (s_q, kBatch * 64
+// partials) meanwhile, which keeps that rare path's registers within the
+// kernel's budget.  When the launch's workgroups start in index order none is
+// missing by then: the publishing workgroups come first in the grid and wait
+// on nothing.
+template <class Late>
+__device__ __forceinline__ void await_slots(const TaggedPartial* row_slots, bool valid, int nT, int G, CallTag tag,
+                                            int polls, Partial* q, Partial* s_q, Late late) {
+    const int lane = lane_id();
+    const int sl = lane & (G - 1);
+    unsigned have = 0;  // bit j: q[j] holds its partial (or the lane has no partial j)
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+        q[j] = Partial{0.f, 0};
+        if (!valid || sl + j * G >= nT) have |= 1u << j;
+    }
+    constexpr unsigned kAll = (1u << kBatch) - 1;
+    bool any = true;
+    for (int it = 0; it < polls && any; ++it) {
+        if (it > 0) __builtin_amdgcn_s_sleep(kPollSleep);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (!((have >> j) & 1u) && load_partial_tagged(row_slots + sl + j * G, tag, q[j])) have |= 1u << j;
+        }
+        any = __builtin_amdgcn_ballot_w64(have != kAll) != 0;
+    }
+    if (!any) return;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) s_q[j * kWave + lane] = q[j];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int j = 0; j < kBatch; ++j) {
+        uint64_t m = __builtin_amdgcn_ballot_w64(!((have >> j) & 1u));
+        while (m != 0) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            const Partial p = late(l / G, static_cast<int64_t>((l & (G - 1)) + j * G));
+            if (lane == l) s_q[j * kWave + l] = p;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) q[j] = s_q[j * kWave + lane];
+}
+
 // Small calls run in one launch, one workgroup of kSmallBlock threads per
 // sequence, with at most kSmallMaxParts row tiles held in LDS.
 constexpr int kSmallBlock = 1024;

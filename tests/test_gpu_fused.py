@@ -1,7 +1,7 @@
 """The one-launch chain path: rows streamed and the final draw made in one
 launch (chain_fused_kernel), its drawing workgroups reading the row
 statistics that its streaming workgroups publish, tagged for the call (a
-graph being captured clears the slots first, chain_clear_kernel).
+graph being captured clears the slots first, clear_slots_kernel).
 
 Checked here: which calls take it (the draw fits one round of 2048
 workgroups, the 2k rows' partials fit one wave: 2k <= 64 and at most 8
@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_common import chain_tensors, compare_chain, run_chain
+from gpu_common import chain_tensors, compare_chain, run_chain, run_greedy
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +174,41 @@ def test_fused_workspace_reuse_garbage_and_graphs(svl, orc):
         _same(_np(out), first[i], f"graph replay {rep} (inputs {i})")
         j = (i + 1) % len(sets)
         _same(eager(sets[j]), first[j], f"eager call {rep} between replays (inputs {j})")
+
+
+GREEDY_FUSED = [
+    # B, k, V, dtype, match rate, expect both phases in one launch (rows of >= 256 MiB take two phases)
+    (256, 5, 128256, W.BF16, 0.7, True),    # the greedy workload: s = 3, 32 tiles per row
+    (64, 4, 262144, W.F32, 0.8, True),      # s = 2: 128 tiles per row, 4 partials per lane of 32
+    (40, 15, 211111, W.BF16, 0.9, True),    # s = 8, odd V: element loads
+    (16, 15, 300000, W.F32, 0.9, False),    # s = 8: 147 tiles per row, more than one wave holds
+]
+
+
+@pytest.mark.parametrize("shape", GREEDY_FUSED, ids=lambda s: f"B{s[0]}k{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}")
+def test_greedy_two_phases_in_one_launch(svl, orc, shape):
+    """Two-phase greedy chains run both phases in one launch (greedy_fused)
+    when the first phase's partials of a sequence fit one wave; the outputs
+    equal the oracle's, and equal themselves bit for bit when the second
+    phase's checks compute every first-phase partial themselves."""
+    B, k, V, dt, match_p, fused = shape
+    inp = W.greedy_inputs(B, k, V, dt, 23, match_p=match_p)
+    label = f"greedy B{B} k{k} V{V} {W.DTYPE_NAMES[dt]}"
+    print(f"[fused] {label}", flush=True)
+    ref = orc.verify_greedy(inp)
+    svl.profile_begin(64)
+    got = run_greedy(svl, inp)
+    launched = set(svl.profile_end())
+    print(f"[fused] {label}: {sorted(launched)}, mean accepted {got['accepted_len'].mean():.2f}", flush=True)
+    assert launched == ({"greedy_fused", "greedy_finalize"} if fused
+                        else {"greedy_rows", "greedy_rows_rest", "greedy_finalize"}), launched
+    for key in ("accepted_len", "emitted"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{label}: {key}")
+    if fused:
+        prev = svl.set_handoff_polls(0)
+        try:
+            computed = run_greedy(svl, inp)
+        finally:
+            svl.set_handoff_polls(prev)
+        for key in ("accepted_len", "emitted"):
+            np.testing.assert_array_equal(computed[key], ref[key], err_msg=f"{label}: {key}, computed")
