@@ -120,7 +120,8 @@ LIBRARY_KERNELS = {"chain_rowstats", "chain_prefix", "chain_rowstats_rest", "cha
                    "chain_final_pick", "chain_row_draw", "chain_small", "clear_slots", "chain_fused", "argmax_rows",
                    "greedy_rows", "greedy_rows_rest", "greedy_fused",
                    "greedy_small",
-                   "greedy_finalize", "tree_root_rows", "tree_plan", "tree_rows_rest", "tree_finalize",
+                   "greedy_finalize", "tree_root_rows", "tree_root_plan", "tree_plan", "tree_rows_rest",
+                   "tree_finalize",
                    "tree_rowstats", "tree_round", "tree_sample", "commit_tokens"}
 
 
@@ -419,7 +420,8 @@ class Workload:
                             while depth[an] > lo:
                                 an = par[an]
                             rest_rows += int(lo <= depth[n] <= hi and acc[an])
-                kb["tree_root_rows"] = B * V * es
+                # trees of at most 256 nodes: the root rows and the first plan in one launch
+                kb["tree_root_plan" if N <= 256 else "tree_root_rows"] = B * V * es
                 kb["tree_rows_rest"] = rest_rows * V * es / len(ranges)
                 launches["tree_rows_rest"] = len(ranges)
             else:

@@ -205,7 +205,7 @@ TreeSampledLayout tree_sampled_layout(int B, int N, int V, sv_dtype dt) {
 // The greedy-tree workspace: the partials of every node's row, then the
 // second phase's node lists and their lengths.
 struct TreeLayout {
-    size_t part, list, count, total;
+    size_t part, list, count, slots, total;
 };
 
 TreeLayout tree_layout(int B, int N, int V, sv_dtype dt) {
@@ -213,7 +213,9 @@ TreeLayout tree_layout(int B, int N, int V, sv_dtype dt) {
     L.part = 0;
     L.list = align_up(sizeof(Partial) * static_cast<size_t>(B) * N * tiles_per_row(V, dt));
     L.count = align_up(L.list + sizeof(int32_t) * static_cast<size_t>(B) * N);
-    L.total = align_up(L.count + sizeof(int32_t) * static_cast<size_t>(B));
+    // the root rows' tagged partials of tree_root_plan_kernel
+    L.slots = align_up(L.count + sizeof(int32_t) * static_cast<size_t>(B));
+    L.total = align_up(L.slots + sizeof(sv::TaggedPartial) * static_cast<size_t>(B) * tiles_per_row(V, dt));
     return L;
 }
 
@@ -479,21 +481,38 @@ constexpr int kTreeThreePhaseMinNodes = 48;
 template <int DT, bool VEC>
 sv_status run_tree_two_phase(const void* logits, const int32_t* tokens, const int32_t* parent, int parent_stride,
                              int B, int N, int V, int nT, bool three, Partial* part, int32_t* list, int32_t* count,
-                             hipStream_t stream) {
+                             sv::TaggedPartial* slots, hipStream_t stream) {
     const int groups = static_cast<int>(blocks_for_waves(nT));
-    sv_status st = launch("tree_root_rows", sv::tree_root_rows_kernel<DT, VEC, kU>,
-                          dim3(static_cast<unsigned>(static_cast<int64_t>(B) * groups)), dim3(sv::kBlock), stream,
-                          logits, N, V, nT, groups, part);
-    if (st != SV_OK) return st;
     // depth ranges of the later phases: [1, inf), or [1, 2] then [3, inf)
     const int ranges[2][2] = {{1, three ? 2 : INT_MAX}, {3, INT_MAX}};
+    // trees of at most kBlock nodes: the root rows and the first plan in one
+    // launch, the root's partials handed over in slots tagged for this call
+    const bool root_plan = N <= sv::kBlock;
+    sv_status st;
+    if (root_plan) {
+        sv::CallTag tag;
+        if ((st = handover_tag(stream, slots, static_cast<int64_t>(B) * nT, tag)) != SV_OK) return st;
+        const int64_t root_blocks = static_cast<int64_t>(B) * groups;
+        st = launch("tree_root_plan", sv::tree_root_plan_kernel<DT, VEC, kU>,
+                    dim3(static_cast<unsigned>(root_blocks + B)), dim3(sv::kBlock), stream, logits, tokens, parent,
+                    parent_stride, N, V, nT, groups, root_blocks, slots, tag,
+                    g_handoff_polls.load(std::memory_order_relaxed), ranges[0][1], part, list, count);
+    } else {
+        st = launch("tree_root_rows", sv::tree_root_rows_kernel<DT, VEC, kU>,
+                    dim3(static_cast<unsigned>(static_cast<int64_t>(B) * groups)), dim3(sv::kBlock), stream, logits, N,
+                    V, nT, groups, part);
+    }
+    if (st != SV_OK) return st;
     const int nodes_threads = (N + sv::kWave - 1) / sv::kWave * sv::kWave;
     for (int ph = 0; ph < (three ? 2 : 1); ++ph) {
         // the root's children alone need one wave per node; later ranges combine every row over at least 256 threads
         const int threads = ph == 0 ? nodes_threads : std::max(256, nodes_threads);
-        st = launch("tree_plan", sv::tree_plan_kernel, dim3(B), dim3(threads), stream, tokens, parent, parent_stride, N,
-                    nT, static_cast<const Partial*>(part), ranges[ph][0], ranges[ph][1], list, count);
-        if (st != SV_OK) return st;
+        if (ph > 0 || !root_plan) {
+            st = launch("tree_plan", sv::tree_plan_kernel, dim3(B), dim3(threads), stream, tokens, parent,
+                        parent_stride, N, nT, static_cast<const Partial*>(part), ranges[ph][0], ranges[ph][1], list,
+                        count);
+            if (st != SV_OK) return st;
+        }
         st = launch("tree_rows_rest", sv::tree_rows_rest_kernel<DT, VEC, kU>,
                     dim3(static_cast<unsigned>(static_cast<int64_t>(B) * (N - 1) * groups)), dim3(sv::kBlock), stream,
                     logits, N, V, nT, groups, static_cast<const int32_t*>(list), static_cast<const int32_t*>(count),
@@ -505,16 +524,16 @@ sv_status run_tree_two_phase(const void* logits, const int32_t* tokens, const in
 
 sv_status tree_two_phase(sv_dtype dt, bool vec, const void* logits, const int32_t* tokens, const int32_t* parent,
                          int parent_stride, int B, int N, int V, int nT, bool three, Partial* part, int32_t* list,
-                         int32_t* count, hipStream_t stream) {
+                         int32_t* count, sv::TaggedPartial* slots, hipStream_t stream) {
     if (dt == SV_BF16)
         return vec ? run_tree_two_phase<SV_BF16, true>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
-                                                       list, count, stream)
+                                                       list, count, slots, stream)
                    : run_tree_two_phase<SV_BF16, false>(logits, tokens, parent, parent_stride, B, N, V, nT, three,
-                                                        part, list, count, stream);
+                                                        part, list, count, slots, stream);
     return vec ? run_tree_two_phase<SV_F32, true>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
-                                                  list, count, stream)
+                                                  list, count, slots, stream)
                : run_tree_two_phase<SV_F32, false>(logits, tokens, parent, parent_stride, B, N, V, nT, three, part,
-                                                   list, count, stream);
+                                                   list, count, slots, stream);
 }
 
 // The greedy workspace: the partials of every row, then the tagged slots of
@@ -736,7 +755,7 @@ sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt, const int32_t* node_t
         auto* count = reinterpret_cast<int32_t*>(ws + L.count);
         if ((st = tree_two_phase(dt, vec, target_logits, node_tokens, parent, parent_stride, B, N, V, nT,
                                  bytes >= kTreeThreePhaseMinBytes && N >= kTreeThreePhaseMinNodes, part, list,
-                                 count, stream)) != SV_OK)
+                                 count, reinterpret_cast<sv::TaggedPartial*>(ws + L.slots), stream)) != SV_OK)
             return st;
     } else if ((st = argmax_rows(dt, vec, target_logits, static_cast<int64_t>(B) * N, V, nT, part, stream)) !=
                SV_OK) {

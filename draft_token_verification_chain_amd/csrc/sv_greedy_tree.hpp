@@ -237,12 +237,17 @@ __global__ __launch_bounds__(kBlock) void tree_root_rows_kernel(const void* __re
 // every row (G lanes per row; the root's alone when d_lo = 1), then depth and
 // path acceptance by pointer jumping, then the ancestor at depth d_lo by
 // pointer jumping.  A malformed tree lists nothing (tree_finalize reports it).
-__global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int32_t* __restrict__ node_tokens,
-                                                                      const int32_t* __restrict__ parent,
-                                                                      int parent_stride, int N, int nT,
-                                                                      const Partial* __restrict__ part, int d_lo,
-                                                                      int d_hi, int32_t* __restrict__ list,
-                                                                      int32_t* __restrict__ count) {
+// With SHARED (d_lo = 1 only, in tree_root_plan_kernel) the root row's
+// partials are read from the tagged slots that the same launch's first
+// workgroups fill (await_slots, a missing one computed with their own
+// tile_argmax_any); `logits` is only read then.
+template <bool SHARED, int DT, bool VEC, int U>
+__device__ __forceinline__ void tree_plan(const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parent,
+                                          int parent_stride, int N, int nT, const Partial* __restrict__ part, int d_lo,
+                                          int d_hi, int32_t* __restrict__ list, int32_t* __restrict__ count, int64_t b,
+                                          const void* __restrict__ logits = nullptr, int V = 0,
+                                          const TaggedPartial* __restrict__ slots = nullptr, CallTag tag = {},
+                                          int polls = 0) {
     __shared__ int s_g[SV_MAX_TREE_NODES];
     __shared__ int s_tok[SV_MAX_TREE_NODES];
     __shared__ int s_anc[SV_MAX_TREE_NODES];
@@ -250,7 +255,6 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int3
     __shared__ int s_ok[SV_MAX_TREE_NODES];
     __shared__ int s_wave[SV_MAX_TREE_NODES / kWave];
     __shared__ int s_bad;
-    const int64_t b = blockIdx.x;
     const int n = threadIdx.x;
     const int lane = lane_id();
     const int nthreads = blockDim.x;
@@ -262,7 +266,17 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int3
     const int per_pass = nthreads / G;
     const Partial* rows_base = part + b * N * static_cast<int64_t>(nT);
     Partial q[kBatch];
-    group_load(rows_base + (n / G < rows ? n / G : 0) * static_cast<int64_t>(nT), nT, G, n / G < rows, q);
+    if constexpr (SHARED) {
+        // one row, read by the lanes of wave 0 (G = 64); the other waves hold no partial
+        __shared__ Partial s_q[kBatch * kWave];
+        await_slots(slots + b * static_cast<int64_t>(nT), n / G < rows, nT, G, tag, polls, q, s_q,
+                    [&](int, int64_t tile) {
+                        const ArgMax a = tile_argmax_any<DT, VEC, U>(logits, b * N * static_cast<int64_t>(V), V, tile);
+                        return Partial{a.val, a.idx};
+                    });
+    } else {
+        group_load(rows_base + (n / G < rows ? n / G : 0) * static_cast<int64_t>(nT), nT, G, n / G < rows, q);
+    }
     int p = 0;
     if (n < N) {
         s_tok[n] = node_tokens[b * N + n];
@@ -339,6 +353,39 @@ __global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int3
         for (int i = 0; i < nthreads / kWave; ++i) total += s_wave[i];
         count[b] = total;
     }
+}
+
+__global__ __launch_bounds__(SV_MAX_TREE_NODES) void tree_plan_kernel(const int32_t* __restrict__ node_tokens,
+                                                                      const int32_t* __restrict__ parent,
+                                                                      int parent_stride, int N, int nT,
+                                                                      const Partial* __restrict__ part, int d_lo,
+                                                                      int d_hi, int32_t* __restrict__ list,
+                                                                      int32_t* __restrict__ count) {
+    tree_plan<false, SV_F32, false, 1>(node_tokens, parent, parent_stride, N, nT, part, d_lo, d_hi, list, count,
+                                       blockIdx.x);
+}
+
+// The root rows and the first plan (d_lo = 1) in one launch, for trees of at
+// most kBlock nodes: workgroups 0 .. root_blocks - 1 stream every sequence's
+// root row as tree_root_rows_kernel does and publish its partials in tagged
+// slots; workgroup root_blocks + b then lists sequence b's nodes as
+// tree_plan_kernel does, reading the root's partials as they are published.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kBlock) void tree_root_plan_kernel(const void* __restrict__ logits,
+                                                                const int32_t* __restrict__ node_tokens,
+                                                                const int32_t* __restrict__ parent,
+                                                                int parent_stride, int N, int V, int nT, int groups,
+                                                                int64_t root_blocks, TaggedPartial* __restrict__ slots,
+                                                                CallTag tag, int polls, int d_hi,
+                                                                Partial* __restrict__ part, int32_t* __restrict__ list,
+                                                                int32_t* __restrict__ count) {
+    if (blockIdx.x < root_blocks) {
+        greedy_rows<DT, VEC, U, false, 1, true>(logits, nullptr, N - 1, V, nT, groups, 1, 0, part, blockIdx.x, slots,
+                                                1, tag);
+        return;
+    }
+    tree_plan<true, DT, VEC, U>(node_tokens, parent, parent_stride, N, nT, part, 1, d_hi, list, count,
+                                blockIdx.x - root_blocks, logits, V, slots, tag, polls);
 }
 
 // Argmax partials of the listed rows: one workgroup per (sequence, list

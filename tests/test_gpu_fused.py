@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_common import chain_tensors, compare_chain, run_chain, run_greedy
+from gpu_common import chain_tensors, compare_chain, run_chain, run_greedy, run_tree
 
 pytestmark = pytest.mark.gpu
 
@@ -211,4 +211,44 @@ def test_greedy_two_phases_in_one_launch(svl, orc, shape):
         finally:
             svl.set_handoff_polls(prev)
         for key in ("accepted_len", "emitted"):
+            np.testing.assert_array_equal(computed[key], ref[key], err_msg=f"{label}: {key}, computed")
+
+
+TREE_ROOT_PLAN = [
+    # B, N, V, dtype, max_depth, distinct siblings, expect the root rows and the first plan in one launch
+    (16, 64, 128256, W.BF16, 6, False, True),   # the EAGLE-style workload's shape: three phases
+    (16, 64, 128256, W.BF16, 6, True, True),
+    (8, 256, 32768, W.F32, 8, False, True),     # 256 nodes, one per thread of the plan's workgroup
+    (4, 300, 50000, W.BF16, 8, False, False),   # 300 nodes: tree_root_rows, then tree_plan
+    (12, 100, 50001, W.BF16, 5, True, True),    # two phases, odd V: element loads
+]
+
+
+@pytest.mark.parametrize("shape", TREE_ROOT_PLAN,
+                         ids=lambda s: f"B{s[0]}N{s[1]}V{s[2]}{W.DTYPE_NAMES[s[3]]}{'d' if s[5] else ''}")
+def test_tree_root_rows_and_first_plan_in_one_launch(svl, orc, shape):
+    """Greedy trees streamed in phases run the root rows and the first plan
+    in one launch (tree_root_plan) up to 256 nodes; the outputs equal the
+    oracle's, also when the plan computes the root's partials itself."""
+    B, N, V, dt, depth, distinct, merged = shape
+    inp = W.tree_inputs(B, N, V, dt, 24, target_sigma=3.0, max_depth=depth, match_p=0.7,
+                        distinct_siblings=distinct)
+    assert B * N * V * (2 if dt == W.BF16 else 4) >= 96 << 20
+    label = f"tree B{B} N{N} V{V} {W.DTYPE_NAMES[dt]}"
+    print(f"[fused] {label}", flush=True)
+    ref = orc.verify_tree(inp)
+    svl.profile_begin(64)
+    got = run_tree(svl, inp)
+    launched = set(svl.profile_end())
+    print(f"[fused] {label}: {sorted(launched)}, mean accepted {got['accepted_len'].mean():.2f}", flush=True)
+    assert ("tree_root_plan" in launched) == merged and ("tree_root_rows" in launched) == (not merged), launched
+    for key in ("accepted_len", "emitted", "accepted_nodes"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{label}: {key}")
+    if merged:
+        prev = svl.set_handoff_polls(0)
+        try:
+            computed = run_tree(svl, inp)
+        finally:
+            svl.set_handoff_polls(prev)
+        for key in ("accepted_len", "emitted", "accepted_nodes"):
             np.testing.assert_array_equal(computed[key], ref[key], err_msg=f"{label}: {key}, computed")
