@@ -409,7 +409,6 @@ __device__ __forceinline__ bool load_partial_tagged(const TaggedPartial* p, Call
     return static_cast<uint32_t>(w0 >> 32) == tag.t0 && static_cast<uint32_t>(w1 >> 32) == tag.t1;
 }
 
-
 // Sets n tagged partial slots to zero words (tag (0, 0), which no call
 // uses), ahead of a launch that hands partials over in them when its stream
 // is being captured into a graph, whose replays all carry one tag.
