@@ -20,9 +20,16 @@
 //              over the segment masses, picks the segment holding u * W and
 //              rescans only that segment to find the token (the workgroup
 //              forms the masses again when the correction cannot be trusted).
-// Plain sampling of many rows draws each row in one workgroup (row_draw).
+// When one wave can hold a sequence's 2k rows' partials and the draw fits one
+// round of workgroups, rowstats and final_part run as one launch (fused):
+// the drawing workgroups, after the streaming ones in the grid, read their
+// sequence's partials as those are published, each tagged for the call, with
+// no fence.  Small chains run in one workgroup per sequence (small), and
+// plain sampling of many rows draws each row in one workgroup (row_draw).
 // sv_verify_greedy and sv_verify_tree use argmax_rows (the streaming argmax)
-// followed by a per-sequence finaliser.  sv_verify_tree_sampled streams the
+// followed by a per-sequence finaliser; large calls stream in phases, a
+// greedy chain's two phases in one launch (greedy_fused) and a tree's root
+// rows with its first plan (tree_root_plan), handed over the same way.  sv_verify_tree_sampled streams the
 // tree's rows (tree_rowstats), then walks every tree in rounds of launches
 // (tree_round), with a one-workgroup walk (tree_sample) that finishes what
 // the rounds leave.  sv_commit_tokens is one workgroup (commit_tokens).
