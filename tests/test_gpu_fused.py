@@ -252,3 +252,33 @@ def test_tree_root_rows_and_first_plan_in_one_launch(svl, orc, shape):
             svl.set_handoff_polls(prev)
         for key in ("accepted_len", "emitted", "accepted_nodes"):
             np.testing.assert_array_equal(computed[key], ref[key], err_msg=f"{label}: {key}, computed")
+
+
+def test_fused_emitted_distribution_chi_square(svl, orc):
+    """The one-launch chain path's draws, bit-exact with the oracle outside
+    the band, are distributed as speculative sampling says: 40 calls of 2048
+    trials at V = 16, k = 4 (each call takes chain_fused), and the token
+    emitted at position j given j accepted drafts follows target row j
+    (chi-square)."""
+    from scipy import special, stats
+
+    rng = np.random.default_rng(2031)
+    t = (1.5 * rng.standard_normal((5, 16))).astype(np.float32)
+    d = (t[:4] + rng.standard_normal((4, 16))).astype(np.float32)
+    accs, ems = [], []
+    for blk in range(40):
+        inp = W.repeated_trials(t, d, 1.0, 2048, seed=78, block=blk)
+        if blk == 0:
+            svl.profile_begin(16)
+        got = run_chain(svl, inp)
+        if blk == 0:
+            assert "chain_fused" in set(svl.profile_end())
+        compare_chain(inp, got, orc.verify_chain(inp), f"fused chi block{blk}")
+        accs.append(got["accepted_len"])
+        ems.append(got["emitted"])
+    acc, em = np.concatenate(accs), np.concatenate(ems)
+    for j in range(5):
+        sel = acc >= j
+        counts = np.bincount(em[sel, j], minlength=16)
+        p = special.softmax(t[j].astype(np.float64))
+        assert stats.chisquare(counts, p * sel.sum()).pvalue > 1e-4, j
