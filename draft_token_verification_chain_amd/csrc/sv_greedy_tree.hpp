@@ -267,7 +267,8 @@ __device__ __forceinline__ void tree_plan(const int32_t* __restrict__ node_token
     const Partial* rows_base = part + b * N * static_cast<int64_t>(nT);
     Partial q[kBatch];
     if constexpr (SHARED) {
-        // one row, read by the lanes of wave 0 (G = 64); the other waves hold no partial
+        // one row, read by the lanes of wave 0 (G = 64); the other waves hold no
+        // partial, so only wave 0 ever uses s_q
         __shared__ Partial s_q[kBatch * kWave];
         await_slots(slots + b * static_cast<int64_t>(nT), n / G < rows, nT, G, tag, polls, q, s_q,
                     [&](int, int64_t tile) {

@@ -430,7 +430,7 @@ constexpr int kPollSleep = 8;
 // partials) meanwhile, which keeps that rare path's registers within the
 // kernel's budget.  When the launch's workgroups start in index order none is
 // missing by then: the publishing workgroups come first in the grid and wait
-// on nothing.
+// on nothing.  Waves that share one s_q must not both hold partials.
 template <class Late>
 __device__ __forceinline__ void await_slots(const TaggedPartial* row_slots, bool valid, int nT, int G, CallTag tag,
                                             int polls, Partial* q, Partial* s_q, Late late) {
@@ -443,7 +443,9 @@ __device__ __forceinline__ void await_slots(const TaggedPartial* row_slots, bool
         if (!valid || sl + j * G >= nT) have |= 1u << j;
     }
     constexpr unsigned kAll = (1u << kBatch) - 1;
-    bool any = true;
+    // a wave that holds no partial (every slot invalid) leaves at once, so it
+    // never touches s_q, which may be another wave's
+    bool any = __builtin_amdgcn_ballot_w64(have != kAll) != 0;
     for (int it = 0; it < polls && any; ++it) {
         if (it > 0) __builtin_amdgcn_s_sleep(kPollSleep);
 #pragma unroll
