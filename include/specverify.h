@@ -89,14 +89,15 @@ int sv_version(void);
 /* Static text for a status code (never NULL). */
 const char *sv_status_string(sv_status s);
 
-/* Testing aid for the one-launch chain path (see sv_verify_chain): how many
- * times a drawing workgroup reads the row statistics that the streaming
- * workgroups of the same launch publish, before it computes any still
- * missing itself with the same arithmetic (the outputs do not change).
- * Default 65536 (a bound far beyond any call's streaming); 0 makes the
- * drawing workgroups compute every statistic themselves; a negative value
- * restores the default.  Returns the previous value.  Applies to launches
- * issued after it returns, from any thread. */
+/* Testing aid for the one-launch paths (the chain path of sv_verify_chain,
+ * the two-phase greedy chain of sv_verify_greedy, the root rows and first
+ * plan of sv_verify_tree): how many times a waiting workgroup reads the row
+ * statistics that other workgroups of the same launch publish, before it
+ * computes any still missing itself with the same arithmetic (the outputs
+ * do not change).  Default 65536 (a bound far beyond any call's streaming);
+ * 0 makes the waiting workgroups compute every statistic themselves; a
+ * negative value restores the default.  Returns the previous value.
+ * Applies to launches issued after it returns, from any thread. */
 int sv_set_handoff_polls(int polls);
 
 /* Workspace bytes for one call of the matching entry point with these sizes;

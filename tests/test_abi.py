@@ -63,6 +63,19 @@ def test_version_and_status_strings(lib):
     assert "unknown" in bnd.status_string(99)
 
 
+def test_handoff_polls_setter(lib):
+    # host state only: returns the previous bound; a negative value restores 65536
+    first = lib.sv_set_handoff_polls(0)
+    try:
+        assert lib.sv_set_handoff_polls(17) == 0
+        assert lib.sv_set_handoff_polls(-1) == 17
+        assert lib.sv_set_handoff_polls(-5) == 65536
+        assert bnd.set_handoff_polls(3) == 65536
+        assert bnd.set_handoff_polls(-1) == 3
+    finally:
+        lib.sv_set_handoff_polls(first)
+
+
 def test_workspace_queries(lib):
     a = lib.sv_chain_workspace_bytes(64, 4, 128256, BF16)
     b = lib.sv_chain_workspace_bytes(64, 4, 128256, F32)
