@@ -195,7 +195,11 @@ sv_status sv_verify_chain_static(int B, int k, int V, sv_dtype dt,
  *
  * When the target rows reach 256 MiB they are read in two phases: rows
  * 0..(k+1)/2-1 of every sequence, then the rest only for the sequences whose
- * drafts match in all of those rows.
+ * drafts match in all of those rows.  When a sequence's first-phase rows
+ * have at most 512 tiles of 8 KiB together, both phases run in one launch:
+ * each second-phase workgroup waits within a bound for its sequence's
+ * first-phase statistics (sv_set_handoff_polls), which pass through the
+ * workspace tagged per call as in sv_verify_chain.
  */
 sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt,
                            const int32_t *draft_tokens, const void *target_logits,
@@ -229,7 +233,10 @@ sv_status sv_verify_greedy(int B, int k, int V, sv_dtype dt,
  * From 96 MiB of rows the root rows are read first, then only the rows of
  * nodes whose depth-1 ancestor is accepted (from 192 MiB and N >= 48: nodes
  * of depth 1-2 below an accepted depth-1 node, then deeper nodes below an
- * accepted depth-3 node).  The outputs are the same.
+ * accepted depth-3 node).  The outputs are the same.  With at most 256
+ * nodes, the root rows and the first choice of rows share one launch, the
+ * root rows' statistics passing through the workspace tagged per call as in
+ * sv_verify_chain.
  */
 sv_status sv_verify_tree(int B, int N, int V, sv_dtype dt,
                          const int32_t *node_tokens, const int32_t *parent, int parent_stride,
