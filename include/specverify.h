@@ -139,9 +139,10 @@ size_t sv_tree_sampled_workspace_bytes(int B, int N, int V, sv_dtype dt);
  * Without accept_prob, from k >= 6 and 128 MiB of draft and target rows
  * 0..k-1, the rows of positions max(1, k/4) and later are read only for the
  * sequences that accept all drafts before them.  The outputs are the same.
- * When the final draw takes at most 2048 workgroups and a sequence's 2k rows
- * have at most 512 tiles of 8 KiB (k <= 32), the rows are streamed and the
- * draw made in one launch: each sequence's draw starts once its own rows are
+ * When the final draw takes at most 2048 workgroups and each row has at most
+ * 8 G tiles of 8 KiB, G the largest power of two with 2k G <= 64 (k <= 32;
+ * 512 tiles over the 2k rows when 2k is a power of two), the rows are
+ * streamed and the draw made in one launch: each sequence's draw starts once its own rows are
  * streamed, waiting within a bound for their statistics
  * (sv_set_handoff_polls).  The statistics pass through the workspace tagged
  * with a 64-bit value unique to the call, so whatever the workspace held
@@ -195,8 +196,9 @@ sv_status sv_verify_chain_static(int B, int k, int V, sv_dtype dt,
  *
  * When the target rows reach 256 MiB they are read in two phases: rows
  * 0..(k+1)/2-1 of every sequence, then the rest only for the sequences whose
- * drafts match in all of those rows.  When a sequence's first-phase rows
- * have at most 512 tiles of 8 KiB together, both phases run in one launch:
+ * drafts match in all of those rows.  When each row has at most 8 G tiles
+ * of 8 KiB, G the largest power of two with G (k+1)/2 <= 64, both phases
+ * run in one launch:
  * each second-phase workgroup waits within a bound for its sequence's
  * first-phase statistics (sv_set_handoff_polls), which pass through the
  * workspace tagged per call as in sv_verify_chain.
